@@ -1,0 +1,337 @@
+"""Python binding of libvcoll, the single-GPU virtual-cluster collectives.
+
+Functions carry the C names of ``include/vcoll.h`` and only marshal
+arguments: tensors become device pointers, torch's current HIP stream becomes
+the launch stream, and status codes become exceptions. Every collective runs
+in libvcoll's HIP kernels; there is no other code path. If ``libvcoll.so``
+has not been built this module raises on import.
+
+Rank buffers are given either as one 2-D tensor [p, n] (row r is rank r) or
+as a sequence of p 1-D tensors, all on the same GPU, contiguous, same dtype
+(torch.float32 or torch.bfloat16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvcoll.so")
+
+RING, RECURSIVE_DOUBLING, RABENSEIFNER, BINARY_TREE = 0, 1, 2, 3
+ALGOS = {"ring": RING, "rd": RECURSIVE_DOUBLING, "recursive_doubling": RECURSIVE_DOUBLING,
+         "rabenseifner": RABENSEIFNER, "tree": BINARY_TREE, "binary_tree": BINARY_TREE}
+F32, BF16 = 0, 1
+OP_ALLREDUCE, OP_REDUCE_SCATTER, OP_ALL_GATHER, OP_ALL_TO_ALL = 0, 1, 2, 3
+OPS = {"allreduce": OP_ALLREDUCE, "reduce_scatter": OP_REDUCE_SCATTER,
+       "all_gather": OP_ALL_GATHER, "all_to_all": OP_ALL_TO_ALL}
+MAX_RANKS = 128
+
+
+class VcollError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = _lib()
+        detail = lib.vcoll_status_str(status).decode()
+        if status == 4:
+            detail += f" ({lib.vcoll_last_hip_error().decode()})"
+        super().__init__(f"{what}: {detail} (status {status})")
+        self.status = status
+
+
+class Msg(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("src", ctypes.c_int32), ("dst", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("src_off", ctypes.c_int64),
+                ("dst_off", ctypes.c_int64), ("count", ctypes.c_int64), ("bytes", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        # torch ships its own copy of the HIP runtime under the same soname;
+        # loading torch first makes libvcoll bind to that copy, so there is
+        # one runtime in the process and torch's streams and memory are ours
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python collective_communication_algorithms_vcoll_amd/csrc/build.py`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, I64, VP = ctypes.POINTER, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+        lib.vcoll_abi_version.restype = I
+        lib.vcoll_status_str.restype = ctypes.c_char_p
+        lib.vcoll_status_str.argtypes = [I]
+        lib.vcoll_chunk.argtypes = [I, I64, I, P(I64), P(I64)]
+        for name in ("vcoll_allreduce", "vcoll_reduce_scatter", "vcoll_all_gather"):
+            getattr(lib, name).argtypes = [I, I, I64, I, P(VP), P(VP), VP]
+            getattr(lib, name).restype = I
+        lib.vcoll_all_to_all.argtypes = [I, I64, I, P(I64), P(VP), P(VP), P(VP), P(I64), P(VP),
+                                         P(I64), VP]
+        lib.vcoll_all_to_all.restype = I
+        lib.vcoll_ledger.argtypes = [I, I, I, I64, I, P(I64), I64, P(Msg), I64, P(I64), P(I64),
+                                     P(I64), P(ctypes.c_int32)]
+        lib.vcoll_ledger.restype = I
+        lib.vcoll_moe_plan.argtypes = [I, I64, I, I, P(ctypes.c_int32), P(I64),
+                                       P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.vcoll_moe_plan.restype = I
+        lib.vcoll_last_hip_error.restype = ctypes.c_char_p
+        lib.vcoll_bench_copy.argtypes = [VP, VP, I64, VP]
+        lib.vcoll_bench_copy.restype = I
+        if lib.vcoll_abi_version() != 1:
+            raise ImportError("libvcoll ABI version mismatch")
+        _LIB = lib
+    return _LIB
+
+
+_lib()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise VcollError(status, what)
+
+
+def _algo(algo) -> int:
+    if isinstance(algo, str):
+        if algo not in ALGOS:
+            raise ValueError(f"unknown algorithm {algo!r}")
+        return ALGOS[algo]
+    return int(algo)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ranks(bufs) -> list:
+    import torch
+    if isinstance(bufs, torch.Tensor):
+        if bufs.dim() != 2:
+            raise ValueError("a single tensor of rank buffers must be 2-D [p, n]")
+        return [bufs[r] for r in range(bufs.shape[0])]
+    return list(bufs)
+
+
+def _ptrs(ts: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr() if t is not None and t.numel() > 0 else None
+    return arr
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _validate(ts: list, what: str, n: int | None = None):
+    import torch
+    if not 1 <= len(ts) <= MAX_RANKS:
+        raise ValueError(f"{what}: p={len(ts)} outside [1, {MAX_RANKS}]")
+    dev, dt = ts[0].device, ts[0].dtype
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.device != dev or t.dtype != dt:
+            raise ValueError(f"{what}: all rank buffers must be tensors on one device with one dtype")
+        if dev.type != "cuda":
+            raise ValueError(f"{what}: rank buffers must be on a GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: rank buffers must be contiguous")
+        if n is not None and t.numel() != n:
+            raise ValueError(f"{what}: expected {n} elements per rank, got {t.numel()}")
+
+
+def _span(t):
+    return t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()
+
+
+def _no_overlap(a: list, b: list, what: str) -> None:
+    spans_a = [_span(t) for t in a if t is not None and t.numel() > 0]
+    spans_b = [_span(t) for t in b if t is not None and t.numel() > 0]
+    for s0, s1 in spans_a:
+        for d0, d1 in spans_b:
+            if s0 < d1 and d0 < s1:
+                raise ValueError(f"{what}: input and output buffers overlap")
+
+
+# -----------------------------------------------------------------------------
+
+
+def vcoll_chunk(p: int, n: int, c: int) -> tuple:
+    off, cnt = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib().vcoll_chunk(p, n, c, ctypes.byref(off), ctypes.byref(cnt)), "vcoll_chunk")
+    return off.value, cnt.value
+
+
+def vcoll_allreduce(algo, send, recv=None):
+    """All-reduce; returns recv (allocated like send when None; recv may be send)."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_allreduce")
+    n = s[0].numel()
+    _validate(s, "vcoll_allreduce", n)
+    if recv is None:
+        recv = torch.empty_like(send) if isinstance(send, torch.Tensor) else [torch.empty_like(t) for t in s]
+    r = _ranks(recv)
+    _validate(r, "vcoll_allreduce", n)
+    if len(r) != len(s) or r[0].dtype != s[0].dtype or r[0].device != s[0].device:
+        raise ValueError("vcoll_allreduce: send and recv must match in p, dtype and device")
+    for i, a in enumerate(s):
+        for j, b in enumerate(r):
+            if i != j or a.data_ptr() != b.data_ptr():
+                _no_overlap([a], [b], "vcoll_allreduce")
+    _check(_lib().vcoll_allreduce(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
+                                  _stream(s[0])), "vcoll_allreduce")
+    return recv
+
+
+def vcoll_reduce_scatter(algo, send, recv=None):
+    """Reduce-scatter; recv[c] gets chunk c (vcoll_chunk(p, n, c) bounds)."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_reduce_scatter")
+    n = s[0].numel()
+    _validate(s, "vcoll_reduce_scatter", n)
+    p = len(s)
+    if recv is None:
+        recv = [torch.empty(vcoll_chunk(p, n, c)[1], dtype=s[0].dtype, device=s[0].device) for c in range(p)]
+    r = list(recv)
+    if len(r) != p:
+        raise ValueError("vcoll_reduce_scatter: need p output buffers")
+    for c in range(p):
+        if r[c].numel() != vcoll_chunk(p, n, c)[1] or r[c].dtype != s[0].dtype or not r[c].is_contiguous():
+            raise ValueError(f"vcoll_reduce_scatter: output {c} must hold chunk {c}")
+    _no_overlap(s, r, "vcoll_reduce_scatter")
+    _check(_lib().vcoll_reduce_scatter(_algo(algo), p, n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
+                                       _stream(s[0])), "vcoll_reduce_scatter")
+    return recv
+
+
+def vcoll_all_gather(algo, send, recv=None):
+    """All-gather of p equal blocks; recv[r] holds p*m elements."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_all_gather")
+    m = s[0].numel()
+    _validate(s, "vcoll_all_gather", m)
+    p = len(s)
+    if recv is None:
+        recv = torch.empty((p, p * m), dtype=s[0].dtype, device=s[0].device)
+    r = _ranks(recv)
+    _validate(r, "vcoll_all_gather", p * m)
+    _no_overlap(s, r, "vcoll_all_gather")
+    _check(_lib().vcoll_all_gather(_algo(algo), p, m, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
+                                   _stream(s[0])), "vcoll_all_gather")
+    return recv
+
+
+def vcoll_all_to_all(send, splits, recv=None, src_rows=None, dst_rows=None, dst_table_rows=None):
+    """Variable-split all-to-all of rows (see vcoll.h).
+
+    send: p 2-D tensors [rows, H] (row-major, contiguous). splits: host
+    [p, p] integers. src_rows / dst_rows: optional per-rank int32 GPU tensors
+    (entries may be None) of gather / scatter indices. recv: p tensors, made
+    when None ([sum_i splits[i][j], H], or [dst_table_rows[j], H] for ranks
+    that scatter).
+    """
+    import torch
+    s = list(send)
+    p = len(s)
+    sp = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
+    H = s[0].shape[1] if s[0].dim() == 2 else 1
+    dt = s[0].dtype
+    dev = s[0].device
+    for t in s:
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or (t.dim() == 2 and t.shape[1] != H):
+            raise ValueError("vcoll_all_to_all: send buffers must share dtype, device, row width")
+    scat = list(dst_rows) if dst_rows is not None else [None] * p
+    gath = list(src_rows) if src_rows is not None else [None] * p
+    if recv is None:
+        recv = []
+        for j in range(p):
+            rows = int(sp[:, j].sum()) if scat[j] is None else int(dst_table_rows[j])
+            recv.append(torch.empty((rows, H), dtype=dt, device=dev))
+    r = list(recv)
+    if len(r) != p:
+        raise ValueError("vcoll_all_to_all: need p receive buffers")
+    # the kernels trust the splits: every buffer must hold the rows they name
+    for i in range(p):
+        rows_i = s[i].shape[0] if s[i].dim() == 2 else s[i].numel()
+        if gath[i] is None and rows_i < int(sp[i].sum()):
+            raise ValueError(f"vcoll_all_to_all: send[{i}] has {rows_i} rows, splits send {int(sp[i].sum())}")
+        if gath[i] is not None and gath[i].numel() < int(sp[i].sum()):
+            raise ValueError(f"vcoll_all_to_all: src_rows[{i}] is shorter than the rows rank {i} sends")
+        t = r[i]
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or (t.dim() == 2 and t.shape[1] != H):
+            raise ValueError("vcoll_all_to_all: recv buffers must match send in dtype, device, row width")
+        rows_r = t.shape[0] if t.dim() == 2 else t.numel()
+        if scat[i] is None and rows_r < int(sp[:, i].sum()):
+            raise ValueError(f"vcoll_all_to_all: recv[{i}] has {rows_r} rows, splits bring {int(sp[:, i].sum())}")
+        if scat[i] is not None and scat[i].numel() < int(sp[:, i].sum()):
+            raise ValueError(f"vcoll_all_to_all: dst_rows[{i}] is shorter than the rows rank {i} receives")
+    _no_overlap(s, r, "vcoll_all_to_all")
+    src_tab = (ctypes.c_int64 * p)(*[t.shape[0] if t.dim() == 2 else t.numel() for t in s])
+    dst_tab = (ctypes.c_int64 * p)(*[t.shape[0] if t.dim() == 2 else t.numel() for t in r])
+    for idx in gath + scat:
+        if idx is not None and (idx.dtype != torch.int32 or idx.device != dev or not idx.is_contiguous()):
+            raise ValueError("vcoll_all_to_all: row maps must be contiguous int32 tensors on the GPU")
+    _check(_lib().vcoll_all_to_all(
+        p, H, _dtype_code(s[0]), sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptrs(s), _ptrs(r),
+        _ptrs(gath) if src_rows is not None else None, src_tab,
+        _ptrs(scat) if dst_rows is not None else None, dst_tab, _stream(s[0])), "vcoll_all_to_all")
+    return recv
+
+
+def vcoll_ledger(op, algo, p: int, n: int, dtype: str = "f32", splits=None, row_elems: int = 0):
+    """Messages of a collective: (list of (step, src, dst, src_off, dst_off,
+    count, bytes), sent bytes per rank, received bytes per rank, step count)."""
+    lib = _lib()
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    dtc = {"f32": F32, "bf16": BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    sp = None
+    if splits is not None:
+        sp_arr = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
+        sp = sp_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    count = ctypes.c_int64()
+    _check(lib.vcoll_ledger(opc, _algo(algo), p, n, dtc, sp, row_elems, None, 0, ctypes.byref(count),
+                            None, None, None), "vcoll_ledger")
+    msgs = (Msg * max(1, count.value))()
+    sent = (ctypes.c_int64 * p)()
+    got = (ctypes.c_int64 * p)()
+    steps = ctypes.c_int32()
+    _check(lib.vcoll_ledger(opc, _algo(algo), p, n, dtc, sp, row_elems, msgs, count.value,
+                            ctypes.byref(count), sent, got, ctypes.byref(steps)), "vcoll_ledger")
+    out = [(m.step, m.src, m.dst, m.src_off, m.dst_off, m.count, m.bytes) for m in msgs[:count.value]]
+    return out, list(sent), list(got), steps.value
+
+
+def vcoll_moe_plan(topk_ids: np.ndarray, experts_per_rank: int):
+    """topk_ids: int32 [p, tokens, topk]. Returns (splits [p, p] int64,
+    src_rows [p, tokens*topk] int32, dst_rows [p, tokens*topk] int32)."""
+    ids = np.ascontiguousarray(np.asarray(topk_ids, dtype=np.int32))
+    p, tokens, topk = ids.shape
+    splits = np.zeros((p, p), dtype=np.int64)
+    src = np.zeros((p, tokens * topk), dtype=np.int32)
+    dst = np.zeros((p, tokens * topk), dtype=np.int32)
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    _check(_lib().vcoll_moe_plan(p, tokens, topk, experts_per_rank, ids.ctypes.data_as(i32),
+                                 splits.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 src.ctypes.data_as(i32), dst.ctypes.data_as(i32)), "vcoll_moe_plan")
+    return splits, src, dst
+
+
+def vcoll_bench_copy(dst, src) -> None:
+    """Plain streaming copy of src into dst (equal byte sizes, 16-byte multiple)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("vcoll_bench_copy: size mismatch")
+    _check(_lib().vcoll_bench_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(src)),
+           "vcoll_bench_copy")

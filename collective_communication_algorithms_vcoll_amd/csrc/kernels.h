@@ -1,0 +1,78 @@
+// Device kernels of libvcoll for gfx950 (MI355X, CDNA4, wave64).
+//
+// The collectives of a p-rank virtual cluster run in one GPU's HBM, so the
+// message hops of an algorithm are not data movement any more: an element's
+// value after the collective is a fixed float32 expression over the p input
+// values at that element. The reduce kernels evaluate that expression in
+// registers, in the exact association the algorithm's steps produce, reading
+// each input once and writing each output once -- an HBM-streaming pass with
+// no reuse, so the design goals are coalesced 16-byte accesses, many bytes in
+// flight per wave, and no arithmetic beyond the p-1 adds (no MFMA: nothing
+// here is a contraction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "order.h"
+#include "vcoll.h"
+
+namespace vcoll {
+
+constexpr int kBlock = 256;          // threads per workgroup (4 waves)
+constexpr int kA2ABlocks = 64;       // all-to-all blocks described per launch
+
+struct RankPtrs {
+  const void* src[kMaxRanks];
+  void* dst[kMaxRanks];
+};
+
+// Reduce (all-reduce / reduce-scatter). Grid: x = tiles of a chunk, y = chunk.
+struct ReduceArgs {
+  RankPtrs ptr;
+  int64_t q, r;               // chunk c: off = c*q + min(c, r), count = q + (c < r)
+  int32_t p;
+  int32_t vec;                // every pointer 16-byte aligned: vector path allowed
+  int32_t final_merges;       // order program (used when p is not compiled in)
+  uint8_t rank[kMaxRanks];
+  uint8_t merges[kMaxRanks];
+};
+
+// All-gather. Grid: x = tiles of one block, y = source rank.
+struct GatherArgs {
+  RankPtrs ptr;
+  int64_t m;                  // elements per rank
+  int32_t p;
+  int32_t vec;                // pointers aligned and m * esize a multiple of 16
+};
+
+// One (i -> j) block of an all-to-all.
+struct A2ABlock {
+  const char* src;            // first row (contiguous) or gather table base
+  char* dst;                  // first row (contiguous) or scatter table base
+  const int32_t* src_idx;     // per-row gather index, or nullptr
+  const int32_t* dst_idx;     // per-row scatter index, or nullptr
+  int32_t rows;
+  int32_t tile_start;         // first workgroup of this block
+  int32_t src_limit;          // rows of the gather table (index bound)
+  int32_t dst_limit;          // rows of the scatter table (index bound)
+};
+
+struct A2AArgs {
+  int64_t row_bytes;
+  int32_t nblocks;
+  int32_t rows_per_tile;
+  int32_t vec;                // row_bytes % 16 == 0 and all bases aligned
+  int32_t esize;
+  A2ABlock b[kA2ABlocks];
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
+                         int64_t max_chunk, hipStream_t stream);
+hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream);
+hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+}  // namespace vcoll

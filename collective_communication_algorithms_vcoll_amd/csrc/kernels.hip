@@ -1,0 +1,555 @@
+// Device kernels of libvcoll for gfx950 (MI355X): fused reduce + fan-out,
+// all-gather fan-out, variable-split all-to-all row mover, plain copy.
+//
+// Summation orders come from "Networks and Collective Communication" (cs349e
+// prerequisite lecture 5), sections 5.1 (ring) and 5.2 (recursive doubling,
+// Rabenseifner, binomial tree); order.h writes each as a push / add program.
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace vcoll {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------
+// storage types: float32, or bfloat16 widened exactly and rounded once
+
+// Round a float32 to bfloat16, nearest with ties to even, on the bit pattern:
+// adding 0x7FFF plus the lowest kept bit carries exactly when the dropped half
+// is above the midpoint, or at it with an odd kept part. NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int D>
+struct Storage;
+
+template <>
+struct Storage<VCOLL_F32> {
+  static constexpr int kVE = 4;  // elements per 16 bytes
+  using elem = uint32_t;
+  __device__ static __forceinline__ void widen(const u32x4 w, float* f) {
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+  }
+  __device__ static __forceinline__ u32x4 narrow(const float* f) {
+    u32x4 w;
+    w.x = __float_as_uint(f[0]);
+    w.y = __float_as_uint(f[1]);
+    w.z = __float_as_uint(f[2]);
+    w.w = __float_as_uint(f[3]);
+    return w;
+  }
+  __device__ static __forceinline__ float widen1(elem e) { return __uint_as_float(e); }
+  __device__ static __forceinline__ elem narrow1(float f) { return __float_as_uint(f); }
+};
+
+template <>
+struct Storage<VCOLL_BF16> {
+  static constexpr int kVE = 8;
+  using elem = uint16_t;
+  __device__ static __forceinline__ void widen(const u32x4 w, float* f) {
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
+    f[4] = __uint_as_float(w.z << 16);
+    f[5] = __uint_as_float(w.z & 0xffff0000u);
+    f[6] = __uint_as_float(w.w << 16);
+    f[7] = __uint_as_float(w.w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ u32x4 narrow(const float* f) {
+    u32x4 w;
+    w.x = bf16_rne(f[0]) | (bf16_rne(f[1]) << 16);
+    w.y = bf16_rne(f[2]) | (bf16_rne(f[3]) << 16);
+    w.z = bf16_rne(f[4]) | (bf16_rne(f[5]) << 16);
+    w.w = bf16_rne(f[6]) | (bf16_rne(f[7]) << 16);
+    return w;
+  }
+  __device__ static __forceinline__ float widen1(elem e) { return __uint_as_float(uint32_t(e) << 16); }
+  __device__ static __forceinline__ elem narrow1(float f) { return static_cast<elem>(bf16_rne(f)); }
+};
+
+// ----------------------------------------------------------------------------
+// memory access: 16-byte vectors, streamed (each byte is touched once)
+
+__device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off));
+}
+
+__device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off));
+}
+
+template <int K, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<K + 1, N>(f);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// order programs unfolded at compile time (p fixed)
+
+template <int ALGO, int P>
+struct Prog {
+  static constexpr OrderProgram value = order_program(ALGO, P);
+  static constexpr int depth = value.max_depth > 0 ? value.max_depth : 1;
+};
+
+// Replace the top two of DEPTH live stack entries by their sum, M times.
+template <int DEPTH, int M, int SD, int N>
+__device__ __forceinline__ void merge_top(float (&st)[SD][N]) {
+  if constexpr (M > 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) st[DEPTH - 2][i] = st[DEPTH - 2][i] + st[DEPTH - 1][i];
+    merge_top<DEPTH - 1, M - 1>(st);
+  }
+}
+
+// Push leaf K (widened by `leaf`) and apply its merges; recurse to K + 1.
+template <int ALGO, int P, int K, int DEPTH, int SD, int N, class Leaf>
+__device__ __forceinline__ void run_program(float (&st)[SD][N], const Leaf& leaf) {
+  if constexpr (K < P) {
+    leaf(std::integral_constant<int, K>{}, st[DEPTH]);
+    constexpr int M = Prog<ALGO, P>::value.merges[K];
+    merge_top<DEPTH + 1, M>(st);
+    run_program<ALGO, P, K + 1, DEPTH + 1 - M>(st, leaf);
+  } else {
+    merge_top<DEPTH, Prog<ALGO, P>::value.final_merges>(st);
+  }
+}
+
+template <int ALGO, int P, int K>
+__device__ __forceinline__ int leaf_rank(int rot) {
+  if constexpr (ALGO == VCOLL_RING) {
+    return (rot + K) % P;   // the chain starts right after the chunk's owner
+  } else {
+    return Prog<ALGO, P>::value.rank[K];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// order programs read at run time (any p): a shift-register stack keeps every
+// index a compile-time constant, so the stack lives in registers
+
+constexpr int kRuntimeDepth = 9;   // deepest stack of any program with p <= 128
+
+template <int N>
+__device__ __forceinline__ void rt_push(float (&st)[kRuntimeDepth][N], const float* v) {
+#pragma unroll
+  for (int s = kRuntimeDepth - 1; s > 0; --s)
+#pragma unroll
+    for (int i = 0; i < N; ++i) st[s][i] = st[s - 1][i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) st[0][i] = v[i];
+}
+
+template <int N>
+__device__ __forceinline__ void rt_merge(float (&st)[kRuntimeDepth][N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) st[0][i] = st[1][i] + st[0][i];
+#pragma unroll
+  for (int s = 1; s < kRuntimeDepth - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < N; ++i) st[s][i] = st[s + 1][i];
+}
+
+// ----------------------------------------------------------------------------
+// one element (chunk heads and tails, unaligned buffers)
+
+template <int D, int ALGO, int P, bool RS>
+__device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, int rot, int64_t e,
+                                           int64_t off) {
+  using S = Storage<D>;
+  using E = typename S::elem;
+  float result;
+  if constexpr (P > 0) {
+    E raw[P];
+    static_for<0, P>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      raw[k] = static_cast<const E*>(a.ptr.src[leaf_rank<ALGO, P, k>(rot)])[e];
+    });
+    float st[Prog<ALGO, P>::depth][1];
+    run_program<ALGO, P, 0, 0>(st, [&](auto kc, float(&d)[1]) {
+      d[0] = S::widen1(raw[decltype(kc)::value]);
+    });
+    result = st[0][0];
+  } else if constexpr (ALGO == VCOLL_RING) {
+    result = S::widen1(static_cast<const E*>(a.ptr.src[rot % p])[e]);
+    for (int k = 1; k < p; ++k)
+      result = result + S::widen1(static_cast<const E*>(a.ptr.src[(rot + k) % p])[e]);
+  } else {
+    float st[kRuntimeDepth][1];
+    for (int k = 0; k < p; ++k) {
+      const float v = S::widen1(static_cast<const E*>(a.ptr.src[a.rank[k]])[e]);
+      rt_push<1>(st, &v);
+      for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
+    }
+    for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
+    result = st[0][0];
+  }
+  const E out = S::narrow1(result);
+  if constexpr (RS) {
+    static_cast<E*>(a.ptr.dst[c])[e - off] = out;
+  } else {
+    for (int r = 0; r < p; ++r) static_cast<E*>(a.ptr.dst[r])[e] = out;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// V 16-byte vectors per thread, fixed p: all p*V loads are issued before the
+// first add, the order program runs in registers, then p*V (or V) stores.
+
+template <int D, int ALGO, int P, int V, bool RS>
+__device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c, int rot,
+                                                     const int64_t (&boff)[V],
+                                                     const bool (&valid)[V], int64_t out_shift) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  u32x4 raw[P][V];
+  static_for<0, P>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const void* src = a.ptr.src[leaf_rank<ALGO, P, k>(rot)];
+#pragma unroll
+    for (int j = 0; j < V; ++j) raw[k][j] = valid[j] ? ld16(src, boff[j]) : u32x4{0, 0, 0, 0};
+  });
+  float st[Prog<ALGO, P>::depth][V * VE];
+  run_program<ALGO, P, 0, 0>(st, [&](auto kc, float(&d)[V * VE]) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) S::widen(raw[decltype(kc)::value][j], &d[j * VE]);
+  });
+  u32x4 out[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) out[j] = S::narrow(&st[0][j * VE]);
+  if constexpr (RS) {
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if (valid[j]) st16(a.ptr.dst[c], boff[j] - out_shift, out[j]);
+  } else {
+    static_for<0, P>([&](auto rc) {
+      void* dst = a.ptr.dst[decltype(rc)::value];
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (valid[j]) st16(dst, boff[j], out[j]);
+    });
+  }
+}
+
+// Same for a p known only at run time (one vector per thread; loads go out
+// eight ranks at a time).
+template <int D, int ALGO, bool RS>
+__device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c, int p, int rot,
+                                                      int64_t boff, bool valid, int64_t out_shift) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  constexpr int B = 8;
+  float acc[VE];
+  float st[kRuntimeDepth][VE];
+  for (int k0 = 0; k0 < p; k0 += B) {
+    u32x4 raw[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (k0 + b < p) {
+        const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : a.rank[k0 + b];
+        raw[b] = valid ? ld16(a.ptr.src[rank], boff) : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (k0 + b < p) {
+        float v[VE];
+        S::widen(raw[b], v);
+        if constexpr (ALGO == VCOLL_RING) {
+          if (k0 + b == 0) {
+#pragma unroll
+            for (int i = 0; i < VE; ++i) acc[i] = v[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < VE; ++i) acc[i] = acc[i] + v[i];
+          }
+        } else {
+          rt_push<VE>(st, v);
+          for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<VE>(st);
+        }
+      }
+    }
+  }
+  if constexpr (ALGO != VCOLL_RING) {
+    for (int m = 0; m < a.final_merges; ++m) rt_merge<VE>(st);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] = st[0][i];
+  }
+  if (!valid) return;
+  const u32x4 out = S::narrow(acc);
+  if constexpr (RS) {
+    st16(a.ptr.dst[c], boff - out_shift, out);
+  } else {
+    for (int r = 0; r < p; ++r) st16(a.ptr.dst[r], boff, out);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// the reduce kernel: workgroup (x, y) handles tile x of chunk y
+
+template <int D, int ALGO, int P, int V, bool RS>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  constexpr int ES = 16 / VE;
+  const int c = blockIdx.y;
+  const int p = P > 0 ? P : a.p;
+  const int64_t off = c * a.q + (c < a.r ? c : a.r);
+  const int64_t cnt = a.q + (c < a.r ? 1 : 0);
+  const int rot = (ALGO == VCOLL_RING) ? (c + 1) % p : 0;
+  const int tid = threadIdx.x;
+  // a reduce-scatter writes element e of chunk c to recv[c][e - off]: both
+  // sides must be vector aligned, so the chunk start must be
+  const bool vec = a.vec != 0 && (!RS || (off % VE) == 0);
+
+  if (vec) {
+    const int64_t head = (VE - off % VE) % VE < cnt ? (VE - off % VE) % VE : cnt;
+    const int64_t nvec = (cnt - head) / VE;
+    const int64_t e_base = off + head;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + tid;
+    if (static_cast<int64_t>(blockIdx.x) * (V * kBlock) < nvec) {
+      if constexpr (P > 0) {
+        int64_t boff[V];
+        bool valid[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int64_t v = v0 + j * kBlock;
+          valid[j] = v < nvec;
+          boff[j] = (e_base + v * VE) * ES;
+        }
+        reduce_vectors_fixed<D, ALGO, P, V, RS>(a, c, rot, boff, valid, off * ES);
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < V; ++j) {
+          const int64_t v = v0 + j * kBlock;
+          reduce_vector_runtime<D, ALGO, RS>(a, c, p, rot, (e_base + v * VE) * ES, v < nvec,
+                                             off * ES);
+        }
+      }
+    }
+    if (blockIdx.x == 0) {
+      const int64_t tail = cnt - head - nvec * VE;
+      if (tid < head) {
+        reduce_one<D, ALGO, P, RS>(a, c, p, rot, off + tid, off);
+      } else if (tid >= 16 && tid - 16 < tail) {
+        reduce_one<D, ALGO, P, RS>(a, c, p, rot, e_base + nvec * VE + (tid - 16), off);
+      }
+    }
+  } else {
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock * VE);
+#pragma unroll 1
+    for (int j = 0; j < V * VE; ++j) {
+      const int64_t i = e0 + j * kBlock + tid;
+      if (i < cnt) reduce_one<D, ALGO, P, RS>(a, c, p, rot, off + i, off);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// all-gather: block i of every output is a copy of input i
+
+template <int ES, int V>
+__global__ __launch_bounds__(kBlock) void all_gather_kernel(const GatherArgs a) {
+  const int i = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t bytes = a.m * ES;
+  const int64_t dst_off = i * bytes;
+  const void* src = a.ptr.src[i];
+  if (a.vec) {
+    const int64_t nvec = bytes / 16;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + tid;
+    u32x4 x[V];
+    bool valid[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t v = v0 + j * kBlock;
+      valid[j] = v < nvec;
+      x[j] = valid[j] ? ld16(src, v * 16) : u32x4{0, 0, 0, 0};
+    }
+    for (int r = 0; r < a.p; ++r) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (valid[j]) st16(a.ptr.dst[r], dst_off + (v0 + j * kBlock) * 16, x[j]);
+    }
+  } else {
+    using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
+    constexpr int VE = 16 / ES;
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock * VE) + tid;
+#pragma unroll 1
+    for (int j = 0; j < V * VE; ++j) {
+      const int64_t e = e0 + j * kBlock;
+      if (e < a.m) {
+        const E x = static_cast<const E*>(src)[e];
+        for (int r = 0; r < a.p; ++r) static_cast<E*>(a.ptr.dst[r])[i * a.m + e] = x;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// all-to-all: workgroup t moves rows_per_tile rows of one (i -> j) block
+
+__global__ __launch_bounds__(kBlock) void all_to_all_kernel(const A2AArgs a) {
+  const int t = blockIdx.x;
+  // the block this workgroup belongs to: last one whose first tile <= t
+  int lo = 0, hi = a.nblocks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (a.b[mid].tile_start <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const A2ABlock& B = a.b[lo];
+  const int r0 = (t - B.tile_start) * a.rows_per_tile;
+  const int tid = threadIdx.x;
+  for (int rr = 0; rr < a.rows_per_tile; ++rr) {
+    const int k = r0 + rr;
+    if (k >= B.rows) break;
+    const int64_t sr = B.src_idx ? static_cast<int64_t>(B.src_idx[k]) : k;
+    const int64_t dr = B.dst_idx ? static_cast<int64_t>(B.dst_idx[k]) : k;
+    if (sr < 0 || sr >= B.src_limit || dr < 0 || dr >= B.dst_limit) continue;
+    const char* src = B.src + sr * a.row_bytes;
+    char* dst = B.dst + dr * a.row_bytes;
+    if (a.vec) {
+      const int64_t nvec = a.row_bytes / 16;
+      constexpr int U = 4;
+      for (int64_t x0 = tid; x0 < nvec; x0 += U * kBlock) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          v[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          if (x < nvec) st16(dst, x * 16, v[u]);
+        }
+      }
+    } else if (a.esize == 4) {
+      for (int64_t x = tid; x < a.row_bytes / 4; x += kBlock)
+        reinterpret_cast<uint32_t*>(dst)[x] = reinterpret_cast<const uint32_t*>(src)[x];
+    } else {
+      for (int64_t x = tid; x < a.row_bytes / 2; x += kBlock)
+        reinterpret_cast<uint16_t*>(dst)[x] = reinterpret_cast<const uint16_t*>(src)[x];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// plain copy: the streaming ceiling the collectives are measured against
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(const void* src, void* dst, int64_t nvec) {
+  constexpr int V = 4;
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + threadIdx.x;
+  u32x4 x[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t v = v0 + j * kBlock;
+    x[j] = v < nvec ? ld16(src, v * 16) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t v = v0 + j * kBlock;
+    if (v < nvec) st16(dst, v * 16, x[j]);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// launch helpers
+
+template <class K, class Arg>
+hipError_t launch(K kernel, dim3 grid, const Arg& arg, hipStream_t stream) {
+  void* args[] = {const_cast<Arg*>(&arg)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kBlock), args, 0, stream);
+}
+
+template <int P>
+constexpr int vectors_per_thread() {
+  return P == 0 ? 1 : (P <= 4 ? 4 : (P <= 8 ? 2 : 1));
+}
+
+template <int D, int ALGO, bool RS, int P>
+hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, hipStream_t stream) {
+  constexpr int V = vectors_per_thread<P>();
+  constexpr int VE = Storage<D>::kVE;
+  const int64_t per_tile = static_cast<int64_t>(V) * kBlock * VE;
+  const int64_t tiles = (max_chunk + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  return launch(reduce_kernel<D, ALGO, P, V, RS>, dim3(static_cast<unsigned>(tiles), a.p), a, stream);
+}
+
+template <int D, int ALGO, bool RS>
+hipError_t launch_reduce_algo(const ReduceArgs& a, int64_t max_chunk, hipStream_t stream) {
+  switch (a.p) {
+    case 2: return launch_reduce_p<D, ALGO, RS, 2>(a, max_chunk, stream);
+    case 4: return launch_reduce_p<D, ALGO, RS, 4>(a, max_chunk, stream);
+    case 8: return launch_reduce_p<D, ALGO, RS, 8>(a, max_chunk, stream);
+    case 16: return launch_reduce_p<D, ALGO, RS, 16>(a, max_chunk, stream);
+    default: return launch_reduce_p<D, ALGO, RS, 0>(a, max_chunk, stream);
+  }
+}
+
+template <int D>
+hipError_t launch_reduce_dtype(const ReduceArgs& a, vcoll_algo algo, bool scatter, int64_t max_chunk,
+                               hipStream_t stream) {
+  if (scatter) {
+    if (algo == VCOLL_RING) return launch_reduce_algo<D, VCOLL_RING, true>(a, max_chunk, stream);
+    return launch_reduce_algo<D, VCOLL_RABENSEIFNER, true>(a, max_chunk, stream);
+  }
+  switch (algo) {
+    case VCOLL_RING: return launch_reduce_algo<D, VCOLL_RING, false>(a, max_chunk, stream);
+    case VCOLL_RECURSIVE_DOUBLING:
+      return launch_reduce_algo<D, VCOLL_RECURSIVE_DOUBLING, false>(a, max_chunk, stream);
+    case VCOLL_RABENSEIFNER: return launch_reduce_algo<D, VCOLL_RABENSEIFNER, false>(a, max_chunk, stream);
+    default: return launch_reduce_algo<D, VCOLL_BINARY_TREE, false>(a, max_chunk, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
+                         int64_t max_chunk, hipStream_t stream) {
+  if (dtype == VCOLL_F32) return launch_reduce_dtype<VCOLL_F32>(a, algo, scatter, max_chunk, stream);
+  return launch_reduce_dtype<VCOLL_BF16>(a, algo, scatter, max_chunk, stream);
+}
+
+hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream) {
+  constexpr int V = 2;
+  const int ES = dtype == VCOLL_F32 ? 4 : 2;
+  const int64_t per_tile = static_cast<int64_t>(V) * kBlock * (16 / ES);
+  const int64_t tiles = (a.m + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles), a.p);
+  if (ES == 4) return launch(all_gather_kernel<4, V>, grid, a, stream);
+  return launch(all_gather_kernel<2, V>, grid, a, stream);
+}
+
+hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {
+  if (tiles == 0) return hipSuccess;
+  return launch(all_to_all_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  const int64_t nvec = bytes / 16;
+  const int64_t per_tile = 4LL * kBlock;
+  const int64_t tiles = (nvec + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  void* args[] = {const_cast<const void**>(&src), &dst, const_cast<int64_t*>(&nvec)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel), dim3(static_cast<unsigned>(tiles)),
+                         dim3(kBlock), args, 0, stream);
+}
+
+}  // namespace vcoll

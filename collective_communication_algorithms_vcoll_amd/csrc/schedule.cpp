@@ -1,0 +1,222 @@
+// Host-side schedules: combination checks, message ledger, MoE plan.
+//
+// Sources, by page title: "Networks and Collective Communication" (cs349e
+// prerequisite lecture 5) sections 4.1-4.3, 5.1, 5.2 and 7.4; "11-1.
+// Distributed training" (HPC101), "Ring Algorithm". The readings used where
+// the pages leave a step open are stated next to the code that takes them.
+#include "schedule.h"
+
+#include <algorithm>
+#include <tuple>
+
+namespace vcoll {
+
+vcoll_status check_combination(vcoll_op op, vcoll_algo algo, int p) {
+  switch (op) {
+    case VCOLL_OP_ALLREDUCE:
+      return (algo >= VCOLL_RING && algo <= VCOLL_BINARY_TREE) ? VCOLL_OK : VCOLL_ERR_INVALID_ARG;
+    case VCOLL_OP_REDUCE_SCATTER:
+      if (algo == VCOLL_RING) return VCOLL_OK;
+      if (algo == VCOLL_RABENSEIFNER) return is_pow2(p) ? VCOLL_OK : VCOLL_ERR_UNSUPPORTED;
+      return (algo >= VCOLL_RING && algo <= VCOLL_BINARY_TREE) ? VCOLL_ERR_UNSUPPORTED
+                                                               : VCOLL_ERR_INVALID_ARG;
+    case VCOLL_OP_ALL_GATHER:
+      if (algo == VCOLL_RING) return VCOLL_OK;
+      if (algo == VCOLL_RECURSIVE_DOUBLING) return is_pow2(p) ? VCOLL_OK : VCOLL_ERR_UNSUPPORTED;
+      return (algo >= VCOLL_RING && algo <= VCOLL_BINARY_TREE) ? VCOLL_ERR_UNSUPPORTED
+                                                               : VCOLL_ERR_INVALID_ARG;
+    case VCOLL_OP_ALL_TO_ALL:
+      return VCOLL_OK;
+  }
+  return VCOLL_ERR_INVALID_ARG;
+}
+
+void block_offsets(int p, const int64_t* splits, std::vector<int64_t>& send_off,
+                   std::vector<int64_t>& recv_off) {
+  send_off.assign(static_cast<size_t>(p) * p, 0);
+  recv_off.assign(static_cast<size_t>(p) * p, 0);
+  for (int i = 0; i < p; ++i)
+    for (int j = 1; j < p; ++j)
+      send_off[i * p + j] = send_off[i * p + j - 1] + splits[i * p + j - 1];
+  for (int j = 0; j < p; ++j)
+    for (int i = 1; i < p; ++i)
+      recv_off[i * p + j] = recv_off[(i - 1) * p + j] + splits[(i - 1) * p + j];
+}
+
+namespace {
+
+struct LedgerBuilder {
+  std::vector<vcoll_msg>& out;
+  int64_t esize;
+  int32_t steps = 0;
+  void add(int step, int src, int dst, int64_t src_off, int64_t dst_off, int64_t count) {
+    vcoll_msg m{};
+    m.step = step;
+    m.src = src;
+    m.dst = dst;
+    m.src_off = src_off;
+    m.dst_off = dst_off;
+    m.count = count;
+    m.bytes = count * esize;
+    out.push_back(m);
+    steps = std::max(steps, step + 1);
+  }
+};
+
+// Ring reduce-scatter ([NCC] 5.1): step s, rank i passes chunk (i-1-s) mod p
+// to rank i+1 (rank c ends owning chunk c, as [HPC]'s reduce-scatter
+// definition gives process k the k-th piece).
+int ring_rs(LedgerBuilder& L, int p, const Chunks& ch, int step) {
+  for (int s = 0; s < p - 1; ++s)
+    for (int i = 0; i < p; ++i) {
+      const int c = ((i - 1 - s) % p + p) % p;
+      L.add(step + s, i, (i + 1) % p, ch.off(c), ch.off(c), ch.count(c));
+    }
+  return step + (p - 1);
+}
+
+// Ring all-gather: step s, rank i forwards chunk (i-s) mod p, the complete
+// chunk it holds most recently.
+int ring_ag(LedgerBuilder& L, int p, const std::vector<int64_t>& off, int step) {
+  for (int s = 0; s < p - 1; ++s)
+    for (int i = 0; i < p; ++i) {
+      const int c = ((i - s) % p + p) % p;
+      L.add(step + s, i, (i + 1) % p, off[c], off[c], off[c + 1] - off[c]);
+    }
+  return step + (p - 1);
+}
+
+// Recursive halving over new ranks 0..p2-1 (distance p2/2 first), chunk
+// bounds off[0..p2]: keep the half holding your own chunk, send the other.
+int halving(LedgerBuilder& L, const Fold& f, const std::vector<int64_t>& off, int step) {
+  for (int d = f.p2 / 2; d >= 1; d /= 2, ++step)
+    for (int nr = 0; nr < f.p2; ++nr) {
+      const int base = nr & ~(2 * d - 1);
+      const int lo = (nr & d) ? base : base + d;
+      L.add(step, f.old_rank(nr), f.old_rank(nr ^ d), off[lo], off[lo], off[lo + d] - off[lo]);
+    }
+  return step;
+}
+
+// Recursive doubling of complete ranges (distance 1, 2, .., p2/2).
+int doubling(LedgerBuilder& L, const Fold& f, const std::vector<int64_t>& off, int step) {
+  for (int d = 1; d < f.p2; d *= 2, ++step)
+    for (int nr = 0; nr < f.p2; ++nr) {
+      const int base = nr & ~(d - 1);
+      L.add(step, f.old_rank(nr), f.old_rank(nr ^ d), off[base], off[base], off[base + d] - off[base]);
+    }
+  return step;
+}
+
+std::vector<int64_t> chunk_offsets(int64_t n, int p) {
+  Chunks ch(n, p);
+  std::vector<int64_t> off(p + 1);
+  for (int c = 0; c <= p; ++c) off[c] = c < p ? ch.off(c) : n;
+  return off;
+}
+
+}  // namespace
+
+vcoll_status build_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_t elem_bytes,
+                          const int64_t* splits, int64_t row_elems, std::vector<vcoll_msg>& out,
+                          int32_t* n_steps) {
+  out.clear();
+  LedgerBuilder L{out, elem_bytes};
+  if (op == VCOLL_OP_ALL_TO_ALL) {
+    std::vector<int64_t> so, ro;
+    block_offsets(p, splits, so, ro);
+    for (int s = 1; s < p; ++s)
+      for (int i = 0; i < p; ++i) {
+        const int j = (i + s) % p;
+        L.add(s - 1, i, j, so[i * p + j] * row_elems, ro[i * p + j] * row_elems,
+              splits[i * p + j] * row_elems);
+      }
+  } else if (op == VCOLL_OP_ALL_GATHER) {
+    std::vector<int64_t> off(p + 1);
+    for (int c = 0; c <= p; ++c) off[c] = c * n;
+    if (algo == VCOLL_RING) ring_ag(L, p, off, 0);
+    else doubling(L, Fold(p), off, 0);
+  } else if (op == VCOLL_OP_REDUCE_SCATTER) {
+    if (algo == VCOLL_RING) ring_rs(L, p, Chunks(n, p), 0);
+    else halving(L, Fold(p), chunk_offsets(n, p), 0);
+  } else {  // all-reduce
+    if (algo == VCOLL_RING) {
+      const int step = ring_rs(L, p, Chunks(n, p), 0);
+      ring_ag(L, p, chunk_offsets(n, p), step);
+    } else if (algo == VCOLL_BINARY_TREE) {
+      // binomial reduce to rank 0: a rank whose lowest set bit is the mask
+      // sends its full vector to rank - mask; then the mirrored broadcast
+      std::vector<int> masks;
+      for (int m = 1; m < p; m <<= 1) masks.push_back(m);
+      int step = 0;
+      for (int m : masks) {
+        for (int i = 0; i < p; ++i)
+          if ((i & -i) == m) L.add(step, i, i - m, 0, 0, n);
+        ++step;
+      }
+      for (auto it = masks.rbegin(); it != masks.rend(); ++it, ++step)
+        for (int i = 0; i < p; i += 2 * *it)
+          if (i + *it < p) L.add(step, i, i + *it, 0, 0, n);
+    } else {
+      const Fold f(p);
+      int step = 0;
+      if (f.r > 0) {
+        for (int j = 0; j < f.r; ++j) L.add(step, 2 * j, 2 * j + 1, 0, 0, n);
+        ++step;
+      }
+      if (algo == VCOLL_RECURSIVE_DOUBLING) {
+        for (int d = 1; d < f.p2; d *= 2, ++step)
+          for (int nr = 0; nr < f.p2; ++nr) L.add(step, f.old_rank(nr), f.old_rank(nr ^ d), 0, 0, n);
+      } else {
+        const std::vector<int64_t> off = chunk_offsets(n, f.p2);
+        step = halving(L, f, off, step);
+        step = doubling(L, f, off, step);
+      }
+      if (f.r > 0)
+        for (int j = 0; j < f.r; ++j) L.add(step, 2 * j + 1, 2 * j, 0, 0, n);
+    }
+  }
+  std::sort(out.begin(), out.end(), [](const vcoll_msg& a, const vcoll_msg& b) {
+    return std::tie(a.step, a.src, a.dst, a.src_off) < std::tie(b.step, b.src, b.dst, b.src_off);
+  });
+  if (n_steps) *n_steps = L.steps;
+  return VCOLL_OK;
+}
+
+vcoll_status moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
+                      const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
+                      int32_t* dst_rows) {
+  const int64_t experts = static_cast<int64_t>(p) * experts_per_rank;
+  const int64_t rows = tokens * topk;
+  std::vector<int64_t> count(experts), start(experts);
+  for (int i = 0; i < p; ++i) {
+    const int32_t* ids = topk_ids + static_cast<int64_t>(i) * rows;
+    std::fill(count.begin(), count.end(), 0);
+    for (int64_t x = 0; x < rows; ++x) {
+      if (ids[x] < 0 || ids[x] >= experts) return VCOLL_ERR_INVALID_ARG;
+      ++count[ids[x]];
+    }
+    // rows ordered by (destination rank, expert, token): destination rank is
+    // monotone in the expert id, so a counting sort on the expert id, filled
+    // in token order, gives that order
+    int64_t acc = 0;
+    for (int64_t e = 0; e < experts; ++e) { start[e] = acc; acc += count[e]; }
+    for (int j = 0; j < p; ++j) {
+      int64_t s = 0;
+      for (int64_t e = static_cast<int64_t>(j) * experts_per_rank; e < (j + 1LL) * experts_per_rank; ++e)
+        s += count[e];
+      splits[static_cast<int64_t>(i) * p + j] = s;
+    }
+    int32_t* src = src_rows + static_cast<int64_t>(i) * rows;
+    int32_t* dst = dst_rows + static_cast<int64_t>(i) * rows;
+    for (int64_t t = 0; t < tokens; ++t)
+      for (int k = 0; k < topk; ++k) {
+        const int64_t pos = start[ids[t * topk + k]]++;
+        src[pos] = static_cast<int32_t>(t);
+        dst[pos] = static_cast<int32_t>(t * topk + k);
+      }
+  }
+  return VCOLL_OK;
+}
+
+}  // namespace vcoll

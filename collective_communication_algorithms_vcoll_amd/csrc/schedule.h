@@ -1,0 +1,38 @@
+// Host-side schedules of the virtual-cluster collectives: chunk partition,
+// summation-order programs, message ledger, MoE plan. No HIP dependency.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "order.h"
+#include "vcoll.h"
+
+namespace vcoll {
+
+// Balanced partition of n elements into p chunks (first n mod p chunks one longer).
+struct Chunks {
+  int64_t q = 0, r = 0;
+  int p = 1;
+  Chunks(int64_t n, int p_) : q(n / p_), r(n % p_), p(p_) {}
+  int64_t off(int c) const { return c * q + (c < r ? c : r); }
+  int64_t count(int c) const { return q + (c < r ? 1 : 0); }
+};
+
+// Checks (op, algo, p) and returns VCOLL_OK or VCOLL_ERR_UNSUPPORTED.
+vcoll_status check_combination(vcoll_op op, vcoll_algo algo, int p);
+
+// Messages of op/algo, sorted by (step, src, dst, src_off); sets *n_steps.
+vcoll_status build_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_t elem_bytes,
+                          const int64_t* splits, int64_t row_elems,
+                          std::vector<vcoll_msg>& out, int32_t* n_steps);
+
+// Row offsets of block (i -> j): in the sender's buffer and in the receiver's.
+void block_offsets(int p, const int64_t* splits, std::vector<int64_t>& send_off,
+                   std::vector<int64_t>& recv_off);
+
+vcoll_status moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
+                      const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
+                      int32_t* dst_rows);
+
+}  // namespace vcoll

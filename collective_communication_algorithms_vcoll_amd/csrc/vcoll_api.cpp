@@ -1,0 +1,258 @@
+// C ABI of libvcoll: argument validation, launch descriptors, dispatch.
+// Every check happens before the first launch, so an error return means that
+// nothing was enqueued.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+#include "schedule.h"
+#include "vcoll.h"
+#include "vcoll_bench.h"
+
+using namespace vcoll;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+thread_local const char* g_last_hip_error = "";
+
+vcoll_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return VCOLL_OK;
+  g_last_hip_error = hipGetErrorString(e);
+  return VCOLL_ERR_HIP;
+}
+
+int64_t elem_bytes(vcoll_dtype d) { return d == VCOLL_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == VCOLL_F32 || d == VCOLL_BF16; }
+
+bool valid_algo(int a) { return a >= VCOLL_RING && a <= VCOLL_BINARY_TREE; }
+
+bool valid_p(int p) { return p >= 1 && p <= kMaxRanks; }
+
+bool all_set(int p, const void* const* ptrs) {
+  if (!ptrs) return false;
+  for (int r = 0; r < p; ++r)
+    if (!ptrs[r]) return false;
+  return true;
+}
+
+bool all_aligned(int p, const void* const* ptrs) {
+  for (int r = 0; r < p; ++r)
+    if (!aligned16(ptrs[r])) return false;
+  return true;
+}
+
+vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                           const void* const* send, void* const* recv, void* stream, bool scatter) {
+  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+  const vcoll_status combo =
+      check_combination(scatter ? VCOLL_OP_REDUCE_SCATTER : VCOLL_OP_ALLREDUCE, algo, p);
+  if (combo != VCOLL_OK) return combo;
+  if (n == 0) return VCOLL_OK;
+  if (!all_set(p, send) || !all_set(p, const_cast<const void* const*>(recv))) return VCOLL_ERR_INVALID_ARG;
+
+  ReduceArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < p; ++r) {
+    a.ptr.src[r] = send[r];
+    a.ptr.dst[r] = recv[r];
+  }
+  const Chunks ch(n, p);
+  a.q = ch.q;
+  a.r = ch.r;
+  a.p = p;
+  a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv));
+  if (algo != VCOLL_RING) {
+    const OrderProgram prog = order_program(algo, p);
+    for (int k = 0; k < p; ++k) {
+      a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
+      a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
+    }
+    a.final_merges = prog.final_merges;
+  }
+  return from_hip(launch_reduce(a, dtype, algo, scatter, ch.count(0), static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int vcoll_abi_version(void) { return VCOLL_ABI_VERSION; }
+
+const char* vcoll_last_hip_error(void) { return g_last_hip_error; }
+
+const char* vcoll_status_str(vcoll_status status) {
+  switch (status) {
+    case VCOLL_OK: return "ok";
+    case VCOLL_ERR_INVALID_ARG: return "invalid argument";
+    case VCOLL_ERR_UNSUPPORTED: return "unsupported operation/algorithm/p combination";
+    case VCOLL_ERR_BUFFER_TOO_SMALL: return "ledger buffer too small";
+    case VCOLL_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+vcoll_status vcoll_chunk(int p, int64_t n, int c, int64_t* off, int64_t* count) {
+  if (!valid_p(p) || n < 0 || c < 0 || c >= p || !off || !count) return VCOLL_ERR_INVALID_ARG;
+  const Chunks ch(n, p);
+  *off = ch.off(c);
+  *count = ch.count(c);
+  return VCOLL_OK;
+}
+
+vcoll_status vcoll_allreduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                             const void* const* send, void* const* recv, void* stream) {
+  return reduce_common(algo, p, n, dtype, send, recv, stream, false);
+}
+
+vcoll_status vcoll_reduce_scatter(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                  const void* const* send, void* const* recv, void* stream) {
+  return reduce_common(algo, p, n, dtype, send, recv, stream, true);
+}
+
+vcoll_status vcoll_all_gather(vcoll_algo algo, int p, int64_t m, vcoll_dtype dtype,
+                              const void* const* send, void* const* recv, void* stream) {
+  if (!valid_p(p) || m < 0 || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+  const vcoll_status combo = check_combination(VCOLL_OP_ALL_GATHER, algo, p);
+  if (combo != VCOLL_OK) return combo;
+  if (m == 0) return VCOLL_OK;
+  if (!all_set(p, send) || !all_set(p, const_cast<const void* const*>(recv))) return VCOLL_ERR_INVALID_ARG;
+  GatherArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < p; ++r) {
+    a.ptr.src[r] = send[r];
+    a.ptr.dst[r] = recv[r];
+  }
+  a.m = m;
+  a.p = p;
+  a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv)) &&
+          (m * elem_bytes(dtype)) % 16 == 0;
+  return from_hip(launch_all_gather(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const int64_t* splits,
+                              const void* const* send, void* const* recv,
+                              const int32_t* const* src_rows, const int64_t* src_table_rows,
+                              const int32_t* const* dst_rows, const int64_t* dst_table_rows,
+                              void* stream) {
+  if (!valid_p(p) || row_elems < 0 || !valid_dtype(dtype) || !splits) return VCOLL_ERR_INVALID_ARG;
+  const int64_t rb = row_elems * elem_bytes(dtype);
+  std::vector<int64_t> sent(p, 0), got(p, 0);
+  for (int i = 0; i < p; ++i)
+    for (int j = 0; j < p; ++j) {
+      const int64_t s = splits[i * p + j];
+      if (s < 0 || s > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+      sent[i] += s;
+      got[j] += s;
+      if (sent[i] > INT32_MAX || got[j] > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+    }
+  auto gathers = [&](int i) { return src_rows && src_rows[i]; };
+  auto scatters = [&](int j) { return dst_rows && dst_rows[j]; };
+  for (int i = 0; i < p; ++i) {
+    if (sent[i] > 0 && rb > 0 && (!send || !send[i])) return VCOLL_ERR_INVALID_ARG;
+    if (got[i] > 0 && rb > 0 && (!recv || !recv[i])) return VCOLL_ERR_INVALID_ARG;
+    if (gathers(i) && (!src_table_rows || src_table_rows[i] < 0 || src_table_rows[i] > INT32_MAX))
+      return VCOLL_ERR_INVALID_ARG;
+    if (scatters(i) && (!dst_table_rows || dst_table_rows[i] < 0 || dst_table_rows[i] > INT32_MAX))
+      return VCOLL_ERR_INVALID_ARG;
+  }
+  if (rb == 0) return VCOLL_OK;
+  std::vector<int64_t> so, ro;
+  block_offsets(p, splits, so, ro);
+
+  // one descriptor per non-empty block; launches of up to kA2ABlocks blocks
+  const int32_t rows_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / rb)));
+  std::vector<A2ABlock> blocks;
+  std::vector<bool> block_vec;
+  for (int i = 0; i < p; ++i)
+    for (int j = 0; j < p; ++j) {
+      const int64_t rows = splits[i * p + j];
+      if (rows == 0) continue;
+      A2ABlock b{};
+      const bool g = gathers(i), s = scatters(j);
+      b.src = static_cast<const char*>(send[i]) + (g ? 0 : so[i * p + j] * rb);
+      b.dst = static_cast<char*>(recv[j]) + (s ? 0 : ro[i * p + j] * rb);
+      b.src_idx = g ? src_rows[i] + so[i * p + j] : nullptr;
+      b.dst_idx = s ? dst_rows[j] + ro[i * p + j] : nullptr;
+      b.rows = static_cast<int32_t>(rows);
+      b.src_limit = static_cast<int32_t>(g ? src_table_rows[i] : rows);
+      b.dst_limit = static_cast<int32_t>(s ? dst_table_rows[j] : rows);
+      blocks.push_back(b);
+      block_vec.push_back(aligned16(b.src) && aligned16(b.dst));
+    }
+  for (size_t b0 = 0; b0 < blocks.size(); b0 += kA2ABlocks) {
+    A2AArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.row_bytes = rb;
+    a.rows_per_tile = rows_per_tile;
+    a.esize = static_cast<int32_t>(elem_bytes(dtype));
+    a.vec = (rb % 16) == 0;
+    int64_t tiles = 0;
+    const size_t nb = std::min<size_t>(kA2ABlocks, blocks.size() - b0);
+    for (size_t k = 0; k < nb; ++k) {
+      a.b[k] = blocks[b0 + k];
+      a.b[k].tile_start = static_cast<int32_t>(tiles);
+      tiles += (a.b[k].rows + rows_per_tile - 1) / rows_per_tile;
+      if (!block_vec[b0 + k]) a.vec = 0;
+    }
+    a.nblocks = static_cast<int32_t>(nb);
+    const vcoll_status st =
+        from_hip(launch_all_to_all(a, static_cast<int32_t>(tiles), static_cast<hipStream_t>(stream)));
+    if (st != VCOLL_OK) return st;
+  }
+  return VCOLL_OK;
+}
+
+vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                          const int64_t* splits, int64_t row_elems, vcoll_msg* msgs, int64_t cap,
+                          int64_t* n_msgs, int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps) {
+  if (!valid_p(p) || !valid_dtype(dtype) || !n_msgs) return VCOLL_ERR_INVALID_ARG;
+  if (op < VCOLL_OP_ALLREDUCE || op > VCOLL_OP_ALL_TO_ALL) return VCOLL_ERR_INVALID_ARG;
+  if (op == VCOLL_OP_ALL_TO_ALL) {
+    if (!splits || row_elems < 0) return VCOLL_ERR_INVALID_ARG;
+    for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
+      if (splits[k] < 0) return VCOLL_ERR_INVALID_ARG;
+  } else {
+    if (n < 0 || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+    const vcoll_status combo = check_combination(op, algo, p);
+    if (combo != VCOLL_OK) return combo;
+  }
+  std::vector<vcoll_msg> out;
+  int32_t steps = 0;
+  build_ledger(op, algo, p, n, elem_bytes(dtype), splits, row_elems, out, &steps);
+  *n_msgs = static_cast<int64_t>(out.size());
+  if (msgs) {
+    if (cap < static_cast<int64_t>(out.size())) return VCOLL_ERR_BUFFER_TOO_SMALL;
+    std::copy(out.begin(), out.end(), msgs);
+  }
+  if (sent_bytes) std::fill(sent_bytes, sent_bytes + p, 0);
+  if (recv_bytes) std::fill(recv_bytes, recv_bytes + p, 0);
+  for (const vcoll_msg& m : out) {
+    if (sent_bytes) sent_bytes[m.src] += m.bytes;
+    if (recv_bytes) recv_bytes[m.dst] += m.bytes;
+  }
+  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
+}
+
+vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
+                            const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
+                            int32_t* dst_rows) {
+  if (!valid_p(p) || tokens < 0 || topk < 1 || experts_per_rank < 1) return VCOLL_ERR_INVALID_ARG;
+  if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (!splits || (tokens > 0 && (!topk_ids || !src_rows || !dst_rows))) return VCOLL_ERR_INVALID_ARG;
+  return moe_plan(p, tokens, topk, experts_per_rank, topk_ids, splits, src_rows, dst_rows);
+}
+
+vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (bytes < 0 || (bytes % 16) != 0) return VCOLL_ERR_INVALID_ARG;
+  if (bytes == 0) return VCOLL_OK;
+  if (!dst || !src || !aligned16(dst) || !aligned16(src)) return VCOLL_ERR_INVALID_ARG;
+  return from_hip(launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

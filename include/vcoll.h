@@ -1,0 +1,204 @@
+/*
+ * libvcoll -- collectives of a single-GPU "virtual cluster" on MI355X (gfx950).
+ *
+ * p logical ranks each own one buffer in the same GPU's memory. The library
+ * computes what the collective leaves in every rank's buffer, reproducing
+ * each algorithm's summation order exactly, in one streaming pass over the
+ * buffers; the step-by-step message traffic the algorithm would put on a
+ * network is reported separately by vcoll_ledger().
+ *
+ * Sources, by page title:
+ *   [NCC] "Networks and Collective Communication" (semidirectx, cs349e
+ *         prerequisite lecture 5): semantics section 4.1, identities 4.2,
+ *         per-device bytes 4.3, ring 5.1, recursive doubling / Rabenseifner /
+ *         binary tree 5.2, MoE all-to-all 7.4.
+ *   [HPC] "11-1. Distributed training" (HPC101 notes): "Collective
+ *         Communication Primitives", "Ring Algorithm".
+ *   [LDT] "LLM Distributed Training Collectives": "Ring AllReduce".
+ *
+ * Common conventions
+ *   - Every function returns a vcoll_status; nothing throws across the ABI.
+ *   - All arguments are validated before anything is enqueued: an error
+ *     return means no work was launched.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and the call returns before it completes. The library never
+ *     synchronizes, never allocates device memory, and keeps no state
+ *     between calls. A failed launch returns VCOLL_ERR_HIP; faults of
+ *     running kernels surface at the caller's next synchronization.
+ *   - `send` / `recv` are host arrays of p device pointers, read only during
+ *     the call. The caller owns every device buffer.
+ *   - Rank buffers are contiguous arrays of the storage type. When every
+ *     pointer of a call is 16-byte aligned the kernels move 16-byte vectors;
+ *     otherwise they fall back to element-wise access (slower, same result).
+ *   - Arithmetic: float32 adds, round to nearest even, no fused
+ *     multiply-add, denormals kept. bfloat16 inputs widen exactly to
+ *     float32, all p-1 adds of an element happen in float32, and the result
+ *     is rounded to bfloat16 (nearest, ties to even) once.
+ *   - Chunks: an n-element vector is cut into p chunks, chunk c covering
+ *     [off(c), off(c) + count(c)) with off(c) = c*floor(n/p) + min(c, n mod p)
+ *     (the first n mod p chunks hold one extra element).
+ */
+#ifndef VCOLL_H
+#define VCOLL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VCOLL_ABI_VERSION 1
+#define VCOLL_MAX_RANKS 128
+
+typedef enum {
+  VCOLL_OK = 0,
+  VCOLL_ERR_INVALID_ARG = 1,     /* out-of-range p, n, dtype, algo, NULL pointer, bad split */
+  VCOLL_ERR_UNSUPPORTED = 2,     /* the (operation, algorithm, p) combination does not exist */
+  VCOLL_ERR_BUFFER_TOO_SMALL = 3,/* ledger capacity below the number of messages */
+  VCOLL_ERR_HIP = 4              /* the HIP runtime refused a launch */
+} vcoll_status;
+
+typedef enum {
+  VCOLL_RING = 0,                /* [NCC] 5.1, [HPC] "Ring Algorithm", [LDT] */
+  VCOLL_RECURSIVE_DOUBLING = 1,  /* [NCC] 5.2 */
+  VCOLL_RABENSEIFNER = 2,        /* [NCC] 5.2 */
+  VCOLL_BINARY_TREE = 3          /* [NCC] 5.2 (binomial reduce + broadcast) */
+} vcoll_algo;
+
+typedef enum { VCOLL_F32 = 0, VCOLL_BF16 = 1 } vcoll_dtype;
+
+typedef enum {
+  VCOLL_OP_ALLREDUCE = 0,
+  VCOLL_OP_REDUCE_SCATTER = 1,
+  VCOLL_OP_ALL_GATHER = 2,
+  VCOLL_OP_ALL_TO_ALL = 3
+} vcoll_op;
+
+/* One message of an algorithm's schedule. Offsets and count are in elements
+ * of the storage type; bytes = count * element size. */
+typedef struct {
+  int32_t step, src, dst, reserved;
+  int64_t src_off, dst_off, count, bytes;
+} vcoll_msg;
+
+/* Library version of this header's ABI (VCOLL_ABI_VERSION). */
+int vcoll_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* vcoll_status_str(vcoll_status status);
+
+/* Text of the HIP error behind the most recent VCOLL_ERR_HIP returned to the
+ * calling thread ("" if none); static storage, never NULL. */
+const char* vcoll_last_hip_error(void);
+
+/* Bounds of chunk c (0 <= c < p) of an n-element vector, as defined above.
+ * Host only. */
+vcoll_status vcoll_chunk(int p, int64_t n, int c, int64_t* off, int64_t* count);
+
+/*
+ * All-reduce: afterwards every recv[r] holds the elementwise sum of the p
+ * send[r] vectors of n elements, summed in the order the algorithm's steps
+ * produce ([NCC] 4.1 semantics; orders from 5.1 / 5.2):
+ *   RING: chunk c is summed along the ring starting after its owner,
+ *     (((x[c+1] + x[c+2]) + ...) + x[c-1]) + x[c], ranks mod p; the ring runs
+ *     rank i -> i+1 and rank c finishes chunk c. Any p.
+ *   RECURSIVE_DOUBLING: partners i, i xor 2^k add full vectors, k = 0, 1, ..:
+ *     a balanced tree pairing neighbouring ranks first. If p is not a power
+ *     of two, with p2 the largest power of two below p and r = p - p2, rank
+ *     pairs (2j, 2j+1), j < r, are added first and stand as one leaf.
+ *   RABENSEIFNER: recursive halving at distance p2/2, p2/4, .., 1 then
+ *     recursive doubling: a balanced tree pairing ranks p2/2 apart first;
+ *     same pre-addition of rank pairs when p is not a power of two.
+ *   BINARY_TREE: binomial reduce to rank 0 (masks 1, 2, 4, ..) then binomial
+ *     broadcast: for p = 2^k the same tree as recursive doubling; otherwise
+ *     the power-of-two-aligned subtrees of 0..p-1 added right to left.
+ * Every rank receives bitwise the same vector. recv[r] == send[r] (in place)
+ * is allowed; other overlaps are not. 1 <= p <= VCOLL_MAX_RANKS, n >= 0
+ * (0 is a no-op).
+ */
+vcoll_status vcoll_allreduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                             const void* const* send, void* const* recv, void* stream);
+
+/*
+ * Reduce-scatter ([HPC] "Collective Communication Primitives": process k gets
+ * the k-th piece of the sum; [NCC] 4.1): recv[c] (count(c) elements) receives
+ * chunk c of the sum, in the same order as the all-reduce of the same
+ * algorithm. RING for any p; RABENSEIFNER (recursive halving) for p a power
+ * of two. Other algorithms: VCOLL_ERR_UNSUPPORTED. Buffers must not overlap.
+ */
+vcoll_status vcoll_reduce_scatter(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                  const void* const* send, void* const* recv, void* stream);
+
+/*
+ * All-gather ([HPC] primitives; [NCC] 4.1): every recv[r] (p*m elements)
+ * receives send[0] .. send[p-1] (m elements each) concatenated in rank
+ * order, as raw storage words. RING for any p; RECURSIVE_DOUBLING for p a
+ * power of two (the result is the same, only the ledger differs). Buffers
+ * must not overlap.
+ */
+vcoll_status vcoll_all_gather(vcoll_algo algo, int p, int64_t m, vcoll_dtype dtype,
+                              const void* const* send, void* const* recv, void* stream);
+
+/*
+ * Variable-split all-to-all ([NCC] 4.1: block j of device i goes to device j,
+ * the transpose of the device-by-block matrix; 7.4: MoE dispatch/combine).
+ * Rows have row_elems elements. `splits` is a host array [p*p]; splits[i*p+j]
+ * >= 0 rows go from rank i to rank j. send[i] holds its blocks j = 0..p-1 in
+ * order; recv[j] receives the blocks i = 0..p-1 in order. Rows are moved as
+ * raw storage words.
+ *   src_rows (optional, host array of p device int32 pointers, entries may be
+ *   NULL): when src_rows[i] is set, the k-th row rank i sends (block order)
+ *   is row src_rows[i][k] of send[i], a table of src_table_rows[i] rows --
+ *   a fused gather (MoE dispatch from the token buffer).
+ *   dst_rows (optional, likewise): when dst_rows[j] is set, the k-th row rank
+ *   j receives (block order) is written to row dst_rows[j][k] of recv[j], a
+ *   table of dst_table_rows[j] rows -- a fused scatter (MoE combine).
+ *   A gather or scatter index outside its table is skipped by the kernel
+ *   (that row is neither read nor written).
+ * Buffers must not overlap.
+ */
+vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const int64_t* splits,
+                              const void* const* send, void* const* recv,
+                              const int32_t* const* src_rows, const int64_t* src_table_rows,
+                              const int32_t* const* dst_rows, const int64_t* dst_table_rows,
+                              void* stream);
+
+/*
+ * Message ledger ([NCC] code note: a virtual cluster accounts every message;
+ * 4.3 per-device bytes). Host only, no device work. Enumerates the messages
+ * of `op` run with `algo` on p ranks of n elements (all-gather: m elements
+ * per rank; all-to-all: `splits` and `row_elems`, algo ignored, direct
+ * schedule where step s-1 sends block i -> (i+s) mod p, s = 1..p-1, the
+ * diagonal block being local). Each step is synchronous; recursive doubling
+ * and Rabenseifner with p not a power of two add a pre-step (2j -> 2j+1) and
+ * a post-step (2j+1 -> 2j), j < r. Records are sorted by (step, src, dst,
+ * src_off). Two-call use: with msgs == NULL only *n_msgs is set; with
+ * cap < *n_msgs the call returns VCOLL_ERR_BUFFER_TOO_SMALL and sets *n_msgs.
+ * sent_bytes / recv_bytes (p entries) and n_steps may be NULL.
+ */
+vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                          const int64_t* splits, int64_t row_elems,
+                          vcoll_msg* msgs, int64_t cap, int64_t* n_msgs,
+                          int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps);
+
+/*
+ * MoE dispatch plan ([NCC] 7.4: every (token, chosen expert) pair is one row
+ * sent to the rank holding that expert). Host only, integers only.
+ * topk_ids: host int32 [p][tokens][topk], expert ids in
+ * [0, p*experts_per_rank); expert e lives on rank e / experts_per_rank.
+ * Rank i sends its rows ordered by (destination rank, expert, token).
+ * Outputs (host): splits [p*p] int64 rows i -> j; src_rows [p][tokens*topk]
+ * int32, the token each sent row copies; dst_rows [p][tokens*topk] int32,
+ * the (token, slot) position token*topk + slot each returning row lands on
+ * at combine. Dispatch is vcoll_all_to_all(splits, src_rows = src_rows);
+ * combine is vcoll_all_to_all(splits transposed, dst_rows = dst_rows).
+ */
+vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
+                            const int32_t* topk_ids, int64_t* splits,
+                            int32_t* src_rows, int32_t* dst_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VCOLL_H */

@@ -1,0 +1,231 @@
+"""Host-side checks of libvcoll that need no GPU.
+
+The library loads on a machine without a GPU; these tests call only its host
+entry points (ledger, chunk bounds, MoE plan) and its argument validation,
+which rejects bad calls before any device work is attempted.
+"""
+import ctypes
+import re
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+vc = pytest.importorskip("collective_communication_algorithms_vcoll_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ALGOS = oracle.ALGOS
+PS = [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 72]
+
+
+def declared_functions():
+    names = []
+    for h in ("vcoll.h", "vcoll_bench.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names += re.findall(r"^(?:[a-z_]+\s*\*?\s+)(vcoll_[a-z_]+)\(", text, flags=re.M)
+        names += re.findall(r"^const char\*\s+(vcoll_[a-z_]+)\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "vcoll_allreduce" in names and "vcoll_ledger" in names and "vcoll_moe_plan" in names
+    lib = ctypes.CDLL(vc.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.vcoll_abi_version() == 1
+
+
+def _oracle_ledger(op, algo, p, n, dtype="f32"):
+    if op == "allreduce":
+        x = [np.zeros(1, dtype=np.float32 if dtype == "f32" else np.uint16)] * p
+        _, led = oracle.allreduce(x, algo, dtype, n=n, lo=0)
+    elif op == "reduce_scatter":
+        x = [np.zeros(1, dtype=np.float32)] * p
+        _, led = oracle.reduce_scatter(x, algo, dtype, n=n, lo=0)
+    else:
+        x = [np.zeros(n, dtype=np.float32) for _ in range(p)]
+        _, led = oracle.all_gather(x, algo, dtype)
+    return led
+
+
+@pytest.mark.parametrize("p", PS)
+@pytest.mark.parametrize("algo", ALGOS)
+def test_allreduce_ledger_matches_oracle(p, algo):
+    for n in (0, 1, p, 3 * p + 2, 1000):
+        for dtype in ("f32", "bf16"):
+            led = _oracle_ledger("allreduce", algo, p, n, dtype)
+            msgs, sent, got, steps = vc.vcoll_ledger("allreduce", algo, p, n, dtype)
+            assert msgs == [tuple(m) for m in led.sorted()], (p, algo, n, dtype)
+            assert sent == led.sent_bytes() and got == led.recv_bytes()
+            assert steps == led.n_steps
+
+
+@pytest.mark.parametrize("p", PS)
+def test_reduce_scatter_and_all_gather_ledgers_match_oracle(p):
+    for n in (1, p, 5 * p + 3):
+        led = _oracle_ledger("reduce_scatter", "ring", p, n)
+        msgs, sent, _, steps = vc.vcoll_ledger("reduce_scatter", "ring", p, n)
+        assert msgs == [tuple(m) for m in led.sorted()] and steps == led.n_steps
+        led = _oracle_ledger("all_gather", "ring", p, n)
+        msgs, sent, _, steps = vc.vcoll_ledger("all_gather", "ring", p, n)
+        assert msgs == [tuple(m) for m in led.sorted()] and steps == led.n_steps
+        if p & (p - 1) == 0:
+            led = _oracle_ledger("reduce_scatter", "rabenseifner", p, n)
+            msgs, _, _, _ = vc.vcoll_ledger("reduce_scatter", "rabenseifner", p, n)
+            assert msgs == [tuple(m) for m in led.sorted()]
+            led = _oracle_ledger("all_gather", "rd", p, n)
+            msgs, _, _, _ = vc.vcoll_ledger("all_gather", "rd", p, n)
+            assert msgs == [tuple(m) for m in led.sorted()]
+
+
+@pytest.mark.parametrize("p", [1, 2, 3, 8, 16])
+def test_all_to_all_ledger_matches_oracle(p):
+    rng = np.random.default_rng(p)
+    splits = rng.integers(0, 6, size=(p, p))
+    H = 5
+    send = [np.zeros((int(splits[i].sum()), H), dtype=np.uint16) for i in range(p)]
+    _, led = oracle.all_to_all(send, splits, "bf16")
+    msgs, sent, got, steps = vc.vcoll_ledger("all_to_all", "ring", p, 0, "bf16", splits=splits, row_elems=H)
+    assert msgs == [tuple(m) for m in led.sorted()]
+    assert sent == led.sent_bytes() and got == led.recv_bytes() and steps == led.n_steps
+
+
+def test_headline_ledger_closed_form():
+    msgs, sent, got, steps = vc.vcoll_ledger("allreduce", "ring", 8, 6_553_600, "f32")
+    assert sent == [45_875_200] * 8 and got == sent and steps == 14 and len(msgs) == 112
+    msgs, sent, _, steps = vc.vcoll_ledger("allreduce", "rabenseifner", 16, 100_663_296, "bf16")
+    assert sent == [377_487_360] * 16 and steps == 8
+    msgs, sent, _, steps = vc.vcoll_ledger("allreduce", "ring", 16, 100_663_296, "bf16")
+    assert sent == [377_487_360] * 16 and steps == 30
+
+
+@pytest.mark.parametrize("p,n", [(1, 0), (1, 5), (4, 3), (8, 6_553_600), (72, 1000), (128, 129)])
+def test_chunk_bounds_match_oracle(p, n):
+    offs = oracle.chunk_bounds(n, p)
+    for c in range(p):
+        assert vc.vcoll_chunk(p, n, c) == (offs[c], offs[c + 1] - offs[c])
+
+
+def test_moe_plan_matches_oracle():
+    p, T, E, K = 8, 512, 256, 8
+    topk = [workloads.moe_topk(r, T, E, K) for r in range(p)]
+    splits, src, dst = vc.vcoll_moe_plan(np.stack(topk), E // p)
+    o_splits, o_src, o_dst = oracle.moe_plan(topk, E // p)
+    assert np.array_equal(splits, o_splits)
+    for i in range(p):
+        assert np.array_equal(src[i], o_src[i]) and np.array_equal(dst[i], o_dst[i])
+
+
+def test_moe_plan_rejects_bad_expert_ids():
+    ids = np.zeros((2, 4, 2), dtype=np.int32)
+    ids[1, 2, 1] = 99
+    with pytest.raises(vc.VcollError) as e:
+        vc.vcoll_moe_plan(ids, 4)
+    assert e.value.status == 1
+
+
+# ------------------------------------------------------------- validation (no launch happens)
+
+def _lib():
+    return vc._lib()
+
+
+def _ptrs(p, value=0x1000):
+    arr = (ctypes.c_void_p * p)()
+    for i in range(p):
+        arr[i] = value + 256 * i
+    return arr
+
+
+@pytest.mark.parametrize("fn", ["vcoll_allreduce", "vcoll_reduce_scatter", "vcoll_all_gather"])
+def test_reduce_validation_errors(fn):
+    f = getattr(_lib(), fn)
+    ok_algo = 0
+    # p out of range, negative n, bad dtype, bad algo, NULL pointers
+    assert f(ok_algo, 0, 8, 0, _ptrs(1), _ptrs(1), None) == 1
+    assert f(ok_algo, 129, 8, 0, _ptrs(129), _ptrs(129), None) == 1
+    assert f(ok_algo, 4, -1, 0, _ptrs(4), _ptrs(4), None) == 1
+    assert f(ok_algo, 4, 8, 7, _ptrs(4), _ptrs(4), None) == 1
+    assert f(9, 4, 8, 0, _ptrs(4), _ptrs(4), None) == 1
+    assert f(ok_algo, 4, 8, 0, None, _ptrs(4), None) == 1
+    holes = _ptrs(4)
+    holes[2] = None
+    assert f(ok_algo, 4, 8, 0, _ptrs(4), holes, None) == 1
+    # n == 0 is a no-op and never touches the pointers
+    assert f(ok_algo, 4, 0, 0, None, None, None) == 0
+
+
+def test_unsupported_combinations():
+    lib = _lib()
+    P = _ptrs(8)
+    assert lib.vcoll_reduce_scatter(1, 8, 64, 0, P, P, None) == 2      # RS + recursive doubling
+    assert lib.vcoll_reduce_scatter(3, 8, 64, 0, P, P, None) == 2      # RS + tree
+    assert lib.vcoll_reduce_scatter(2, 6, 64, 0, P, P, None) == 2      # RS + Rabenseifner, p = 6
+    assert lib.vcoll_all_gather(2, 8, 64, 0, P, P, None) == 2          # AG + Rabenseifner
+    assert lib.vcoll_all_gather(3, 8, 64, 0, P, P, None) == 2          # AG + tree
+    assert lib.vcoll_all_gather(1, 6, 64, 0, P, P, None) == 2          # AG + RD, p = 6
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_ledger("reduce_scatter", "rd", 8, 64)
+
+
+def test_all_to_all_validation_errors():
+    lib = _lib()
+    p = 3
+    sp = (ctypes.c_int64 * 9)(*([1] * 9))
+    P = _ptrs(p)
+    tab = (ctypes.c_int64 * p)(1, 1, 1)
+    assert lib.vcoll_all_to_all(p, 4, 0, None, P, P, None, tab, None, tab, None) == 1   # no splits
+    neg = (ctypes.c_int64 * 9)(*([1] * 8 + [-1]))
+    assert lib.vcoll_all_to_all(p, 4, 0, neg, P, P, None, tab, None, tab, None) == 1
+    assert lib.vcoll_all_to_all(p, -4, 0, sp, P, P, None, tab, None, tab, None) == 1
+    holes = _ptrs(p)
+    holes[1] = None
+    assert lib.vcoll_all_to_all(p, 4, 0, sp, holes, P, None, tab, None, tab, None) == 1
+    gather = (ctypes.c_void_p * p)(0x2000, None, None)
+    assert lib.vcoll_all_to_all(p, 4, 0, sp, P, P, gather, None, None, tab, None) == 1   # no table rows
+    zero = (ctypes.c_int64 * 9)()
+    assert lib.vcoll_all_to_all(p, 4, 0, zero, None, None, None, None, None, None, None) == 0
+
+
+def test_ledger_two_call_protocol_and_errors():
+    lib = _lib()
+    n = ctypes.c_int64()
+    assert lib.vcoll_ledger(0, 0, 4, 16, 0, None, 0, None, 0, ctypes.byref(n), None, None, None) == 0
+    assert n.value == 24
+    small = (vc.Msg * 3)()
+    assert lib.vcoll_ledger(0, 0, 4, 16, 0, None, 0, small, 3, ctypes.byref(n), None, None, None) == 3
+    assert n.value == 24
+    assert lib.vcoll_ledger(0, 0, 0, 16, 0, None, 0, None, 0, ctypes.byref(n), None, None, None) == 1
+    assert lib.vcoll_ledger(3, 0, 4, 16, 0, None, 0, None, 0, ctypes.byref(n), None, None, None) == 1
+    assert lib.vcoll_ledger(0, 0, 4, 16, 0, None, 0, None, 0, None, None, None, None) == 1
+
+
+def test_chunk_validation():
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_chunk(4, 10, 4)
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_chunk(0, 10, 0)
+
+
+def test_status_strings():
+    lib = _lib()
+    for s in range(5):
+        assert lib.vcoll_status_str(s)
+    assert lib.vcoll_status_str(42) == b"unknown status"
+
+
+def test_one_hip_runtime_in_the_process():
+    # torch bundles its own HIP runtime under the same soname as the system
+    # one; libvcoll must bind to the copy torch uses, never load a second one
+    import torch  # noqa: F401
+    vc._lib()
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    assert len(paths) == 1, paths
