@@ -1,0 +1,397 @@
+#!/usr/bin/env python
+"""Benchmark of the single-GPU virtual-cluster collectives on MI355X.
+
+Headline: the DDP gradient-bucket all-reduce -- p = 8 logical ranks, 25 MiB
+of float32 per rank (6,553,600 elements, normal(0, 1e-3), 25 MB buckets as in
+PyTorch DDP's bucket_cap_mb), ring order rank 0 -> 1 -> .. -> 7, reduce-scatter
+and all-gather fused into one HBM pass. One step is one such all-reduce.
+
+value: whole-job effective HBM bandwidth = algorithmic bytes per step
+(p*S read + p*S written = 419,430,400 B) x steps / wall time of the timed
+steps. Inputs live in HBM; the steps cycle through several input/output
+sets whose total exceeds the 256 MB Infinity Cache, so no step reads what
+the previous one left in cache.
+
+roofline.achieved: the same algorithmic bytes / the kernel's mean launch
+duration: HIP events on the launch stream around the timed region, divided
+by the number of launches. roofline.traffic: HBM bytes per launch from rocprofv3 counters
+(profiles/ summary of the same kernel source), or null.
+
+cpu_baseline: the CPU oracle (step-by-step numpy ring with its message
+ledger) on the same workload, on this host, one thread.
+
+Extras (not the headline): other algorithms and the unfused reduce-scatter +
+all-gather pair on the same bucket, the plain-copy ceiling, the p = 16 x
+192 MiB bfloat16 workload, MoE dispatch/combine, and decode/prefill-sized
+messages.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "all-reduce effective HBM GB/s (p=8, 25 MB/rank fp32) + % of HBM roofline"
+PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
+MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
+KERNEL_SOURCES = ("kernels.hip", "kernels.h", "order.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "collective_communication_algorithms_vcoll_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_key: str):
+    """HBM bytes per launch measured by rocprofv3 for this kernel source, if any."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(kernel_key)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_launches(calls, steps, warmup):
+    """Run calls[k % len(calls)] steps times after warmup, back to back on
+    the current stream. Returns (wall seconds of the timed steps, mean launch
+    ms): HIP events recorded on the launch stream at the start and end of
+    the timed region, divided by the number of launches. (An event pair
+    around every launch would add its own ~7 us per launch on this GPU.)"""
+    import torch
+    for k in range(warmup):
+        calls[k % len(calls)]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        calls[k % len(calls)]()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / steps
+
+
+def rate(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def sets_for(bytes_per_set: int) -> int:
+    """Input/output sets to cycle so that consecutive reuse is out of cache."""
+    return max(2, -(-4 * MALL_BYTES // bytes_per_set))
+
+
+def headline(vc, torch, args):
+    import numpy as np
+    import workloads
+    cfg = workloads.DDP_BUCKET
+    p, n = cfg["p"], cfg["n"]
+    x = workloads.rank_buffers(cfg["tag"], p, n, cfg["dist"], cfg["dtype"])
+    base = torch.from_numpy(np.stack(x)).cuda()
+    S = n * 4
+    nbytes = 2 * p * S
+    R = sets_for(nbytes)
+    ins = [base.clone() for _ in range(R)]
+    outs = [torch.empty_like(base) for _ in range(R)]
+    calls = [vc.prepare_allreduce("ring", ins[i], outs[i]) for i in range(R)]
+    wall, mean_ms = time_launches(calls, args.steps, args.warmup)
+    result = outs[(args.steps - 1) % R].cpu().numpy()       # written by the last timed launch
+    return dict(x=x, p=p, n=n, S=S, nbytes=nbytes, sets=R, wall=wall, mean_ms=mean_ms,
+                result=result, base=base)
+
+
+def cpu_baseline(h, seconds):
+    import numpy as np
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    out = None
+    while True:
+        out, _ = oracle.allreduce(h["x"], "ring", "f32")
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    parity = all(np.array_equal(out[r].view(np.uint32), h["result"][r].view(np.uint32)) for r in range(h["p"]))
+    return {
+        "value": round(h["nbytes"] * reps / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{reps} full ring all-reduces of the same bucket (p=8 x 6,553,600 fp32), "
+                  f"{el:.1f} s, numpy single thread, host has {len(os.sched_getaffinity(0))} cores",
+    }, parity
+
+
+def extras(vc, torch, h, args):
+    import numpy as np
+    import workloads
+    ex = {}
+    p, n, S = h["p"], h["n"], h["S"]
+    base = h["base"]
+    steps, warm = max(20, args.steps // 4), 5
+
+    # other algorithms on the same bucket (fused, one pass each)
+    R = sets_for(2 * p * S)
+    ins = [base.clone() for _ in range(R)]
+    outs = [torch.empty_like(base) for _ in range(R)]
+    for algo in ("rd", "rabenseifner", "tree"):
+        calls = [vc.prepare_allreduce(algo, ins[i], outs[i]) for i in range(R)]
+        _, mean_ms = time_launches(calls, steps, warm)
+        ex[f"ddp_bucket_{algo}_fused"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    # warm: one set reused back to back (partly served by the Infinity Cache)
+    call = vc.prepare_allreduce("ring", ins[0], outs[0])
+    _, mean_ms = time_launches([call], steps, warm)
+    ex["ddp_bucket_ring_fused_warm_cache"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    # unfused ring: reduce-scatter kernel then all-gather kernel
+    rs_out = [[torch.empty(n // p, device="cuda") for _ in range(p)] for _ in range(R)]
+    rs = [vc.prepare_reduce_scatter("ring", ins[i], rs_out[i]) for i in range(R)]
+    ag = [vc.prepare_all_gather("ring", rs_out[i], outs[i]) for i in range(R)]
+    pair = [lambda i=i: (rs[i](), ag[i]()) for i in range(R)]
+    _, mean_ms = time_launches(pair, steps, warm)
+    ex["ddp_bucket_ring_unfused_rs_then_ag"] = {"GBps": rate(2 * p * S + 2 * S, mean_ms),
+                                                "us": round(mean_ms * 1e3, 1),
+                                                "algorithmic_bytes": 2 * p * S + 2 * S}
+    # plain copy ceiling over the same bytes (p*S read, p*S written)
+    src = [torch.empty(p * n, device="cuda") for _ in range(R)]
+    dst = [torch.empty(p * n, device="cuda") for _ in range(R)]
+    copies = [vc.prepare_bench_copy(dst[i], src[i]) for i in range(R)]
+    _, mean_ms = time_launches(copies, steps, warm)
+    ex["copy_ceiling_same_bytes"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    del ins, outs, rs_out, src, dst
+    torch.cuda.empty_cache()
+
+    # decode-like (10 KiB) and prefill-like (80 MiB) messages, p = 8
+    for label, nbytes in (("decode_10KiB", 10 * 1024), ("prefill_80MiB", 80 * 2 ** 20)):
+        m = nbytes // 4
+        g = torch.Generator(device="cuda").manual_seed(5)
+        t = torch.randn((8, m), device="cuda", generator=g)
+        R2 = sets_for(2 * 8 * nbytes)
+        ts = [t.clone() for _ in range(R2)]
+        os_ = [torch.empty_like(t) for _ in range(R2)]
+        for algo in ("ring", "rd", "rabenseifner", "tree"):
+            calls = [vc.prepare_allreduce(algo, ts[i], os_[i]) for i in range(R2)]
+            _, mean_ms = time_launches(calls, steps, warm)
+            ex[f"p8_{label}_{algo}"] = {"GBps": rate(2 * 8 * nbytes, mean_ms), "us": round(mean_ms * 1e3, 2)}
+        del t, ts, os_
+    torch.cuda.empty_cache()
+
+    # p = 16, 192 MiB bf16 per rank, float32 accumulation
+    P16, N16 = 16, 100_663_296
+    g = torch.Generator(device="cuda").manual_seed(3)
+    t16 = (torch.rand((P16, N16), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
+    o16 = torch.empty_like(t16)
+    S16 = N16 * 2
+    for algo in ("ring", "rabenseifner"):
+        call = vc.prepare_allreduce(algo, t16, o16)
+        _, mean_ms = time_launches([call], 10, 2)
+        ex[f"hier16_bf16_{algo}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
+    for algo, ag_algo in (("ring", "ring"), ("rabenseifner", "rd")):
+        call = vc.prepare_reduce_scatter(algo, t16, rs16)
+        _, ms_rs = time_launches([call], 10, 2)
+        call = vc.prepare_all_gather(ag_algo, rs16, o16)
+        _, ms_ag = time_launches([call], 10, 2)
+        ex[f"hier16_bf16_{algo}_reduce_scatter"] = {"GBps": rate(P16 * S16 + S16, ms_rs), "us": round(ms_rs * 1e3, 1)}
+        ex[f"hier16_bf16_{ag_algo}_all_gather"] = {"GBps": rate(S16 + P16 * S16, ms_ag), "us": round(ms_ag * 1e3, 1)}
+    del t16, o16, rs16
+    torch.cuda.empty_cache()
+
+    # MoE dispatch (fused gather) and combine (fused scatter), p = 8
+    M = workloads.MOE
+    p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
+    splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
+    srcs = [torch.from_numpy(src_rows[i]).cuda() for i in range(p8)]
+    dsts = [torch.from_numpy(dst_rows[i]).cuda() for i in range(p8)]
+    rb = H * 2
+    rows = int(splits.sum())
+    recv = vc.vcoll_all_to_all(toks, splits, src_rows=srcs)
+    back = vc.vcoll_all_to_all(recv, splits.T, dst_rows=dsts, dst_table_rows=[T * K] * p8)
+    disp = lambda: vc.vcoll_all_to_all(toks, splits, recv=recv, src_rows=srcs)          # noqa: E731
+    comb = lambda: vc.vcoll_all_to_all(recv, splits.T, recv=back, dst_rows=dsts)         # noqa: E731
+    _, ms_d = time_launches([disp], 10, 2)
+    _, ms_c = time_launches([comb], 10, 2)
+    ok = all(torch.equal(back[i].view(T, K, H).view(torch.int16),
+                         toks[i].view(torch.int16).unsqueeze(1).expand(T, K, H)) for i in range(p8))
+    ex["moe_dispatch_fused_gather"] = {"GBps": rate(p8 * T * rb + rows * rb, ms_d), "us": round(ms_d * 1e3, 1),
+                                       "algorithmic_bytes": p8 * T * rb + rows * rb,
+                                       "rows_to_rank0": float(splits[:, 0].sum() / rows)}
+    ex["moe_combine_fused_scatter"] = {"GBps": rate(2 * rows * rb, ms_c), "us": round(ms_c * 1e3, 1),
+                                       "algorithmic_bytes": 2 * rows * rb,
+                                       "combine_of_dispatch_is_identity": bool(ok)}
+    return ex
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+
+def _csv_rows(root: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True):
+        with open(path, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+HEADLINE_KERNEL = "reduce_kernel<0, 0, 8, 2, false>"
+COPY_KERNEL = "copy_kernel"
+
+
+def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: str) -> int:
+    """Kernel-trace statistics and FETCH_SIZE / WRITE_SIZE counters of the
+    headline kernel, scaled by the same counters of the plain copy kernel of
+    known size, written to profiles/. If TRACE_DIR holds bench.json (the JSON
+    line the profiled command printed), the events-based mean launch time of
+    that same run is set beside rocprof's."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    lines = [f"# rocprofv3 kernel statistics: headline ring all-reduce (p=8, 25 MiB fp32/rank)", "",
+             f"Command: `{command}`", "", "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    bench_json = os.path.join(trace_dir, "bench.json")
+    rocprof_avg = None
+    for r in stats:
+        name = r.get('Name', r.get('KernelName', '?'))
+        lines.append(f"| {name[:90]} | {r.get('Calls')} | "
+                     f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} |")
+        if HEADLINE_KERNEL in name:
+            rocprof_avg = float(r["AverageNs"]) / 1e3
+    if rocprof_avg is not None and os.path.exists(bench_json):
+        with open(bench_json) as f:
+            run = json.loads(f.read().strip().splitlines()[-1])
+        ev = run["roofline"]["mean_launch_us"]
+        lines += ["", f"Same run: bench.py events mean launch {ev} us, rocprofv3 average {rocprof_avg:.2f} us "
+                      f"(the profiler's average includes the {run['warmup']} warm-up launches); "
+                      f"roofline.achieved {run['roofline']['achieved']} GB/s by events, "
+                      f"{419430400 / (rocprof_avg * 1e-6) / 1e9:.1f} GB/s by rocprofv3."]
+
+    def per_dispatch(root, counter):
+        out = {}
+        for r in _csv_rows(root, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            key = "headline" if HEADLINE_KERNEL in name else ("copy" if COPY_KERNEL in name else None)
+            if key:
+                out.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+    traffic = None
+    if "headline" in fetch and "copy" in fetch and "headline" in write and "copy" in write:
+        p, n = 8, 6_553_600
+        copy_bytes = p * n * 4                      # read, and again written, by one copy launch
+        f_scale = copy_bytes / fetch["copy"]
+        w_scale = copy_bytes / write["copy"]
+        traffic = round(fetch["headline"] * f_scale + write["headline"] * w_scale)
+        lines += ["", "## HBM traffic from counters (per launch)", "",
+                  f"FETCH_SIZE headline {fetch['headline']:.0f}, copy {fetch['copy']:.0f} "
+                  f"(copy reads {copy_bytes} B: scale {f_scale:.2f} B/unit)",
+                  f"WRITE_SIZE headline {write['headline']:.0f}, copy {write['copy']:.0f} "
+                  f"(copy writes {copy_bytes} B: scale {w_scale:.2f} B/unit)",
+                  f"headline traffic {traffic} B per launch vs 419430400 algorithmic "
+                  f"({traffic / 419430400:.3f}x)"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "ring_allreduce_f32_p8_25MiB.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(tpath)) if os.path.exists(tpath) else {}
+    data["ring_f32_p8_ddp_bucket"] = {"source_hash": kernel_source_hash(), "bytes_per_launch": traffic,
+                                      "fetch_units": fetch, "write_units": write}
+    with open(tpath, "w") as f:
+        json.dump(data, f, indent=1)
+    print("\n".join(lines))
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="K",
+                    help="after the headline, launch the plain copy K times over the headline's "
+                         "bytes (a known-size kernel to scale hardware counter readings)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 output directories into profiles/ summaries and exit")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
+    args = ap.parse_args()
+    if args.summarize_profile:
+        return summarize_profile(*args.summarize_profile, args.profile_command)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py: --gpus {args.gpus} requested; this build runs its p logical ranks inside one "
+                  "GPU's HBM (a single-GPU virtual cluster) and measures one GPU only.", file=sys.stderr)
+        return 2
+
+    import torch
+    import collective_communication_algorithms_vcoll_amd as vc
+
+    torch.cuda.set_device(0)
+    h = headline(vc, torch, args)
+    value = h["nbytes"] * args.steps / h["wall"] / 1e9
+    achieved = h["nbytes"] / (h["mean_ms"] * 1e-3) / 1e9
+    traffic = counter_traffic("ring_f32_p8_ddp_bucket")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["wall"] * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded normal(0, 1e-3) float32 rank buffers",
+        "config": {
+            "workload": "DDP gradient-bucket all-reduce: p=8 logical ranks x 25 MiB fp32 "
+                        "(6,553,600 elements) per rank, ring order 0->1->..->7, "
+                        "reduce-scatter + all-gather fused in one pass",
+            "p": h["p"], "elements_per_rank": h["n"], "algorithm": "ring",
+            "algorithmic_bytes_per_step": h["nbytes"], "buffer_sets_cycled": h["sets"],
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": "reduce_kernel<f32, ring, p=8>", "mean_launch_us": round(h["mean_ms"] * 1e3, 2),
+        },
+    }
+    if args.copy_reference:
+        p, n = h["p"], h["n"]
+        src, dst = torch.empty(p * n, device="cuda"), torch.empty(p * n, device="cuda")
+        call = vc.prepare_bench_copy(dst, src)
+        time_launches([call], args.copy_reference, 1)
+        line["copy_reference"] = {"bytes_read": p * n * 4, "bytes_written": p * n * 4,
+                                  "launches": args.copy_reference + 1}
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline(h, args.cpu_seconds)
+        line["cpu_baseline"] = cb
+        line["parity_vs_oracle"] = "bit-exact" if parity else "MISMATCH"
+    if not args.no_extras:
+        line["extras"] = extras(vc, torch, h, args)
+    print(json.dumps(line), flush=True)
+    return 0 if line.get("parity_vs_oracle", "bit-exact") == "bit-exact" else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -335,3 +335,44 @@ def vcoll_bench_copy(dst, src) -> None:
         raise ValueError("vcoll_bench_copy: size mismatch")
     _check(_lib().vcoll_bench_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(src)),
            "vcoll_bench_copy")
+
+
+class PreparedCall:
+    """A collective whose arguments were validated and marshalled once; each
+    call enqueues it again on the stream captured at preparation."""
+
+    def __init__(self, name: str, fn, args: tuple, keep: tuple):
+        self._name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args), self._name)
+
+
+def prepare_allreduce(algo, send, recv) -> PreparedCall:
+    s, r = _ranks(send), _ranks(recv)
+    vcoll_allreduce(algo, send, recv)            # validates (and runs) once
+    sp, rp = _ptrs(s), _ptrs(r)
+    args = (_algo(algo), len(s), s[0].numel(), _dtype_code(s[0]), sp, rp, _stream(s[0]))
+    return PreparedCall("vcoll_allreduce", _lib().vcoll_allreduce, args, (send, recv, sp, rp))
+
+
+def prepare_reduce_scatter(algo, send, recv) -> PreparedCall:
+    s, r = _ranks(send), list(recv)
+    vcoll_reduce_scatter(algo, send, recv)
+    sp, rp = _ptrs(s), _ptrs(r)
+    args = (_algo(algo), len(s), s[0].numel(), _dtype_code(s[0]), sp, rp, _stream(s[0]))
+    return PreparedCall("vcoll_reduce_scatter", _lib().vcoll_reduce_scatter, args, (send, recv, sp, rp))
+
+
+def prepare_all_gather(algo, send, recv) -> PreparedCall:
+    s, r = _ranks(send), _ranks(recv)
+    vcoll_all_gather(algo, send, recv)
+    sp, rp = _ptrs(s), _ptrs(r)
+    args = (_algo(algo), len(s), s[0].numel(), _dtype_code(s[0]), sp, rp, _stream(s[0]))
+    return PreparedCall("vcoll_all_gather", _lib().vcoll_all_gather, args, (send, recv, sp, rp))
+
+
+def prepare_bench_copy(dst, src) -> PreparedCall:
+    vcoll_bench_copy(dst, src)
+    args = (dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), _stream(src))
+    return PreparedCall("vcoll_bench_copy", _lib().vcoll_bench_copy, args, (dst, src))
