@@ -22,6 +22,11 @@ namespace vcoll {
 
 constexpr int kBlock = 256;          // threads per workgroup (4 waves)
 constexpr int kA2ABlocks = 64;       // all-to-all blocks described per launch
+constexpr int kFixedMax = 16;        // largest p with a compile-time order program
+
+// The p values with reduce kernels specialised at compile time; every other
+// p runs the kernel that reads its order program at run time.
+constexpr bool has_fixed_kernel(int p) { return p == 2 || p == 4 || p == 8 || p == 16; }
 
 struct RankPtrs {
   const void* src[kMaxRanks];
@@ -29,12 +34,19 @@ struct RankPtrs {
 };
 
 // Reduce (all-reduce / reduce-scatter). Grid: x = tiles of a chunk, y = chunk.
+// For has_fixed_kernel(p), leaf[c * kFixedMax + k] is the buffer of the k-th input
+// in chunk c's summation order (the host resolves the ring's per-chunk
+// rotation and the trees' leaf order), so a workgroup fetches its p source
+// pointers with one wide scalar load. For any other p, leaf[r] = send[r] and
+// the kernel resolves the order itself.
 struct ReduceArgs {
-  RankPtrs ptr;
+  const void* leaf[kFixedMax * kFixedMax];
+  void* dst[kMaxRanks];
   int64_t q, r;               // chunk c: off = c*q + min(c, r), count = q + (c < r)
   int32_t p;
   int32_t vec;                // every pointer 16-byte aligned: vector path allowed
   int32_t final_merges;       // order program (used when p is not compiled in)
+  int32_t pace;               // space out the p-way store fan-out (large grids)
   uint8_t rank[kMaxRanks];
   uint8_t merges[kMaxRanks];
 };

@@ -128,13 +128,57 @@ __device__ __forceinline__ void run_program(float (&st)[SD][N], const Leaf& leaf
   }
 }
 
-template <int ALGO, int P, int K>
-__device__ __forceinline__ int leaf_rank(int rot) {
-  if constexpr (ALGO == VCOLL_RING) {
-    return (rot + K) % P;   // the chain starts right after the chunk's owner
-  } else {
-    return Prog<ALGO, P>::value.rank[K];
-  }
+// Stack entries alive before leaf K is pushed.
+template <int ALGO, int P>
+constexpr int depth_before(int K) {
+  int d = 0;
+  for (int j = 0; j < K; ++j) d += 1 - Prog<ALGO, P>::value.merges[j];
+  return d;
+}
+
+// Push leaf K (already widened) and apply its merges; after the last leaf,
+// the final collapse.
+template <int ALGO, int P, int K, int SD, int N>
+__device__ __forceinline__ void push_leaf(float (&st)[SD][N], const float (&v)[N]) {
+  constexpr int D = depth_before<ALGO, P>(K);
+  constexpr int M = Prog<ALGO, P>::value.merges[K];
+#pragma unroll
+  for (int i = 0; i < N; ++i) st[D][i] = v[i];
+  merge_top<D + 1, M>(st);
+  if constexpr (K == P - 1) merge_top<D + 1 - M, Prog<ALGO, P>::value.final_merges>(st);
+}
+
+// Ranks whose loads a wave keeps in flight ahead of the one it is adding.
+// Issuing all p ranks at once makes the p-way streams collide in the DRAM
+// rows more than a pipeline of a few ranks does. Build-time override:
+// -DVCOLL_LAG=<n>.
+#ifndef VCOLL_LAG
+#define VCOLL_LAG 2
+#endif
+template <int P>
+constexpr int load_lag() { return VCOLL_LAG < P ? VCOLL_LAG : P; }
+
+// Store pacing: with a.pace set, a wave pauses about 64*VCOLL_STORE_SLEEP
+// cycles between the p ranks it stores to. When every wave of a large grid
+// bursts its p loads and then its p-way store fan-out at once, the streams
+// collide in the DRAM rows; spacing the stores out raised the p = 8
+// all-reduce by 3% (25 MiB per rank) to 8% (80 MiB), the p = 16 bf16 one by
+// 1-3%, on MI355X. Small, latency-bound launches lose, so the host sets
+// a.pace only for grids that fill the chip several times over. (The
+// all-gather, one load per p stores, does not gain.)
+// -DVCOLL_LOAD_SLEEP=<n> pauses between the ranks loaded (an experiment).
+#ifndef VCOLL_STORE_SLEEP
+#define VCOLL_STORE_SLEEP 4
+#endif
+#ifndef VCOLL_LOAD_SLEEP
+#define VCOLL_LOAD_SLEEP 0
+#endif
+
+// Row of leaf pointers of chunk c (p compiled in): the ring's order rotates
+// with the chunk, the trees' order is the same for every chunk (row 0).
+template <int ALGO>
+__device__ __forceinline__ const void* const* leaf_row(const ReduceArgs& a, int c) {
+  return &a.leaf[(ALGO == VCOLL_RING ? c : 0) * kFixedMax];
 }
 
 // ----------------------------------------------------------------------------
@@ -173,10 +217,11 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
   using E = typename S::elem;
   float result;
   if constexpr (P > 0) {
+    const void* const* L = leaf_row<ALGO>(a, c);
     E raw[P];
     static_for<0, P>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      raw[k] = static_cast<const E*>(a.ptr.src[leaf_rank<ALGO, P, k>(rot)])[e];
+      raw[k] = static_cast<const E*>(L[k])[e];
     });
     float st[Prog<ALGO, P>::depth][1];
     run_program<ALGO, P, 0, 0>(st, [&](auto kc, float(&d)[1]) {
@@ -184,13 +229,13 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
     });
     result = st[0][0];
   } else if constexpr (ALGO == VCOLL_RING) {
-    result = S::widen1(static_cast<const E*>(a.ptr.src[rot % p])[e]);
+    result = S::widen1(static_cast<const E*>(a.leaf[rot % p])[e]);
     for (int k = 1; k < p; ++k)
-      result = result + S::widen1(static_cast<const E*>(a.ptr.src[(rot + k) % p])[e]);
+      result = result + S::widen1(static_cast<const E*>(a.leaf[(rot + k) % p])[e]);
   } else {
     float st[kRuntimeDepth][1];
     for (int k = 0; k < p; ++k) {
-      const float v = S::widen1(static_cast<const E*>(a.ptr.src[a.rank[k]])[e]);
+      const float v = S::widen1(static_cast<const E*>(a.leaf[a.rank[k]])[e]);
       rt_push<1>(st, &v);
       for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
     }
@@ -199,9 +244,9 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
   }
   const E out = S::narrow1(result);
   if constexpr (RS) {
-    static_cast<E*>(a.ptr.dst[c])[e - off] = out;
+    static_cast<E*>(a.dst[c])[e - off] = out;
   } else {
-    for (int r = 0; r < p; ++r) static_cast<E*>(a.ptr.dst[r])[e] = out;
+    for (int r = 0; r < p; ++r) static_cast<E*>(a.dst[r])[e] = out;
   }
 }
 
@@ -209,23 +254,43 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
 // V 16-byte vectors per thread, fixed p: all p*V loads are issued before the
 // first add, the order program runs in registers, then p*V (or V) stores.
 
-template <int D, int ALGO, int P, int V, bool RS>
-__device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c, int rot,
+template <int D, int ALGO, int P, int V, bool RS, bool FULL>
+__device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
                                                      const int64_t (&boff)[V],
                                                      const bool (&valid)[V], int64_t out_shift) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
+  constexpr int LAG = load_lag<P>();
+  const void* const* L = leaf_row<ALGO>(a, c);
   u32x4 raw[P][V];
-  static_for<0, P>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    const void* src = a.ptr.src[leaf_rank<ALGO, P, k>(rot)];
-#pragma unroll
-    for (int j = 0; j < V; ++j) raw[k][j] = valid[j] ? ld16(src, boff[j]) : u32x4{0, 0, 0, 0};
-  });
   float st[Prog<ALGO, P>::depth][V * VE];
-  run_program<ALGO, P, 0, 0>(st, [&](auto kc, float(&d)[V * VE]) {
+  // software pipeline in summation order: the loads of leaf k go out, then
+  // leaf k - LAG (whose loads went out LAG steps earlier) is added
+  static_for<0, P + LAG>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k < P) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) S::widen(raw[decltype(kc)::value][j], &d[j * VE]);
+      for (int j = 0; j < V; ++j) {
+        if constexpr (FULL) {
+          raw[k][j] = ld16(L[k], boff[j]);
+        } else {
+          raw[k][j] = valid[j] ? ld16(L[k], boff[j]) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#if VCOLL_LOAD_SLEEP > 0
+    if constexpr (k < P) __builtin_amdgcn_s_sleep(VCOLL_LOAD_SLEEP);
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+    if constexpr (k >= LAG) {
+      constexpr int q = k - LAG;
+      float v[V * VE];
+#pragma unroll
+      for (int j = 0; j < V; ++j) S::widen(raw[q][j], &v[j * VE]);
+      push_leaf<ALGO, P, q>(st, v);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   });
   u32x4 out[V];
 #pragma unroll
@@ -233,13 +298,16 @@ __device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
   if constexpr (RS) {
 #pragma unroll
     for (int j = 0; j < V; ++j)
-      if (valid[j]) st16(a.ptr.dst[c], boff[j] - out_shift, out[j]);
+      if (FULL || valid[j]) st16(a.dst[c], boff[j] - out_shift, out[j]);
   } else {
     static_for<0, P>([&](auto rc) {
-      void* dst = a.ptr.dst[decltype(rc)::value];
+      void* dst = a.dst[decltype(rc)::value];
 #pragma unroll
       for (int j = 0; j < V; ++j)
-        if (valid[j]) st16(dst, boff[j], out[j]);
+        if (FULL || valid[j]) st16(dst, boff[j], out[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (a.pace) __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+      __builtin_amdgcn_sched_barrier(0);
     });
   }
 }
@@ -260,7 +328,7 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
     for (int b = 0; b < B; ++b) {
       if (k0 + b < p) {
         const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : a.rank[k0 + b];
-        raw[b] = valid ? ld16(a.ptr.src[rank], boff) : u32x4{0, 0, 0, 0};
+        raw[b] = valid ? ld16(a.leaf[rank], boff) : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
@@ -291,17 +359,28 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
   if (!valid) return;
   const u32x4 out = S::narrow(acc);
   if constexpr (RS) {
-    st16(a.ptr.dst[c], boff - out_shift, out);
+    st16(a.dst[c], boff - out_shift, out);
   } else {
-    for (int r = 0; r < p; ++r) st16(a.ptr.dst[r], boff, out);
+    for (int r = 0; r < p; ++r) {
+      st16(a.dst[r], boff, out);
+      if (a.pace) __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+    }
   }
 }
 
 // ----------------------------------------------------------------------------
 // the reduce kernel: workgroup (x, y) handles tile x of chunk y
 
+// Build-time override: -DVCOLL_REDUCE_WAVES=<n> asks for at least n waves
+// per SIMD (caps VGPRs per wave accordingly).
+#ifdef VCOLL_REDUCE_WAVES
+#define VCOLL_REDUCE_ATTR __attribute__((amdgpu_waves_per_eu(VCOLL_REDUCE_WAVES)))
+#else
+#define VCOLL_REDUCE_ATTR
+#endif
+
 template <int D, int ALGO, int P, int V, bool RS>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a) {
+__global__ __launch_bounds__(kBlock) VCOLL_REDUCE_ATTR void reduce_kernel(const ReduceArgs a) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
   constexpr int ES = 16 / VE;
@@ -330,7 +409,11 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a) {
           valid[j] = v < nvec;
           boff[j] = (e_base + v * VE) * ES;
         }
-        reduce_vectors_fixed<D, ALGO, P, V, RS>(a, c, rot, boff, valid, off * ES);
+        if ((static_cast<int64_t>(blockIdx.x) + 1) * (V * kBlock) <= nvec) {
+          reduce_vectors_fixed<D, ALGO, P, V, RS, true>(a, c, boff, valid, off * ES);
+        } else {
+          reduce_vectors_fixed<D, ALGO, P, V, RS, false>(a, c, boff, valid, off * ES);
+        }
       } else {
 #pragma unroll 1
         for (int j = 0; j < V; ++j) {
@@ -476,10 +559,20 @@ hipError_t launch(K kernel, dim3 grid, const Arg& arg, hipStream_t stream) {
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kBlock), args, 0, stream);
 }
 
+// 16-byte vectors per thread of the reduce kernel (all are loaded before the
+// first add). Build-time override: -DVCOLL_V_P8=<n> for p = 8.
+#ifndef VCOLL_V_P8
+#define VCOLL_V_P8 2
+#endif
 template <int P>
 constexpr int vectors_per_thread() {
-  return P == 0 ? 1 : (P <= 4 ? 4 : (P <= 8 ? 2 : 1));
+  return P == 0 ? 1 : (P <= 4 ? 4 : (P <= 8 ? VCOLL_V_P8 : 1));
 }
+
+// Workgroups from which a launch paces its stores (see VCOLL_STORE_SLEEP).
+#ifndef VCOLL_PACE_MIN_GROUPS
+#define VCOLL_PACE_MIN_GROUPS 2048
+#endif
 
 template <int D, int ALGO, bool RS, int P>
 hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, hipStream_t stream) {
@@ -488,11 +581,15 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, hipStream_t s
   const int64_t per_tile = static_cast<int64_t>(V) * kBlock * VE;
   const int64_t tiles = (max_chunk + per_tile - 1) / per_tile;
   if (tiles == 0) return hipSuccess;
-  return launch(reduce_kernel<D, ALGO, P, V, RS>, dim3(static_cast<unsigned>(tiles), a.p), a, stream);
+  ReduceArgs args = a;
+  args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
+  return launch(reduce_kernel<D, ALGO, P, V, RS>, dim3(static_cast<unsigned>(tiles), a.p), args, stream);
 }
 
 template <int D, int ALGO, bool RS>
 hipError_t launch_reduce_algo(const ReduceArgs& a, int64_t max_chunk, hipStream_t stream) {
+  static_assert(has_fixed_kernel(2) && has_fixed_kernel(4) && has_fixed_kernel(8) && has_fixed_kernel(16),
+                "the host lays out leaf pointers by has_fixed_kernel()");
   switch (a.p) {
     case 2: return launch_reduce_p<D, ALGO, RS, 2>(a, max_chunk, stream);
     case 4: return launch_reduce_p<D, ALGO, RS, 4>(a, max_chunk, stream);

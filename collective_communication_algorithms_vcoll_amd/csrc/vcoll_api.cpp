@@ -57,23 +57,28 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
 
   ReduceArgs a;
   std::memset(&a, 0, sizeof(a));
-  for (int r = 0; r < p; ++r) {
-    a.ptr.src[r] = send[r];
-    a.ptr.dst[r] = recv[r];
-  }
+  for (int r = 0; r < p; ++r) a.dst[r] = recv[r];
   const Chunks ch(n, p);
   a.q = ch.q;
   a.r = ch.r;
   a.p = p;
   a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv));
-  if (algo != VCOLL_RING) {
-    const OrderProgram prog = order_program(algo, p);
-    for (int k = 0; k < p; ++k) {
-      a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
-      a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
-    }
-    a.final_merges = prog.final_merges;
+  const OrderProgram prog = order_program(algo, p);
+  if (has_fixed_kernel(p)) {
+    // leaf pointers in summation order: ring rotated per chunk (chunk c's
+    // chain starts at rank c+1), trees the same for every chunk
+    const int rows = algo == VCOLL_RING ? p : 1;
+    for (int c = 0; c < rows; ++c)
+      for (int k = 0; k < p; ++k)
+        a.leaf[c * kFixedMax + k] = send[algo == VCOLL_RING ? (c + 1 + k) % p : prog.rank[k]];
+  } else {
+    for (int r = 0; r < p; ++r) a.leaf[r] = send[r];
   }
+  for (int k = 0; k < p; ++k) {
+    a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
+    a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
+  }
+  a.final_merges = prog.final_merges;
   return from_hip(launch_reduce(a, dtype, algo, scatter, ch.count(0), static_cast<hipStream_t>(stream)));
 }
 
