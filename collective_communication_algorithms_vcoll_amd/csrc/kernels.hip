@@ -149,16 +149,18 @@ __device__ __forceinline__ void push_leaf(float (&st)[SD][N], const float (&v)[N
 }
 
 // Ranks whose loads a wave keeps in flight ahead of the one it is adding.
-// Issuing all p ranks at once makes the p-way streams collide in the DRAM
-// rows more than a pipeline of a few ranks does. Build-time override:
-// -DVCOLL_LAG=<n>.
+// Large grids (which also pace their stores) issue all p ranks up front;
+// small, latency-bound grids run a pipeline of a few ranks, which measured
+// 10% faster at 1 MiB per rank. Build-time override of the small-grid
+// depth: -DVCOLL_LAG=<n>.
 #ifndef VCOLL_LAG
-#define VCOLL_LAG 2
+#define VCOLL_LAG 4
 #endif
-template <int P>
-constexpr int load_lag() { return VCOLL_LAG < P ? VCOLL_LAG : P; }
+template <int P, bool LARGE>
+constexpr int load_lag() { return LARGE ? P : (VCOLL_LAG < P ? VCOLL_LAG : P); }
 
-// Store pacing: with a.pace set, a wave pauses about 64*VCOLL_STORE_SLEEP
+// Store pacing: in large grids (a.pace; the LARGE kernel variant when p is
+// compiled in) a wave pauses about 64*VCOLL_STORE_SLEEP
 // cycles between the p ranks it stores to. When every wave of a large grid
 // bursts its p loads and then its p-way store fan-out at once, the streams
 // collide in the DRAM rows; spacing the stores out raised the p = 8
@@ -254,13 +256,13 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
 // V 16-byte vectors per thread, fixed p: all p*V loads are issued before the
 // first add, the order program runs in registers, then p*V (or V) stores.
 
-template <int D, int ALGO, int P, int V, bool RS, bool FULL>
+template <int D, int ALGO, int P, int V, bool RS, bool LARGE, bool FULL>
 __device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
                                                      const int64_t (&boff)[V],
                                                      const bool (&valid)[V], int64_t out_shift) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
-  constexpr int LAG = load_lag<P>();
+  constexpr int LAG = load_lag<P, LARGE>();
   const void* const* L = leaf_row<ALGO>(a, c);
   u32x4 raw[P][V];
   float st[Prog<ALGO, P>::depth][V * VE];
@@ -305,9 +307,11 @@ __device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
 #pragma unroll
       for (int j = 0; j < V; ++j)
         if (FULL || valid[j]) st16(dst, boff[j], out[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (a.pace) __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (LARGE) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     });
   }
 }
@@ -379,7 +383,7 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
 #define VCOLL_REDUCE_ATTR
 #endif
 
-template <int D, int ALGO, int P, int V, bool RS>
+template <int D, int ALGO, int P, int V, bool RS, bool LARGE>
 __global__ __launch_bounds__(kBlock) VCOLL_REDUCE_ATTR void reduce_kernel(const ReduceArgs a) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
@@ -410,9 +414,9 @@ __global__ __launch_bounds__(kBlock) VCOLL_REDUCE_ATTR void reduce_kernel(const 
           boff[j] = (e_base + v * VE) * ES;
         }
         if ((static_cast<int64_t>(blockIdx.x) + 1) * (V * kBlock) <= nvec) {
-          reduce_vectors_fixed<D, ALGO, P, V, RS, true>(a, c, boff, valid, off * ES);
+          reduce_vectors_fixed<D, ALGO, P, V, RS, LARGE, true>(a, c, boff, valid, off * ES);
         } else {
-          reduce_vectors_fixed<D, ALGO, P, V, RS, false>(a, c, boff, valid, off * ES);
+          reduce_vectors_fixed<D, ALGO, P, V, RS, LARGE, false>(a, c, boff, valid, off * ES);
         }
       } else {
 #pragma unroll 1
@@ -581,9 +585,16 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, hipStream_t s
   const int64_t per_tile = static_cast<int64_t>(V) * kBlock * VE;
   const int64_t tiles = (max_chunk + per_tile - 1) / per_tile;
   if (tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles), a.p);
   ReduceArgs args = a;
   args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
-  return launch(reduce_kernel<D, ALGO, P, V, RS>, dim3(static_cast<unsigned>(tiles), a.p), args, stream);
+  if constexpr (P > 0) {
+    // the compile-time variant carries the pacing (and its load pipeline)
+    if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true>, grid, args, stream);
+    return launch(reduce_kernel<D, ALGO, P, V, RS, false>, grid, args, stream);
+  } else {
+    return launch(reduce_kernel<D, ALGO, P, V, RS, false>, grid, args, stream);
+  }
 }
 
 template <int D, int ALGO, bool RS>
