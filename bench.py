@@ -248,7 +248,7 @@ def _csv_rows(root: str, suffix: str):
     return rows
 
 
-HEADLINE_KERNEL = "reduce_kernel<0, 0, 8, 2, false>"
+HEADLINE_KERNEL = "reduce_kernel<0, 0, 8, 2, false, true>"
 COPY_KERNEL = "copy_kernel"
 
 
