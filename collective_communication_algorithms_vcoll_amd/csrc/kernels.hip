@@ -168,13 +168,10 @@ constexpr int load_lag() { return LARGE ? P : (VCOLL_LAG < P ? VCOLL_LAG : P); }
 // 1-3%, on MI355X. Small, latency-bound launches lose, so the host sets
 // a.pace only for grids that fill the chip several times over. (The
 // all-gather, one load per p stores, does not gain.)
-// -DVCOLL_LOAD_SLEEP=<n> pauses between the ranks loaded (an experiment).
 #ifndef VCOLL_STORE_SLEEP
 #define VCOLL_STORE_SLEEP 4
 #endif
-#ifndef VCOLL_LOAD_SLEEP
-#define VCOLL_LOAD_SLEEP 0
-#endif
+
 
 // Row of leaf pointers of chunk c (p compiled in): the ring's order rotates
 // with the chunk, the trees' order is the same for every chunk (row 0).
@@ -266,6 +263,7 @@ __device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
   const void* const* L = leaf_row<ALGO>(a, c);
   u32x4 raw[P][V];
   float st[Prog<ALGO, P>::depth][V * VE];
+
   // software pipeline in summation order: the loads of leaf k go out, then
   // leaf k - LAG (whose loads went out LAG steps earlier) is added
   static_for<0, P + LAG>([&](auto kc) {
@@ -281,10 +279,6 @@ __device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-#if VCOLL_LOAD_SLEEP > 0
-    if constexpr (k < P) __builtin_amdgcn_s_sleep(VCOLL_LOAD_SLEEP);
-    __builtin_amdgcn_sched_barrier(0);
-#endif
     if constexpr (k >= LAG) {
       constexpr int q = k - LAG;
       float v[V * VE];
@@ -375,16 +369,8 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
 // ----------------------------------------------------------------------------
 // the reduce kernel: workgroup (x, y) handles tile x of chunk y
 
-// Build-time override: -DVCOLL_REDUCE_WAVES=<n> asks for at least n waves
-// per SIMD (caps VGPRs per wave accordingly).
-#ifdef VCOLL_REDUCE_WAVES
-#define VCOLL_REDUCE_ATTR __attribute__((amdgpu_waves_per_eu(VCOLL_REDUCE_WAVES)))
-#else
-#define VCOLL_REDUCE_ATTR
-#endif
-
 template <int D, int ALGO, int P, int V, bool RS, bool LARGE>
-__global__ __launch_bounds__(kBlock) VCOLL_REDUCE_ATTR void reduce_kernel(const ReduceArgs a) {
+__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
   constexpr int ES = 16 / VE;
