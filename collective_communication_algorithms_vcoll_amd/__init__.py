@@ -79,6 +79,11 @@ def _lib():
                                        P(ctypes.c_int32), P(ctypes.c_int32)]
         lib.vcoll_moe_plan.restype = I
         lib.vcoll_last_hip_error.restype = ctypes.c_char_p
+        D = ctypes.c_double
+        lib.vcoll_model_formula.argtypes = [I, I, D, D, D, P(D)]
+        lib.vcoll_model_formula.restype = I
+        lib.vcoll_model_ledger_time.argtypes = [I, I, I, I64, I, P(I64), I64, D, D, P(D), P(ctypes.c_int32)]
+        lib.vcoll_model_ledger_time.restype = I
         lib.vcoll_bench_copy.argtypes = [VP, VP, I64, VP]
         lib.vcoll_bench_copy.restype = I
         if lib.vcoll_abi_version() != 1:
@@ -311,6 +316,30 @@ def vcoll_ledger(op, algo, p: int, n: int, dtype: str = "f32", splits=None, row_
                             ctypes.byref(count), sent, got, ctypes.byref(steps)), "vcoll_ledger")
     out = [(m.step, m.src, m.dst, m.src_off, m.dst_off, m.count, m.bytes) for m in msgs[:count.value]]
     return out, list(sent), list(got), steps.value
+
+
+def vcoll_model_formula(algo, p: int, nbytes: float, alpha: float, beta: float) -> float:
+    """Closed-form alpha-beta all-reduce time in seconds (see vcoll.h)."""
+    t = ctypes.c_double()
+    _check(_lib().vcoll_model_formula(_algo(algo), p, float(nbytes), float(alpha), float(beta),
+                                      ctypes.byref(t)), "vcoll_model_formula")
+    return t.value
+
+
+def vcoll_model_ledger_time(op, algo, p: int, n: int, alpha: float, beta: float, dtype: str = "f32",
+                            splits=None, row_elems: int = 0) -> tuple:
+    """Simulated alpha-beta clock over the ledger: (seconds, steps)."""
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    dtc = {"f32": F32, "bf16": BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    sp = None
+    if splits is not None:
+        sp_arr = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
+        sp = sp_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    t, steps = ctypes.c_double(), ctypes.c_int32()
+    _check(_lib().vcoll_model_ledger_time(opc, _algo(algo), p, n, dtc, sp, row_elems, float(alpha),
+                                          float(beta), ctypes.byref(t), ctypes.byref(steps)),
+           "vcoll_model_ledger_time")
+    return t.value, steps.value
 
 
 def vcoll_moe_plan(topk_ids: np.ndarray, experts_per_rank: int):

@@ -1,0 +1,90 @@
+// Alpha-beta (Hockney) cost model: closed forms and a simulated clock over
+// the message ledger. Host only.
+//
+// "Networks and Collective Communication" (cs349e prerequisite lecture 5):
+// section 2.1 prices one n-byte message at alpha + n/beta; sections 5.1 and
+// 5.2 (and exercise 2) give the all-reduce closed forms; the lecture's
+// comm_sim advances a clock step by step, which the ledger version does with
+// full-duplex ports (a device sends and receives concurrently at beta).
+#include <algorithm>
+#include <cmath>
+#include <map>
+#include <vector>
+
+#include "schedule.h"
+#include "vcoll.h"
+
+using namespace vcoll;
+
+extern "C" {
+
+vcoll_status vcoll_model_formula(vcoll_algo algo, int p, double bytes, double alpha, double beta,
+                                 double* seconds) {
+  if (p < 1 || p > (1 << 20) || !(bytes >= 0) || !(alpha >= 0) || !(beta > 0) || !seconds)
+    return VCOLL_ERR_INVALID_ARG;
+  if (algo < VCOLL_RING || algo > VCOLL_BINARY_TREE) return VCOLL_ERR_INVALID_ARG;
+  if (p == 1) {
+    *seconds = 0.0;
+    return VCOLL_OK;
+  }
+  const double full = alpha + bytes / beta;
+  switch (algo) {
+    case VCOLL_RING:  // 2(p-1) steps of n/p bytes
+      *seconds = 2.0 * (p - 1) * (alpha + bytes / (p * beta));
+      return VCOLL_OK;
+    case VCOLL_BINARY_TREE: {  // 2 ceil(log2 p) full-vector steps
+      int k = 0;
+      while ((1 << k) < p) ++k;
+      *seconds = 2.0 * k * full;
+      return VCOLL_OK;
+    }
+    default: {
+      // powers of two as printed; otherwise the fold adds a full-vector
+      // pre-step and post-step around the p2 = 2^floor(log2 p) core
+      const int p2 = 1 << floor_log2(p);
+      const int k = floor_log2(p2);
+      const double extra = p2 == p ? 0.0 : 2.0 * full;
+      if (algo == VCOLL_RECURSIVE_DOUBLING) *seconds = k * full + extra;
+      else *seconds = 2.0 * k * alpha + 2.0 * (p2 - 1) / p2 * bytes / beta + extra;
+      return VCOLL_OK;
+    }
+  }
+}
+
+vcoll_status vcoll_model_ledger_time(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                     const int64_t* splits, int64_t row_elems, double alpha, double beta,
+                                     double* seconds, int32_t* n_steps) {
+  if (!(alpha >= 0) || !(beta > 0) || !seconds) return VCOLL_ERR_INVALID_ARG;
+  int64_t count = 0;
+  vcoll_status st = vcoll_ledger(op, algo, p, n, dtype, splits, row_elems, nullptr, 0, &count,
+                                 nullptr, nullptr, nullptr);
+  if (st != VCOLL_OK) return st;
+  std::vector<vcoll_msg> msgs(static_cast<size_t>(std::max<int64_t>(count, 1)));
+  int32_t steps = 0;
+  st = vcoll_ledger(op, algo, p, n, dtype, splits, row_elems, msgs.data(), count, &count, nullptr,
+                    nullptr, &steps);
+  if (st != VCOLL_OK) return st;
+  // per step: bytes each rank sends and receives; the busiest port sets the pace
+  std::map<int32_t, std::pair<std::vector<int64_t>, std::vector<int64_t>>> per_step;
+  for (int64_t i = 0; i < count; ++i) {
+    const vcoll_msg& m = msgs[static_cast<size_t>(i)];
+    auto& slot = per_step[m.step];
+    if (slot.first.empty()) {
+      slot.first.assign(p, 0);
+      slot.second.assign(p, 0);
+    }
+    slot.first[m.src] += m.bytes;
+    slot.second[m.dst] += m.bytes;
+  }
+  double t = 0.0;
+  for (const auto& kv : per_step) {
+    int64_t busiest = 0;
+    for (int r = 0; r < p; ++r) busiest = std::max({busiest, kv.second.first[r], kv.second.second[r]});
+    t += alpha + static_cast<double>(busiest) / beta;
+  }
+  *seconds = t;
+  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
+}
+
+}  // extern "C"

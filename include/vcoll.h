@@ -197,6 +197,31 @@ vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_ran
                             const int32_t* topk_ids, int64_t* splits,
                             int32_t* src_rows, int32_t* dst_rows);
 
+/*
+ * Alpha-beta cost model ([NCC] 2.1: a message of b bytes costs alpha + b/beta,
+ * alpha in seconds, beta in bytes per second). Host only.
+ *
+ * vcoll_model_formula: closed-form all-reduce time for `bytes` per rank
+ * ([NCC] 5.1 and exercise 2: ring 2(p-1)(alpha + bytes/(p beta)); 5.2:
+ * recursive doubling log2 p (alpha + bytes/beta), Rabenseifner
+ * 2 log2 p alpha + 2(p-1)/p bytes/beta, binary tree
+ * 2 ceil(log2 p)(alpha + bytes/beta)). For p not a power of two, recursive
+ * doubling and Rabenseifner run on p2 = 2^floor(log2 p) ranks plus two
+ * full-vector fold steps. 1 <= p <= 2^20 (host arithmetic only).
+ *
+ * vcoll_model_ledger_time: a simulated clock over vcoll_ledger's messages of
+ * the same arguments: each step costs alpha plus the largest byte count any
+ * rank sends or receives in that step, divided by beta (full-duplex ports).
+ * For p dividing n it equals the closed form.
+ * Errors: VCOLL_ERR_INVALID_ARG for alpha < 0, beta <= 0, NULL outputs, or
+ * what vcoll_ledger rejects.
+ */
+vcoll_status vcoll_model_formula(vcoll_algo algo, int p, double bytes, double alpha, double beta,
+                                 double* seconds);
+vcoll_status vcoll_model_ledger_time(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                     const int64_t* splits, int64_t row_elems, double alpha, double beta,
+                                     double* seconds, int32_t* n_steps);
+
 #ifdef __cplusplus
 }
 #endif
