@@ -171,6 +171,29 @@ def extras(vc, torch, h, args):
     del ins, outs, rs_out, src, dst
     torch.cuda.empty_cache()
 
+    # stepwise execution (one launch per algorithm step, messages through
+    # memory) against the fused kernels: the per-step latency and the memory
+    # round trips that fusion removes
+    for label, nbytes in (("10KiB", 10 * 1024), ("25MiB", 25 * 2 ** 20)):
+        m = nbytes // 4
+        g = torch.Generator(device="cuda").manual_seed(6)
+        t = torch.randn((8, m), device="cuda", generator=g)
+        R2 = sets_for(2 * 8 * nbytes)
+        ts = [t.clone() for _ in range(R2)]
+        os_ = [torch.empty_like(t) for _ in range(R2)]
+        for algo in ("ring", "rd", "rabenseifner", "tree"):
+            _, launches = vc.vcoll_allreduce_stepwise(algo, ts[0], os_[0])
+            calls = [vc.prepare_allreduce_stepwise(algo, ts[i], os_[i]) for i in range(R2)]
+            _, ms_step = time_launches(calls, steps if nbytes < 2 ** 20 else 20, warm)
+            calls = [vc.prepare_allreduce(algo, ts[i], os_[i]) for i in range(R2)]
+            _, ms_fused = time_launches(calls, steps if nbytes < 2 ** 20 else 20, warm)
+            ex[f"stepwise_p8_{label}_{algo}"] = {
+                "us": round(ms_step * 1e3, 2), "launches": launches,
+                "us_per_launch": round(ms_step * 1e3 / launches, 2),
+                "fused_us": round(ms_fused * 1e3, 2), "slowdown_vs_fused": round(ms_step / ms_fused, 2)}
+        del t, ts, os_
+    torch.cuda.empty_cache()
+
     # decode-like (10 KiB) and prefill-like (80 MiB) messages, p = 8
     for label, nbytes in (("decode_10KiB", 10 * 1024), ("prefill_80MiB", 80 * 2 ** 20)):
         m = nbytes // 4

@@ -79,6 +79,8 @@ def _lib():
                                        P(ctypes.c_int32), P(ctypes.c_int32)]
         lib.vcoll_moe_plan.restype = I
         lib.vcoll_last_hip_error.restype = ctypes.c_char_p
+        lib.vcoll_allreduce_stepwise.argtypes = [I, I, I64, I, P(VP), P(VP), VP, I64, P(ctypes.c_int32), VP]
+        lib.vcoll_allreduce_stepwise.restype = I
         D = ctypes.c_double
         lib.vcoll_model_formula.argtypes = [I, I, D, D, D, P(D)]
         lib.vcoll_model_formula.restype = I
@@ -196,6 +198,38 @@ def vcoll_allreduce(algo, send, recv=None):
     _check(_lib().vcoll_allreduce(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                   _stream(s[0])), "vcoll_allreduce")
     return recv
+
+
+def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
+    """Stepwise all-reduce (one launch per algorithm step); returns
+    (recv, launches). bf16 needs a float32 workspace of p*n elements, made
+    when None."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_allreduce_stepwise")
+    n = s[0].numel()
+    _validate(s, "vcoll_allreduce_stepwise", n)
+    if recv is None:
+        recv = torch.empty_like(send) if isinstance(send, torch.Tensor) else [torch.empty_like(t) for t in s]
+    r = _ranks(recv)
+    _validate(r, "vcoll_allreduce_stepwise", n)
+    for i, a in enumerate(s):
+        for j, b in enumerate(r):
+            if i != j or a.data_ptr() != b.data_ptr():
+                _no_overlap([a], [b], "vcoll_allreduce_stepwise")
+    ws_ptr, ws_bytes = None, 0
+    if _dtype_code(s[0]) == BF16:
+        if workspace is None:
+            workspace = torch.empty(len(s) * n, dtype=torch.float32, device=s[0].device)
+        if workspace.dtype != torch.float32 or workspace.numel() < len(s) * n:
+            raise ValueError("vcoll_allreduce_stepwise: workspace must hold p*n float32")
+        _no_overlap([workspace], s + r, "vcoll_allreduce_stepwise")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * 4
+    launches = ctypes.c_int32()
+    _check(_lib().vcoll_allreduce_stepwise(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
+                                           ws_ptr, ws_bytes, ctypes.byref(launches), _stream(s[0])),
+           "vcoll_allreduce_stepwise")
+    return recv, launches.value
 
 
 def vcoll_reduce_scatter(algo, send, recv=None):
@@ -405,3 +439,18 @@ def prepare_bench_copy(dst, src) -> PreparedCall:
     vcoll_bench_copy(dst, src)
     args = (dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), _stream(src))
     return PreparedCall("vcoll_bench_copy", _lib().vcoll_bench_copy, args, (dst, src))
+
+
+def prepare_allreduce_stepwise(algo, send, recv, workspace=None) -> PreparedCall:
+    import torch
+    s, r = _ranks(send), _ranks(recv)
+    n = s[0].numel()
+    if _dtype_code(s[0]) == BF16 and workspace is None:
+        workspace = torch.empty(len(s) * n, dtype=torch.float32, device=s[0].device)
+    vcoll_allreduce_stepwise(algo, send, recv, workspace)      # validates (and runs) once
+    sp, rp = _ptrs(s), _ptrs(r)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * 4 if workspace is not None else 0
+    args = (_algo(algo), len(s), n, _dtype_code(s[0]), sp, rp, ws_ptr, ws_bytes, None, _stream(s[0]))
+    return PreparedCall("vcoll_allreduce_stepwise", _lib().vcoll_allreduce_stepwise, args,
+                        (send, recv, workspace, sp, rp))

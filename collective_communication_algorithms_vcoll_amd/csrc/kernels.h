@@ -71,6 +71,28 @@ struct A2ABlock {
   int32_t dst_limit;          // rows of the scatter table (index bound)
 };
 
+// Stepwise all-reduce: one launch applies up to kStepOps operations of one
+// step to float32 working buffers (kinds as in schedule.h, plus the widening
+// of bfloat16 inputs and the final bfloat16 store). src/dst point at the
+// operation's first element.
+constexpr int kStepOps = 64;
+constexpr int kStepTile = 4096;      // elements per workgroup
+enum StepLaunchKind : int32_t {
+  SK_ADD = 0, SK_COPY = 1, SK_XADD = 2, SK_NARROW = 3, SK_WIDEN_BF16 = 4, SK_STORE_BF16 = 5
+};
+struct StepLaunchOp {
+  const void* src;
+  void* dst;
+  int64_t count;
+  int32_t kind;
+  int32_t tile_start;
+};
+struct StepArgs {
+  int32_t nops;
+  int32_t pad;
+  StepLaunchOp op[kStepOps];
+};
+
 struct A2AArgs {
   int64_t row_bytes;
   int32_t nblocks;
@@ -86,5 +108,6 @@ hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo
 hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+hipError_t launch_step(const StepArgs& a, int32_t tiles, hipStream_t stream);
 
 }  // namespace vcoll

@@ -183,6 +183,64 @@ vcoll_status build_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_
   return VCOLL_OK;
 }
 
+int build_step_program(vcoll_algo algo, int p, int64_t n, bool narrow,
+                       std::vector<std::vector<StepOp>>& steps) {
+  // Start from the ledger: it is the list of messages, step by step. Each
+  // algorithm's phases decide whether a message adds or copies.
+  std::vector<vcoll_msg> msgs;
+  int32_t n_steps = 0;
+  build_ledger(VCOLL_OP_ALLREDUCE, algo, p, n, 4, nullptr, 0, msgs, &n_steps);
+  std::vector<std::vector<vcoll_msg>> by_step(static_cast<size_t>(n_steps));
+  for (const vcoll_msg& m : msgs) by_step[static_cast<size_t>(m.step)].push_back(m);
+  steps.assign(static_cast<size_t>(n_steps), {});
+  std::vector<StepOp> narrowing;
+  auto add_narrow = [&](int rank, int64_t off, int64_t count) {
+    if (count > 0) narrowing.push_back({STEP_NARROW, rank, rank, off, count});
+  };
+  const Fold f(p);
+  // kind of every message step, and where results become complete
+  int rs_end = 0;                 // steps [first_rs, rs_end) add; later ones copy
+  int first_rs = 0;
+  if (algo == VCOLL_RING) {
+    rs_end = p - 1;
+  } else if (algo == VCOLL_BINARY_TREE) {
+    int k = 0;
+    while ((1 << k) < p) ++k;
+    rs_end = k;
+  } else {
+    first_rs = f.r > 0 ? 1 : 0;                        // fold pre-step adds too
+    rs_end = first_rs + floor_log2(f.p2);
+  }
+  for (int s = 0; s < n_steps; ++s) {
+    const bool adds = s < rs_end;
+    for (const vcoll_msg& m : by_step[static_cast<size_t>(s)]) {
+      if (algo == VCOLL_RECURSIVE_DOUBLING && adds && s >= first_rs) {
+        // core steps exchange full vectors: one XADD per partner pair
+        if (m.src < m.dst) steps[s].push_back({STEP_XADD, m.src, m.dst, m.src_off, m.count});
+      } else {
+        steps[s].push_back({adds ? STEP_ADD : STEP_COPY, m.src, m.dst, m.src_off, m.count});
+      }
+    }
+  }
+  // results are complete after the last adding step; rounding them to
+  // bfloat16 is a step of its own, so that it follows every add
+  if (narrow && rs_end > 0) {
+    if (algo == VCOLL_RING) {
+      const Chunks ch(n, p);
+      for (int c = 0; c < p; ++c) add_narrow(c, ch.off(c), ch.count(c));
+    } else if (algo == VCOLL_BINARY_TREE) {
+      add_narrow(0, 0, n);
+    } else if (algo == VCOLL_RECURSIVE_DOUBLING) {
+      for (int nr = 0; nr < f.p2; ++nr) add_narrow(f.old_rank(nr), 0, n);
+    } else {
+      const Chunks ch(n, f.p2);
+      for (int nr = 0; nr < f.p2; ++nr) add_narrow(f.old_rank(nr), ch.off(nr), ch.count(nr));
+    }
+    steps.insert(steps.begin() + rs_end, narrowing);
+  }
+  return n_steps;
+}
+
 vcoll_status moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
                       const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
                       int32_t* dst_rows) {

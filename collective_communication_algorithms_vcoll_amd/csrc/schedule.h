@@ -31,6 +31,29 @@ vcoll_status build_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_
 void block_offsets(int p, const int64_t* splits, std::vector<int64_t>& send_off,
                    std::vector<int64_t>& recv_off);
 
+// One operation of a step of the stepwise (unfused) all-reduce, on float32
+// working buffers W[r] of n elements, over elements [off, off + count):
+//   ADD    W[dst] += W[src]          (the receiver adds what arrives)
+//   COPY   W[dst]  = W[src]
+//   XADD   W[src] = W[dst] = W[src] + W[dst]   (both partners of an exchange)
+//   NARROW W[dst] = W[dst] rounded to bfloat16 (a finished result, once)
+// Operations of one step never read what another operation of the same step
+// writes, so a step may run as any number of launches in sequence.
+// With bfloat16 storage, the NARROW operations form one step of their own,
+// right after the last adding step.
+enum StepKind : int32_t { STEP_ADD = 0, STEP_COPY = 1, STEP_XADD = 2, STEP_NARROW = 3 };
+
+struct StepOp {
+  int32_t kind, src, dst;
+  int64_t off, count;
+};
+
+// Steps of `algo`'s all-reduce; message steps follow build_ledger exactly.
+// Returns the number of message steps (steps.size() is one more when
+// `narrow` adds the rounding step).
+int build_step_program(vcoll_algo algo, int p, int64_t n, bool narrow,
+                       std::vector<std::vector<StepOp>>& steps);
+
 vcoll_status moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
                       const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
                       int32_t* dst_rows);

@@ -253,6 +253,84 @@ vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_ran
   return moe_plan(p, tokens, topk, experts_per_rank, topk_ids, splits, src_rows, dst_rows);
 }
 
+namespace {
+
+// Enqueue a list of step operations as launches of at most kStepOps each.
+vcoll_status run_step_ops(const std::vector<StepLaunchOp>& ops, hipStream_t stream, int32_t* launches) {
+  for (size_t b0 = 0; b0 < ops.size(); b0 += kStepOps) {
+    StepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    int64_t tiles = 0;
+    const size_t nb = std::min<size_t>(kStepOps, ops.size() - b0);
+    for (size_t k = 0; k < nb; ++k) {
+      a.op[k] = ops[b0 + k];
+      a.op[k].tile_start = static_cast<int32_t>(tiles);
+      tiles += (a.op[k].count + kStepTile - 1) / kStepTile;
+    }
+    a.nops = static_cast<int32_t>(nb);
+    if (tiles > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+    const vcoll_status st = from_hip(launch_step(a, static_cast<int32_t>(tiles), stream));
+    if (st != VCOLL_OK) return st;
+    if (launches) ++*launches;
+  }
+  return VCOLL_OK;
+}
+
+}  // namespace
+
+vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                      const void* const* send, void* const* recv, void* workspace,
+                                      int64_t workspace_bytes, int32_t* n_launches, void* stream) {
+  if (n_launches) *n_launches = 0;
+  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+  if (n == 0) return VCOLL_OK;
+  if (!all_set(p, send) || !all_set(p, const_cast<const void* const*>(recv))) return VCOLL_ERR_INVALID_ARG;
+  const bool bf16 = dtype == VCOLL_BF16;
+  if (bf16) {
+    if (!workspace) return VCOLL_ERR_INVALID_ARG;
+    if (workspace_bytes < static_cast<int64_t>(p) * n * 4) return VCOLL_ERR_BUFFER_TOO_SMALL;
+  }
+  // working buffers: recv itself for float32, the float32 workspace for bf16
+  std::vector<float*> W(p);
+  for (int r = 0; r < p; ++r)
+    W[r] = bf16 ? static_cast<float*>(workspace) + static_cast<int64_t>(r) * n : static_cast<float*>(recv[r]);
+  std::vector<std::vector<StepOp>> steps;
+  build_step_program(algo, p, n, bf16, steps);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto op = [](int32_t kind, const void* src, void* dst, int64_t count) {
+    StepLaunchOp o{};
+    o.src = src;
+    o.dst = dst;
+    o.count = count;
+    o.kind = kind;
+    return o;
+  };
+  // load the inputs into the working buffers
+  std::vector<StepLaunchOp> ops;
+  for (int r = 0; r < p; ++r) {
+    if (bf16) ops.push_back(op(SK_WIDEN_BF16, send[r], W[r], n));
+    else if (send[r] != recv[r]) ops.push_back(op(SK_COPY, send[r], W[r], n));
+  }
+  vcoll_status st = run_step_ops(ops, s, n_launches);
+  if (st != VCOLL_OK) return st;
+  // one launch (or more, for many operations) per algorithm step
+  for (const std::vector<StepOp>& step : steps) {
+    ops.clear();
+    for (const StepOp& o : step) {
+      if (o.count == 0) continue;
+      ops.push_back(op(o.kind, W[o.src] + o.off, W[o.dst] + o.off, o.count));
+    }
+    st = run_step_ops(ops, s, n_launches);
+    if (st != VCOLL_OK) return st;
+  }
+  if (bf16) {
+    ops.clear();
+    for (int r = 0; r < p; ++r) ops.push_back(op(SK_STORE_BF16, W[r], recv[r], n));
+    st = run_step_ops(ops, s, n_launches);
+  }
+  return st;
+}
+
 vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {
   if (bytes < 0 || (bytes % 16) != 0) return VCOLL_ERR_INVALID_ARG;
   if (bytes == 0) return VCOLL_OK;

@@ -120,6 +120,23 @@ vcoll_status vcoll_allreduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtyp
                              const void* const* send, void* const* recv, void* stream);
 
 /*
+ * Stepwise all-reduce: the same result as vcoll_allreduce, bit for bit, but
+ * executed the way the algorithm runs on a network ([NCC] code note: a
+ * virtual cluster with real data, message by message): one launch per step
+ * of the schedule vcoll_ledger lists, each moving that step's messages
+ * through memory (receivers add or copy what arrives; recursive-doubling
+ * partners exchange). It costs the memory round trips and per-step launch
+ * latency that the fused vcoll_allreduce avoids, which is what it measures.
+ * float32: works in recv (in place allowed); workspace unused (may be NULL).
+ * bfloat16: partial sums stay float32 in `workspace`, at least p*n*4 bytes
+ * (VCOLL_ERR_BUFFER_TOO_SMALL otherwise), rounded once as in vcoll_allreduce.
+ * *n_launches (may be NULL) receives the number of kernel launches enqueued.
+ */
+vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                      const void* const* send, void* const* recv, void* workspace,
+                                      int64_t workspace_bytes, int32_t* n_launches, void* stream);
+
+/*
  * Reduce-scatter ([HPC] "Collective Communication Primitives": process k gets
  * the k-th piece of the sum; [NCC] 4.1): recv[c] (count(c) elements) receives
  * chunk c of the sum, in the same order as the all-reduce of the same

@@ -229,3 +229,14 @@ def test_one_hip_runtime_in_the_process():
             if "libamdhip64" in line:
                 paths.add(line.split()[-1])
     assert len(paths) == 1, paths
+
+
+def test_stepwise_validation():
+    lib = _lib()
+    P = _ptrs(4)
+    # bf16 needs a float32 workspace of p*n*4 bytes
+    assert lib.vcoll_allreduce_stepwise(0, 4, 16, 1, P, P, None, 0, None, None) == 1
+    assert lib.vcoll_allreduce_stepwise(0, 4, 16, 1, P, P, 0x9000, 4 * 16 * 4 - 1, None, None) == 3
+    assert lib.vcoll_allreduce_stepwise(0, 0, 16, 0, P, P, None, 0, None, None) == 1
+    assert lib.vcoll_allreduce_stepwise(5, 4, 16, 0, P, P, None, 0, None, None) == 1
+    assert lib.vcoll_allreduce_stepwise(0, 4, 0, 0, None, None, None, 0, None, None) == 0
