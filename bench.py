@@ -149,6 +149,12 @@ def extras(vc, torch, h, args):
         calls = [vc.prepare_allreduce(algo, ins[i], outs[i]) for i in range(R)]
         _, mean_ms = time_launches(calls, steps, warm)
         ex[f"ddp_bucket_{algo}_fused"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    # hierarchical (2 groups of 4, and 4 of 2) on the same bucket
+    for nodes, local in ((2, 4), (4, 2)):
+        calls = [vc.prepare_allreduce_hierarchical(nodes, local, ins[i], outs[i]) for i in range(R)]
+        _, mean_ms = time_launches(calls, steps, warm)
+        ex[f"ddp_bucket_hierarchical_{nodes}x{local}_fused"] = {"GBps": rate(2 * p * S, mean_ms),
+                                                               "us": round(mean_ms * 1e3, 1)}
     # warm: one set reused back to back (partly served by the Infinity Cache)
     call = vc.prepare_allreduce("ring", ins[0], outs[0])
     _, mean_ms = time_launches([call], steps, warm)
@@ -219,6 +225,11 @@ def extras(vc, torch, h, args):
         call = vc.prepare_allreduce(algo, t16, o16)
         _, mean_ms = time_launches([call], 10, 2)
         ex[f"hier16_bf16_{algo}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    for nodes, local in ((2, 8), (4, 4)):
+        call = vc.prepare_allreduce_hierarchical(nodes, local, t16, o16)
+        _, mean_ms = time_launches([call], 10, 2)
+        ex[f"hier16_bf16_hierarchical_{nodes}x{local}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms),
+                                                                "us": round(mean_ms * 1e3, 1)}
     rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
     for algo, ag_algo in (("ring", "ring"), ("rabenseifner", "rd")):
         call = vc.prepare_reduce_scatter(algo, t16, rs16)

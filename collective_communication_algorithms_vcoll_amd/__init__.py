@@ -79,6 +79,15 @@ def _lib():
                                        P(ctypes.c_int32), P(ctypes.c_int32)]
         lib.vcoll_moe_plan.restype = I
         lib.vcoll_last_hip_error.restype = ctypes.c_char_p
+        lib.vcoll_allreduce_hierarchical.argtypes = [I, I, I64, I, P(VP), P(VP), VP]
+        lib.vcoll_allreduce_hierarchical.restype = I
+        lib.vcoll_ledger_hierarchical.argtypes = [I, I, I64, I, P(Msg), I64, P(I64), P(I64), P(I64),
+                                                  P(ctypes.c_int32)]
+        lib.vcoll_ledger_hierarchical.restype = I
+        lib.vcoll_model_ledger_time_nodes.argtypes = [I, I, I, I, I64, I, ctypes.c_double, ctypes.c_double,
+                                                      ctypes.c_double, ctypes.c_double,
+                                                      P(ctypes.c_double), P(ctypes.c_int32)]
+        lib.vcoll_model_ledger_time_nodes.restype = I
         lib.vcoll_allreduce_stepwise.argtypes = [I, I, I64, I, P(VP), P(VP), VP, I64, P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise.restype = I
         D = ctypes.c_double
@@ -230,6 +239,56 @@ def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
                                            ws_ptr, ws_bytes, ctypes.byref(launches), _stream(s[0])),
            "vcoll_allreduce_stepwise")
     return recv, launches.value
+
+
+def vcoll_allreduce_hierarchical(nodes: int, local: int, send, recv=None):
+    """Hierarchical (or 2D torus: nodes = rows, local = columns) all-reduce."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_allreduce_hierarchical")
+    n = s[0].numel()
+    _validate(s, "vcoll_allreduce_hierarchical", n)
+    if len(s) != nodes * local:
+        raise ValueError("vcoll_allreduce_hierarchical: p must equal nodes * local")
+    if recv is None:
+        recv = torch.empty_like(send) if isinstance(send, torch.Tensor) else [torch.empty_like(t) for t in s]
+    r = _ranks(recv)
+    _validate(r, "vcoll_allreduce_hierarchical", n)
+    for i, a in enumerate(s):
+        for j, b in enumerate(r):
+            if i != j or a.data_ptr() != b.data_ptr():
+                _no_overlap([a], [b], "vcoll_allreduce_hierarchical")
+    _check(_lib().vcoll_allreduce_hierarchical(nodes, local, n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
+                                               _stream(s[0])), "vcoll_allreduce_hierarchical")
+    return recv
+
+
+def vcoll_ledger_hierarchical(nodes: int, local: int, n: int, dtype: str = "f32"):
+    """Ledger of the hierarchical all-reduce: (messages, sent, received, steps)."""
+    lib = _lib()
+    p = nodes * local
+    dtc = {"f32": F32, "bf16": BF16}[dtype]
+    count = ctypes.c_int64()
+    _check(lib.vcoll_ledger_hierarchical(nodes, local, n, dtc, None, 0, ctypes.byref(count), None, None, None),
+           "vcoll_ledger_hierarchical")
+    msgs = (Msg * max(1, count.value))()
+    sent, got, steps = (ctypes.c_int64 * p)(), (ctypes.c_int64 * p)(), ctypes.c_int32()
+    _check(lib.vcoll_ledger_hierarchical(nodes, local, n, dtc, msgs, count.value, ctypes.byref(count), sent, got,
+                                         ctypes.byref(steps)), "vcoll_ledger_hierarchical")
+    out = [(m.step, m.src, m.dst, m.src_off, m.dst_off, m.count, m.bytes) for m in msgs[:count.value]]
+    return out, list(sent), list(got), steps.value
+
+
+def vcoll_model_ledger_time_nodes(algo, nodes: int, local: int, n: int, alpha_in: float, beta_in: float,
+                                  alpha_out: float, beta_out: float, dtype: str = "f32") -> tuple:
+    """Two-level alpha-beta clock; algo 'hierarchical' or a flat algorithm."""
+    hier = algo == "hierarchical"
+    t, steps = ctypes.c_double(), ctypes.c_int32()
+    _check(_lib().vcoll_model_ledger_time_nodes(int(hier), 0 if hier else _algo(algo), nodes, local, n,
+                                                {"f32": F32, "bf16": BF16}[dtype], alpha_in, beta_in,
+                                                alpha_out, beta_out, ctypes.byref(t), ctypes.byref(steps)),
+           "vcoll_model_ledger_time_nodes")
+    return t.value, steps.value
 
 
 def vcoll_reduce_scatter(algo, send, recv=None):
@@ -417,6 +476,15 @@ def prepare_allreduce(algo, send, recv) -> PreparedCall:
     sp, rp = _ptrs(s), _ptrs(r)
     args = (_algo(algo), len(s), s[0].numel(), _dtype_code(s[0]), sp, rp, _stream(s[0]))
     return PreparedCall("vcoll_allreduce", _lib().vcoll_allreduce, args, (send, recv, sp, rp))
+
+
+def prepare_allreduce_hierarchical(nodes: int, local: int, send, recv) -> PreparedCall:
+    s, r = _ranks(send), _ranks(recv)
+    vcoll_allreduce_hierarchical(nodes, local, send, recv)
+    sp, rp = _ptrs(s), _ptrs(r)
+    args = (nodes, local, s[0].numel(), _dtype_code(s[0]), sp, rp, _stream(s[0]))
+    return PreparedCall("vcoll_allreduce_hierarchical", _lib().vcoll_allreduce_hierarchical, args,
+                        (send, recv, sp, rp))
 
 
 def prepare_reduce_scatter(algo, send, recv) -> PreparedCall:

@@ -51,6 +51,17 @@ struct ReduceArgs {
   uint8_t merges[kMaxRanks];
 };
 
+// Hierarchical / 2D all-reduce of nodes x local ranks. Grid: x = tiles of a
+// segment, y = segment u = l * nodes + j (piece j of chunk l), inside which
+// the summation order is fixed.
+struct HierArgs {
+  RankPtrs ptr;
+  int64_t n;
+  int32_t nodes, local;
+  int32_t vec;
+  int32_t pad;
+};
+
 // All-gather. Grid: x = tiles of one block, y = source rank.
 struct GatherArgs {
   RankPtrs ptr;
@@ -109,5 +120,6 @@ hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int32_t tiles, hipStream_t stream);
+hipError_t launch_hierarchical(const HierArgs& a, vcoll_dtype dtype, int64_t max_segment, hipStream_t stream);
 
 }  // namespace vcoll

@@ -87,4 +87,55 @@ vcoll_status vcoll_model_ledger_time(vcoll_op op, vcoll_algo algo, int p, int64_
   return VCOLL_OK;
 }
 
+vcoll_status vcoll_model_ledger_time_nodes(int hierarchical, vcoll_algo algo, int nodes, int local, int64_t n,
+                                           vcoll_dtype dtype, double alpha_in, double beta_in,
+                                           double alpha_out, double beta_out, double* seconds,
+                                           int32_t* n_steps) {
+  if (!(alpha_in >= 0) || !(beta_in > 0) || !(alpha_out >= 0) || !(beta_out > 0) || !seconds)
+    return VCOLL_ERR_INVALID_ARG;
+  if (nodes < 1 || local < 1) return VCOLL_ERR_INVALID_ARG;
+  const int p = nodes * local;
+  int64_t count = 0;
+  vcoll_status st = hierarchical
+                        ? vcoll_ledger_hierarchical(nodes, local, n, dtype, nullptr, 0, &count, nullptr, nullptr, nullptr)
+                        : vcoll_ledger(VCOLL_OP_ALLREDUCE, algo, p, n, dtype, nullptr, 0, nullptr, 0, &count,
+                                       nullptr, nullptr, nullptr);
+  if (st != VCOLL_OK) return st;
+  std::vector<vcoll_msg> msgs(static_cast<size_t>(std::max<int64_t>(count, 1)));
+  int32_t steps = 0;
+  st = hierarchical ? vcoll_ledger_hierarchical(nodes, local, n, dtype, msgs.data(), count, &count, nullptr,
+                                                nullptr, &steps)
+                    : vcoll_ledger(VCOLL_OP_ALLREDUCE, algo, p, n, dtype, nullptr, 0, msgs.data(), count,
+                                   &count, nullptr, nullptr, &steps);
+  if (st != VCOLL_OK) return st;
+  // per step and rank: bytes sent and received inside the node and across
+  std::map<int32_t, std::vector<int64_t>> per_step;   // [4*p]: in-send, in-recv, out-send, out-recv
+  for (int64_t i = 0; i < count; ++i) {
+    const vcoll_msg& m = msgs[static_cast<size_t>(i)];
+    std::vector<int64_t>& b = per_step[m.step];
+    if (b.empty()) b.assign(static_cast<size_t>(4 * p), 0);
+    const bool across = m.src / local != m.dst / local;
+    b[static_cast<size_t>((across ? 2 : 0) * p + m.src)] += m.bytes;
+    b[static_cast<size_t>((across ? 3 : 1) * p + m.dst)] += m.bytes;
+  }
+  double t = 0.0;
+  for (const auto& kv : per_step) {
+    // the step ends when its slowest port is done; a port that carries
+    // nothing in this step costs nothing
+    double slowest = 0.0;
+    for (int r = 0; r < p; ++r)
+      for (int k = 0; k < 4; ++k) {
+        const int64_t bytes = kv.second[static_cast<size_t>(k * p + r)];
+        bool used = bytes > 0;
+        if (!used) continue;
+        const bool across = k >= 2;
+        slowest = std::max(slowest, (across ? alpha_out : alpha_in) + bytes / (across ? beta_out : beta_in));
+      }
+    t += slowest;
+  }
+  *seconds = t;
+  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
+}
+
 }  // extern "C"

@@ -183,6 +183,51 @@ vcoll_status build_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_
   return VCOLL_OK;
 }
 
+vcoll_status build_ledger_hierarchical(int nodes, int local, int64_t n, int64_t elem_bytes,
+                                       std::vector<vcoll_msg>& out, int32_t* n_steps) {
+  out.clear();
+  LedgerBuilder L{out, elem_bytes};
+  const int N = nodes, Lc = local;
+  const Chunks ch(n, Lc);
+  // piece j of chunk l
+  auto piece = [&](int l, int j, int64_t* off, int64_t* cnt) {
+    const Chunks sub(ch.count(l), N);
+    *off = ch.off(l) + sub.off(j);
+    *cnt = sub.count(j);
+  };
+  int step = 0;
+  // (1) reduce-scatter inside every group: group rank i sends chunk (i-1-s)
+  for (int s = 0; s < Lc - 1; ++s, ++step)
+    for (int g = 0; g < N; ++g)
+      for (int i = 0; i < Lc; ++i) {
+        const int c = ((i - 1 - s) % Lc + Lc) % Lc;
+        L.add(step, g * Lc + i, g * Lc + (i + 1) % Lc, ch.off(c), ch.off(c), ch.count(c));
+      }
+  // (2) across groups, for every index l: ring reduce-scatter then all-gather
+  // of chunk l's N pieces (group g sends piece (g-1-s), then (g-s))
+  for (int phase = 0; phase < 2; ++phase)
+    for (int s = 0; s < N - 1; ++s, ++step)
+      for (int l = 0; l < Lc; ++l)
+        for (int g = 0; g < N; ++g) {
+          const int j = ((g - (phase == 0 ? 1 : 0) - s) % N + N) % N;
+          int64_t off, cnt;
+          piece(l, j, &off, &cnt);
+          L.add(step, g * Lc + l, ((g + 1) % N) * Lc + l, off, off, cnt);
+        }
+  // (3) all-gather inside every group: group rank i forwards chunk (i-s)
+  for (int s = 0; s < Lc - 1; ++s, ++step)
+    for (int g = 0; g < N; ++g)
+      for (int i = 0; i < Lc; ++i) {
+        const int c = ((i - s) % Lc + Lc) % Lc;
+        L.add(step, g * Lc + i, g * Lc + (i + 1) % Lc, ch.off(c), ch.off(c), ch.count(c));
+      }
+  std::sort(out.begin(), out.end(), [](const vcoll_msg& a, const vcoll_msg& b) {
+    return std::tie(a.step, a.src, a.dst, a.src_off) < std::tie(b.step, b.src, b.dst, b.src_off);
+  });
+  if (n_steps) *n_steps = L.steps;
+  return VCOLL_OK;
+}
+
 int build_step_program(vcoll_algo algo, int p, int64_t n, bool narrow,
                        std::vector<std::vector<StepOp>>& steps) {
   // Start from the ledger: it is the list of messages, step by step. Each

@@ -31,6 +31,13 @@ vcoll_status build_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_
 void block_offsets(int p, const int64_t* splits, std::vector<int64_t>& send_off,
                    std::vector<int64_t>& recv_off);
 
+// Hierarchical / 2D all-reduce of nodes x local ranks (rank = g*local + l):
+// ring reduce-scatter inside each group over `local` chunks, ring all-reduce
+// of chunk l across the same-index ranks (chunk l cut into `nodes` pieces),
+// ring all-gather inside each group; all rings of a phase in lockstep.
+vcoll_status build_ledger_hierarchical(int nodes, int local, int64_t n, int64_t elem_bytes,
+                                       std::vector<vcoll_msg>& out, int32_t* n_steps);
+
 // One operation of a step of the stepwise (unfused) all-reduce, on float32
 // working buffers W[r] of n elements, over elements [off, off + count):
 //   ADD    W[dst] += W[src]          (the receiver adds what arrives)

@@ -331,6 +331,52 @@ vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_d
   return st;
 }
 
+vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype,
+                                          const void* const* send, void* const* recv, void* stream) {
+  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || n < 0 || !valid_dtype(dtype))
+    return VCOLL_ERR_INVALID_ARG;
+  if (n == 0) return VCOLL_OK;
+  const int p = nodes * local;
+  if (!all_set(p, send) || !all_set(p, const_cast<const void* const*>(recv))) return VCOLL_ERR_INVALID_ARG;
+  HierArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < p; ++r) {
+    a.ptr.src[r] = send[r];
+    a.ptr.dst[r] = recv[r];
+  }
+  a.n = n;
+  a.nodes = nodes;
+  a.local = local;
+  a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv));
+  const Chunks ch(n, local);
+  const int64_t max_segment = (ch.count(0) + nodes - 1) / nodes;
+  return from_hip(launch_hierarchical(a, dtype, max_segment, static_cast<hipStream_t>(stream)));
+}
+
+vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype, vcoll_msg* msgs,
+                                       int64_t cap, int64_t* n_msgs, int64_t* sent_bytes,
+                                       int64_t* recv_bytes, int32_t* n_steps) {
+  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || n < 0 || !valid_dtype(dtype) || !n_msgs)
+    return VCOLL_ERR_INVALID_ARG;
+  const int p = nodes * local;
+  std::vector<vcoll_msg> out;
+  int32_t steps = 0;
+  build_ledger_hierarchical(nodes, local, n, elem_bytes(dtype), out, &steps);
+  *n_msgs = static_cast<int64_t>(out.size());
+  if (msgs) {
+    if (cap < static_cast<int64_t>(out.size())) return VCOLL_ERR_BUFFER_TOO_SMALL;
+    std::copy(out.begin(), out.end(), msgs);
+  }
+  if (sent_bytes) std::fill(sent_bytes, sent_bytes + p, 0);
+  if (recv_bytes) std::fill(recv_bytes, recv_bytes + p, 0);
+  for (const vcoll_msg& m : out) {
+    if (sent_bytes) sent_bytes[m.src] += m.bytes;
+    if (recv_bytes) recv_bytes[m.dst] += m.bytes;
+  }
+  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
+}
+
 vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {
   if (bytes < 0 || (bytes % 16) != 0) return VCOLL_ERR_INVALID_ARG;
   if (bytes == 0) return VCOLL_OK;

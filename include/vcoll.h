@@ -137,6 +137,30 @@ vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_d
                                       int64_t workspace_bytes, int32_t* n_launches, void* stream);
 
 /*
+ * Hierarchical all-reduce ([NCC] 6.3; [LDT] 16 ranks as 2 nodes x 8): p =
+ * nodes*local ranks, rank = g*local + l. (1) Inside every group of `local`
+ * ranks a ring reduce-scatter over `local` chunks; (2) for every index l, the
+ * `nodes` ranks g*local + l run a ring all-reduce of chunk l, cut into
+ * `nodes` pieces; (3) inside every group a ring all-gather. The 2D torus
+ * all-reduce of an a x b grid ([NCC] 6.1: rows, then columns, then back) is
+ * the same with nodes = a and local = b. In piece j of chunk l the sum is an
+ * outer chain over the groups starting after group j, of inner chains over
+ * each group's ranks starting after rank l. Chunks and pieces are balanced
+ * as above. Every rank receives the same vector; in place allowed.
+ * 1 <= nodes*local <= VCOLL_MAX_RANKS.
+ */
+vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype,
+                                          const void* const* send, void* const* recv, void* stream);
+
+/* Message ledger of vcoll_allreduce_hierarchical, conventions as vcoll_ledger:
+ * steps 0..local-2 in-group reduce-scatter, then nodes-1 cross-group
+ * reduce-scatter and nodes-1 cross-group all-gather steps, then local-1
+ * in-group all-gather steps. Host only. */
+vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype, vcoll_msg* msgs,
+                                       int64_t cap, int64_t* n_msgs, int64_t* sent_bytes,
+                                       int64_t* recv_bytes, int32_t* n_steps);
+
+/*
  * Reduce-scatter ([HPC] "Collective Communication Primitives": process k gets
  * the k-th piece of the sum; [NCC] 4.1): recv[c] (count(c) elements) receives
  * chunk c of the sum, in the same order as the all-reduce of the same
@@ -238,6 +262,21 @@ vcoll_status vcoll_model_formula(vcoll_algo algo, int p, double bytes, double al
 vcoll_status vcoll_model_ledger_time(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                                      const int64_t* splits, int64_t row_elems, double alpha, double beta,
                                      double* seconds, int32_t* n_steps);
+
+/*
+ * Alpha-beta clock on a two-level network ([NCC] 2.3 scale-up / scale-out;
+ * 6.3 and exercise 6): ranks r and s share a node when r/local == s/local;
+ * a message inside a node costs (alpha_in, beta_in), across nodes
+ * (alpha_out, beta_out). Each step lasts as long as its slowest port: the
+ * largest of alpha + bytes/beta over every rank's sending and receiving
+ * port of each class that carries bytes in the step. hierarchical != 0
+ * clocks vcoll_ledger_hierarchical(nodes, local, ...) (algo ignored);
+ * otherwise vcoll_ledger's all-reduce with `algo` on nodes*local ranks.
+ */
+vcoll_status vcoll_model_ledger_time_nodes(int hierarchical, vcoll_algo algo, int nodes, int local, int64_t n,
+                                           vcoll_dtype dtype, double alpha_in, double beta_in,
+                                           double alpha_out, double beta_out, double* seconds,
+                                           int32_t* n_steps);
 
 #ifdef __cplusplus
 }

@@ -12,8 +12,8 @@ algorithm's steps produce (numpy float32 arrays, no fused multiply-add, no
 flush-to-zero); bfloat16 values widen exactly and round once (numerics.py).
 """
 from .cluster import ADD, COPY, Ledger, Msg
-from .collectives import (ALGOS, all_gather, all_to_all, allreduce, block_offsets,
-                          chunk_bounds, reduce_scatter)
+from .collectives import (ALGOS, all_gather, all_to_all, allreduce, allreduce_hierarchical,
+                          block_offsets, chunk_bounds, reduce_scatter)
 from .moe import combine as moe_combine
 from .moe import dispatch as moe_dispatch
 from .moe import plan as moe_plan
@@ -21,6 +21,7 @@ from .numerics import ELEM_BYTES, bf16_to_f32, f32_to_bf16, round_to_bf16
 
 __all__ = [
     "ADD", "COPY", "Ledger", "Msg", "ALGOS", "all_gather", "all_to_all", "allreduce",
+    "allreduce_hierarchical",
     "block_offsets", "chunk_bounds", "reduce_scatter", "moe_plan", "moe_dispatch",
     "moe_combine", "ELEM_BYTES", "bf16_to_f32", "f32_to_bf16", "round_to_bf16",
 ]

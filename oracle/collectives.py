@@ -40,6 +40,11 @@ R5  binary tree: binomial reduce to root 0 (a rank whose lowest set bit is
 R6  bfloat16 storage: inputs widen exactly to float32, every add is a
     float32 add, and each result is rounded to bfloat16 once, when it is
     complete (end of the reduce phase); the ledger counts storage bytes.
+R8  hierarchical and 2D all-reduce (P2 sections 6.1, 6.3): ranks form N
+    groups of L consecutive ranks (nodes, or torus rows); the group
+    reduce-scatter cuts the vector into L chunks, the cross-group ring cuts
+    chunk l into N pieces, both balanced as in R1, rings run i -> i+1 with
+    the piece owner rule of R2; every ring in a phase runs in lockstep.
 R7  all-to-all: receive buffers hold the blocks in source-rank order (the
     transpose of section 4.1); the ledger follows the direct schedule, step
     s = 1..p-1 has rank i send its block for rank (i+s) mod p; the diagonal
@@ -245,6 +250,71 @@ def _allreduce_tree(cl: Cluster, p: int, n: int, dtype: str) -> None:
         sends = [Send(i, i + m, 0, 0, n, COPY) for i in range(0, p, 2 * m) if i + m < p]
         cl.step(step, sends)
         step += 1
+
+
+# --------------------------------------------------------------------------
+# hierarchical / 2D all-reduce (P2 sections 6.1 and 6.3): ranks form N groups
+# of L (rank = g*L + l); reading R8 below
+
+
+def allreduce_hierarchical_steps(cl: Cluster, nodes: int, local: int, n: int, dtype: str) -> None:
+    """R8: (1) inside each group, a ring reduce-scatter over L chunks (group
+    rank l ends with chunk l of the group's sum); (2) for every l, the N ranks
+    with that index run a ring all-reduce on chunk l, cut into N pieces (ring
+    reduce-scatter then all-gather); (3) inside each group a ring all-gather.
+    All groups (and all same-index rings) run their steps together."""
+    L, N = local, nodes
+    chunks = chunk_bounds(n, L)
+    cpieces = [(chunks[c], chunks[c + 1] - chunks[c]) for c in range(L)]
+    sub = []                                       # sub[l][j] = piece j of chunk l
+    for l in range(L):
+        b = chunk_bounds(cpieces[l][1], N)
+        sub.append([(cpieces[l][0] + b[j], b[j + 1] - b[j]) for j in range(N)])
+
+    def together(step0, rings):
+        """Run several rings in lockstep; rings = (members in ring order,
+        their pieces, op, shift). Step s: member i sends piece
+        (i - shift - s) mod m to member i+1 (shift 1 reduce-scatters so that
+        member i finishes piece i; shift 0 all-gathers)."""
+        steps = max(len(m) for m, _, _, _ in rings) - 1
+        for s in range(steps):
+            sends = []
+            for members, pieces, op, shift in rings:
+                m = len(members)
+                for i in range(m):
+                    off, cnt = pieces[(i - shift - s) % m]
+                    sends.append(Send(members[i], members[(i + 1) % m], off, off, cnt, op))
+            cl.step(step0 + s, sends)
+        return step0 + steps
+
+    groups = [[g * L + l for l in range(L)] for g in range(N)]
+    same = [[g * L + l for g in range(N)] for l in range(L)]
+    step = 0
+    if L > 1:
+        step = together(step, [(grp, cpieces, ADD, 1) for grp in groups])
+    if N > 1:
+        step = together(step, [(same[l], sub[l], ADD, 1) for l in range(L)])
+    for l in range(L):                              # piece j of chunk l is complete on group j
+        for j in range(N):
+            off, cnt = sub[l][j]
+            _narrow(cl, j * L + l, off, cnt, dtype)
+    if N > 1:
+        step = together(step, [(same[l], sub[l], COPY, 0) for l in range(L)])
+    if L > 1:
+        together(step, [(grp, cpieces, COPY, 0) for grp in groups])
+
+
+def allreduce_hierarchical(x: list, nodes: int, local: int, dtype: str = "f32", n: int | None = None,
+                           lo: int = 0):
+    """Hierarchical all-reduce of nodes*local ranks; 2D torus all-reduce of an
+    a x b grid is the same with nodes = a, local = b (rows first)."""
+    p = len(x)
+    if nodes * local != p:
+        raise ValueError("p must equal nodes * local")
+    n = len(x[0]) if n is None else n
+    cl, ledger = _start(x, dtype, lo)
+    allreduce_hierarchical_steps(cl, nodes, local, n, dtype)
+    return _finish(cl, dtype), ledger
 
 
 _AR = {

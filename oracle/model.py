@@ -78,3 +78,26 @@ def algbw(nbytes: float, t: float) -> float:
 
 def busbw(nbytes: float, t: float, p: int) -> float:
     return nbytes / t * 2 * (p - 1) / p
+
+
+def ledger_time_nodes(ledger, local: int, alpha_in: float, beta_in: float, alpha_out: float,
+                      beta_out: float) -> float:
+    """Two-level clock (sections 2.3 and 6.3, exercise 6): ranks r and s share
+    a node when r // local == s // local. A message inside a node costs
+    (alpha_in, beta_in), one across nodes (alpha_out, beta_out). Every rank has
+    one sending and one receiving port of each class; a step lasts as long as
+    its slowest busy port, alpha + bytes / beta of that port's class."""
+    per_step: dict = {}
+    for m in ledger.msgs:
+        ports = per_step.setdefault(m.step, {})
+        cls = "out" if m.src // local != m.dst // local else "in"
+        ports[(cls, "send", m.src)] = ports.get((cls, "send", m.src), 0) + m.bytes
+        ports[(cls, "recv", m.dst)] = ports.get((cls, "recv", m.dst), 0) + m.bytes
+    t = 0.0
+    for step in sorted(per_step):
+        slowest = 0.0
+        for (cls, _, _), nbytes in per_step[step].items():
+            a, b = (alpha_out, beta_out) if cls == "out" else (alpha_in, beta_in)
+            slowest = max(slowest, a + nbytes / b)
+        t += slowest
+    return t

@@ -1,0 +1,281 @@
+"""Hierarchical / two-dimensional all-reduce (the 'next' row over the
+two-level network): the oracle pinned to what the pages print and to its
+own flat collectives, and the library's ledger and two-level clock against
+the oracle. CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import model
+
+vc = pytest.importorskip("collective_communication_algorithms_vcoll_amd")
+
+with open(os.path.join(os.path.dirname(__file__), "golden", "hierarchical.json")) as f:
+    G = json.load(f)
+
+SHAPES = [(2, 2), (2, 4), (4, 2), (3, 5), (2, 8), (4, 4), (1, 6), (6, 1), (1, 1)]
+
+
+def rand(p, n, dtype, seed):
+    return [workloads.rank_window(workloads.TAG_TEST * 1000 + 500 + seed, r, 0, n, ("normal", 0.0, 1.0), dtype)
+            for r in range(p)]
+
+
+def f32bits(v):
+    return np.asarray(v, dtype=np.float32).view(np.uint32)
+
+
+# --------------------------------------------------------------------------- oracle pins
+
+def test_worked_example_two_by_two():
+    x = workloads.worked_example()
+    out, led = oracle.allreduce_hierarchical(x, 2, 2)
+    for r in range(4):
+        assert out[r].tolist() == [60, 64, 68, 72]
+    assert led.n_steps == 4
+
+
+@pytest.mark.parametrize("nodes,local", SHAPES)
+def test_integer_inputs_give_the_exact_sum(nodes, local):
+    """Small integers add exactly in float32 in any order: every rank ends
+    with the plain column sum."""
+    p, n = nodes * local, 37
+    rng = np.random.default_rng(nodes * 100 + local)
+    x = [rng.integers(-1000, 1000, size=n).astype(np.float32) for _ in range(p)]
+    out, _ = oracle.allreduce_hierarchical(x, nodes, local)
+    want = np.sum(np.stack(x).astype(np.int64), axis=0)
+    for r in range(p):
+        assert out[r].astype(np.int64).tolist() == want.tolist()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p", [1, 2, 5, 8])
+def test_one_node_or_one_rank_per_node_is_the_flat_ring(p, dtype):
+    """With a single group the cross stage vanishes; with one rank per group
+    the in-group stages vanish. Either way it is the flat ring, message for
+    message and bit for bit."""
+    n = 3 * p + 2
+    x = rand(p, n, dtype, p)
+    ring, led_ring = oracle.allreduce(x, "ring", dtype)
+    for nodes, local in ((1, p), (p, 1)):
+        out, led = oracle.allreduce_hierarchical(x, nodes, local, dtype)
+        for r in range(p):
+            assert out[r].tobytes() == ring[r].tobytes()
+        assert led.sorted() == led_ring.sorted()
+
+
+@pytest.mark.parametrize("nodes,local", [(2, 4), (3, 5), (4, 4), (2, 8), (4, 2)])
+def test_is_group_reduce_scatter_then_same_index_ring_allreduce(nodes, local):
+    """Section 6.3 as a composition of the flat collectives (each pinned on
+    its own): ring reduce-scatter inside every group, a ring all-reduce of
+    chunk l over the ranks with group index l, then (all-gather) every rank
+    holds the result."""
+    p, n = nodes * local, 9 * local * nodes + 5
+    x = rand(p, n, "f32", 40 + p)
+    out, _ = oracle.allreduce_hierarchical(x, nodes, local)
+    offs = oracle.chunk_bounds(n, local)
+    stage1 = [oracle.reduce_scatter(x[g * local:(g + 1) * local], "ring")[0] for g in range(nodes)]
+    want = np.zeros(n, np.float32)
+    for l in range(local):
+        col, _ = oracle.allreduce([stage1[g][l] for g in range(nodes)], "ring")
+        for g in range(nodes):
+            assert col[g].tobytes() == col[0].tobytes()
+        want[offs[l]:offs[l + 1]] = col[0]
+    for r in range(p):
+        assert out[r].tobytes() == want.tobytes()
+
+
+def test_bf16_rounds_once_after_the_float32_composition():
+    nodes, local, n = 2, 4, 301
+    x = rand(8, n, "bf16", 61)
+    out, _ = oracle.allreduce_hierarchical(x, nodes, local, "bf16")
+    wide = [oracle.bf16_to_f32(v) for v in x]
+    ref, _ = oracle.allreduce_hierarchical(wide, nodes, local, "f32")
+    want = oracle.f32_to_bf16(ref[0])
+    for r in range(8):
+        assert out[r].tobytes() == want.tobytes()
+
+
+def test_order_probes_of_inner_and_outer_chains():
+    """Worked by hand from the order the two ring stages produce (2^24 + 1
+    rounds back to 2^24 in float32, so each chain's start shows).
+
+    Inner chain: 2 groups x 3 ranks, group 0 holds 2^24, 1, -2^24 and group 1
+    zeros, n = 6 (chunk l = elements 2l, 2l+1). Chunk l's chain starts after
+    rank l: l=0: (1 - 2^24) + 2^24 = 1; l=1: (-2^24 + 2^24) + 1 = 1;
+    l=2: (2^24 + 1) - 2^24 = 0.
+
+    Outer chain: 3 groups x 2 ranks, group sums 2^24, 1, -2^24 (second rank
+    zero), n = 6 (chunk l = elements 3l..3l+2, piece j = element 3l+j).
+    Piece j's chain starts after group j: j=0: (1 - 2^24) + 2^24 = 1;
+    j=1: (-2^24 + 2^24) + 1 = 1; j=2: (2^24 + 1) - 2^24 = 0."""
+    big = 2.0 ** 24
+    inner = [big, 1.0, -big, 0.0, 0.0, 0.0]
+    out, _ = oracle.allreduce_hierarchical([np.full(6, v, np.float32) for v in inner], 2, 3)
+    for r in range(6):
+        assert out[r].tolist() == [1, 1, 1, 1, 0, 0]
+    outer = [big, 0.0, 1.0, 0.0, -big, 0.0]
+    out, _ = oracle.allreduce_hierarchical([np.full(6, v, np.float32) for v in outer], 3, 2)
+    for r in range(6):
+        assert out[r].tolist() == [1, 1, 0, 1, 1, 0]
+    # 2 x 2 on the flat probe: every inner chain is two terms, so every
+    # element is 1, where the flat ring gives 2, 2, 0, 1 (section 5.1 order)
+    probe = [big, 1.0, -big, 1.0]
+    out, _ = oracle.allreduce_hierarchical([np.full(4, v, np.float32) for v in probe], 2, 2)
+    assert out[0].tolist() == [1, 1, 1, 1]
+    flat, _ = oracle.allreduce([np.full(4, v, np.float32) for v in probe], "ring")
+    assert flat[0].tolist() == [2, 2, 0, 1]
+
+
+def test_ledger_bytes_and_steps():
+    nodes, local, n = 4, 8, 4096 * 32
+    x = [np.zeros(1, np.float32)] * 32
+    _, led = oracle.allreduce_hierarchical(x, nodes, local, n=n, lo=0)
+    assert led.n_steps == 2 * (local - 1) + 2 * (nodes - 1)
+    cross = sum(m.bytes for m in led.msgs if m.src // local != m.dst // local)
+    inside = sum(m.bytes for m in led.msgs if m.src // local == m.dst // local)
+    e = 4
+    # per rank: 2 (L-1)/L n inside; 2 (N-1)/N n/L across
+    assert inside == 32 * 2 * (local - 1) * (n // local) * e
+    assert cross == 32 * 2 * (nodes - 1) * (n // local // nodes) * e
+    for m in led.msgs:
+        across = m.src // local != m.dst // local
+        assert across == (local - 1 <= m.step < local - 1 + 2 * (nodes - 1))
+
+
+# --------------------------------------------------------------------------- pages' numbers
+
+def test_two_d_torus_section_6_1():
+    e = G["torus_2d"]
+    p, n = e["rows"] * e["cols"], e["bytes"] // 4
+    x = [np.zeros(1, np.float32)] * p
+    _, flat = oracle.allreduce(x, "ring", n=n, lo=0)
+    _, two = oracle.allreduce_hierarchical(x, e["rows"], e["cols"], n=n, lo=0)
+    assert flat.n_steps == e["flat_steps"] and two.n_steps == e["two_d_steps"]
+    a, b = e["alpha"], e["beta"]
+    t_flat = model.ledger_time_nodes(flat, e["cols"], a, b, a, b)
+    t_two = model.ledger_time_nodes(two, e["cols"], a, b, a, b)
+    assert t_flat == pytest.approx(e["flat_seconds"], rel=e["rel"])
+    assert t_two == pytest.approx(e["two_d_seconds"], rel=e["rel"])
+    # same bytes as the single ring
+    assert sum(m.bytes for m in two.msgs) == sum(m.bytes for m in flat.msgs)
+    for side in ("flat", "hierarchical"):
+        t, steps = vc.vcoll_model_ledger_time_nodes("ring" if side == "flat" else "hierarchical", e["rows"],
+                                                    e["cols"], n, a, b, a, b)
+        assert t == pytest.approx(t_flat if side == "flat" else t_two, rel=1e-12)
+
+
+def test_exercise_6_stage_times():
+    e = G["exercise_6"]
+    nodes, local = e["nodes"], e["local"]
+    p, n = nodes * local, int(e["bytes"]) // 4
+    x = [np.zeros(1, np.float32)] * p
+    _, hier = oracle.allreduce_hierarchical(x, nodes, local, n=n, lo=0)
+    _, flat = oracle.allreduce(x, "ring", n=n, lo=0)
+    bi, bo = e["beta_in"], e["beta_out"]
+    t_h = model.ledger_time_nodes(hier, local, 0.0, bi, 0.0, bo)
+    t_f = model.ledger_time_nodes(flat, local, 0.0, bi, 0.0, bo)
+    assert t_h == pytest.approx(e["hierarchical_seconds"], rel=e["rel"])
+    assert t_f == pytest.approx(e["flat_ring_seconds"], rel=e["rel"])
+    assert round(t_f / t_h) == e["speedup_about"]
+    # stage by stage: steps [0, L-1) in-node RS, then 2(N-1) cross, then AG
+    def stage(lo, hi):
+        sub = oracle.Ledger(p, 4)
+        sub.msgs = [m for m in hier.msgs if lo <= m.step < hi]
+        return model.ledger_time_nodes(sub, local, 0.0, bi, 0.0, bo)
+    s1, s2 = local - 1, local - 1 + 2 * (nodes - 1)
+    assert stage(0, s1) == pytest.approx(e["in_node_reduce_scatter_seconds"], rel=e["rel"])
+    assert stage(s1, s2) == pytest.approx(e["cross_node_allreduce_seconds"], rel=e["rel"])
+    assert stage(s2, hier.n_steps) == pytest.approx(e["in_node_all_gather_seconds"], rel=e["rel"])
+    for algo, want in (("hierarchical", t_h), ("ring", t_f)):
+        t, _ = vc.vcoll_model_ledger_time_nodes(algo, nodes, local, n, 0.0, bi, 0.0, bo)
+        assert t == pytest.approx(want, rel=1e-12)
+
+
+def test_hierarchical_gradient_cross_node_bytes():
+    e = G["hierarchical_gradient"]
+    nodes, local = e["nodes"], e["local"]
+    p, n = nodes * local, e["bytes"] // 4
+    x = [np.zeros(1, np.float32)] * p
+    for algo, led in (("flat", oracle.allreduce(x, "ring", n=n, lo=0)[1]),
+                      ("hierarchical", oracle.allreduce_hierarchical(x, nodes, local, n=n, lo=0)[1])):
+        cross = [m for m in led.msgs if m.src // local != m.dst // local]
+        assert sum(m.bytes for m in cross) == e[f"{algo}_cross_node_bytes"]
+        # how many distinct ranks of node 0 send across: the NICs in use
+        nics = {m.src for m in cross if m.src // local == 0}
+        assert len(nics) == e[f"{algo}_nics"]
+
+
+@pytest.mark.parametrize("nodes", G["step_counts"]["nodes"])
+def test_small_message_step_counts(nodes):
+    local = G["step_counts"]["local"]
+    p = nodes * local
+    x = [np.zeros(1, np.float32)] * p
+    _, flat = oracle.allreduce(x, "ring", n=p, lo=0)
+    _, hier = oracle.allreduce_hierarchical(x, nodes, local, n=p, lo=0)
+    assert flat.n_steps == 2 * (8 * nodes - 1)
+    nic_steps = {m.step for m in hier.msgs if m.src // local != m.dst // local}
+    assert len(nic_steps) == 2 * (nodes - 1)
+    assert hier.n_steps - len(nic_steps) == 2 * 7
+
+
+# --------------------------------------------------------------------------- library against the oracle
+
+@pytest.mark.parametrize("nodes,local,n", [(2, 2, 4), (2, 8, 1000), (4, 4, 16000), (3, 5, 77), (4, 8, 1003),
+                                           (1, 6, 50), (6, 1, 50), (2, 4, 3), (8, 16, 4099), (1, 1, 9)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_library_ledger_matches_oracle(nodes, local, n, dtype):
+    p = nodes * local
+    x = [np.zeros(1, np.float32 if dtype == "f32" else np.uint16)] * p
+    _, led = oracle.allreduce_hierarchical(x, nodes, local, dtype, n=n, lo=0)
+    msgs, sent, got, steps = vc.vcoll_ledger_hierarchical(nodes, local, n, dtype)
+    assert msgs == [tuple(m) for m in led.sorted()]
+    assert steps == led.n_steps
+    assert sent == led.sent_bytes() and got == led.recv_bytes()
+
+
+@pytest.mark.parametrize("nodes,local", [(2, 8), (4, 4), (3, 5), (1, 8), (8, 1)])
+@pytest.mark.parametrize("algo", ["ring", "rd", "rabenseifner", "tree", "hierarchical"])
+def test_library_two_level_clock_matches_oracle(nodes, local, algo):
+    p, n = nodes * local, 123457
+    x = [np.zeros(1, np.float32)] * p
+    if algo == "hierarchical":
+        _, led = oracle.allreduce_hierarchical(x, nodes, local, n=n, lo=0)
+    else:
+        _, led = oracle.allreduce(x, algo, n=n, lo=0)
+    a_in, b_in, a_out, b_out = 2e-6, 450e9, 5e-6, 50e9
+    want = model.ledger_time_nodes(led, local, a_in, b_in, a_out, b_out)
+    t, steps = vc.vcoll_model_ledger_time_nodes(algo, nodes, local, n, a_in, b_in, a_out, b_out)
+    assert t == pytest.approx(want, rel=1e-12)
+    assert steps == led.n_steps
+    # one class everywhere: the two-level clock is the one-level clock
+    one = model.ledger_time(led, a_in, b_in)
+    assert model.ledger_time_nodes(led, local, a_in, b_in, a_in, b_in) == pytest.approx(one, rel=1e-12)
+
+
+def test_library_rejects_bad_shapes():
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_ledger_hierarchical(0, 4, 10)
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_ledger_hierarchical(16, 16, 10)          # 256 ranks
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_model_ledger_time_nodes("hierarchical", 2, 4, 10, 1e-6, 0.0, 1e-6, 1e9)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_windowed_oracle_equals_full_run(dtype):
+    """The GPU tests at full size compare windows of the output with the
+    oracle run on those windows only; the windowed run must agree with the
+    full run wherever both exist."""
+    nodes, local, n = 3, 4, 5003
+    x = rand(12, n, dtype, 77)
+    full, led = oracle.allreduce_hierarchical(x, nodes, local, dtype)
+    for lo, hi in ((0, 100), (400, 1300), (4990, 5003), (2080, 2090)):
+        part, led_w = oracle.allreduce_hierarchical([v[lo:hi] for v in x], nodes, local, dtype, n=n, lo=lo)
+        for r in range(12):
+            assert part[r].tobytes() == full[r][lo:hi].tobytes()
+        assert led_w.sorted() == led.sorted()
