@@ -155,6 +155,17 @@ def extras(vc, torch, h, args):
         _, mean_ms = time_launches(calls, steps, warm)
         ex[f"ddp_bucket_hierarchical_{nodes}x{local}_fused"] = {"GBps": rate(2 * p * S, mean_ms),
                                                                "us": round(mean_ms * 1e3, 1)}
+    # rooted collectives on the same bucket: broadcast of one rank's 25 MiB to
+    # 8 receive buffers (S read + 8 S written), reduce to rank 0 (8 S + S)
+    bsrc = [base[i % p].clone() for i in range(R)]
+    calls = [vc.prepare_broadcast(bsrc[i], outs[i], 0) for i in range(R)]
+    _, mean_ms = time_launches(calls, steps, warm)
+    ex["ddp_bucket_broadcast_p8"] = {"GBps": rate((p + 1) * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    rout = [torch.empty(n, device="cuda") for _ in range(R)]
+    calls = [vc.prepare_reduce(ins[i], rout[i], 0) for i in range(R)]
+    _, mean_ms = time_launches(calls, steps, warm)
+    ex["ddp_bucket_reduce_tree_p8"] = {"GBps": rate((p + 1) * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    del bsrc, rout
     # warm: one set reused back to back (partly served by the Infinity Cache)
     call = vc.prepare_allreduce("ring", ins[0], outs[0])
     _, mean_ms = time_launches([call], steps, warm)

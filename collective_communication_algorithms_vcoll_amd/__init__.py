@@ -22,12 +22,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvcoll.so")
 
 RING, RECURSIVE_DOUBLING, RABENSEIFNER, BINARY_TREE = 0, 1, 2, 3
+NAIVE, SCATTER_ALLGATHER, PIPELINED_CHAIN = 4, 5, 6
 ALGOS = {"ring": RING, "rd": RECURSIVE_DOUBLING, "recursive_doubling": RECURSIVE_DOUBLING,
-         "rabenseifner": RABENSEIFNER, "tree": BINARY_TREE, "binary_tree": BINARY_TREE}
+         "rabenseifner": RABENSEIFNER, "tree": BINARY_TREE, "binary_tree": BINARY_TREE,
+         "naive": NAIVE, "scatter_allgather": SCATTER_ALLGATHER, "chain": PIPELINED_CHAIN,
+         "pipelined_chain": PIPELINED_CHAIN}
 F32, BF16 = 0, 1
 OP_ALLREDUCE, OP_REDUCE_SCATTER, OP_ALL_GATHER, OP_ALL_TO_ALL = 0, 1, 2, 3
+OP_BROADCAST, OP_REDUCE = 4, 5
 OPS = {"allreduce": OP_ALLREDUCE, "reduce_scatter": OP_REDUCE_SCATTER,
-       "all_gather": OP_ALL_GATHER, "all_to_all": OP_ALL_TO_ALL}
+       "all_gather": OP_ALL_GATHER, "all_to_all": OP_ALL_TO_ALL,
+       "broadcast": OP_BROADCAST, "reduce": OP_REDUCE}
 MAX_RANKS = 128
 
 
@@ -88,6 +93,20 @@ def _lib():
                                                       ctypes.c_double, ctypes.c_double,
                                                       P(ctypes.c_double), P(ctypes.c_int32)]
         lib.vcoll_model_ledger_time_nodes.restype = I
+        lib.vcoll_broadcast.argtypes = [I, I64, I, I, VP, P(VP), VP]
+        lib.vcoll_broadcast.restype = I
+        lib.vcoll_reduce.argtypes = [I, I, I64, I, I, P(VP), VP, VP]
+        lib.vcoll_reduce.restype = I
+        lib.vcoll_ledger_rooted.argtypes = [I, I, I, I64, I, I, I64, P(Msg), I64, P(I64), P(I64), P(I64),
+                                            P(ctypes.c_int32)]
+        lib.vcoll_ledger_rooted.restype = I
+        D = ctypes.c_double
+        lib.vcoll_model_broadcast_formula.argtypes = [I, I, D, I64, D, D, P(D)]
+        lib.vcoll_model_broadcast_formula.restype = I
+        lib.vcoll_model_chain_optimum.argtypes = [I, D, D, D, P(D), P(D)]
+        lib.vcoll_model_chain_optimum.restype = I
+        lib.vcoll_model_clock.argtypes = [P(Msg), I64, I, I, D, D, D, D, P(D)]
+        lib.vcoll_model_clock.restype = I
         lib.vcoll_allreduce_stepwise.argtypes = [I, I, I64, I, P(VP), P(VP), VP, I64, P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise.restype = I
         D = ctypes.c_double
@@ -239,6 +258,95 @@ def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
                                            ws_ptr, ws_bytes, ctypes.byref(launches), _stream(s[0])),
            "vcoll_allreduce_stepwise")
     return recv, launches.value
+
+
+def vcoll_broadcast(send, recv, root: int = 0):
+    """Copy the root's buffer `send` into every rank's buffer of `recv` (a
+    [p, n] tensor or a list of p tensors; recv[root] may be `send` itself)."""
+    r = _ranks(recv)
+    _validate(r, "vcoll_broadcast")
+    n = r[0].numel()
+    _validate(r, "vcoll_broadcast", n)
+    if not 0 <= root < len(r):
+        raise ValueError("vcoll_broadcast: root out of range")
+    _validate([send], "vcoll_broadcast", n)
+    if send.dtype != r[0].dtype or send.device != r[0].device:
+        raise ValueError("vcoll_broadcast: send and recv differ in dtype or device")
+    targets = [t for i, t in enumerate(r) if not (i == root and t.data_ptr() == send.data_ptr())]
+    _no_overlap([send], targets, "vcoll_broadcast")
+    for i, a in enumerate(targets):
+        _no_overlap([a], targets[i + 1:], "vcoll_broadcast")
+    _check(_lib().vcoll_broadcast(len(r), n, _dtype_code(send), root, send.data_ptr() if n else None, _ptrs(r),
+                                  _stream(send)), "vcoll_broadcast")
+    return recv
+
+
+def vcoll_reduce(send, recv=None, root: int = 0, algo="tree"):
+    """Sum the p rank buffers of `send` into the root's buffer `recv`
+    (binomial tree on ranks relative to the root). Returns recv."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_reduce")
+    n = s[0].numel()
+    _validate(s, "vcoll_reduce", n)
+    if not 0 <= root < len(s):
+        raise ValueError("vcoll_reduce: root out of range")
+    if recv is None:
+        recv = torch.empty_like(s[0])
+    _validate([recv], "vcoll_reduce", n)
+    if recv.dtype != s[0].dtype or recv.device != s[0].device:
+        raise ValueError("vcoll_reduce: send and recv differ in dtype or device")
+    others = [t for i, t in enumerate(s) if not (i == root and t.data_ptr() == recv.data_ptr())]
+    _no_overlap(others, [recv], "vcoll_reduce")
+    _check(_lib().vcoll_reduce(_algo(algo), len(s), n, _dtype_code(s[0]), root, _ptrs(s),
+                               recv.data_ptr() if n else None, _stream(s[0])), "vcoll_reduce")
+    return recv
+
+
+def vcoll_ledger_rooted(op, algo, p: int, n: int, dtype: str = "f32", root: int = 0, blocks: int = 1):
+    """Ledger of a broadcast or reduce: (messages, sent, received, steps)."""
+    lib = _lib()
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    dtc = {"f32": F32, "bf16": BF16}[dtype]
+    count = ctypes.c_int64()
+    _check(lib.vcoll_ledger_rooted(opc, _algo(algo), p, n, dtc, root, blocks, None, 0, ctypes.byref(count), None,
+                                   None, None), "vcoll_ledger_rooted")
+    msgs = (Msg * max(1, count.value))()
+    sent, got, steps = (ctypes.c_int64 * p)(), (ctypes.c_int64 * p)(), ctypes.c_int32()
+    _check(lib.vcoll_ledger_rooted(opc, _algo(algo), p, n, dtc, root, blocks, msgs, count.value,
+                                   ctypes.byref(count), sent, got, ctypes.byref(steps)), "vcoll_ledger_rooted")
+    out = [(m.step, m.src, m.dst, m.src_off, m.dst_off, m.count, m.bytes) for m in msgs[:count.value]]
+    return out, list(sent), list(got), steps.value
+
+
+def vcoll_model_broadcast_formula(algo, p: int, nbytes: float, alpha: float, beta: float, blocks: int = 1) -> float:
+    t = ctypes.c_double()
+    _check(_lib().vcoll_model_broadcast_formula(_algo(algo), p, float(nbytes), blocks, float(alpha), float(beta),
+                                                ctypes.byref(t)), "vcoll_model_broadcast_formula")
+    return t.value
+
+
+def vcoll_model_chain_optimum(p: int, nbytes: float, alpha: float, beta: float) -> tuple:
+    k, t = ctypes.c_double(), ctypes.c_double()
+    _check(_lib().vcoll_model_chain_optimum(p, float(nbytes), float(alpha), float(beta), ctypes.byref(k),
+                                            ctypes.byref(t)), "vcoll_model_chain_optimum")
+    return k.value, t.value
+
+
+def vcoll_model_clock(msgs, p: int, alpha: float, beta: float, local: int | None = None,
+                      alpha_out: float | None = None, beta_out: float | None = None) -> float:
+    """Simulated clock over a ledger given as (step, src, dst, src_off,
+    dst_off, count, bytes) records; one link class unless `local` is set."""
+    arr = (Msg * max(1, len(msgs)))()
+    for i, m in enumerate(msgs):
+        arr[i] = Msg(m[0], m[1], m[2], 0, m[3], m[4], m[5], m[6])
+    t = ctypes.c_double()
+    local = p if local is None else local
+    _check(_lib().vcoll_model_clock(arr, len(msgs), p, local, float(alpha), float(beta),
+                                    float(alpha if alpha_out is None else alpha_out),
+                                    float(beta if beta_out is None else beta_out), ctypes.byref(t)),
+           "vcoll_model_clock")
+    return t.value
 
 
 def vcoll_allreduce_hierarchical(nodes: int, local: int, send, recv=None):
@@ -485,6 +593,22 @@ def prepare_allreduce_hierarchical(nodes: int, local: int, send, recv) -> Prepar
     args = (nodes, local, s[0].numel(), _dtype_code(s[0]), sp, rp, _stream(s[0]))
     return PreparedCall("vcoll_allreduce_hierarchical", _lib().vcoll_allreduce_hierarchical, args,
                         (send, recv, sp, rp))
+
+
+def prepare_broadcast(send, recv, root: int = 0) -> PreparedCall:
+    r = _ranks(recv)
+    vcoll_broadcast(send, recv, root)
+    rp = _ptrs(r)
+    args = (len(r), r[0].numel(), _dtype_code(send), root, send.data_ptr(), rp, _stream(send))
+    return PreparedCall("vcoll_broadcast", _lib().vcoll_broadcast, args, (send, recv, rp))
+
+
+def prepare_reduce(send, recv, root: int = 0) -> PreparedCall:
+    s = _ranks(send)
+    vcoll_reduce(send, recv, root)
+    sp = _ptrs(s)
+    args = (BINARY_TREE, len(s), s[0].numel(), _dtype_code(s[0]), root, sp, recv.data_ptr(), _stream(s[0]))
+    return PreparedCall("vcoll_reduce", _lib().vcoll_reduce, args, (send, recv, sp))
 
 
 def prepare_reduce_scatter(algo, send, recv) -> PreparedCall:

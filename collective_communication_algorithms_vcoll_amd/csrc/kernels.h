@@ -62,6 +62,15 @@ struct HierArgs {
   int32_t pad;
 };
 
+// Broadcast: the root's n elements copied to q receive buffers. Grid: x = tiles.
+struct BcastArgs {
+  const void* src;
+  void* dst[kMaxRanks];
+  int64_t n;
+  int32_t q;
+  int32_t vec;                // every pointer 16-byte aligned
+};
+
 // All-gather. Grid: x = tiles of one block, y = source rank.
 struct GatherArgs {
   RankPtrs ptr;
@@ -114,8 +123,11 @@ struct A2AArgs {
 };
 
 // Launchers (return hipError_t of the launch).
+// grid y = chunks: p for all-reduce and reduce-scatter, 1 for a reduce to
+// one root (q = n, r = 0, dst[0] = the root's buffer, scatter = true).
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
-                         int64_t max_chunk, hipStream_t stream);
+                         int64_t max_chunk, int chunks, hipStream_t stream);
+hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);

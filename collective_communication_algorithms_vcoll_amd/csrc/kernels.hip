@@ -611,6 +611,56 @@ __global__ __launch_bounds__(kBlock) void all_gather_kernel(const GatherArgs a) 
 }
 
 // ----------------------------------------------------------------------------
+// broadcast: every receive buffer gets the root's words ("Networks and
+// Collective Communication", section 4.1). Whatever the algorithm, the
+// result is a copy, so one pass reads the root once and writes q copies.
+
+template <int ES, int V, bool PACE>
+__global__ __launch_bounds__(kBlock) void broadcast_kernel(const BcastArgs a) {
+  using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
+  constexpr int VE = 16 / ES;
+  const int tid = threadIdx.x;
+  if (a.vec) {
+    const int64_t nvec = a.n / VE;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + tid;
+    u32x4 x[V];
+    bool valid[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t v = v0 + j * kBlock;
+      valid[j] = v < nvec;
+      x[j] = valid[j] ? ld16(a.src, v * 16) : u32x4{0, 0, 0, 0};
+    }
+    for (int r = 0; r < a.q; ++r) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (valid[j]) st16(a.dst[r], (v0 + j * kBlock) * 16, x[j]);
+      if constexpr (PACE) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the last n mod VE elements
+    if (blockIdx.x == 0 && tid < a.n - nvec * VE) {
+      const int64_t e = nvec * VE + tid;
+      const E w = static_cast<const E*>(a.src)[e];
+      for (int r = 0; r < a.q; ++r) static_cast<E*>(a.dst[r])[e] = w;
+    }
+  } else {
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock * VE) + tid;
+#pragma unroll 1
+    for (int j = 0; j < V * VE; ++j) {
+      const int64_t e = e0 + j * kBlock;
+      if (e < a.n) {
+        const E w = static_cast<const E*>(a.src)[e];
+        for (int r = 0; r < a.q; ++r) static_cast<E*>(a.dst[r])[e] = w;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // all-to-all: workgroup t moves rows_per_tile rows of one (i -> j) block
 
 __global__ __launch_bounds__(kBlock) void all_to_all_kernel(const A2AArgs a) {
@@ -788,13 +838,13 @@ constexpr int vectors_per_thread() {
 #endif
 
 template <int D, int ALGO, bool RS, int P>
-hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, hipStream_t stream) {
+hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, hipStream_t stream) {
   constexpr int V = vectors_per_thread<P>();
   constexpr int VE = Storage<D>::kVE;
   const int64_t per_tile = static_cast<int64_t>(V) * kBlock * VE;
   const int64_t tiles = (max_chunk + per_tile - 1) / per_tile;
   if (tiles == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(tiles), a.p);
+  const dim3 grid(static_cast<unsigned>(tiles), chunks);
   ReduceArgs args = a;
   args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
   if constexpr (P > 0) {
@@ -807,40 +857,59 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, hipStream_t s
 }
 
 template <int D, int ALGO, bool RS>
-hipError_t launch_reduce_algo(const ReduceArgs& a, int64_t max_chunk, hipStream_t stream) {
+hipError_t launch_reduce_algo(const ReduceArgs& a, int64_t max_chunk, int chunks, hipStream_t stream) {
   static_assert(has_fixed_kernel(2) && has_fixed_kernel(4) && has_fixed_kernel(8) && has_fixed_kernel(16),
                 "the host lays out leaf pointers by has_fixed_kernel()");
   switch (a.p) {
-    case 2: return launch_reduce_p<D, ALGO, RS, 2>(a, max_chunk, stream);
-    case 4: return launch_reduce_p<D, ALGO, RS, 4>(a, max_chunk, stream);
-    case 8: return launch_reduce_p<D, ALGO, RS, 8>(a, max_chunk, stream);
-    case 16: return launch_reduce_p<D, ALGO, RS, 16>(a, max_chunk, stream);
-    default: return launch_reduce_p<D, ALGO, RS, 0>(a, max_chunk, stream);
+    case 2: return launch_reduce_p<D, ALGO, RS, 2>(a, max_chunk, chunks, stream);
+    case 4: return launch_reduce_p<D, ALGO, RS, 4>(a, max_chunk, chunks, stream);
+    case 8: return launch_reduce_p<D, ALGO, RS, 8>(a, max_chunk, chunks, stream);
+    case 16: return launch_reduce_p<D, ALGO, RS, 16>(a, max_chunk, chunks, stream);
+    default: return launch_reduce_p<D, ALGO, RS, 0>(a, max_chunk, chunks, stream);
   }
 }
 
 template <int D>
 hipError_t launch_reduce_dtype(const ReduceArgs& a, vcoll_algo algo, bool scatter, int64_t max_chunk,
-                               hipStream_t stream) {
+                               int chunks, hipStream_t stream) {
   if (scatter) {
-    if (algo == VCOLL_RING) return launch_reduce_algo<D, VCOLL_RING, true>(a, max_chunk, stream);
-    return launch_reduce_algo<D, VCOLL_RABENSEIFNER, true>(a, max_chunk, stream);
+    if (algo == VCOLL_RING) return launch_reduce_algo<D, VCOLL_RING, true>(a, max_chunk, chunks, stream);
+    if (algo == VCOLL_BINARY_TREE)
+      return launch_reduce_algo<D, VCOLL_BINARY_TREE, true>(a, max_chunk, chunks, stream);
+    return launch_reduce_algo<D, VCOLL_RABENSEIFNER, true>(a, max_chunk, chunks, stream);
   }
   switch (algo) {
-    case VCOLL_RING: return launch_reduce_algo<D, VCOLL_RING, false>(a, max_chunk, stream);
+    case VCOLL_RING: return launch_reduce_algo<D, VCOLL_RING, false>(a, max_chunk, chunks, stream);
     case VCOLL_RECURSIVE_DOUBLING:
-      return launch_reduce_algo<D, VCOLL_RECURSIVE_DOUBLING, false>(a, max_chunk, stream);
-    case VCOLL_RABENSEIFNER: return launch_reduce_algo<D, VCOLL_RABENSEIFNER, false>(a, max_chunk, stream);
-    default: return launch_reduce_algo<D, VCOLL_BINARY_TREE, false>(a, max_chunk, stream);
+      return launch_reduce_algo<D, VCOLL_RECURSIVE_DOUBLING, false>(a, max_chunk, chunks, stream);
+    case VCOLL_RABENSEIFNER:
+      return launch_reduce_algo<D, VCOLL_RABENSEIFNER, false>(a, max_chunk, chunks, stream);
+    default: return launch_reduce_algo<D, VCOLL_BINARY_TREE, false>(a, max_chunk, chunks, stream);
   }
 }
 
 }  // namespace
 
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
-                         int64_t max_chunk, hipStream_t stream) {
-  if (dtype == VCOLL_F32) return launch_reduce_dtype<VCOLL_F32>(a, algo, scatter, max_chunk, stream);
-  return launch_reduce_dtype<VCOLL_BF16>(a, algo, scatter, max_chunk, stream);
+                         int64_t max_chunk, int chunks, hipStream_t stream) {
+  if (dtype == VCOLL_F32) return launch_reduce_dtype<VCOLL_F32>(a, algo, scatter, max_chunk, chunks, stream);
+  return launch_reduce_dtype<VCOLL_BF16>(a, algo, scatter, max_chunk, chunks, stream);
+}
+
+hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream) {
+  constexpr int V = 2;
+  const int ES = dtype == VCOLL_F32 ? 4 : 2;
+  const int64_t per_tile = static_cast<int64_t>(V) * kBlock * (16 / ES);
+  const int64_t tiles = (a.n + per_tile - 1) / per_tile;
+  if (tiles == 0 || a.q == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  const bool pace = a.vec && tiles >= VCOLL_PACE_MIN_GROUPS;
+  if (ES == 4) {
+    if (pace) return launch(broadcast_kernel<4, V, true>, grid, a, stream);
+    return launch(broadcast_kernel<4, V, false>, grid, a, stream);
+  }
+  if (pace) return launch(broadcast_kernel<2, V, true>, grid, a, stream);
+  return launch(broadcast_kernel<2, V, false>, grid, a, stream);
 }
 
 hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream) {

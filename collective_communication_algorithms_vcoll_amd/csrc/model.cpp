@@ -16,6 +16,39 @@
 
 using namespace vcoll;
 
+namespace {
+
+// Two link classes ([NCC] 2.3): ranks r and s share a node when
+// r / local == s / local. Each rank has a sending and a receiving port per
+// class; a step lasts as long as its slowest port that carries a message
+// (alpha + bytes / beta of that port's class; a 0-byte message still costs
+// alpha). With local >= p every message is of the inner class.
+double two_class_clock(const vcoll_msg* msgs, int64_t count, int p, int local, double alpha_in, double beta_in,
+                       double alpha_out, double beta_out) {
+  // per step: port key (class, direction, rank) -> bytes
+  std::map<int32_t, std::map<int64_t, int64_t>> per_step;
+  for (int64_t i = 0; i < count; ++i) {
+    const vcoll_msg& m = msgs[i];
+    const int across = (m.src / local != m.dst / local) ? 1 : 0;
+    std::map<int64_t, int64_t>& ports = per_step[m.step];
+    ports[(static_cast<int64_t>(across) * 2 + 0) * p + m.src] += m.bytes;
+    ports[(static_cast<int64_t>(across) * 2 + 1) * p + m.dst] += m.bytes;
+  }
+  double t = 0.0;
+  for (const auto& step : per_step) {
+    double slowest = 0.0;
+    for (const auto& port : step.second) {
+      const bool across = port.first >= 2 * p;
+      slowest = std::max(slowest, (across ? alpha_out : alpha_in) +
+                                      static_cast<double>(port.second) / (across ? beta_out : beta_in));
+    }
+    t += slowest;
+  }
+  return t;
+}
+
+}  // namespace
+
 extern "C" {
 
 vcoll_status vcoll_model_formula(vcoll_algo algo, int p, double bytes, double alpha, double beta,
@@ -108,33 +141,54 @@ vcoll_status vcoll_model_ledger_time_nodes(int hierarchical, vcoll_algo algo, in
                     : vcoll_ledger(VCOLL_OP_ALLREDUCE, algo, p, n, dtype, nullptr, 0, msgs.data(), count,
                                    &count, nullptr, nullptr, &steps);
   if (st != VCOLL_OK) return st;
-  // per step and rank: bytes sent and received inside the node and across
-  std::map<int32_t, std::vector<int64_t>> per_step;   // [4*p]: in-send, in-recv, out-send, out-recv
-  for (int64_t i = 0; i < count; ++i) {
-    const vcoll_msg& m = msgs[static_cast<size_t>(i)];
-    std::vector<int64_t>& b = per_step[m.step];
-    if (b.empty()) b.assign(static_cast<size_t>(4 * p), 0);
-    const bool across = m.src / local != m.dst / local;
-    b[static_cast<size_t>((across ? 2 : 0) * p + m.src)] += m.bytes;
-    b[static_cast<size_t>((across ? 3 : 1) * p + m.dst)] += m.bytes;
-  }
+  *seconds = two_class_clock(msgs.data(), count, p, local, alpha_in, beta_in, alpha_out, beta_out);
+  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
+}
+
+vcoll_status vcoll_model_clock(const vcoll_msg* msgs, int64_t n_msgs, int p, int local, double alpha_in,
+                               double beta_in, double alpha_out, double beta_out, double* seconds) {
+  if (!(alpha_in >= 0) || !(beta_in > 0) || !(alpha_out >= 0) || !(beta_out > 0) || !seconds)
+    return VCOLL_ERR_INVALID_ARG;
+  if (p < 1 || local < 1 || n_msgs < 0 || (n_msgs > 0 && !msgs)) return VCOLL_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < n_msgs; ++i)
+    if (msgs[i].src < 0 || msgs[i].src >= p || msgs[i].dst < 0 || msgs[i].dst >= p || msgs[i].bytes < 0)
+      return VCOLL_ERR_INVALID_ARG;
+  *seconds = two_class_clock(msgs, n_msgs, p, local, alpha_in, beta_in, alpha_out, beta_out);
+  return VCOLL_OK;
+}
+
+vcoll_status vcoll_model_broadcast_formula(vcoll_algo algo, int p, double nbytes, int64_t blocks, double alpha,
+                                           double beta, double* seconds) {
+  if (p < 1 || p > (1 << 20) || !(nbytes >= 0) || !(alpha >= 0) || !(beta > 0) || !seconds)
+    return VCOLL_ERR_INVALID_ARG;
+  if (algo == VCOLL_PIPELINED_CHAIN && blocks < 1) return VCOLL_ERR_INVALID_ARG;
   double t = 0.0;
-  for (const auto& kv : per_step) {
-    // the step ends when its slowest port is done; a port that carries
-    // nothing in this step costs nothing
-    double slowest = 0.0;
-    for (int r = 0; r < p; ++r)
-      for (int k = 0; k < 4; ++k) {
-        const int64_t bytes = kv.second[static_cast<size_t>(k * p + r)];
-        bool used = bytes > 0;
-        if (!used) continue;
-        const bool across = k >= 2;
-        slowest = std::max(slowest, (across ? alpha_out : alpha_in) + bytes / (across ? beta_out : beta_in));
-      }
-    t += slowest;
+  int k = 0;
+  while ((1 << k) < p) ++k;
+  switch (algo) {
+    case VCOLL_NAIVE: t = (p - 1) * (alpha + nbytes / beta); break;
+    case VCOLL_BINARY_TREE: t = k * (alpha + nbytes / beta); break;
+    case VCOLL_PIPELINED_CHAIN:
+      t = p == 1 ? 0.0 : (p - 2 + static_cast<double>(blocks)) * (alpha + nbytes / (static_cast<double>(blocks) * beta));
+      break;
+    case VCOLL_SCATTER_ALLGATHER:
+      t = p == 1 ? 0.0
+                 : (alpha + (p - 1.0) / p * nbytes / beta) + (p - 1) * (alpha + nbytes / (static_cast<double>(p) * beta));
+      break;
+    default: return VCOLL_ERR_INVALID_ARG;
   }
   *seconds = t;
-  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
+}
+
+vcoll_status vcoll_model_chain_optimum(int p, double nbytes, double alpha, double beta, double* blocks,
+                                       double* seconds) {
+  if (p < 3 || !(nbytes > 0) || !(alpha > 0) || !(beta > 0) || !blocks || !seconds) return VCOLL_ERR_INVALID_ARG;
+  // minimise (p-2+k)(alpha + n/(k beta)) over real k
+  *blocks = std::sqrt((p - 2) * nbytes / (alpha * beta));
+  const double root = std::sqrt((p - 2) * alpha) + std::sqrt(nbytes / beta);
+  *seconds = root * root;
   return VCOLL_OK;
 }
 

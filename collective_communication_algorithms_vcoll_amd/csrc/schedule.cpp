@@ -228,6 +228,68 @@ vcoll_status build_ledger_hierarchical(int nodes, int local, int64_t n, int64_t 
   return VCOLL_OK;
 }
 
+vcoll_status build_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_t elem_bytes, int root,
+                                 int64_t blocks, std::vector<vcoll_msg>& out, int32_t* n_steps) {
+  if (p < 1 || root < 0 || root >= p || n < 0) return VCOLL_ERR_INVALID_ARG;
+  out.clear();
+  LedgerBuilder L{out, elem_bytes};
+  auto abs = [&](int v) { return (v + root) % p; };
+  int masks = 0;                                  // ceil(log2 p)
+  while ((1 << masks) < p) ++masks;
+  if (op == VCOLL_OP_REDUCE) {
+    if (algo != VCOLL_BINARY_TREE) return VCOLL_ERR_UNSUPPORTED;
+    // [NCC] 5.2 binomial reduce: masks ascending, a relative rank whose
+    // lowest set bit is the mask sends its whole vector to v - mask
+    for (int s = 0; s < masks; ++s)
+      for (int v = 1; v < p; ++v)
+        if ((v & -v) == (1 << s)) L.add(s, abs(v), abs(v - (1 << s)), 0, 0, n);
+  } else if (op == VCOLL_OP_BROADCAST) {
+    switch (algo) {
+      case VCOLL_NAIVE:                           // [NCC] 5.5: one receiver per step
+        for (int s = 0; s + 1 < p; ++s) L.add(s, abs(0), abs(s + 1), 0, 0, n);
+        break;
+      case VCOLL_BINARY_TREE:                     // masks descending
+        for (int s = 0; s < masks; ++s) {
+          const int m = 1 << (masks - 1 - s);
+          for (int v = 0; v + m < p; v += 2 * m) L.add(s, abs(v), abs(v + m), 0, 0, n);
+        }
+        break;
+      case VCOLL_SCATTER_ALLGATHER: {             // [NCC] 4.2: scatter in one step, ring all-gather
+        if (p == 1) break;
+        const Chunks ch(n, p);
+        for (int v = 1; v < p; ++v) L.add(0, abs(0), abs(v), ch.off(v), ch.off(v), ch.count(v));
+        for (int s = 0; s < p - 1; ++s)
+          for (int v = 0; v < p; ++v) {
+            const int c = ((v - s) % p + p) % p;
+            L.add(1 + s, abs(v), abs((v + 1) % p), ch.off(c), ch.off(c), ch.count(c));
+          }
+        break;
+      }
+      case VCOLL_PIPELINED_CHAIN: {               // [NCC] 5.5: k blocks down the chain 0 -> 1 -> .. -> p-1
+        if (blocks < 1) return VCOLL_ERR_INVALID_ARG;
+        if (p == 1) break;
+        const int64_t qb = n / blocks, rb = n % blocks;
+        auto boff = [&](int64_t b) { return b * qb + (b < rb ? b : rb); };
+        for (int64_t t = 0; t < p - 2 + blocks; ++t)
+          for (int v = 0; v + 1 < p; ++v) {
+            const int64_t b = t - v;
+            if (b >= 0 && b < blocks) L.add(static_cast<int>(t), abs(v), abs(v + 1), boff(b), boff(b), qb + (b < rb ? 1 : 0));
+          }
+        break;
+      }
+      default:
+        return (algo >= VCOLL_RING && algo <= VCOLL_PIPELINED_CHAIN) ? VCOLL_ERR_UNSUPPORTED : VCOLL_ERR_INVALID_ARG;
+    }
+  } else {
+    return VCOLL_ERR_INVALID_ARG;
+  }
+  std::sort(out.begin(), out.end(), [](const vcoll_msg& a, const vcoll_msg& b) {
+    return std::tie(a.step, a.src, a.dst, a.src_off) < std::tie(b.step, b.src, b.dst, b.src_off);
+  });
+  if (n_steps) *n_steps = L.steps;
+  return VCOLL_OK;
+}
+
 int build_step_program(vcoll_algo algo, int p, int64_t n, bool narrow,
                        std::vector<std::vector<StepOp>>& steps) {
   // Start from the ledger: it is the list of messages, step by step. Each

@@ -38,6 +38,13 @@ void block_offsets(int p, const int64_t* splits, std::vector<int64_t>& send_off,
 vcoll_status build_ledger_hierarchical(int nodes, int local, int64_t n, int64_t elem_bytes,
                                        std::vector<vcoll_msg>& out, int32_t* n_steps);
 
+// Broadcast (op VCOLL_OP_BROADCAST; algo BINARY_TREE, NAIVE,
+// SCATTER_ALLGATHER or PIPELINED_CHAIN with `blocks` blocks) or binomial
+// reduce (VCOLL_OP_REDUCE, BINARY_TREE) rooted at `root`; ranks are taken
+// relative to the root, v = (r - root) mod p.
+vcoll_status build_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n, int64_t elem_bytes, int root,
+                                 int64_t blocks, std::vector<vcoll_msg>& out, int32_t* n_steps);
+
 // One operation of a step of the stepwise (unfused) all-reduce, on float32
 // working buffers W[r] of n elements, over elements [off, off + count):
 //   ADD    W[dst] += W[src]          (the receiver adds what arrives)

@@ -79,7 +79,25 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
     a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
   }
   a.final_merges = prog.final_merges;
-  return from_hip(launch_reduce(a, dtype, algo, scatter, ch.count(0), static_cast<hipStream_t>(stream)));
+  return from_hip(launch_reduce(a, dtype, algo, scatter, ch.count(0), p, static_cast<hipStream_t>(stream)));
+}
+
+// Two-call ledger convention shared by every ledger entry point.
+vcoll_status emit_ledger(const std::vector<vcoll_msg>& out, int32_t steps, int p, vcoll_msg* msgs, int64_t cap,
+                         int64_t* n_msgs, int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps) {
+  *n_msgs = static_cast<int64_t>(out.size());
+  if (msgs) {
+    if (cap < static_cast<int64_t>(out.size())) return VCOLL_ERR_BUFFER_TOO_SMALL;
+    std::copy(out.begin(), out.end(), msgs);
+  }
+  if (sent_bytes) std::fill(sent_bytes, sent_bytes + p, 0);
+  if (recv_bytes) std::fill(recv_bytes, recv_bytes + p, 0);
+  for (const vcoll_msg& m : out) {
+    if (sent_bytes) sent_bytes[m.src] += m.bytes;
+    if (recv_bytes) recv_bytes[m.dst] += m.bytes;
+  }
+  if (n_steps) *n_steps = steps;
+  return VCOLL_OK;
 }
 
 }  // namespace
@@ -229,19 +247,68 @@ vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_
   std::vector<vcoll_msg> out;
   int32_t steps = 0;
   build_ledger(op, algo, p, n, elem_bytes(dtype), splits, row_elems, out, &steps);
-  *n_msgs = static_cast<int64_t>(out.size());
-  if (msgs) {
-    if (cap < static_cast<int64_t>(out.size())) return VCOLL_ERR_BUFFER_TOO_SMALL;
-    std::copy(out.begin(), out.end(), msgs);
+  return emit_ledger(out, steps, p, msgs, cap, n_msgs, sent_bytes, recv_bytes, n_steps);
+}
+
+vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
+                                 int64_t blocks, vcoll_msg* msgs, int64_t cap, int64_t* n_msgs,
+                                 int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps) {
+  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || !n_msgs || root < 0 || root >= p)
+    return VCOLL_ERR_INVALID_ARG;
+  if (op != VCOLL_OP_BROADCAST && op != VCOLL_OP_REDUCE) return VCOLL_ERR_INVALID_ARG;
+  std::vector<vcoll_msg> out;
+  int32_t steps = 0;
+  const vcoll_status st = build_ledger_rooted(op, algo, p, n, elem_bytes(dtype), root, blocks, out, &steps);
+  if (st != VCOLL_OK) return st;
+  return emit_ledger(out, steps, p, msgs, cap, n_msgs, sent_bytes, recv_bytes, n_steps);
+}
+
+vcoll_status vcoll_broadcast(int p, int64_t n, vcoll_dtype dtype, int root, const void* send, void* const* recv,
+                             void* stream) {
+  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
+  if (n == 0) return VCOLL_OK;
+  if (!send || !recv) return VCOLL_ERR_INVALID_ARG;
+  BcastArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src = send;
+  a.n = n;
+  a.vec = aligned16(send);
+  for (int r = 0; r < p; ++r) {
+    if (r == root && (recv[r] == nullptr || recv[r] == send)) continue;
+    if (!recv[r]) return VCOLL_ERR_INVALID_ARG;
+    a.dst[a.q++] = recv[r];
+    a.vec = a.vec && aligned16(recv[r]);
   }
-  if (sent_bytes) std::fill(sent_bytes, sent_bytes + p, 0);
-  if (recv_bytes) std::fill(recv_bytes, recv_bytes + p, 0);
-  for (const vcoll_msg& m : out) {
-    if (sent_bytes) sent_bytes[m.src] += m.bytes;
-    if (recv_bytes) recv_bytes[m.dst] += m.bytes;
+  return from_hip(launch_broadcast(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
+                          const void* const* send, void* recv, void* stream) {
+  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
+  if (algo != VCOLL_BINARY_TREE)
+    return (algo >= VCOLL_RING && algo <= VCOLL_PIPELINED_CHAIN) ? VCOLL_ERR_UNSUPPORTED : VCOLL_ERR_INVALID_ARG;
+  if (n == 0) return VCOLL_OK;
+  if (!all_set(p, send) || !recv) return VCOLL_ERR_INVALID_ARG;
+  ReduceArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.dst[0] = recv;                  // the whole vector is one chunk, written to the root only
+  a.q = n;
+  a.r = 0;
+  a.p = p;
+  a.vec = all_aligned(p, send) && aligned16(recv);
+  // the tree runs on ranks relative to the root: leaf v is rank (v + root) mod p
+  const OrderProgram prog = order_program(VCOLL_BINARY_TREE, p);
+  if (has_fixed_kernel(p)) {
+    for (int k = 0; k < p; ++k) a.leaf[k] = send[(prog.rank[k] + root) % p];
+  } else {
+    for (int v = 0; v < p; ++v) a.leaf[v] = send[(v + root) % p];
   }
-  if (n_steps) *n_steps = steps;
-  return VCOLL_OK;
+  for (int k = 0; k < p; ++k) {
+    a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
+    a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
+  }
+  a.final_merges = prog.final_merges;
+  return from_hip(launch_reduce(a, dtype, VCOLL_BINARY_TREE, true, n, 1, static_cast<hipStream_t>(stream)));
 }
 
 vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
@@ -362,19 +429,7 @@ vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dt
   std::vector<vcoll_msg> out;
   int32_t steps = 0;
   build_ledger_hierarchical(nodes, local, n, elem_bytes(dtype), out, &steps);
-  *n_msgs = static_cast<int64_t>(out.size());
-  if (msgs) {
-    if (cap < static_cast<int64_t>(out.size())) return VCOLL_ERR_BUFFER_TOO_SMALL;
-    std::copy(out.begin(), out.end(), msgs);
-  }
-  if (sent_bytes) std::fill(sent_bytes, sent_bytes + p, 0);
-  if (recv_bytes) std::fill(recv_bytes, recv_bytes + p, 0);
-  for (const vcoll_msg& m : out) {
-    if (sent_bytes) sent_bytes[m.src] += m.bytes;
-    if (recv_bytes) recv_bytes[m.dst] += m.bytes;
-  }
-  if (n_steps) *n_steps = steps;
-  return VCOLL_OK;
+  return emit_ledger(out, steps, p, msgs, cap, n_msgs, sent_bytes, recv_bytes, n_steps);
 }
 
 vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {

@@ -62,7 +62,10 @@ typedef enum {
   VCOLL_RING = 0,                /* [NCC] 5.1, [HPC] "Ring Algorithm", [LDT] */
   VCOLL_RECURSIVE_DOUBLING = 1,  /* [NCC] 5.2 */
   VCOLL_RABENSEIFNER = 2,        /* [NCC] 5.2 */
-  VCOLL_BINARY_TREE = 3          /* [NCC] 5.2 (binomial reduce + broadcast) */
+  VCOLL_BINARY_TREE = 3,         /* [NCC] 5.2 (binomial reduce + broadcast) */
+  VCOLL_NAIVE = 4,               /* [NCC] 5.5 broadcast: the root sends to one rank per step */
+  VCOLL_SCATTER_ALLGATHER = 5,   /* [NCC] 4.2 broadcast: scatter, then ring all-gather */
+  VCOLL_PIPELINED_CHAIN = 6      /* [NCC] 5.5 broadcast: k blocks down a chain of ranks */
 } vcoll_algo;
 
 typedef enum { VCOLL_F32 = 0, VCOLL_BF16 = 1 } vcoll_dtype;
@@ -71,7 +74,9 @@ typedef enum {
   VCOLL_OP_ALLREDUCE = 0,
   VCOLL_OP_REDUCE_SCATTER = 1,
   VCOLL_OP_ALL_GATHER = 2,
-  VCOLL_OP_ALL_TO_ALL = 3
+  VCOLL_OP_ALL_TO_ALL = 3,
+  VCOLL_OP_BROADCAST = 4,        /* ledger through vcoll_ledger_rooted only */
+  VCOLL_OP_REDUCE = 5            /* ledger through vcoll_ledger_rooted only */
 } vcoll_op;
 
 /* One message of an algorithm's schedule. Offsets and count are in elements
@@ -135,6 +140,46 @@ vcoll_status vcoll_allreduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtyp
 vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                                       const void* const* send, void* const* recv, void* workspace,
                                       int64_t workspace_bytes, int32_t* n_launches, void* stream);
+
+/*
+ * Broadcast ([NCC] 4.1): every rank's buffer receives the root's n elements,
+ * bit for bit. All broadcast algorithms ([NCC] 4.2 scatter + all-gather,
+ * 5.5 naive, binomial tree, pipelined chain) leave the same bytes; they
+ * differ only in their messages (vcoll_ledger_rooted), so one pass reads
+ * `send` (the root's buffer) once and writes every recv[r]. recv holds p
+ * device pointers; recv[root] may be NULL or equal to send (then nothing is
+ * written there). Receive buffers must not overlap send or each other.
+ * 0 <= root < p.
+ */
+vcoll_status vcoll_broadcast(int p, int64_t n, vcoll_dtype dtype, int root, const void* send, void* const* recv,
+                             void* stream);
+
+/*
+ * Reduce to a root ([NCC] 4.1: elementwise sum, result on the root only) by
+ * the binomial tree of [NCC] 5.2 on ranks relative to the root,
+ * v = (r - root) mod p: masks 1, 2, 4, ..; the relative rank whose lowest
+ * set bit is the mask adds its partial sum into v - mask. `recv` is the
+ * root's output buffer (n elements; may equal send[root]); no other buffer
+ * is written. algo must be VCOLL_BINARY_TREE (others: VCOLL_ERR_UNSUPPORTED).
+ */
+vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
+                          const void* const* send, void* recv, void* stream);
+
+/*
+ * Message ledger of a rooted collective, conventions as vcoll_ledger. op
+ * VCOLL_OP_BROADCAST with algo VCOLL_NAIVE (p-1 steps, the root sends the
+ * whole vector to relative rank s+1 in step s), VCOLL_BINARY_TREE
+ * (ceil(log2 p) steps, masks descending: relative rank v, a multiple of 2m,
+ * sends to v+m), VCOLL_SCATTER_ALLGATHER (step 0: the root sends chunk v to
+ * every relative rank v != 0; then ring all-gather step s, in ledger step
+ * 1+s, has v forward chunk (v-s) mod p to v+1) or
+ * VCOLL_PIPELINED_CHAIN (`blocks` >= 1 balanced blocks; in step t relative
+ * rank v passes block t-v to v+1; p-2+blocks steps); op VCOLL_OP_REDUCE with
+ * VCOLL_BINARY_TREE. `blocks` is read only by the chain. Host only.
+ */
+vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
+                                 int64_t blocks, vcoll_msg* msgs, int64_t cap, int64_t* n_msgs,
+                                 int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps);
 
 /*
  * Hierarchical all-reduce ([NCC] 6.3; [LDT] 16 ranks as 2 nodes x 8): p =
@@ -277,6 +322,27 @@ vcoll_status vcoll_model_ledger_time_nodes(int hierarchical, vcoll_algo algo, in
                                            vcoll_dtype dtype, double alpha_in, double beta_in,
                                            double alpha_out, double beta_out, double* seconds,
                                            int32_t* n_steps);
+
+/*
+ * Closed-form broadcast times of nbytes ([NCC] 4.2, 5.5): NAIVE
+ * (p-1)(alpha + n/beta); BINARY_TREE ceil(log2 p)(alpha + n/beta);
+ * PIPELINED_CHAIN (p-2+blocks)(alpha + n/(blocks beta)); SCATTER_ALLGATHER
+ * (alpha + (p-1)/p n/beta) + (p-1)(alpha + n/(p beta)). p = 1 gives 0.
+ */
+vcoll_status vcoll_model_broadcast_formula(vcoll_algo algo, int p, double nbytes, int64_t blocks, double alpha,
+                                           double beta, double* seconds);
+
+/* The chain's optimum ([NCC] 5.5, exercise 9): blocks* = sqrt((p-2) n /
+ * (alpha beta)) (real, before rounding) and T* = (sqrt((p-2) alpha) +
+ * sqrt(n/beta))^2. Needs p >= 3. */
+vcoll_status vcoll_model_chain_optimum(int p, double nbytes, double alpha, double beta, double* blocks,
+                                       double* seconds);
+
+/* The simulated clock of vcoll_model_ledger_time_nodes over any ledger the
+ * caller holds (n_msgs records on p ranks; local = p gives the one-class
+ * clock of vcoll_model_ledger_time). Host only. */
+vcoll_status vcoll_model_clock(const vcoll_msg* msgs, int64_t n_msgs, int p, int local, double alpha_in,
+                               double beta_in, double alpha_out, double beta_out, double* seconds);
 
 #ifdef __cplusplus
 }

@@ -101,3 +101,30 @@ def ledger_time_nodes(ledger, local: int, alpha_in: float, beta_in: float, alpha
             slowest = max(slowest, a + nbytes / b)
         t += slowest
     return t
+
+
+def broadcast_formula(algo: str, p: int, nbytes: float, alpha: float, beta: float, k: int = 1) -> float:
+    """Closed-form broadcast times ("Networks and Collective Communication",
+    sections 4.2 and 5.5): naive (p-1)(alpha + n/beta); binomial tree
+    ceil(log2 p)(alpha + n/beta); pipelined chain of k blocks
+    (p-2+k)(alpha + n/(k beta)); scatter + all-gather: one scatter step that
+    puts (p-1)/p n through the root's port, then p-1 ring steps of n/p."""
+    if p == 1:
+        return 0.0
+    if algo == "naive":
+        return (p - 1) * (alpha + nbytes / beta)
+    if algo == "tree":
+        return math.ceil(math.log2(p)) * (alpha + nbytes / beta)
+    if algo == "chain":
+        return (p - 2 + k) * (alpha + nbytes / (k * beta))
+    if algo == "scatter_allgather":
+        return (alpha + (p - 1) / p * nbytes / beta) + (p - 1) * (alpha + nbytes / (p * beta))
+    raise ValueError(algo)
+
+
+def chain_optimum(p: int, nbytes: float, alpha: float, beta: float) -> tuple:
+    """Section 5.5 / exercise 9: d/dk of (p-2+k)(alpha + n/(k beta)) = 0 gives
+    k* = sqrt((p-2) n / (alpha beta)) and T* = (sqrt((p-2) alpha) + sqrt(n/beta))^2."""
+    k = math.sqrt((p - 2) * nbytes / (alpha * beta))
+    t = (math.sqrt((p - 2) * alpha) + math.sqrt(nbytes / beta)) ** 2
+    return k, t
