@@ -277,6 +277,32 @@ def extras(vc, torch, h, args):
     ex["moe_combine_fused_scatter"] = {"GBps": rate(2 * rows * rb, ms_c), "us": round(ms_c * 1e3, 1),
                                        "algorithmic_bytes": 2 * rows * rb,
                                        "combine_of_dispatch_is_identity": bool(ok)}
+    # dispatch variants: FP8 payload (quantised at the sender) and
+    # per-destination deduplication (unique rows + local expansion)
+    src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
+    f8 = vc.vcoll_moe_dispatch_fp8(toks, splits, src_g)
+    fp8_call = lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, f8)        # noqa: E731
+    _, ms_f = time_launches([fp8_call], 10, 2)
+    orb = H + H // 32
+    ex["moe_dispatch_fp8_fused_gather_quantise"] = {
+        "GBps": rate(rows * rb + rows * orb, ms_f), "us": round(ms_f * 1e3, 1),
+        "algorithmic_bytes": rows * rb + rows * orb, "payload_bytes_per_row": orb}
+    su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p8)
+    src_ug = [torch.from_numpy(x).cuda() for x in src_u]
+    exp_g = [torch.from_numpy(x).cuda() for x in expand]
+    ru = vc.vcoll_all_to_all(toks, su, src_rows=src_ug)
+    ex_out = vc.vcoll_moe_expand(ru, exp_g)
+    rows_u = int(su.sum())
+    d1 = lambda: vc.vcoll_all_to_all(toks, su, recv=ru, src_rows=src_ug)         # noqa: E731
+    d2 = lambda: vc.vcoll_moe_expand(ru, exp_g, ex_out)                           # noqa: E731
+    _, ms_u = time_launches([d1], 10, 2)
+    _, ms_x = time_launches([d2], 10, 2)
+    offrank = lambda sp: int(sp.sum() - np.trace(sp))                              # noqa: E731
+    ex["moe_dispatch_dedup"] = {
+        "rows": rows_u, "rows_plain": rows, "offrank_rows": offrank(su), "offrank_rows_plain": offrank(splits),
+        "all_to_all_us": round(ms_u * 1e3, 1), "expand_us": round(ms_x * 1e3, 1),
+        "message_bytes_bf16": offrank(su) * rb, "message_bytes_fp8": offrank(su) * orb,
+        "message_bytes_plain_bf16": offrank(splits) * rb}
     return ex
 
 

@@ -27,7 +27,7 @@ ALGOS = {"ring": RING, "rd": RECURSIVE_DOUBLING, "recursive_doubling": RECURSIVE
          "rabenseifner": RABENSEIFNER, "tree": BINARY_TREE, "binary_tree": BINARY_TREE,
          "naive": NAIVE, "scatter_allgather": SCATTER_ALLGATHER, "chain": PIPELINED_CHAIN,
          "pipelined_chain": PIPELINED_CHAIN}
-F32, BF16 = 0, 1
+F32, BF16, U8 = 0, 1, 2
 OP_ALLREDUCE, OP_REDUCE_SCATTER, OP_ALL_GATHER, OP_ALL_TO_ALL = 0, 1, 2, 3
 OP_BROADCAST, OP_REDUCE = 4, 5
 OPS = {"allreduce": OP_ALLREDUCE, "reduce_scatter": OP_REDUCE_SCATTER,
@@ -107,6 +107,11 @@ def _lib():
         lib.vcoll_model_chain_optimum.restype = I
         lib.vcoll_model_clock.argtypes = [P(Msg), I64, I, I, D, D, D, D, P(D)]
         lib.vcoll_model_clock.restype = I
+        lib.vcoll_moe_plan_dedup.argtypes = [I, I64, I, I, P(ctypes.c_int32), P(I64), P(ctypes.c_int32),
+                                             P(ctypes.c_int32), P(I64)]
+        lib.vcoll_moe_plan_dedup.restype = I
+        lib.vcoll_moe_dispatch_fp8.argtypes = [I, I64, P(I64), P(VP), P(I64), P(VP), P(VP), VP]
+        lib.vcoll_moe_dispatch_fp8.restype = I
         lib.vcoll_allreduce_stepwise.argtypes = [I, I, I64, I, P(VP), P(VP), VP, I64, P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise.restype = I
         D = ctypes.c_double
@@ -144,6 +149,8 @@ def _dtype_code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
+    if t.dtype == torch.uint8:
+        return U8                     # accepted by the all-to-all only
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -501,7 +508,7 @@ def vcoll_ledger(op, algo, p: int, n: int, dtype: str = "f32", splits=None, row_
     count, bytes), sent bytes per rank, received bytes per rank, step count)."""
     lib = _lib()
     opc = OPS[op] if isinstance(op, str) else int(op)
-    dtc = {"f32": F32, "bf16": BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    dtc = {"f32": F32, "bf16": BF16, "u8": U8}[dtype] if isinstance(dtype, str) else int(dtype)
     sp = None
     if splits is not None:
         sp_arr = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
@@ -531,7 +538,7 @@ def vcoll_model_ledger_time(op, algo, p: int, n: int, alpha: float, beta: float,
                             splits=None, row_elems: int = 0) -> tuple:
     """Simulated alpha-beta clock over the ledger: (seconds, steps)."""
     opc = OPS[op] if isinstance(op, str) else int(op)
-    dtc = {"f32": F32, "bf16": BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    dtc = {"f32": F32, "bf16": BF16, "u8": U8}[dtype] if isinstance(dtype, str) else int(dtype)
     sp = None
     if splits is not None:
         sp_arr = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
@@ -556,6 +563,68 @@ def vcoll_moe_plan(topk_ids: np.ndarray, experts_per_rank: int):
                                  splits.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                  src.ctypes.data_as(i32), dst.ctypes.data_as(i32)), "vcoll_moe_plan")
     return splits, src, dst
+
+
+def vcoll_moe_plan_dedup(topk_ids: np.ndarray, experts_per_rank: int):
+    """Deduplicated dispatch plan (see vcoll.h). Returns (splits_unique [p, p],
+    src_unique: list of p int32 arrays (the token of each sent row), expand:
+    list of p int32 arrays (for each plain-layout row, the deduplicated row))."""
+    ids = np.ascontiguousarray(np.asarray(topk_ids, dtype=np.int32))
+    p, tokens, topk = ids.shape
+    rows = tokens * topk
+    splits = np.zeros((p, p), dtype=np.int64)
+    src = np.zeros((p, rows), dtype=np.int32)
+    expand = np.zeros((p, p * rows), dtype=np.int32)
+    count = np.zeros(p, dtype=np.int64)
+    i32, i64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    _check(_lib().vcoll_moe_plan_dedup(p, tokens, topk, experts_per_rank, ids.ctypes.data_as(i32),
+                                       splits.ctypes.data_as(i64), src.ctypes.data_as(i32),
+                                       expand.ctypes.data_as(i32), count.ctypes.data_as(i64)),
+           "vcoll_moe_plan_dedup")
+    return (splits, [src[i, :int(splits[i].sum())].copy() for i in range(p)],
+            [expand[j, :int(count[j])].copy() for j in range(p)])
+
+
+def vcoll_moe_expand(recv_unique, expand, out=None):
+    """Local expansion of a deduplicated dispatch: out[j][x] = recv_unique[j][expand[j][x]]
+    (the diagonal blocks of one all-to-all; no message)."""
+    p = len(recv_unique)
+    counts = [int(e.numel()) for e in expand]
+    return vcoll_all_to_all(recv_unique, np.diag(counts).astype(np.int64), recv=out, src_rows=expand)
+
+
+def vcoll_moe_dispatch_fp8(tokens, splits, src_rows, recv=None):
+    """Dispatch bfloat16 token rows quantised to E4M3 with a power-of-two
+    scale per 128 elements (see vcoll.h). tokens: p bfloat16 tensors
+    [T_i, hidden]; src_rows: p int32 GPU tensors. Returns p uint8 tensors
+    [rows_j, hidden + hidden // 32]."""
+    import torch
+    t = list(tokens)
+    p = len(t)
+    sp = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
+    H = t[0].shape[1]
+    dev = t[0].device
+    for x in t:
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != H or not x.is_contiguous() or x.device != dev:
+            raise ValueError("vcoll_moe_dispatch_fp8: tokens must be contiguous bfloat16 [T, hidden] on one GPU")
+    if H % 128:
+        raise ValueError("vcoll_moe_dispatch_fp8: hidden must be a multiple of 128")
+    orb = H + H // 32
+    if recv is None:
+        recv = [torch.empty((int(sp[:, j].sum()), orb), dtype=torch.uint8, device=dev) for j in range(p)]
+    r = list(recv)
+    for j in range(p):
+        if r[j].dtype != torch.uint8 or not r[j].is_contiguous() or r[j].numel() < int(sp[:, j].sum()) * orb:
+            raise ValueError(f"vcoll_moe_dispatch_fp8: recv[{j}] too small or not contiguous uint8")
+    g = list(src_rows)
+    for i in range(p):
+        if g[i].dtype != torch.int32 or g[i].device != dev or g[i].numel() < int(sp[i].sum()):
+            raise ValueError(f"vcoll_moe_dispatch_fp8: src_rows[{i}] must be int32 on the GPU, one per sent row")
+    _no_overlap(t, r, "vcoll_moe_dispatch_fp8")
+    rows = (ctypes.c_int64 * p)(*[x.shape[0] for x in t])
+    _check(_lib().vcoll_moe_dispatch_fp8(p, H, sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptrs(t), rows,
+                                         _ptrs(g), _ptrs(r), _stream(t[0])), "vcoll_moe_dispatch_fp8")
+    return recv
 
 
 def vcoll_bench_copy(dst, src) -> None:

@@ -122,12 +122,23 @@ struct A2AArgs {
   A2ABlock b[kA2ABlocks];
 };
 
+// FP8 dispatch: per (block, row tile) workgroup as the all-to-all, each row
+// gathered from a bfloat16 token table and quantised on the way.
+struct Fp8Args {
+  int64_t hidden;             // elements per row, a multiple of 128
+  int64_t out_row_bytes;      // hidden + hidden / 32
+  int32_t nblocks;
+  int32_t rows_per_tile;
+  A2ABlock b[kA2ABlocks];     // src = token table, src_idx = gather map, dst = first row of the block
+};
+
 // Launchers (return hipError_t of the launch).
 // grid y = chunks: p for all-reduce and reduce-scatter, 1 for a reduce to
 // one root (q = n, r = 0, dst[0] = the root's buffer, scatter = true).
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
                          int64_t max_chunk, int chunks, hipStream_t stream);
 hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream);
+hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);

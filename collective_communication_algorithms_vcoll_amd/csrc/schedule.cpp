@@ -384,4 +384,57 @@ vcoll_status moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
   return VCOLL_OK;
 }
 
+vcoll_status moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank,
+                            const int32_t* topk_ids, int64_t* splits_unique, int32_t* src_unique,
+                            int32_t* expand, int64_t* expand_count) {
+  const int64_t rows = tokens * topk;
+  std::vector<int64_t> splits(static_cast<size_t>(p) * p);
+  std::vector<int32_t> src(static_cast<size_t>(p) * rows), dst(static_cast<size_t>(p) * rows);
+  const vcoll_status st = moe_plan(p, tokens, topk, experts_per_rank, topk_ids, splits.data(), src.data(), dst.data());
+  if (st != VCOLL_OK) return st;
+  // where[j * tokens + t]: position of token t inside rank i's block for
+  // rank j of the deduplicated send (-1: t does not go to j)
+  std::vector<int32_t> where(static_cast<size_t>(p) * tokens);
+  auto dedup_rank = [&](int i) {
+    std::fill(where.begin(), where.end(), -1);
+    const int32_t* ids = topk_ids + static_cast<int64_t>(i) * rows;
+    for (int64_t t = 0; t < tokens; ++t)
+      for (int k = 0; k < topk; ++k) where[static_cast<size_t>(ids[t * topk + k] / experts_per_rank) * tokens + t] = 0;
+    int64_t pos = 0;
+    for (int j = 0; j < p; ++j) {
+      int32_t n = 0;
+      for (int64_t t = 0; t < tokens; ++t) {
+        int32_t& w = where[static_cast<size_t>(j) * tokens + t];
+        if (w < 0) continue;
+        w = n++;
+        src_unique[static_cast<int64_t>(i) * rows + pos++] = static_cast<int32_t>(t);
+      }
+      splits_unique[static_cast<int64_t>(i) * p + j] = n;
+    }
+  };
+  for (int i = 0; i < p; ++i) dedup_rank(i);
+  // rank j's plain layout holds the blocks of ranks 0..p-1, each in the
+  // sender's (expert, token) order; its deduplicated buffer the same blocks,
+  // each in token order
+  const int64_t cap = static_cast<int64_t>(p) * rows;
+  std::vector<int64_t> xoff(p, 0), uoff(p, 0);
+  for (int i = 0; i < p; ++i) {
+    dedup_rank(i);
+    int64_t s0 = 0;                       // offset of block (i -> j) in rank i's plain send order
+    for (int j = 0; j < p; ++j) {
+      const int64_t nij = splits[static_cast<size_t>(i) * p + j];
+      for (int64_t r = 0; r < nij; ++r) {
+        const int32_t t = src[static_cast<size_t>(i) * rows + s0 + r];
+        expand[static_cast<int64_t>(j) * cap + xoff[j] + r] =
+            static_cast<int32_t>(uoff[j] + where[static_cast<size_t>(j) * tokens + t]);
+      }
+      s0 += nij;
+      xoff[j] += nij;
+      uoff[j] += splits_unique[static_cast<int64_t>(i) * p + j];
+    }
+  }
+  for (int j = 0; j < p; ++j) expand_count[j] = xoff[j];
+  return VCOLL_OK;
+}
+
 }  // namespace vcoll

@@ -72,4 +72,10 @@ vcoll_status moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
                       const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
                       int32_t* dst_rows);
 
+// Deduplicated dispatch plan (one row per (token, destination rank)) and the
+// expansion map back to the plain layout of moe_plan; see vcoll.h.
+vcoll_status moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank,
+                            const int32_t* topk_ids, int64_t* splits_unique, int32_t* src_unique,
+                            int32_t* expand, int64_t* expand_count);
+
 }  // namespace vcoll

@@ -25,9 +25,12 @@ vcoll_status from_hip(hipError_t e) {
   return VCOLL_ERR_HIP;
 }
 
-int64_t elem_bytes(vcoll_dtype d) { return d == VCOLL_F32 ? 4 : 2; }
+int64_t elem_bytes(vcoll_dtype d) { return d == VCOLL_F32 ? 4 : (d == VCOLL_BF16 ? 2 : 1); }
 
 bool valid_dtype(int d) { return d == VCOLL_F32 || d == VCOLL_BF16; }
+
+// the all-to-all only moves rows, so it also takes raw bytes
+bool valid_a2a_dtype(int d) { return valid_dtype(d) || d == VCOLL_U8; }
 
 bool valid_algo(int a) { return a >= VCOLL_RING && a <= VCOLL_BINARY_TREE; }
 
@@ -162,7 +165,7 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
                               const int32_t* const* src_rows, const int64_t* src_table_rows,
                               const int32_t* const* dst_rows, const int64_t* dst_table_rows,
                               void* stream) {
-  if (!valid_p(p) || row_elems < 0 || !valid_dtype(dtype) || !splits) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || row_elems < 0 || !valid_a2a_dtype(dtype) || !splits) return VCOLL_ERR_INVALID_ARG;
   const int64_t rb = row_elems * elem_bytes(dtype);
   std::vector<int64_t> sent(p, 0), got(p, 0);
   for (int i = 0; i < p; ++i)
@@ -233,8 +236,9 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
 vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                           const int64_t* splits, int64_t row_elems, vcoll_msg* msgs, int64_t cap,
                           int64_t* n_msgs, int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps) {
-  if (!valid_p(p) || !valid_dtype(dtype) || !n_msgs) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !n_msgs) return VCOLL_ERR_INVALID_ARG;
   if (op < VCOLL_OP_ALLREDUCE || op > VCOLL_OP_ALL_TO_ALL) return VCOLL_ERR_INVALID_ARG;
+  if (!(op == VCOLL_OP_ALL_TO_ALL ? valid_a2a_dtype(dtype) : valid_dtype(dtype))) return VCOLL_ERR_INVALID_ARG;
   if (op == VCOLL_OP_ALL_TO_ALL) {
     if (!splits || row_elems < 0) return VCOLL_ERR_INVALID_ARG;
     for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
@@ -430,6 +434,79 @@ vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dt
   int32_t steps = 0;
   build_ledger_hierarchical(nodes, local, n, elem_bytes(dtype), out, &steps);
   return emit_ledger(out, steps, p, msgs, cap, n_msgs, sent_bytes, recv_bytes, n_steps);
+}
+
+vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank, const int32_t* topk_ids,
+                                  int64_t* splits_unique, int32_t* src_unique, int32_t* expand,
+                                  int64_t* expand_count) {
+  if (!valid_p(p) || tokens < 0 || topk < 1 || experts_per_rank < 1 || !topk_ids || !splits_unique ||
+      !src_unique || !expand || !expand_count)
+    return VCOLL_ERR_INVALID_ARG;
+  if (tokens * topk > INT32_MAX || static_cast<int64_t>(p) * tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  return moe_plan_dedup(p, tokens, topk, experts_per_rank, topk_ids, splits_unique, src_unique, expand,
+                        expand_count);
+}
+
+vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits, const void* const* tokens,
+                                    const int64_t* token_rows, const int32_t* const* src_rows,
+                                    void* const* recv, void* stream) {
+  if (!valid_p(p) || hidden <= 0 || hidden % 128 != 0 || !splits || !token_rows || !src_rows)
+    return VCOLL_ERR_INVALID_ARG;
+  std::vector<int64_t> sent(p, 0), got(p, 0);
+  for (int i = 0; i < p; ++i)
+    for (int j = 0; j < p; ++j) {
+      const int64_t s = splits[i * p + j];
+      if (s < 0 || s > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+      sent[i] += s;
+      got[j] += s;
+      if (sent[i] > INT32_MAX || got[j] > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+    }
+  for (int i = 0; i < p; ++i) {
+    if (sent[i] > 0 && (!tokens || !tokens[i] || !aligned16(tokens[i]) || !src_rows[i] ||
+                        token_rows[i] < 0 || token_rows[i] > INT32_MAX))
+      return VCOLL_ERR_INVALID_ARG;
+    if (got[i] > 0 && (!recv || !recv[i] || (reinterpret_cast<uintptr_t>(recv[i]) & 3u) != 0))
+      return VCOLL_ERR_INVALID_ARG;
+  }
+  if (hidden * 2 > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  const int64_t orb = hidden + hidden / 32;
+  std::vector<int64_t> so, ro;
+  block_offsets(p, splits, so, ro);
+  const int32_t rows_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / (2 * hidden))));
+  std::vector<A2ABlock> blocks;
+  for (int i = 0; i < p; ++i)
+    for (int j = 0; j < p; ++j) {
+      const int64_t rows = splits[i * p + j];
+      if (rows == 0) continue;
+      A2ABlock b{};
+      b.src = static_cast<const char*>(tokens[i]);
+      b.dst = static_cast<char*>(recv[j]) + ro[i * p + j] * orb;
+      b.src_idx = src_rows[i] + so[i * p + j];
+      b.dst_idx = nullptr;
+      b.rows = static_cast<int32_t>(rows);
+      b.src_limit = static_cast<int32_t>(token_rows[i]);
+      b.dst_limit = static_cast<int32_t>(rows);
+      blocks.push_back(b);
+    }
+  for (size_t b0 = 0; b0 < blocks.size(); b0 += kA2ABlocks) {
+    Fp8Args a;
+    std::memset(&a, 0, sizeof(a));
+    a.hidden = hidden;
+    a.out_row_bytes = orb;
+    a.rows_per_tile = rows_per_tile;
+    int64_t tiles = 0;
+    const size_t nb = std::min<size_t>(kA2ABlocks, blocks.size() - b0);
+    for (size_t k = 0; k < nb; ++k) {
+      a.b[k] = blocks[b0 + k];
+      a.b[k].tile_start = static_cast<int32_t>(tiles);
+      tiles += (a.b[k].rows + rows_per_tile - 1) / rows_per_tile;
+    }
+    a.nblocks = static_cast<int32_t>(nb);
+    const vcoll_status st =
+        from_hip(launch_dispatch_fp8(a, static_cast<int32_t>(tiles), static_cast<hipStream_t>(stream)));
+    if (st != VCOLL_OK) return st;
+  }
+  return VCOLL_OK;
 }
 
 vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {

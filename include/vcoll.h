@@ -68,7 +68,11 @@ typedef enum {
   VCOLL_PIPELINED_CHAIN = 6      /* [NCC] 5.5 broadcast: k blocks down a chain of ranks */
 } vcoll_algo;
 
-typedef enum { VCOLL_F32 = 0, VCOLL_BF16 = 1 } vcoll_dtype;
+typedef enum {
+  VCOLL_F32 = 0,
+  VCOLL_BF16 = 1,
+  VCOLL_U8 = 2                   /* raw bytes: vcoll_all_to_all and its ledger only */
+} vcoll_dtype;
 
 typedef enum {
   VCOLL_OP_ALLREDUCE = 0,
@@ -180,6 +184,45 @@ vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, 
 vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
                                  int64_t blocks, vcoll_msg* msgs, int64_t cap, int64_t* n_msgs,
                                  int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps);
+
+/*
+ * Deduplicated MoE dispatch plan ([NCC] 7.4 and exercise 10: a token goes
+ * once to each place that needs it and is then copied locally). Host only,
+ * integers only; topk_ids and expert placement as vcoll_moe_plan. Rank i
+ * sends each token once to every rank j holding at least one of its chosen
+ * experts, rows ordered by (j, token): splits_unique [p*p] int64 rows i -> j,
+ * src_unique [p][tokens*topk] int32 the token of each sent row (the first
+ * sum_j splits_unique[i][j] entries are used). Rank j's deduplicated
+ * receive buffer holds the blocks of ranks 0..p-1 in order; expand
+ * [p][p*tokens*topk] int32 gives, for each row of the plain dispatch layout
+ * of vcoll_moe_plan at rank j (expand_count[j] = sum_i splits[i][j] rows),
+ * the deduplicated row it copies. Dispatch is vcoll_all_to_all(
+ * splits_unique, src_rows = src_unique) followed by the local expansion
+ * vcoll_all_to_all with diagonal splits expand_count and src_rows = expand;
+ * the result equals the plain dispatch bit for bit.
+ */
+vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank, const int32_t* topk_ids,
+                                  int64_t* splits_unique, int32_t* src_unique, int32_t* expand,
+                                  int64_t* expand_count);
+
+/*
+ * MoE dispatch with an FP8 payload ([NCC] 7.4: DeepSeek-V3 dispatches in
+ * FP8, combines in BF16). Rank i's k-th sent row is token src_rows[i][k] of
+ * its bfloat16 table tokens[i] ([token_rows[i]][hidden]); it is quantised
+ * at the sender and lands, in the all-to-all layout of vcoll_all_to_all, in
+ * recv[j] as a row of hidden + hidden/32 bytes: hidden E4M3 codes (OCP FP8
+ * E4M3, no infinities, largest 448, round to nearest even), then one
+ * float32 scale per group of 128 elements. A group's scale is 2^k, k the
+ * smallest integer with amax <= 448 * 2^k (amax the largest finite |x| of
+ * the group; k clamped to [-126, 126]; k = 0 for an all-zero group), and
+ * element x is stored as E4M3(x * 2^-k); non-finite elements store 0x7F.
+ * hidden must be a positive multiple of 128; token tables 16-byte aligned
+ * and receive buffers 4-byte aligned; an index outside [0, token_rows[i])
+ * skips its row.
+ */
+vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits, const void* const* tokens,
+                                    const int64_t* token_rows, const int32_t* const* src_rows,
+                                    void* const* recv, void* stream);
 
 /*
  * Hierarchical all-reduce ([NCC] 6.3; [LDT] 16 ranks as 2 nodes x 8): p =

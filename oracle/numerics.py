@@ -37,7 +37,7 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_to_f32(f32_to_bf16(x))
 
 
-ELEM_BYTES = {"f32": 4, "bf16": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "u8": 1}         # u8: raw bytes (all-to-all payloads only)
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:

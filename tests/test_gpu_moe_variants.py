@@ -1,0 +1,170 @@
+"""GPU parity of the MoE dispatch variants: the FP8-payload dispatch against
+the oracle's quantiser, byte for byte (codes and scales), and the
+deduplicated dispatch plus local expansion against the plain dispatch, bit
+for bit, up to the full MoE workload."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import fp8, moe
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vc():
+    import torch
+    assert torch.cuda.is_available()
+    import collective_communication_algorithms_vcoll_amd as m
+    return m
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def to_gpu_bf16(rows):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def gpu_i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def small_routing(p, T, K, E, seed):
+    return [np.stack([np.sort(np.random.default_rng([seed, i, t]).choice(E, K, replace=False))
+                      for t in range(T)]).astype(np.int32) for i in range(p)]
+
+
+def check_fp8(vc, toks, topk, epr, what):
+    p = len(toks)
+    splits, src, _ = vc.vcoll_moe_plan(np.stack(topk), epr)
+    say(f"vcoll_moe_dispatch_fp8 {what}")
+    recv = vc.vcoll_moe_dispatch_fp8([to_gpu_bf16(t) for t in toks], splits, [gpu_i32(s) for s in src])
+    sync()
+    want, _ = moe.dispatch_fp8(toks, splits, list(src))
+    for j in range(p):
+        got = recv[j].cpu().numpy()
+        assert got.shape == want[j].shape
+        bad = np.argwhere(got != want[j])
+        assert bad.size == 0, f"{what}: rank {j}: {len(bad)} bytes differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("H", [128, 384, 7168])
+def test_fp8_dispatch_matches_oracle(vc, H):
+    p, T, K, E = 4, 48, 3, 16
+    topk = small_routing(p, T, K, E, H)
+    toks = [workloads.rank_window(workloads.TAG_TEST * 1000 + 950, i, 0, T * H, ("normal", 0.0, 1.0),
+                                  "bf16").reshape(T, H) for i in range(p)]
+    check_fp8(vc, toks, topk, E // p, f"H={H}")
+
+
+def test_fp8_dispatch_special_values(vc):
+    """Rounding ties, the subnormal grid, zero and negative zero, group
+    maxima exactly at 448 * 2^k, all-zero groups, tiny and huge groups, and
+    non-finite elements."""
+    p, T, H = 2, 8, 256
+    rng = np.random.default_rng(5)
+    rows = np.zeros((T, H), np.float32)
+    rows[0] = rng.normal(0, 1, H)
+    rows[1, :128] = np.ldexp(rng.integers(1, 16, 128) * (1 + rng.integers(0, 2, 128) / 16.0), -12)   # ties below 2^-6
+    rows[1, 128:] = 448.0 * np.ldexp(1.0, rng.integers(-20, 20))
+    rows[2, :128] = 0.0
+    rows[2, 128:] = -0.0
+    rows[3] = np.ldexp(rng.normal(0, 1, H), 100)
+    rows[4] = np.ldexp(rng.normal(0, 1, H), -100)
+    rows[5, :128] = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -10, 1.5 * 2.0 ** -10, 448.0] + [0.0] * 122)
+    rows[6, :4] = [np.nan, np.inf, -np.inf, 1.0]
+    rows[7] = rng.uniform(-1, 1, H)
+    bf = oracle.f32_to_bf16(rows)
+    toks = [bf, bf[::-1].copy()]
+    topk = [np.array([[0], [1], [0], [1], [0], [1], [0], [1]], np.int32)] * p
+    check_fp8(vc, toks, topk, 1, "special values")
+
+
+def test_fp8_dispatch_skips_out_of_range_rows(vc):
+    import torch
+    p, T, H = 2, 4, 128
+    toks = [to_gpu_bf16(np.zeros((T, H), np.uint16)) for _ in range(p)]
+    recv = [torch.full((2, H + 4), 7, dtype=torch.uint8, device="cuda") for _ in range(p)]
+    splits = np.array([[1, 1], [1, 1]])
+    src = [gpu_i32([0, 99]), gpu_i32([-1, 3])]
+    vc.vcoll_moe_dispatch_fp8(toks, splits, src, recv)
+    sync()
+    assert torch.all(recv[0][0, :H] == 0) and torch.all(recv[0][1] == 7)      # row 1 came from index -1
+    assert torch.all(recv[1][0] == 7) and torch.all(recv[1][1, :H] == 0)      # index 99 skipped
+
+
+def test_dedup_dispatch_and_expand_equal_plain(vc):
+    """Full MoE workload (p = 8, 4096 tokens x 7168 bf16, top-8 of 256):
+    the deduplicated all-to-all plus the local expansion equals the plain
+    dispatch bit for bit."""
+    import torch
+    M = workloads.MOE
+    p, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    say("plans")
+    splits, src, _ = vc.vcoll_moe_plan(topk, E // p)
+    su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
+    say("plain dispatch")
+    plain = vc.vcoll_all_to_all(toks, splits, src_rows=[gpu_i32(s) for s in src])
+    say("deduplicated dispatch + expansion")
+    recv_u = vc.vcoll_all_to_all(toks, su, src_rows=[gpu_i32(s) for s in src_u])
+    out = vc.vcoll_moe_expand(recv_u, [gpu_i32(e) for e in expand])
+    sync()
+    for j in range(p):
+        assert torch.equal(out[j].view(torch.int16), plain[j].view(torch.int16))
+    assert int(su.sum()) < int(splits.sum())
+
+
+def test_fp8_dedup_combination(vc):
+    """FP8 payload over the deduplicated plan, then the byte-row expansion,
+    equals the FP8 dispatch over the plain plan."""
+    import torch
+    p, T, K, E, H = 8, 200, 8, 256, 7168
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    splits, src, _ = vc.vcoll_moe_plan(topk, E // p)
+    su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
+    plain = vc.vcoll_moe_dispatch_fp8(toks, splits, [gpu_i32(s) for s in src])
+    recv_u = vc.vcoll_moe_dispatch_fp8(toks, su, [gpu_i32(s) for s in src_u])
+    out = vc.vcoll_moe_expand(recv_u, [gpu_i32(e) for e in expand])
+    sync()
+    for j in range(p):
+        assert torch.equal(out[j], plain[j])
+
+
+def test_fp8_full_workload_sampled_rows(vc):
+    """Full MoE workload in FP8: 64 sampled received rows per rank against
+    the oracle's quantiser applied to the token row each one carries."""
+    M = workloads.MOE
+    p, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    splits, src, _ = vc.vcoll_moe_plan(topk, E // p)
+    say("generating MoE tokens")
+    toks = [workloads.moe_tokens(r, T, H) for r in range(p)]
+    recv = vc.vcoll_moe_dispatch_fp8([to_gpu_bf16(t) for t in toks], splits, [gpu_i32(s) for s in src])
+    sync()
+    # received row x of rank j: from sender i with recv offset, token src[i][so + r]
+    send_off = np.concatenate([np.zeros((p, 1), np.int64), np.cumsum(splits, axis=1)[:, :-1]], axis=1)
+    rng = np.random.default_rng(1)
+    for j in range(p):
+        base = 0
+        rows, want_tok = [], []
+        for i in range(p):
+            n = int(splits[i, j])
+            for r in rng.choice(n, size=min(8, n), replace=False) if n else []:
+                rows.append(base + int(r))
+                want_tok.append((i, int(src[i][send_off[i, j] + r])))
+            base += n
+        got = recv[j][rows].cpu().numpy()
+        want = fp8.quantize_rows(np.stack([oracle.bf16_to_f32(toks[i][t]) for i, t in want_tok]))
+        assert np.array_equal(got, want), f"rank {j}"
