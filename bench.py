@@ -40,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "all-reduce effective HBM GB/s (p=8, 25 MB/rank fp32) + % of HBM roofline"
 PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
-KERNEL_SOURCES = ("kernels.hip", "kernels.h", "order.h")
+KERNEL_SOURCES = ("reduce.hip", "device.h", "kernels.h", "order.h")   # what defines the headline kernel
 
 
 def kernel_source_hash() -> str:

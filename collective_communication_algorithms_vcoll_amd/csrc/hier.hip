@@ -1,0 +1,181 @@
+// The fused hierarchical / 2D all-reduce kernel of libvcoll for gfx950.
+#include "device.h"
+
+namespace vcoll {
+namespace {
+
+using namespace dev;
+
+// ----------------------------------------------------------------------------
+// hierarchical / 2D all-reduce ("Networks and Collective Communication",
+// sections 6.1 and 6.3): ranks form `nodes` groups of `local`. In piece j of
+// chunk l the value is an outer chain over the groups, starting after group
+// j (the cross-group ring reduce-scatter), of inner chains over each group's
+// ranks, starting after rank l of the group (the in-group ring
+// reduce-scatter).
+
+__device__ __forceinline__ void hier_segment(const HierArgs& a, int u, int& l, int& j, int64_t& off,
+                                             int64_t& cnt) {
+  const int N = a.nodes, Lc = a.local;
+  l = u / N;
+  j = u - l * N;
+  const int64_t qL = a.n / Lc, rL = a.n % Lc;
+  const int64_t offL = l * qL + (l < rL ? l : rL);
+  const int64_t lenL = qL + (l < rL ? 1 : 0);
+  const int64_t qN = lenL / N, rN = lenL % N;
+  off = offL + j * qN + (j < rN ? j : rN);
+  cnt = qN + (j < rN ? 1 : 0);
+}
+
+template <int D>
+__device__ __forceinline__ void hier_one(const HierArgs& a, int N, int Lc, int l, int j, int64_t e) {
+  using S = Storage<D>;
+  using E = typename S::elem;
+  float outer = 0.0f;
+  for (int ko = 0; ko < N; ++ko) {
+    const int g = (j + 1 + ko) % N;
+    float inner = 0.0f;
+    for (int ki = 0; ki < Lc; ++ki) {
+      const float v = S::widen1(static_cast<const E*>(a.ptr.src[g * Lc + (l + 1 + ki) % Lc])[e]);
+      inner = ki == 0 ? v : inner + v;
+    }
+    outer = ko == 0 ? inner : outer + inner;
+  }
+  const E out = S::narrow1(outer);
+  for (int r = 0; r < N * Lc; ++r) static_cast<E*>(a.ptr.dst[r])[e] = out;
+}
+
+// One 16-byte vector per thread; the loads of group ko+1 go out before group
+// ko is added (NN, LL compiled in; 0 = read from the arguments).
+template <int D, int NN, int LL, bool LARGE, bool FULL>
+__device__ __forceinline__ void hier_vector(const HierArgs& a, int l, int j, int64_t boff, bool valid) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  float outer[VE], inner[VE], v[VE];
+  if constexpr (NN > 0) {
+    u32x4 raw[2][LL];
+    static_for<0, NN + 1>([&](auto kc) {
+      constexpr int ko = decltype(kc)::value;
+      if constexpr (ko < NN) {
+        const int g = (j + 1 + ko) % NN;
+#pragma unroll
+        for (int ki = 0; ki < LL; ++ki) {
+          const void* src = a.ptr.src[g * LL + (l + 1 + ki) % LL];
+          raw[ko & 1][ki] = (FULL || valid) ? ld16(src, boff) : u32x4{0, 0, 0, 0};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ko >= 1) {
+        constexpr int q = ko - 1;
+#pragma unroll
+        for (int ki = 0; ki < LL; ++ki) {
+          S::widen(raw[q & 1][ki], v);
+#pragma unroll
+          for (int i = 0; i < VE; ++i) inner[i] = ki == 0 ? v[i] : inner[i] + v[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VE; ++i) outer[i] = q == 0 ? inner[i] : outer[i] + inner[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    const int N = a.nodes, Lc = a.local;
+    for (int ko = 0; ko < N; ++ko) {
+      const int g = (j + 1 + ko) % N;
+      for (int ki = 0; ki < Lc; ++ki) {
+        const u32x4 w = valid ? ld16(a.ptr.src[g * Lc + (l + 1 + ki) % Lc], boff) : u32x4{0, 0, 0, 0};
+        S::widen(w, v);
+        for (int i = 0; i < VE; ++i) inner[i] = ki == 0 ? v[i] : inner[i] + v[i];
+      }
+      for (int i = 0; i < VE; ++i) outer[i] = ko == 0 ? inner[i] : outer[i] + inner[i];
+    }
+  }
+  if (!FULL && !valid) return;
+  const u32x4 out = S::narrow(outer);
+  if constexpr (NN > 0) {
+    static_for<0, NN * LL>([&](auto rc) {
+      st16(a.ptr.dst[decltype(rc)::value], boff, out);
+      if constexpr (LARGE) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  } else {
+    for (int r = 0; r < a.nodes * a.local; ++r) st16(a.ptr.dst[r], boff, out);
+  }
+}
+
+template <int D, int NN, int LL, bool LARGE>
+__global__ __launch_bounds__(kBlock) void hier_kernel(const HierArgs a) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  constexpr int ES = 16 / VE;
+  const int N = NN > 0 ? NN : a.nodes, Lc = LL > 0 ? LL : a.local;
+  int l, j;
+  int64_t off, cnt;
+  hier_segment(a, blockIdx.y, l, j, off, cnt);
+  const int tid = threadIdx.x;
+  if (a.vec) {
+    const int64_t head = (VE - off % VE) % VE < cnt ? (VE - off % VE) % VE : cnt;
+    const int64_t nvec = (cnt - head) / VE;
+    const int64_t e_base = off + head;
+    const int64_t v = static_cast<int64_t>(blockIdx.x) * kBlock + tid;
+    if (static_cast<int64_t>(blockIdx.x) * kBlock < nvec) {
+      const int64_t boff = (e_base + v * VE) * ES;
+      if ((static_cast<int64_t>(blockIdx.x) + 1) * kBlock <= nvec) {
+        hier_vector<D, NN, LL, LARGE, true>(a, l, j, boff, true);
+      } else {
+        hier_vector<D, NN, LL, LARGE, false>(a, l, j, boff, v < nvec);
+      }
+    }
+    if (blockIdx.x == 0) {
+      const int64_t tail = cnt - head - nvec * VE;
+      if (tid < head) hier_one<D>(a, N, Lc, l, j, off + tid);
+      else if (tid >= 16 && tid - 16 < tail) hier_one<D>(a, N, Lc, l, j, e_base + nvec * VE + (tid - 16));
+    }
+  } else {
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (kBlock * VE);
+#pragma unroll 1
+    for (int k = 0; k < VE; ++k) {
+      const int64_t i = e0 + k * kBlock + tid;
+      if (i < cnt) hier_one<D>(a, N, Lc, l, j, off + i);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// launchers
+
+template <int D, int NN, int LL>
+hipError_t launch_hier_shape(const HierArgs& a, dim3 grid, bool large, hipStream_t stream) {
+  if (large) return launch(hier_kernel<D, NN, LL, true>, grid, a, stream);
+  return launch(hier_kernel<D, NN, LL, false>, grid, a, stream);
+}
+
+template <int D>
+hipError_t launch_hier_dtype(const HierArgs& a, dim3 grid, bool large, hipStream_t stream) {
+  const int N = a.nodes, L = a.local;
+  if (N == 2 && L == 8) return launch_hier_shape<D, 2, 8>(a, grid, large, stream);
+  if (N == 4 && L == 4) return launch_hier_shape<D, 4, 4>(a, grid, large, stream);
+  if (N == 4 && L == 8) return launch_hier_shape<D, 4, 8>(a, grid, large, stream);
+  if (N == 2 && L == 4) return launch_hier_shape<D, 2, 4>(a, grid, large, stream);
+  if (N == 8 && L == 8) return launch_hier_shape<D, 8, 8>(a, grid, large, stream);
+  if (N == 4 && L == 2) return launch_hier_shape<D, 4, 2>(a, grid, large, stream);
+  return launch(hier_kernel<D, 0, 0, false>, grid, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_hierarchical(const HierArgs& a, vcoll_dtype dtype, int64_t max_segment, hipStream_t stream) {
+  const int64_t per_tile = static_cast<int64_t>(kBlock) * (dtype == VCOLL_F32 ? 4 : 8);
+  const int64_t tiles = (max_segment + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  const int p = a.nodes * a.local;
+  const dim3 grid(static_cast<unsigned>(tiles), p);
+  const bool large = tiles * p >= VCOLL_PACE_MIN_GROUPS;
+  if (dtype == VCOLL_F32) return launch_hier_dtype<VCOLL_F32>(a, grid, large, stream);
+  return launch_hier_dtype<VCOLL_BF16>(a, grid, large, stream);
+}
+
+}  // namespace vcoll

@@ -1,0 +1,327 @@
+// Data-movement kernels of libvcoll for gfx950: all-gather fan-out,
+// broadcast, variable-split all-to-all, FP8 MoE dispatch and the plain copy
+// the collectives are measured against. Nothing here adds; every byte is
+// read once and written to its destinations.
+#include "device.h"
+
+namespace vcoll {
+namespace {
+
+using namespace dev;
+
+// ----------------------------------------------------------------------------
+// all-gather: block i of every output is a copy of input i
+
+template <int ES, int V>
+__global__ __launch_bounds__(kBlock) void all_gather_kernel(const GatherArgs a) {
+  const int i = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t bytes = a.m * ES;
+  const int64_t dst_off = i * bytes;
+  const void* src = a.ptr.src[i];
+  if (a.vec) {
+    const int64_t nvec = bytes / 16;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + tid;
+    u32x4 x[V];
+    bool valid[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t v = v0 + j * kBlock;
+      valid[j] = v < nvec;
+      x[j] = valid[j] ? ld16(src, v * 16) : u32x4{0, 0, 0, 0};
+    }
+    for (int r = 0; r < a.p; ++r) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (valid[j]) st16(a.ptr.dst[r], dst_off + (v0 + j * kBlock) * 16, x[j]);
+    }
+  } else {
+    using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
+    constexpr int VE = 16 / ES;
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock * VE) + tid;
+#pragma unroll 1
+    for (int j = 0; j < V * VE; ++j) {
+      const int64_t e = e0 + j * kBlock;
+      if (e < a.m) {
+        const E x = static_cast<const E*>(src)[e];
+        for (int r = 0; r < a.p; ++r) static_cast<E*>(a.ptr.dst[r])[i * a.m + e] = x;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// broadcast: every receive buffer gets the root's words ("Networks and
+// Collective Communication", section 4.1). Whatever the algorithm, the
+// result is a copy, so one pass reads the root once and writes q copies.
+
+template <int ES, int V, bool PACE>
+__global__ __launch_bounds__(kBlock) void broadcast_kernel(const BcastArgs a) {
+  using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
+  constexpr int VE = 16 / ES;
+  const int tid = threadIdx.x;
+  if (a.vec) {
+    const int64_t nvec = a.n / VE;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + tid;
+    u32x4 x[V];
+    bool valid[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t v = v0 + j * kBlock;
+      valid[j] = v < nvec;
+      x[j] = valid[j] ? ld16(a.src, v * 16) : u32x4{0, 0, 0, 0};
+    }
+    for (int r = 0; r < a.q; ++r) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (valid[j]) st16(a.dst[r], (v0 + j * kBlock) * 16, x[j]);
+      if constexpr (PACE) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the last n mod VE elements
+    if (blockIdx.x == 0 && tid < a.n - nvec * VE) {
+      const int64_t e = nvec * VE + tid;
+      const E w = static_cast<const E*>(a.src)[e];
+      for (int r = 0; r < a.q; ++r) static_cast<E*>(a.dst[r])[e] = w;
+    }
+  } else {
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock * VE) + tid;
+#pragma unroll 1
+    for (int j = 0; j < V * VE; ++j) {
+      const int64_t e = e0 + j * kBlock;
+      if (e < a.n) {
+        const E w = static_cast<const E*>(a.src)[e];
+        for (int r = 0; r < a.q; ++r) static_cast<E*>(a.dst[r])[e] = w;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// all-to-all: workgroup t moves rows_per_tile rows of one (i -> j) block
+
+__global__ __launch_bounds__(kBlock) void all_to_all_kernel(const A2AArgs a) {
+  const int t = blockIdx.x;
+  // the block this workgroup belongs to: last one whose first tile <= t
+  int lo = 0, hi = a.nblocks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (a.b[mid].tile_start <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const A2ABlock& B = a.b[lo];
+  const int r0 = (t - B.tile_start) * a.rows_per_tile;
+  const int tid = threadIdx.x;
+  for (int rr = 0; rr < a.rows_per_tile; ++rr) {
+    const int k = r0 + rr;
+    if (k >= B.rows) break;
+    const int64_t sr = B.src_idx ? static_cast<int64_t>(B.src_idx[k]) : k;
+    const int64_t dr = B.dst_idx ? static_cast<int64_t>(B.dst_idx[k]) : k;
+    if (sr < 0 || sr >= B.src_limit || dr < 0 || dr >= B.dst_limit) continue;
+    const char* src = B.src + sr * a.row_bytes;
+    char* dst = B.dst + dr * a.row_bytes;
+    if (a.vec) {
+      const int64_t nvec = a.row_bytes / 16;
+      constexpr int U = 4;
+      for (int64_t x0 = tid; x0 < nvec; x0 += U * kBlock) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          v[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          if (x < nvec) st16(dst, x * 16, v[u]);
+        }
+      }
+    } else if (a.esize == 4) {
+      for (int64_t x = tid; x < a.row_bytes / 4; x += kBlock)
+        reinterpret_cast<uint32_t*>(dst)[x] = reinterpret_cast<const uint32_t*>(src)[x];
+    } else if (a.esize == 2) {
+      for (int64_t x = tid; x < a.row_bytes / 2; x += kBlock)
+        reinterpret_cast<uint16_t*>(dst)[x] = reinterpret_cast<const uint16_t*>(src)[x];
+    } else {
+      for (int64_t x = tid; x < a.row_bytes; x += kBlock)
+        reinterpret_cast<uint8_t*>(dst)[x] = reinterpret_cast<const uint8_t*>(src)[x];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// FP8 dispatch ("Networks and Collective Communication", section 7.4): rows
+// gathered from a bfloat16 token table and quantised on the way to E4M3
+// (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 448
+// the largest value) with one power-of-two scale per 128 elements.
+
+// Smallest k with amax <= 448 * 2^k, clamped to [-126, 126]; 0 for amax = 0.
+// amax = 1.m * 2^(E-127) and 448 = 1.75 * 2^8, so k = E - 135 when
+// 1.m <= 1.75 (fraction field <= 0x600000) and E - 134 otherwise.
+__device__ __forceinline__ int fp8_group_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  if (u == 0) return 0;
+  const int E = static_cast<int>(u >> 23);
+  if (E == 0) return -126;
+  const int k = (u & 0x7FFFFFu) <= 0x600000u ? E - 135 : E - 134;
+  return k < -126 ? -126 : (k > 126 ? 126 : k);
+}
+
+// |y| <= 448 (or non-finite) -> E4M3 code, round to nearest, ties to even,
+// done on the float32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t u = b & 0x7FFFFFFFu;
+  if (u >= 0x7F800000u) return 0x7Fu;                 // infinity or NaN
+  const int E = static_cast<int>(u >> 23);
+  if (E == 0) return sign;                             // zero, or a float32 subnormal (< 2^-126)
+  const int e = E - 127;
+  const uint32_t mant = (u & 0x7FFFFFu) | 0x800000u;   // 1.f times 2^23
+  // normal results keep 1 + 3 fraction bits; below 2^-6 the grid is 2^-9:
+  // y * 2^9 = mant * 2^(e - 14)
+  const int shift = e >= -6 ? 20 : 14 - e;
+  if (shift > 24) return sign;                         // below 2^-10: rounds to zero
+  uint32_t q = mant >> shift;
+  const uint32_t rem = mant & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  if (e >= -6) {
+    int ee = e;
+    if (q == 16u) {
+      q = 8u;
+      ++ee;
+    }
+    return sign | (static_cast<uint32_t>(ee + 7) << 3) | (q - 8u);
+  }
+  return sign | q;                                     // 0..8 (8 is 2^-6: exponent field 1)
+}
+
+__global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
+  const int t = blockIdx.x;
+  int lo = 0, hi = a.nblocks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (a.b[mid].tile_start <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const A2ABlock& B = a.b[lo];
+  const int r0 = (t - B.tile_start) * a.rows_per_tile;
+  const int tid = threadIdx.x;
+  const int64_t nvec = a.hidden / 8;                   // 16-byte vectors; 16 of them per group
+  for (int rr = 0; rr < a.rows_per_tile; ++rr) {
+    const int k = r0 + rr;
+    if (k >= B.rows) break;
+    const int64_t sr = B.src_idx[k];
+    if (sr < 0 || sr >= B.src_limit) continue;
+    const char* src = B.src + sr * a.hidden * 2;
+    char* dst = B.dst + static_cast<int64_t>(k) * a.out_row_bytes;
+    // nvec and kBlock are multiples of 16, so the 16 lanes of a group are
+    // always active together for the shuffles below
+    for (int64_t x = tid; x < nvec; x += kBlock) {
+      const u32x4 w = ld16(src, x * 16);
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = fabsf(f[i]);
+        m = v <= 3.402823466e38f ? fmaxf(m, v) : m;    // finite values only
+      }
+      m = fmaxf(m, __shfl_xor(m, 8, 16));
+      m = fmaxf(m, __shfl_xor(m, 4, 16));
+      m = fmaxf(m, __shfl_xor(m, 2, 16));
+      m = fmaxf(m, __shfl_xor(m, 1, 16));
+      const int kx = fp8_group_exponent(m);
+      const float inv = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
+      uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c0 |= e4m3_code(f[i] * inv) << (8 * i);
+        c1 |= e4m3_code(f[4 + i] * inv) << (8 * i);
+      }
+      reinterpret_cast<uint32_t*>(dst + x * 8)[0] = c0;
+      reinterpret_cast<uint32_t*>(dst + x * 8)[1] = c1;
+      if ((x & 15) == 0)
+        *reinterpret_cast<float*>(dst + a.hidden + (x / 16) * 4) =
+            __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// plain copy: the streaming ceiling the collectives are measured against
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(const void* src, void* dst, int64_t nvec) {
+  constexpr int V = 4;
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + threadIdx.x;
+  u32x4 x[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t v = v0 + j * kBlock;
+    x[j] = v < nvec ? ld16(src, v * 16) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t v = v0 + j * kBlock;
+    if (v < nvec) st16(dst, v * 16, x[j]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream) {
+  constexpr int V = 2;
+  const int ES = dtype == VCOLL_F32 ? 4 : 2;
+  const int64_t per_tile = static_cast<int64_t>(V) * kBlock * (16 / ES);
+  const int64_t tiles = (a.n + per_tile - 1) / per_tile;
+  if (tiles == 0 || a.q == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  const bool pace = a.vec && tiles >= VCOLL_PACE_MIN_GROUPS;
+  if (ES == 4) {
+    if (pace) return launch(broadcast_kernel<4, V, true>, grid, a, stream);
+    return launch(broadcast_kernel<4, V, false>, grid, a, stream);
+  }
+  if (pace) return launch(broadcast_kernel<2, V, true>, grid, a, stream);
+  return launch(broadcast_kernel<2, V, false>, grid, a, stream);
+}
+
+hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream) {
+  constexpr int V = 2;
+  const int ES = dtype == VCOLL_F32 ? 4 : 2;
+  const int64_t per_tile = static_cast<int64_t>(V) * kBlock * (16 / ES);
+  const int64_t tiles = (a.m + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles), a.p);
+  if (ES == 4) return launch(all_gather_kernel<4, V>, grid, a, stream);
+  return launch(all_gather_kernel<2, V>, grid, a, stream);
+}
+
+hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stream) {
+  if (tiles == 0) return hipSuccess;
+  return launch(dispatch_fp8_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
+}
+
+hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {
+  if (tiles == 0) return hipSuccess;
+  return launch(all_to_all_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  const int64_t nvec = bytes / 16;
+  const int64_t per_tile = 4LL * kBlock;
+  const int64_t tiles = (nvec + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  void* args[] = {const_cast<const void**>(&src), &dst, const_cast<int64_t*>(&nvec)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel), dim3(static_cast<unsigned>(tiles)),
+                         dim3(kBlock), args, 0, stream);
+}
+
+}  // namespace vcoll

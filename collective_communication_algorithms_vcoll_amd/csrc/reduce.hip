@@ -1,0 +1,405 @@
+// The fused reduce kernels of libvcoll for gfx950: all-reduce, reduce-scatter
+// and reduce to a root, each evaluating its algorithm's summation order in
+// registers in one streaming pass.
+//
+// Summation orders come from "Networks and Collective Communication" (cs349e
+// prerequisite lecture 5), sections 5.1 (ring) and 5.2 (recursive doubling,
+// Rabenseifner, binomial tree); order.h writes each as a push / add program.
+#include "device.h"
+
+namespace vcoll {
+namespace {
+
+using namespace dev;
+
+// ----------------------------------------------------------------------------
+// order programs unfolded at compile time (p fixed)
+
+template <int ALGO, int P>
+struct Prog {
+  static constexpr OrderProgram value = order_program(ALGO, P);
+  static constexpr int depth = value.max_depth > 0 ? value.max_depth : 1;
+};
+
+// Replace the top two of DEPTH live stack entries by their sum, M times.
+template <int DEPTH, int M, int SD, int N>
+__device__ __forceinline__ void merge_top(float (&st)[SD][N]) {
+  if constexpr (M > 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) st[DEPTH - 2][i] = st[DEPTH - 2][i] + st[DEPTH - 1][i];
+    merge_top<DEPTH - 1, M - 1>(st);
+  }
+}
+
+// Push leaf K (widened by `leaf`) and apply its merges; recurse to K + 1.
+template <int ALGO, int P, int K, int DEPTH, int SD, int N, class Leaf>
+__device__ __forceinline__ void run_program(float (&st)[SD][N], const Leaf& leaf) {
+  if constexpr (K < P) {
+    leaf(std::integral_constant<int, K>{}, st[DEPTH]);
+    constexpr int M = Prog<ALGO, P>::value.merges[K];
+    merge_top<DEPTH + 1, M>(st);
+    run_program<ALGO, P, K + 1, DEPTH + 1 - M>(st, leaf);
+  } else {
+    merge_top<DEPTH, Prog<ALGO, P>::value.final_merges>(st);
+  }
+}
+
+// Stack entries alive before leaf K is pushed.
+template <int ALGO, int P>
+constexpr int depth_before(int K) {
+  int d = 0;
+  for (int j = 0; j < K; ++j) d += 1 - Prog<ALGO, P>::value.merges[j];
+  return d;
+}
+
+// Push leaf K (already widened) and apply its merges; after the last leaf,
+// the final collapse.
+template <int ALGO, int P, int K, int SD, int N>
+__device__ __forceinline__ void push_leaf(float (&st)[SD][N], const float (&v)[N]) {
+  constexpr int D = depth_before<ALGO, P>(K);
+  constexpr int M = Prog<ALGO, P>::value.merges[K];
+#pragma unroll
+  for (int i = 0; i < N; ++i) st[D][i] = v[i];
+  merge_top<D + 1, M>(st);
+  if constexpr (K == P - 1) merge_top<D + 1 - M, Prog<ALGO, P>::value.final_merges>(st);
+}
+
+// Ranks whose loads a wave keeps in flight ahead of the one it is adding.
+// Large grids (which also pace their stores) issue all p ranks up front;
+// small, latency-bound grids run a pipeline of a few ranks, which measured
+// 10% faster at 1 MiB per rank. Build-time override of the small-grid
+// depth: -DVCOLL_LAG=<n>.
+#ifndef VCOLL_LAG
+#define VCOLL_LAG 4
+#endif
+template <int P, bool LARGE>
+constexpr int load_lag() { return LARGE ? P : (VCOLL_LAG < P ? VCOLL_LAG : P); }
+
+// Row of leaf pointers of chunk c (p compiled in): the ring's order rotates
+// with the chunk, the trees' order is the same for every chunk (row 0).
+template <int ALGO>
+__device__ __forceinline__ const void* const* leaf_row(const ReduceArgs& a, int c) {
+  return &a.leaf[(ALGO == VCOLL_RING ? c : 0) * kFixedMax];
+}
+
+// ----------------------------------------------------------------------------
+// order programs read at run time (any p): a shift-register stack keeps every
+// index a compile-time constant, so the stack lives in registers
+
+constexpr int kRuntimeDepth = 9;   // deepest stack of any program with p <= 128
+
+template <int N>
+__device__ __forceinline__ void rt_push(float (&st)[kRuntimeDepth][N], const float* v) {
+#pragma unroll
+  for (int s = kRuntimeDepth - 1; s > 0; --s)
+#pragma unroll
+    for (int i = 0; i < N; ++i) st[s][i] = st[s - 1][i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) st[0][i] = v[i];
+}
+
+template <int N>
+__device__ __forceinline__ void rt_merge(float (&st)[kRuntimeDepth][N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) st[0][i] = st[1][i] + st[0][i];
+#pragma unroll
+  for (int s = 1; s < kRuntimeDepth - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < N; ++i) st[s][i] = st[s + 1][i];
+}
+
+// ----------------------------------------------------------------------------
+// one element (chunk heads and tails, unaligned buffers)
+
+template <int D, int ALGO, int P, bool RS>
+__device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, int rot, int64_t e,
+                                           int64_t off) {
+  using S = Storage<D>;
+  using E = typename S::elem;
+  float result;
+  if constexpr (P > 0) {
+    const void* const* L = leaf_row<ALGO>(a, c);
+    E raw[P];
+    static_for<0, P>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      raw[k] = static_cast<const E*>(L[k])[e];
+    });
+    float st[Prog<ALGO, P>::depth][1];
+    run_program<ALGO, P, 0, 0>(st, [&](auto kc, float(&d)[1]) {
+      d[0] = S::widen1(raw[decltype(kc)::value]);
+    });
+    result = st[0][0];
+  } else if constexpr (ALGO == VCOLL_RING) {
+    result = S::widen1(static_cast<const E*>(a.leaf[rot % p])[e]);
+    for (int k = 1; k < p; ++k)
+      result = result + S::widen1(static_cast<const E*>(a.leaf[(rot + k) % p])[e]);
+  } else {
+    float st[kRuntimeDepth][1];
+    for (int k = 0; k < p; ++k) {
+      const float v = S::widen1(static_cast<const E*>(a.leaf[a.rank[k]])[e]);
+      rt_push<1>(st, &v);
+      for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
+    }
+    for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
+    result = st[0][0];
+  }
+  const E out = S::narrow1(result);
+  if constexpr (RS) {
+    static_cast<E*>(a.dst[c])[e - off] = out;
+  } else {
+    for (int r = 0; r < p; ++r) static_cast<E*>(a.dst[r])[e] = out;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// V 16-byte vectors per thread, fixed p: all p*V loads are issued before the
+// first add, the order program runs in registers, then p*V (or V) stores.
+
+template <int D, int ALGO, int P, int V, bool RS, bool LARGE, bool FULL>
+__device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
+                                                     const int64_t (&boff)[V],
+                                                     const bool (&valid)[V], int64_t out_shift) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  constexpr int LAG = load_lag<P, LARGE>();
+  const void* const* L = leaf_row<ALGO>(a, c);
+  u32x4 raw[P][V];
+  float st[Prog<ALGO, P>::depth][V * VE];
+
+  // software pipeline in summation order: the loads of leaf k go out, then
+  // leaf k - LAG (whose loads went out LAG steps earlier) is added
+  static_for<0, P + LAG>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k < P) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        if constexpr (FULL) {
+          raw[k][j] = ld16(L[k], boff[j]);
+        } else {
+          raw[k][j] = valid[j] ? ld16(L[k], boff[j]) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (k >= LAG) {
+      constexpr int q = k - LAG;
+      float v[V * VE];
+#pragma unroll
+      for (int j = 0; j < V; ++j) S::widen(raw[q][j], &v[j * VE]);
+      push_leaf<ALGO, P, q>(st, v);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  u32x4 out[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) out[j] = S::narrow(&st[0][j * VE]);
+  if constexpr (RS) {
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if (FULL || valid[j]) st16(a.dst[c], boff[j] - out_shift, out[j]);
+  } else {
+    static_for<0, P>([&](auto rc) {
+      void* dst = a.dst[decltype(rc)::value];
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (FULL || valid[j]) st16(dst, boff[j], out[j]);
+      if constexpr (LARGE) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  }
+}
+
+// Same for a p known only at run time (one vector per thread; loads go out
+// eight ranks at a time).
+template <int D, int ALGO, bool RS>
+__device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c, int p, int rot,
+                                                      int64_t boff, bool valid, int64_t out_shift) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  constexpr int B = 8;
+  float acc[VE];
+  float st[kRuntimeDepth][VE];
+  for (int k0 = 0; k0 < p; k0 += B) {
+    u32x4 raw[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (k0 + b < p) {
+        const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : a.rank[k0 + b];
+        raw[b] = valid ? ld16(a.leaf[rank], boff) : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (k0 + b < p) {
+        float v[VE];
+        S::widen(raw[b], v);
+        if constexpr (ALGO == VCOLL_RING) {
+          if (k0 + b == 0) {
+#pragma unroll
+            for (int i = 0; i < VE; ++i) acc[i] = v[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < VE; ++i) acc[i] = acc[i] + v[i];
+          }
+        } else {
+          rt_push<VE>(st, v);
+          for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<VE>(st);
+        }
+      }
+    }
+  }
+  if constexpr (ALGO != VCOLL_RING) {
+    for (int m = 0; m < a.final_merges; ++m) rt_merge<VE>(st);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] = st[0][i];
+  }
+  if (!valid) return;
+  const u32x4 out = S::narrow(acc);
+  if constexpr (RS) {
+    st16(a.dst[c], boff - out_shift, out);
+  } else {
+    for (int r = 0; r < p; ++r) {
+      st16(a.dst[r], boff, out);
+      if (a.pace) __builtin_amdgcn_s_sleep(VCOLL_STORE_SLEEP);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// the reduce kernel: workgroup (x, y) handles tile x of chunk y
+
+template <int D, int ALGO, int P, int V, bool RS, bool LARGE>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a) {
+  using S = Storage<D>;
+  constexpr int VE = S::kVE;
+  constexpr int ES = 16 / VE;
+  const int c = blockIdx.y;
+  const int p = P > 0 ? P : a.p;
+  const int64_t off = c * a.q + (c < a.r ? c : a.r);
+  const int64_t cnt = a.q + (c < a.r ? 1 : 0);
+  const int rot = (ALGO == VCOLL_RING) ? (c + 1) % p : 0;
+  const int tid = threadIdx.x;
+  // a reduce-scatter writes element e of chunk c to recv[c][e - off]: both
+  // sides must be vector aligned, so the chunk start must be
+  const bool vec = a.vec != 0 && (!RS || (off % VE) == 0);
+
+  if (vec) {
+    const int64_t head = (VE - off % VE) % VE < cnt ? (VE - off % VE) % VE : cnt;
+    const int64_t nvec = (cnt - head) / VE;
+    const int64_t e_base = off + head;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + tid;
+    if (static_cast<int64_t>(blockIdx.x) * (V * kBlock) < nvec) {
+      if constexpr (P > 0) {
+        int64_t boff[V];
+        bool valid[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int64_t v = v0 + j * kBlock;
+          valid[j] = v < nvec;
+          boff[j] = (e_base + v * VE) * ES;
+        }
+        if ((static_cast<int64_t>(blockIdx.x) + 1) * (V * kBlock) <= nvec) {
+          reduce_vectors_fixed<D, ALGO, P, V, RS, LARGE, true>(a, c, boff, valid, off * ES);
+        } else {
+          reduce_vectors_fixed<D, ALGO, P, V, RS, LARGE, false>(a, c, boff, valid, off * ES);
+        }
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < V; ++j) {
+          const int64_t v = v0 + j * kBlock;
+          reduce_vector_runtime<D, ALGO, RS>(a, c, p, rot, (e_base + v * VE) * ES, v < nvec,
+                                             off * ES);
+        }
+      }
+    }
+    if (blockIdx.x == 0) {
+      const int64_t tail = cnt - head - nvec * VE;
+      if (tid < head) {
+        reduce_one<D, ALGO, P, RS>(a, c, p, rot, off + tid, off);
+      } else if (tid >= 16 && tid - 16 < tail) {
+        reduce_one<D, ALGO, P, RS>(a, c, p, rot, e_base + nvec * VE + (tid - 16), off);
+      }
+    }
+  } else {
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock * VE);
+#pragma unroll 1
+    for (int j = 0; j < V * VE; ++j) {
+      const int64_t i = e0 + j * kBlock + tid;
+      if (i < cnt) reduce_one<D, ALGO, P, RS>(a, c, p, rot, off + i, off);
+    }
+  }
+}
+
+// 16-byte vectors per thread of the reduce kernel (all are loaded before the
+// first add). Build-time override: -DVCOLL_V_P8=<n> for p = 8.
+#ifndef VCOLL_V_P8
+#define VCOLL_V_P8 2
+#endif
+template <int P>
+constexpr int vectors_per_thread() {
+  return P == 0 ? 1 : (P <= 4 ? 4 : (P <= 8 ? VCOLL_V_P8 : 1));
+}
+
+template <int D, int ALGO, bool RS, int P>
+hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, hipStream_t stream) {
+  constexpr int V = vectors_per_thread<P>();
+  constexpr int VE = Storage<D>::kVE;
+  const int64_t per_tile = static_cast<int64_t>(V) * kBlock * VE;
+  const int64_t tiles = (max_chunk + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles), chunks);
+  ReduceArgs args = a;
+  args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
+  if constexpr (P > 0) {
+    // the compile-time variant carries the pacing (and its load pipeline)
+    if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true>, grid, args, stream);
+    return launch(reduce_kernel<D, ALGO, P, V, RS, false>, grid, args, stream);
+  } else {
+    return launch(reduce_kernel<D, ALGO, P, V, RS, false>, grid, args, stream);
+  }
+}
+
+template <int D, int ALGO, bool RS>
+hipError_t launch_reduce_algo(const ReduceArgs& a, int64_t max_chunk, int chunks, hipStream_t stream) {
+  static_assert(has_fixed_kernel(2) && has_fixed_kernel(4) && has_fixed_kernel(8) && has_fixed_kernel(16),
+                "the host lays out leaf pointers by has_fixed_kernel()");
+  switch (a.p) {
+    case 2: return launch_reduce_p<D, ALGO, RS, 2>(a, max_chunk, chunks, stream);
+    case 4: return launch_reduce_p<D, ALGO, RS, 4>(a, max_chunk, chunks, stream);
+    case 8: return launch_reduce_p<D, ALGO, RS, 8>(a, max_chunk, chunks, stream);
+    case 16: return launch_reduce_p<D, ALGO, RS, 16>(a, max_chunk, chunks, stream);
+    default: return launch_reduce_p<D, ALGO, RS, 0>(a, max_chunk, chunks, stream);
+  }
+}
+
+template <int D>
+hipError_t launch_reduce_dtype(const ReduceArgs& a, vcoll_algo algo, bool scatter, int64_t max_chunk,
+                               int chunks, hipStream_t stream) {
+  if (scatter) {
+    if (algo == VCOLL_RING) return launch_reduce_algo<D, VCOLL_RING, true>(a, max_chunk, chunks, stream);
+    if (algo == VCOLL_BINARY_TREE)
+      return launch_reduce_algo<D, VCOLL_BINARY_TREE, true>(a, max_chunk, chunks, stream);
+    return launch_reduce_algo<D, VCOLL_RABENSEIFNER, true>(a, max_chunk, chunks, stream);
+  }
+  switch (algo) {
+    case VCOLL_RING: return launch_reduce_algo<D, VCOLL_RING, false>(a, max_chunk, chunks, stream);
+    case VCOLL_RECURSIVE_DOUBLING:
+      return launch_reduce_algo<D, VCOLL_RECURSIVE_DOUBLING, false>(a, max_chunk, chunks, stream);
+    case VCOLL_RABENSEIFNER:
+      return launch_reduce_algo<D, VCOLL_RABENSEIFNER, false>(a, max_chunk, chunks, stream);
+    default: return launch_reduce_algo<D, VCOLL_BINARY_TREE, false>(a, max_chunk, chunks, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
+                         int64_t max_chunk, int chunks, hipStream_t stream) {
+  if (dtype == VCOLL_F32) return launch_reduce_dtype<VCOLL_F32>(a, algo, scatter, max_chunk, chunks, stream);
+  return launch_reduce_dtype<VCOLL_BF16>(a, algo, scatter, max_chunk, chunks, stream);
+}
+
+}  // namespace vcoll
