@@ -40,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "all-reduce effective HBM GB/s (p=8, 25 MB/rank fp32) + % of HBM roofline"
 PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
-KERNEL_SOURCES = ("reduce.hip", "device.h", "kernels.h", "order.h")   # what defines the headline kernel
+KERNEL_SOURCES = ("reduce.hip", "reduce.h", "device.h", "common.h", "order.h")   # what defines the headline kernel
 
 
 def kernel_source_hash() -> str:
@@ -287,6 +287,25 @@ def extras(vc, torch, h, args):
     ex["moe_dispatch_fp8_fused_gather_quantise"] = {
         "GBps": rate(rows * rb + rows * orb, ms_f), "us": round(ms_f * 1e3, 1),
         "algorithmic_bytes": rows * rb + rows * orb, "payload_bytes_per_row": orb}
+    # token-major dispatch: each token row read once, written to its 8 slots
+    slots = vc.vcoll_moe_slots(splits, dst_rows)
+    slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
+    recv_rows = splits.sum(axis=0)
+    tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
+    tm_ok = all(torch.equal(tm[j].view(torch.int16), recv[j].view(torch.int16)) for j in range(p8))
+    tm8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
+    tm8_ok = all(torch.equal(tm8[j], f8[j]) for j in range(p8))
+    push = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=tm)              # noqa: E731
+    push8 = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=tm8)  # noqa: E731
+    _, ms_p = time_launches([push], 10, 2)
+    _, ms_p8 = time_launches([push8], 10, 2)
+    ex["moe_dispatch_token_major"] = {"GBps": rate(p8 * T * rb + rows * rb, ms_p), "us": round(ms_p * 1e3, 1),
+                                      "algorithmic_bytes": p8 * T * rb + rows * rb,
+                                      "equals_gather_dispatch": bool(tm_ok)}
+    ex["moe_dispatch_token_major_fp8"] = {"GBps": rate(p8 * T * rb + rows * orb, ms_p8),
+                                          "us": round(ms_p8 * 1e3, 1),
+                                          "algorithmic_bytes": p8 * T * rb + rows * orb,
+                                          "equals_row_major_fp8": bool(tm8_ok)}
     su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p8)
     src_ug = [torch.from_numpy(x).cuda() for x in src_u]
     exp_g = [torch.from_numpy(x).cuda() for x in expand]

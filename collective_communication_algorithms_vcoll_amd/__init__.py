@@ -107,6 +107,10 @@ def _lib():
         lib.vcoll_model_chain_optimum.restype = I
         lib.vcoll_model_clock.argtypes = [P(Msg), I64, I, I, D, D, D, D, P(D)]
         lib.vcoll_model_clock.restype = I
+        lib.vcoll_moe_slots.argtypes = [I, I64, I, P(I64), P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.vcoll_moe_slots.restype = I
+        lib.vcoll_moe_dispatch.argtypes = [I, I64, I, I64, I, I, P(VP), P(VP), P(VP), P(I64), VP]
+        lib.vcoll_moe_dispatch.restype = I
         lib.vcoll_moe_plan_dedup.argtypes = [I, I64, I, I, P(ctypes.c_int32), P(I64), P(ctypes.c_int32),
                                              P(ctypes.c_int32), P(I64)]
         lib.vcoll_moe_plan_dedup.restype = I
@@ -563,6 +567,55 @@ def vcoll_moe_plan(topk_ids: np.ndarray, experts_per_rank: int):
                                  splits.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                  src.ctypes.data_as(i32), dst.ctypes.data_as(i32)), "vcoll_moe_plan")
     return splits, src, dst
+
+
+def vcoll_moe_slots(splits, dst_rows) -> np.ndarray:
+    """Token-major view of a vcoll_moe_plan: int32 [p, tokens*topk, 2]
+    (destination rank, destination row) per (token, slot)."""
+    sp = np.ascontiguousarray(np.asarray(splits, dtype=np.int64))
+    dr = np.ascontiguousarray(np.asarray(dst_rows, dtype=np.int32))
+    p, rows = dr.shape
+    topk = 1
+    slots = np.zeros((p, rows, 2), dtype=np.int32)
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    _check(_lib().vcoll_moe_slots(p, rows // topk, topk, sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                  dr.ctypes.data_as(i32), slots.ctypes.data_as(i32)), "vcoll_moe_slots")
+    return slots
+
+
+def vcoll_moe_dispatch(tokens, slots, recv_rows, topk: int, fp8: bool = False, recv=None):
+    """Token-major dispatch (see vcoll.h): tokens p tensors [T, hidden];
+    slots p int32 GPU tensors [T*topk, 2]; recv_rows the rows each rank
+    receives. Returns recv (p tensors; uint8 rows of hidden + hidden//32
+    bytes for FP8)."""
+    import torch
+    t = list(tokens)
+    p = len(t)
+    T, H = t[0].shape
+    dev, dt = t[0].device, t[0].dtype
+    for x in t:
+        if x.shape != (T, H) or x.dtype != dt or x.device != dev or not x.is_contiguous():
+            raise ValueError("vcoll_moe_dispatch: token tables must be contiguous [T, hidden] of one dtype")
+    rr = [int(r) for r in recv_rows]
+    if recv is None:
+        if fp8:
+            recv = [torch.empty((rr[j], H + H // 32), dtype=torch.uint8, device=dev) for j in range(p)]
+        else:
+            recv = [torch.empty((rr[j], H), dtype=dt, device=dev) for j in range(p)]
+    r = list(recv)
+    orb = H + H // 32 if fp8 else H * t[0].element_size()
+    for j in range(p):
+        if not r[j].is_contiguous() or r[j].numel() * r[j].element_size() < rr[j] * orb:
+            raise ValueError(f"vcoll_moe_dispatch: recv[{j}] holds fewer than {rr[j]} rows")
+    s = list(slots)
+    for x in s:
+        if x.dtype != torch.int32 or x.device != dev or x.numel() < 2 * T * topk:
+            raise ValueError("vcoll_moe_dispatch: slots must be int32 GPU tensors of T*topk pairs")
+    _no_overlap(t, r, "vcoll_moe_dispatch")
+    rows = (ctypes.c_int64 * p)(*rr)
+    _check(_lib().vcoll_moe_dispatch(p, T, topk, H, _dtype_code(t[0]), int(bool(fp8)), _ptrs(t), _ptrs(s),
+                                     _ptrs(r), rows, _stream(t[0])), "vcoll_moe_dispatch")
+    return recv
 
 
 def vcoll_moe_plan_dedup(topk_ids: np.ndarray, experts_per_rank: int):

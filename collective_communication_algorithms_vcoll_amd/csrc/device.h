@@ -7,7 +7,7 @@
 
 #include <type_traits>
 
-#include "kernels.h"
+#include "common.h"
 
 namespace vcoll {
 namespace dev {

@@ -1,5 +1,6 @@
 // The fused hierarchical / 2D all-reduce kernel of libvcoll for gfx950.
 #include "device.h"
+#include "hier.h"
 
 namespace vcoll {
 namespace {

@@ -3,6 +3,7 @@
 // the collectives are measured against. Nothing here adds; every byte is
 // read once and written to its destinations.
 #include "device.h"
+#include "move.h"
 
 namespace vcoll {
 namespace {
@@ -200,6 +201,39 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | q;                                     // 0..8 (8 is 2^-6: exponent field 1)
 }
 
+// Quantise 8 bfloat16 values (one 16-byte vector) of a 128-element group
+// spread over 16 consecutive lanes: the group's amax by shuffles within the
+// 16 lanes (all 16 must call this together), its power-of-two scale, and the
+// 8 codes packed little-endian into c0 (elements 0-3) and c1 (4-7).
+__device__ __forceinline__ void quantise8(const u32x4 w, uint32_t& c0, uint32_t& c1, float& scale) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = fabsf(f[i]);
+    m = v <= 3.402823466e38f ? fmaxf(m, v) : m;        // finite values only
+  }
+  m = fmaxf(m, __shfl_xor(m, 8, 16));
+  m = fmaxf(m, __shfl_xor(m, 4, 16));
+  m = fmaxf(m, __shfl_xor(m, 2, 16));
+  m = fmaxf(m, __shfl_xor(m, 1, 16));
+  const int kx = fp8_group_exponent(m);
+  const float inv = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
+  c0 = 0;
+  c1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c0 |= e4m3_code(f[i] * inv) << (8 * i);
+    c1 |= e4m3_code(f[4 + i] * inv) << (8 * i);
+  }
+  scale = __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+}
+
 __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
   const int t = blockIdx.x;
   int lo = 0, hi = a.nblocks - 1;
@@ -222,36 +256,89 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
     // nvec and kBlock are multiples of 16, so the 16 lanes of a group are
     // always active together for the shuffles below
     for (int64_t x = tid; x < nvec; x += kBlock) {
-      const u32x4 w = ld16(src, x * 16);
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = fabsf(f[i]);
-        m = v <= 3.402823466e38f ? fmaxf(m, v) : m;    // finite values only
-      }
-      m = fmaxf(m, __shfl_xor(m, 8, 16));
-      m = fmaxf(m, __shfl_xor(m, 4, 16));
-      m = fmaxf(m, __shfl_xor(m, 2, 16));
-      m = fmaxf(m, __shfl_xor(m, 1, 16));
-      const int kx = fp8_group_exponent(m);
-      const float inv = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
-      uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c0 |= e4m3_code(f[i] * inv) << (8 * i);
-        c1 |= e4m3_code(f[4 + i] * inv) << (8 * i);
-      }
+      uint32_t c0, c1;
+      float scale;
+      quantise8(ld16(src, x * 16), c0, c1, scale);
       reinterpret_cast<uint32_t*>(dst + x * 8)[0] = c0;
       reinterpret_cast<uint32_t*>(dst + x * 8)[1] = c1;
-      if ((x & 15) == 0)
-        *reinterpret_cast<float*>(dst + a.hidden + (x / 16) * 4) =
-            __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+      if ((x & 15) == 0) *reinterpret_cast<float*>(dst + a.hidden + (x / 16) * 4) = scale;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// token-major MoE dispatch of one sending rank: each token row is read once
+// and written to the received-row slot of every (token, chosen expert) pair,
+// copied as it is or quantised to FP8 once for all its copies
+
+constexpr int kPushUnroll = 4;     // 16-byte vectors in flight per thread (a 7168 bf16 row is 3.5)
+
+template <bool FP8>
+__global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * a.tokens_per_tile;
+  for (int64_t t = t0; t < t0 + a.tokens_per_tile && t < a.tokens; ++t) {
+    const char* src = static_cast<const char*>(a.table) + t * a.row_bytes;
+    const int32_t* slot = a.slots + 2 * t * a.topk;
+    // destination k of this token (uniform across the workgroup), or null
+    auto dest = [&](int k) -> char* {
+      const int j = slot[2 * k], r = slot[2 * k + 1];
+      if (j < 0 || j >= a.p || r < 0 || r >= a.recv_rows[j]) return nullptr;
+      return static_cast<char*>(a.recv[j]) + static_cast<int64_t>(r) * a.out_row_bytes;
+    };
+    if constexpr (FP8) {
+      // hidden / 8 vectors, a multiple of 16: each 16-lane group is whole
+      const int64_t nvec = a.hidden / 8;
+      for (int64_t x0 = tid; x0 < nvec; x0 += kPushUnroll * kBlock) {
+        u32x4 w[kPushUnroll];
+#pragma unroll
+        for (int u = 0; u < kPushUnroll; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          w[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kPushUnroll; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          if (x >= nvec) break;                      // uniform over each 16-lane group
+          uint32_t c0, c1;
+          float scale;
+          quantise8(w[u], c0, c1, scale);
+          for (int k = 0; k < a.topk; ++k) {
+            char* d = dest(k);
+            if (!d) continue;
+            reinterpret_cast<uint32_t*>(d + x * 8)[0] = c0;
+            reinterpret_cast<uint32_t*>(d + x * 8)[1] = c1;
+            if ((x & 15) == 0) *reinterpret_cast<float*>(d + a.hidden + (x / 16) * 4) = scale;
+          }
+        }
+      }
+    } else if (a.vec) {
+      const int64_t nvec = a.row_bytes / 16;
+      for (int64_t x0 = tid; x0 < nvec; x0 += kPushUnroll * kBlock) {
+        u32x4 v[kPushUnroll];
+#pragma unroll
+        for (int u = 0; u < kPushUnroll; ++u) {
+          const int64_t x = x0 + u * kBlock;
+          v[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
+        }
+        for (int k = 0; k < a.topk; ++k) {
+          char* d = dest(k);
+          if (!d) continue;
+#pragma unroll
+          for (int u = 0; u < kPushUnroll; ++u) {
+            const int64_t x = x0 + u * kBlock;
+            if (x < nvec) st16(d, x * 16, v[u]);
+          }
+        }
+      }
+    } else {
+      for (int64_t x = tid; x < a.row_bytes / 2; x += kBlock) {
+        const uint16_t v = reinterpret_cast<const uint16_t*>(src)[x];
+        for (int k = 0; k < a.topk; ++k) {
+          char* d = dest(k);
+          if (d) reinterpret_cast<uint16_t*>(d)[x] = v;
+        }
+      }
     }
   }
 }
@@ -307,6 +394,14 @@ hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t
 hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   return launch(dispatch_fp8_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
+}
+
+hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream) {
+  const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (fp8) return launch(dispatch_push_kernel<true>, grid, a, stream);
+  return launch(dispatch_push_kernel<false>, grid, a, stream);
 }
 
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {

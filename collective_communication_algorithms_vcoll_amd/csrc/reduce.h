@@ -1,0 +1,53 @@
+// Device kernels of libvcoll for gfx950 (MI355X, CDNA4, wave64).
+//
+// The collectives of a p-rank virtual cluster run in one GPU's HBM, so the
+// message hops of an algorithm are not data movement any more: an element's
+// value after the collective is a fixed float32 expression over the p input
+// values at that element. The reduce kernels evaluate that expression in
+// registers, in the exact association the algorithm's steps produce, reading
+// each input once and writing each output once -- an HBM-streaming pass with
+// no reuse, so the design goals are coalesced 16-byte accesses, many bytes in
+// flight per wave, and no arithmetic beyond the p-1 adds (no MFMA: nothing
+// here is a contraction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+#include "order.h"
+#include "vcoll.h"
+
+namespace vcoll {
+
+constexpr int kFixedMax = 16;        // largest p with a compile-time order program
+
+// The p values with reduce kernels specialised at compile time; every other
+// p runs the kernel that reads its order program at run time.
+constexpr bool has_fixed_kernel(int p) { return p == 2 || p == 4 || p == 8 || p == 16; }
+
+// Reduce (all-reduce / reduce-scatter). Grid: x = tiles of a chunk, y = chunk.
+// For has_fixed_kernel(p), leaf[c * kFixedMax + k] is the buffer of the k-th input
+// in chunk c's summation order (the host resolves the ring's per-chunk
+// rotation and the trees' leaf order), so a workgroup fetches its p source
+// pointers with one wide scalar load. For any other p, leaf[r] = send[r] and
+// the kernel resolves the order itself.
+struct ReduceArgs {
+  const void* leaf[kFixedMax * kFixedMax];
+  void* dst[kMaxRanks];
+  int64_t q, r;               // chunk c: off = c*q + min(c, r), count = q + (c < r)
+  int32_t p;
+  int32_t vec;                // every pointer 16-byte aligned: vector path allowed
+  int32_t final_merges;       // order program (used when p is not compiled in)
+  int32_t pace;               // space out the p-way store fan-out (large grids)
+  uint8_t rank[kMaxRanks];
+  uint8_t merges[kMaxRanks];
+};
+
+// grid y = chunks: p for all-reduce and reduce-scatter, 1 for a reduce to
+// one root (q = n, r = 0, dst[0] = the root's buffer, scatter = true).
+hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
+                         int64_t max_chunk, int chunks, hipStream_t stream);
+
+}  // namespace vcoll

@@ -6,6 +6,7 @@
 // prerequisite lecture 5), sections 5.1 (ring) and 5.2 (recursive doubling,
 // Rabenseifner, binomial tree); order.h writes each as a push / add program.
 #include "device.h"
+#include "reduce.h"
 
 namespace vcoll {
 namespace {

@@ -437,4 +437,26 @@ vcoll_status moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_ran
   return VCOLL_OK;
 }
 
+vcoll_status moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
+                       int32_t* slots) {
+  const int64_t rows = tokens * topk;
+  std::vector<int64_t> so, ro;
+  block_offsets(p, splits, so, ro);
+  for (int i = 0; i < p; ++i) {
+    int32_t* out = slots + 2 * static_cast<int64_t>(i) * rows;
+    std::fill(out, out + 2 * rows, -1);
+    const int32_t* pairs = dst_rows + static_cast<int64_t>(i) * rows;
+    int64_t pos = 0;
+    for (int j = 0; j < p; ++j)
+      for (int64_t r = 0; r < splits[static_cast<size_t>(i) * p + j]; ++r, ++pos) {
+        if (pos >= rows) return VCOLL_ERR_INVALID_ARG;
+        const int32_t pair = pairs[pos];            // t * topk + k
+        if (pair < 0 || pair >= rows) return VCOLL_ERR_INVALID_ARG;
+        out[2 * pair] = j;
+        out[2 * pair + 1] = static_cast<int32_t>(ro[static_cast<size_t>(i) * p + j] + r);
+      }
+  }
+  return VCOLL_OK;
+}
+
 }  // namespace vcoll

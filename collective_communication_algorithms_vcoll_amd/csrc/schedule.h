@@ -78,4 +78,9 @@ vcoll_status moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_ran
                             const int32_t* topk_ids, int64_t* splits_unique, int32_t* src_unique,
                             int32_t* expand, int64_t* expand_count);
 
+// Token-major view of a moe_plan: slots[i][2(t*topk+k)] = destination rank,
+// [.. + 1] = row in that rank's receive buffer, of rank i's pair (t, k).
+vcoll_status moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
+                       int32_t* slots);
+
 }  // namespace vcoll

@@ -1,5 +1,6 @@
 // The stepwise (one launch per algorithm step) all-reduce kernel of libvcoll.
 #include "device.h"
+#include "step.h"
 
 namespace vcoll {
 namespace {

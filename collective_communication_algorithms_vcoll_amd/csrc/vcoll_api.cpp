@@ -6,7 +6,10 @@
 #include <cstring>
 #include <vector>
 
-#include "kernels.h"
+#include "hier.h"
+#include "move.h"
+#include "reduce.h"
+#include "step.h"
 #include "schedule.h"
 #include "vcoll.h"
 #include "vcoll_bench.h"
@@ -434,6 +437,62 @@ vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dt
   int32_t steps = 0;
   build_ledger_hierarchical(nodes, local, n, elem_bytes(dtype), out, &steps);
   return emit_ledger(out, steps, p, msgs, cap, n_msgs, sent_bytes, recv_bytes, n_steps);
+}
+
+vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
+                             int32_t* slots) {
+  if (!valid_p(p) || tokens < 0 || topk < 1 || !splits || (tokens > 0 && (!dst_rows || !slots)))
+    return VCOLL_ERR_INVALID_ARG;
+  if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
+    if (splits[k] < 0) return VCOLL_ERR_INVALID_ARG;
+  return moe_slots(p, tokens, topk, splits, dst_rows, slots);
+}
+
+vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden, vcoll_dtype dtype, int fp8,
+                                const void* const* token_tables, const int32_t* const* slots,
+                                void* const* recv, const int64_t* recv_rows, void* stream) {
+  if (!valid_p(p) || tokens < 0 || topk < 1 || hidden < 0 || !valid_dtype(dtype) || !recv_rows)
+    return VCOLL_ERR_INVALID_ARG;
+  if (fp8 && (dtype != VCOLL_BF16 || hidden % 128 != 0)) return VCOLL_ERR_INVALID_ARG;
+  if (tokens * topk > INT32_MAX || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
+  if (tokens == 0 || hidden == 0) return VCOLL_OK;
+  if (!token_tables || !slots || !recv) return VCOLL_ERR_INVALID_ARG;
+  const int64_t rb = hidden * elem_bytes(dtype);
+  const int64_t orb = fp8 ? hidden + hidden / 32 : rb;
+  bool vec = rb % 16 == 0;
+  for (int j = 0; j < p; ++j) {
+    if (recv_rows[j] < 0 || recv_rows[j] > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+    if (recv_rows[j] > 0 && !recv[j]) return VCOLL_ERR_INVALID_ARG;
+    if (recv_rows[j] > 0 && fp8 && (reinterpret_cast<uintptr_t>(recv[j]) & 3u) != 0) return VCOLL_ERR_INVALID_ARG;
+    if (recv_rows[j] > 0) vec = vec && aligned16(recv[j]);
+  }
+  for (int i = 0; i < p; ++i) {
+    if (!token_tables[i] || !slots[i]) return VCOLL_ERR_INVALID_ARG;
+    if (fp8 && !aligned16(token_tables[i])) return VCOLL_ERR_INVALID_ARG;
+    vec = vec && aligned16(token_tables[i]);
+  }
+  PushArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int j = 0; j < p; ++j) {
+    a.recv[j] = recv[j];
+    a.recv_rows[j] = static_cast<int32_t>(recv_rows[j]);
+  }
+  a.tokens = tokens;
+  a.row_bytes = rb;
+  a.out_row_bytes = orb;
+  a.hidden = hidden;
+  a.topk = topk;
+  a.p = p;
+  a.vec = vec;
+  a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / rb)));
+  for (int i = 0; i < p; ++i) {       // one launch per sending rank
+    a.table = token_tables[i];
+    a.slots = slots[i];
+    const vcoll_status st = from_hip(launch_dispatch_push(a, fp8 != 0, static_cast<hipStream_t>(stream)));
+    if (st != VCOLL_OK) return st;
+  }
+  return VCOLL_OK;
 }
 
 vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank, const int32_t* topk_ids,

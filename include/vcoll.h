@@ -186,6 +186,32 @@ vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n,
                                  int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps);
 
 /*
+ * Token-major form of a vcoll_moe_plan ([NCC] 7.4), for vcoll_moe_dispatch.
+ * Host only. From splits [p*p] and dst_rows [p][tokens*topk] of
+ * vcoll_moe_plan it fills slots [p][tokens*topk][2] int32: for rank i's
+ * pair (t, k), the destination rank j and the row of recv[j] that the
+ * plain dispatch (vcoll_all_to_all with src_rows) writes it to.
+ */
+vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
+                             int32_t* slots);
+
+/*
+ * MoE dispatch, token-major ([NCC] 7.4): every token row of every rank is
+ * read once and written to each of its topk slots (slots[i] on the device,
+ * as filled by vcoll_moe_slots), so the token tables are read once instead
+ * of once per (token, expert) pair. fp8 = 0 copies rows of `hidden`
+ * elements of dtype (F32 or BF16); the receive buffers then equal those of
+ * the plain dispatch bit for bit. fp8 != 0 (dtype BF16, hidden a multiple
+ * of 128) stores each row as the FP8 payload of vcoll_moe_dispatch_fp8,
+ * quantised once per token. recv_rows[j] bounds recv[j]; a slot outside
+ * [0, p) x [0, recv_rows[j]) is skipped. Token tables 16-byte aligned for
+ * FP8; receive buffers 4-byte aligned for FP8.
+ */
+vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden, vcoll_dtype dtype, int fp8,
+                                const void* const* token_tables, const int32_t* const* slots,
+                                void* const* recv, const int64_t* recv_rows, void* stream);
+
+/*
  * Deduplicated MoE dispatch plan ([NCC] 7.4 and exercise 10: a token goes
  * once to each place that needs it and is then copied locally). Host only,
  * integers only; topk_ids and expert placement as vcoll_moe_plan. Rank i

@@ -168,3 +168,79 @@ def test_fp8_full_workload_sampled_rows(vc):
         got = recv[j][rows].cpu().numpy()
         want = fp8.quantize_rows(np.stack([oracle.bf16_to_f32(toks[i][t]) for i, t in want_tok]))
         assert np.array_equal(got, want), f"rank {j}"
+
+
+# --------------------------------------------------------------------------- token-major dispatch
+
+def slots_gpu(vc, splits, dst):
+    import torch
+    s = vc.vcoll_moe_slots(splits, np.stack(dst))
+    return [torch.from_numpy(np.ascontiguousarray(s[i])).cuda() for i in range(len(dst))]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_token_major_dispatch_equals_gather_dispatch(vc, dtype):
+    """Full MoE workload: reading each token once and writing it to its 8
+    slots gives the plain dispatch's receive buffers bit for bit."""
+    import torch
+    M = workloads.MOE
+    p, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    if dtype == "f32":
+        T, H = 1024, 2048 + 6                           # rows of 8216 bytes: the element path
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    splits, src, dst = vc.vcoll_moe_plan(topk, E // p)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+            for _ in range(p)]
+    say(f"gather dispatch {dtype}")
+    want = vc.vcoll_all_to_all(toks, splits, src_rows=[gpu_i32(s) for s in src])
+    say(f"token-major dispatch {dtype}")
+    got = vc.vcoll_moe_dispatch(toks, slots_gpu(vc, splits, dst), splits.sum(axis=0), K)
+    sync()
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    for j in range(p):
+        assert torch.equal(got[j].view(iv), want[j].view(iv))
+
+
+def test_token_major_fp8_dispatch_equals_oracle_and_row_major(vc):
+    import torch
+    p, T, K, E, H = 4, 64, 3, 16, 384
+    topk = small_routing(p, T, K, E, 3)
+    toks = [workloads.rank_window(workloads.TAG_TEST * 1000 + 960, i, 0, T * H, ("normal", 0.0, 1.0),
+                                  "bf16").reshape(T, H) for i in range(p)]
+    splits, src, dst = vc.vcoll_moe_plan(np.stack(topk), E // p)
+    got = vc.vcoll_moe_dispatch([to_gpu_bf16(t) for t in toks], slots_gpu(vc, splits, dst), splits.sum(axis=0),
+                                K, fp8=True)
+    sync()
+    want, _ = moe.dispatch_fp8(toks, splits, list(src))
+    for j in range(p):
+        assert np.array_equal(got[j].cpu().numpy(), want[j]), f"rank {j}"
+
+
+def test_token_major_fp8_full_workload_equals_row_major(vc):
+    import torch
+    M = workloads.MOE
+    p, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    splits, src, dst = vc.vcoll_moe_plan(topk, E // p)
+    g = torch.Generator(device="cuda").manual_seed(14)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
+    want = vc.vcoll_moe_dispatch_fp8(toks, splits, [gpu_i32(s) for s in src])
+    got = vc.vcoll_moe_dispatch(toks, slots_gpu(vc, splits, dst), splits.sum(axis=0), K, fp8=True)
+    sync()
+    for j in range(p):
+        assert torch.equal(got[j], want[j])
+
+
+def test_token_major_dispatch_skips_bad_slots(vc):
+    import torch
+    p, T, H, K = 2, 3, 64, 2
+    toks = [torch.arange(T * H, device="cuda", dtype=torch.float32).reshape(T, H) + 1000 * i for i in range(p)]
+    # rank 0: token 0 -> (1, 0) and an out-of-range rank; token 1 -> (0, 0), row 9 (too big); token 2 -> (0, 1), (1, 1)
+    s0 = torch.tensor([[1, 0], [5, 0], [0, 0], [0, 9], [0, 1], [1, 1]], dtype=torch.int32, device="cuda")
+    s1 = torch.full((T * K, 2), -1, dtype=torch.int32, device="cuda")
+    recv = [torch.full((2, H), -7.0, device="cuda") for _ in range(p)]
+    vc.vcoll_moe_dispatch(toks, [s0, s1], [2, 2], K, recv=recv)
+    sync()
+    assert torch.equal(recv[1][0], toks[0][0]) and torch.equal(recv[0][0], toks[0][1])
+    assert torch.equal(recv[0][1], toks[0][2]) and torch.equal(recv[1][1], toks[0][2])

@@ -194,3 +194,26 @@ def test_fp8_ledger_counts_payload_bytes():
     msgs, sent, _, _ = vc.vcoll_ledger("all_to_all", "ring", p, 0, "u8", splits, fp8.row_bytes(H))
     for i in range(p):
         assert sent[i] == sum(int(splits[i, j]) for j in range(p) if j != i) * (H + H // 32)
+
+
+# --------------------------------------------------------------------------- token-major dispatch map
+
+@pytest.mark.parametrize("p,T,K,E", [(2, 9, 2, 4), (4, 40, 3, 16), (8, 64, 8, 256), (3, 11, 2, 3)])
+def test_slots_invert_the_plan(p, T, K, E):
+    """slots[i][t*K + k] names the rank and row the plain dispatch writes
+    rank i's pair (t, k) to: receive row r of rank j comes from the sender
+    block that covers r, at the pair the oracle's plan puts there."""
+    topk = small_routing(p, T, K, E, 70 + p)
+    splits, src, dst = moe.plan(topk, E // p)
+    slots = vc.vcoll_moe_slots(splits, np.stack(dst))
+    assert slots.shape == (p, T * K, 2)
+    for j in range(p):
+        r = 0
+        for i in range(p):
+            s0 = int(splits[i, :j].sum())
+            for q in range(int(splits[i, j])):
+                pair = int(dst[i][s0 + q])                 # (t, k) of this sent row
+                assert slots[i, pair].tolist() == [j, r]
+                assert pair // K == int(src[i][s0 + q])    # the token it carries
+                r += 1
+    assert np.all(slots[:, :, 0] >= 0)                      # every pair has a destination
