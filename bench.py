@@ -40,15 +40,68 @@ sys.path.insert(0, ROOT)
 METRIC = "all-reduce effective HBM GB/s (p=8, 25 MB/rank fp32) + % of HBM roofline"
 PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
-KERNEL_SOURCES = ("reduce.hip", "reduce.h", "device.h", "common.h", "order.h")   # what defines the headline kernel
+# the headline kernel in libvcoll.so: reduce_kernel<f32, ring, p = 8, 2 vectors per thread,
+# all-reduce, large-grid variant>
+HEADLINE_SYMBOL = "reduce_kernelILi0ELi0ELi8ELi2ELb0ELb1EE"
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "collective_communication_algorithms_vcoll_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def _elf_sections(data: bytes) -> list:
+    """(name, type, addr, offset, size, link) of every section of an ELF64
+    little-endian image, in header order."""
+    import struct
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    raw = [struct.unpack_from("<IIQQQQI", data, shoff + i * shentsize) for i in range(shnum)]
+    strtab = raw[shstrndx][4]
+
+    def name(o):
+        return data[strtab + o:data.index(b"\0", strtab + o)].decode()
+    return [(name(r[0]), r[1], r[3], r[4], r[5], r[6]) for r in raw]
+
+
+def kernel_code_hash(symbol: str = HEADLINE_SYMBOL) -> str | None:
+    """Hash of the gfx950 machine code of one kernel of the built libvcoll.so
+    (read from the library's own offload bundles), or None. Counter traffic
+    measured for a kernel stays valid exactly as long as this hash does."""
+    import struct
+    lib = os.path.join(ROOT, "collective_communication_algorithms_vcoll_amd", "libvcoll.so")
+    if not os.path.exists(lib):
+        return None
+    data = open(lib, "rb").read()
+    fats = [x for x in _elf_sections(data) if x[0] == ".hip_fatbin"]
+    if not fats:
+        return None
+    _, _, _, off, size, _ = fats[0]
+    fat = data[off:off + size]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    pos = fat.find(magic)
+    while pos >= 0:
+        count = struct.unpack_from("<Q", fat, pos + 24)[0]
+        q = pos + 32
+        for _ in range(count):
+            e_off, e_size, id_len = struct.unpack_from("<QQQ", fat, q)
+            ident = fat[q + 24:q + 24 + id_len]
+            q += 24 + id_len
+            if b"gfx950" not in ident:
+                continue
+            code = fat[pos + e_off:pos + e_off + e_size]
+            csec = _elf_sections(code)
+            symtabs = [x for x in csec if x[1] == 2]            # SHT_SYMTAB
+            texts = [x for x in csec if x[0] == ".text"]
+            if not symtabs or not texts:
+                continue
+            _, _, _, so, ss, link = symtabs[0]
+            strtab = csec[link][3]
+
+            for k in range(ss // 24):
+                st_name, st_info, _, _, st_value, st_size = struct.unpack_from("<IBBHQQ", code, so + 24 * k)
+                nm = code[strtab + st_name:code.index(b"\0", strtab + st_name)].decode()
+                if symbol in nm and not nm.endswith(".kd") and st_size > 0:
+                    text = texts[0]
+                    start = text[3] + (st_value - text[2])
+                    return hashlib.sha256(code[start:start + st_size]).hexdigest()[:16]
+        pos = fat.find(magic, pos + len(magic))
+    return None
 
 
 def counter_traffic(kernel_key: str):
@@ -59,7 +112,8 @@ def counter_traffic(kernel_key: str):
     with open(path) as f:
         data = json.load(f)
     entry = data.get(kernel_key)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    code = kernel_code_hash()
+    if not entry or code is None or entry.get("code_hash") != code:
         return None
     return entry.get("bytes_per_launch")
 
@@ -352,6 +406,10 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
     lines = [f"# rocprofv3 kernel statistics: headline ring all-reduce (p=8, 25 MiB fp32/rank)", "",
              f"Command: `{command}`", "", "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     bench_json = os.path.join(trace_dir, "bench.json")
+    code_hash = None                                # of the library the profiled run loaded
+    if os.path.exists(bench_json):
+        with open(bench_json) as f:
+            code_hash = json.loads(f.read().strip().splitlines()[-1])["roofline"].get("kernel_code")
     rocprof_avg = None
     for r in stats:
         name = r.get('Name', r.get('KernelName', '?'))
@@ -400,12 +458,131 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
         f.write("\n".join(lines) + "\n")
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(tpath)) if os.path.exists(tpath) else {}
-    data["ring_f32_p8_ddp_bucket"] = {"source_hash": kernel_source_hash(), "bytes_per_launch": traffic,
+    data["ring_f32_p8_ddp_bucket"] = {"code_hash": code_hash, "bytes_per_launch": traffic,
                                       "fetch_units": fetch, "write_units": write}
     with open(tpath, "w") as f:
         json.dump(data, f, indent=1)
     print("\n".join(lines))
     return 0
+
+
+def sweep(vc, torch, out_path: str, max_bytes: int) -> int:
+    """Message-size sweep of the fused all-reduce: every p in SWEEP_P, every
+    per-rank size in SWEEP_BYTES up to max_bytes, every algorithm. Each point
+    is timed (events over back-to-back launches on one buffer set, so points
+    whose 2*p*S fits the 256 MB Infinity Cache run partly from it) and
+    verified: every rank equal to rank 0; the oracle on the whole vector
+    (p*n <= 2^25) or on windows (every chunk boundary plus 32 random
+    windows of 1024 elements); and, where memory allows, the stepwise
+    (one launch per step) execution of the same algorithm over all
+    elements. One JSON line per point goes to out_path."""
+    import numpy as np
+    import oracle
+    import workloads
+    fails = 0
+    with open(out_path, "w") as out:
+        for p in workloads.SWEEP_P:
+            for nbytes in workloads.SWEEP_BYTES:
+                if nbytes > max_bytes:
+                    continue
+                n = nbytes // 4
+                host = p * n <= 2 ** 25
+                if host:
+                    x = [workloads.rank_window(workloads.TAG_SWEEP, r, 0, n, workloads.SWEEP_DIST, "f32")
+                         for r in range(p)]
+                    t = torch.from_numpy(np.stack(x)).cuda()
+                else:
+                    # too large to draw on the host in reasonable time: torch's
+                    # device generator, windows copied back for the oracle
+                    g = torch.Generator(device="cuda").manual_seed(workloads.TAG_SWEEP * 10 ** 6 + p * 1000 + nbytes % 997)
+                    t = torch.randn((p, n), device="cuda", generator=g)
+                o = torch.empty_like(t)
+                offs = oracle.chunk_bounds(n, p)
+                rng = np.random.default_rng([p, nbytes])
+                w = min(1024, n)
+                wins = sorted({(max(0, min(b - w // 2, n - w)), max(0, min(b - w // 2, n - w)) + w) for b in offs[1:-1]} |
+                              {(int(s0), int(s0) + w) for s0 in rng.integers(0, n - w + 1, size=32)})
+                step_ok = 3 * p * nbytes <= 64 * 2 ** 30
+                for algo in oracle.ALGOS:
+                    call = vc.prepare_allreduce(algo, t, o)
+                    K = int(min(200, max(5, 4e9 / (2 * p * nbytes))))
+                    _, ms = time_launches([call], K, 3)
+                    rec = {"p": p, "bytes_per_rank": nbytes, "algo": algo, "us": round(ms * 1e3, 2),
+                           "GBps": rate(2 * p * nbytes, ms), "launches": K}
+                    call()
+                    torch.cuda.synchronize()
+                    rec["ranks_equal"] = all(torch.equal(o[r].view(torch.int32), o[0].view(torch.int32))
+                                             for r in range(1, p))
+                    if host:
+                        want, _ = oracle.allreduce(x, algo, "f32")
+                        rec["oracle_equal"] = bool(np.array_equal(o.cpu().numpy().view(np.uint32),
+                                                                   np.stack(want).view(np.uint32)))
+                        rec["oracle_fraction"] = 1.0
+                    else:
+                        ok = True
+                        for lo, hi in wins:
+                            xw = [t[r, lo:hi].cpu().numpy() for r in range(p)]
+                            want, _ = oracle.allreduce(xw, algo, "f32", n=n, lo=lo)
+                            ok = ok and bool(np.array_equal(o[:, lo:hi].cpu().numpy().view(np.uint32),
+                                                            np.stack(want).view(np.uint32)))
+                        mask = np.zeros(n, bool)              # windows may overlap
+                        for lo, hi in wins:
+                            mask[lo:hi] = True
+                        rec["oracle_equal"] = ok
+                        rec["oracle_fraction"] = round(float(mask.mean()), 6)
+                    if step_ok:
+                        st = torch.empty_like(t)
+                        vc.vcoll_allreduce_stepwise(algo, t, st)
+                        torch.cuda.synchronize()
+                        rec["stepwise_equal"] = bool(torch.equal(st.view(torch.int32), o.view(torch.int32)))
+                        del st
+                    good = rec["ranks_equal"] and rec["oracle_equal"] and rec.get("stepwise_equal", True)
+                    fails += 0 if good else 1
+                    out.write(json.dumps(rec) + "\n")
+                    out.flush()
+                    print(f"sweep p={p} {nbytes} B {algo}: {rec['us']} us {rec['GBps']} GB/s "
+                          f"{'ok' if good else 'MISMATCH'}", file=sys.stderr, flush=True)
+                del t, o
+                torch.cuda.empty_cache()
+    return 1 if fails else 0
+
+
+def summarize_sweep(jsonl: str, command: str) -> int:
+    """The sweep's JSON lines as a table in profiles/: microseconds where the
+    whole all-reduce moves less than 64 MiB (latency-bound), GB/s above."""
+    recs = [json.loads(x) for x in open(jsonl)]
+    sizes = sorted({r["bytes_per_rank"] for r in recs})
+
+    def label(b):
+        return f"{b >> 30} GiB" if b >= 2 ** 30 else (f"{b >> 20} MiB" if b >= 2 ** 20 else f"{b >> 10} KiB")
+    bad = [r for r in recs if not (r["ranks_equal"] and r["oracle_equal"] and r.get("stepwise_equal", True))]
+    lines = ["# Fused all-reduce message-size sweep (reduce_kernel, float32, one buffer set)", "",
+             f"Command: `{command}`", "",
+             f"{len(recs)} points, {len(bad)} mismatches. Every point: all ranks equal; oracle on the whole "
+             f"vector for {sum(r['oracle_fraction'] == 1.0 for r in recs)} points, on windows for the rest "
+             f"(smallest verified fraction {min(r['oracle_fraction'] for r in recs):.2e}); stepwise execution "
+             f"equal on every element for {sum('stepwise_equal' in r for r in recs)} points.", "",
+             "Cells: microseconds per all-reduce when 2*p*S < 64 MiB, else GB/s of algorithmic bytes (2*p*S). "
+             "Buffers are reused, so points whose 2*p*S fits the 256 MB Infinity Cache run partly from it.", ""]
+    for algo in ("ring", "rd", "rabenseifner", "tree"):
+        lines += [f"## {algo}", "", "| p | " + " | ".join(label(b) for b in sizes) + " |",
+                  "|---|" + "---|" * len(sizes)]
+        for p in sorted({r["p"] for r in recs}):
+            cells = []
+            for b in sizes:
+                r = [x for x in recs if x["p"] == p and x["bytes_per_rank"] == b and x["algo"] == algo]
+                if not r:
+                    cells.append("")
+                elif 2 * p * b < 64 * 2 ** 20:
+                    cells.append(f"{r[0]['us']:.1f} us")
+                else:
+                    cells.append(f"{r[0]['GBps']:.0f}")
+            lines.append(f"| {p} | " + " | ".join(cells) + " |")
+        lines.append("")
+    with open(os.path.join(ROOT, "profiles", "reduce_kernel_sweep_p2-72_1KiB-1GiB.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return 1 if bad else 0
 
 
 def main() -> int:
@@ -422,9 +599,16 @@ def main() -> int:
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 output directories into profiles/ summaries and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
+    ap.add_argument("--sweep", metavar="OUT_JSONL", help="run the message-size sweep instead, one JSON line per "
+                    "(p, size, algorithm) point written to OUT_JSONL, and exit")
+    ap.add_argument("--sweep-max-bytes", type=int, default=2 ** 30, help="largest per-rank size of the sweep")
+    ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", help="turn a sweep's JSON lines into a table in "
+                    "profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_profile:
         return summarize_profile(*args.summarize_profile, args.profile_command)
+    if args.summarize_sweep:
+        return summarize_sweep(args.summarize_sweep, args.profile_command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -436,6 +620,8 @@ def main() -> int:
     import collective_communication_algorithms_vcoll_amd as vc
 
     torch.cuda.set_device(0)
+    if args.sweep:
+        return sweep(vc, torch, args.sweep, args.sweep_max_bytes)
     h = headline(vc, torch, args)
     value = h["nbytes"] * args.steps / h["wall"] / 1e9
     achieved = h["nbytes"] / (h["mean_ms"] * 1e-3) / 1e9
@@ -464,6 +650,7 @@ def main() -> int:
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
             "kernel": "reduce_kernel<f32, ring, p=8>", "mean_launch_us": round(h["mean_ms"] * 1e3, 2),
+            "kernel_code": kernel_code_hash(),
         },
     }
     if args.copy_reference:

@@ -130,19 +130,36 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
       d[0] = S::widen1(raw[decltype(kc)::value]);
     });
     result = st[0][0];
-  } else if constexpr (ALGO == VCOLL_RING) {
-    result = S::widen1(static_cast<const E*>(a.leaf[rot % p])[e]);
-    for (int k = 1; k < p; ++k)
-      result = result + S::widen1(static_cast<const E*>(a.leaf[(rot + k) % p])[e]);
   } else {
+    // loads go out kOneBatch ranks at a time, so a long program (p up to
+    // 128) waits for memory p / kOneBatch times rather than p times
+    constexpr int kOneBatch = 16;
     float st[kRuntimeDepth][1];
-    for (int k = 0; k < p; ++k) {
-      const float v = S::widen1(static_cast<const E*>(a.leaf[a.rank[k]])[e]);
-      rt_push<1>(st, &v);
-      for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
+    result = 0.0f;
+    for (int k0 = 0; k0 < p; k0 += kOneBatch) {
+      E raw[kOneBatch];
+#pragma unroll
+      for (int b = 0; b < kOneBatch; ++b)
+        if (k0 + b < p) {
+          const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : a.rank[k0 + b];
+          raw[b] = static_cast<const E*>(a.leaf[rank])[e];
+        }
+#pragma unroll
+      for (int b = 0; b < kOneBatch; ++b)
+        if (k0 + b < p) {
+          const float v = S::widen1(raw[b]);
+          if constexpr (ALGO == VCOLL_RING) {
+            result = k0 + b == 0 ? v : result + v;
+          } else {
+            rt_push<1>(st, &v);
+            for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<1>(st);
+          }
+        }
     }
-    for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
-    result = st[0][0];
+    if constexpr (ALGO != VCOLL_RING) {
+      for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
+      result = st[0][0];
+    }
   }
   const E out = S::narrow1(result);
   if constexpr (RS) {
@@ -220,7 +237,7 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
                                                       int64_t boff, bool valid, int64_t out_shift) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
-  constexpr int B = 8;
+  constexpr int B = 8;               // ranks whose loads are in flight together
   float acc[VE];
   float st[kRuntimeDepth][VE];
   for (int k0 = 0; k0 < p; k0 += B) {

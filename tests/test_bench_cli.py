@@ -19,3 +19,13 @@ def test_help_lists_the_contract_flags():
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup"):
         assert flag in r.stdout
+
+
+def test_headline_kernel_code_is_found_in_the_library():
+    """The counter traffic is keyed to the headline kernel's machine code,
+    read back from the built library's gfx950 code object."""
+    sys.path.insert(0, ROOT)
+    import bench
+    h = bench.kernel_code_hash()
+    assert h is not None and len(h) == 16
+    assert bench.kernel_code_hash("copy_kernel") not in (None, h)
