@@ -280,6 +280,27 @@ def extras(vc, torch, h, args):
         del t, ts, os_
     torch.cuda.empty_cache()
 
+    # decode-sized all-reduces replayed from a HIP graph: the per-call cost
+    # without the host's launch path (100 captured calls per replay)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    t = torch.randn((8, 2560), device="cuda", generator=g)
+    o = torch.empty_like(t)
+    for algo in ("ring", "rd", "rabenseifner", "tree"):
+        vc.vcoll_allreduce(algo, t, o)
+        vc.vcoll_allreduce_stepwise(algo, t, o)
+    torch.cuda.synchronize()
+    for label, fn in (("fused", vc.vcoll_allreduce), ("stepwise", lambda a, x, y: vc.vcoll_allreduce_stepwise(a, x, y))):
+        for algo in ("ring", "rd", "rabenseifner", "tree"):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(100):
+                    fn(algo, t, o)
+            _, ms = time_launches([graph.replay], 20, 3)
+            ex[f"p8_decode_10KiB_{algo}_{label}_graph"] = {"us_per_allreduce": round(ms * 1e3 / 100, 2)}
+            del graph
+    del t, o
+    torch.cuda.empty_cache()
+
     # p = 16, 192 MiB bf16 per rank, float32 accumulation
     P16, N16 = 16, 100_663_296
     g = torch.Generator(device="cuda").manual_seed(3)
@@ -288,19 +309,19 @@ def extras(vc, torch, h, args):
     S16 = N16 * 2
     for algo in ("ring", "rabenseifner"):
         call = vc.prepare_allreduce(algo, t16, o16)
-        _, mean_ms = time_launches([call], 10, 2)
+        _, mean_ms = time_launches([call], 30, 5)
         ex[f"hier16_bf16_{algo}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms), "us": round(mean_ms * 1e3, 1)}
     for nodes, local in ((2, 8), (4, 4)):
         call = vc.prepare_allreduce_hierarchical(nodes, local, t16, o16)
-        _, mean_ms = time_launches([call], 10, 2)
+        _, mean_ms = time_launches([call], 30, 5)
         ex[f"hier16_bf16_hierarchical_{nodes}x{local}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms),
                                                                 "us": round(mean_ms * 1e3, 1)}
     rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
     for algo, ag_algo in (("ring", "ring"), ("rabenseifner", "rd")):
         call = vc.prepare_reduce_scatter(algo, t16, rs16)
-        _, ms_rs = time_launches([call], 10, 2)
+        _, ms_rs = time_launches([call], 30, 5)
         call = vc.prepare_all_gather(ag_algo, rs16, o16)
-        _, ms_ag = time_launches([call], 10, 2)
+        _, ms_ag = time_launches([call], 30, 5)
         ex[f"hier16_bf16_{algo}_reduce_scatter"] = {"GBps": rate(P16 * S16 + S16, ms_rs), "us": round(ms_rs * 1e3, 1)}
         ex[f"hier16_bf16_{ag_algo}_all_gather"] = {"GBps": rate(S16 + P16 * S16, ms_ag), "us": round(ms_ag * 1e3, 1)}
     del t16, o16, rs16
