@@ -351,6 +351,80 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// small chunks with the run-time order program (p not compiled in): a
+// workgroup stages a [p][kSmallTile] tile of its chunk in LDS with every load
+// of the tile in flight at once, runs the order program for each element out
+// of LDS, and fans the results out. Where the per-thread path would wait for
+// memory once per 8 or 16 ranks, this waits once.
+
+constexpr int kSmallTile = 64;                                   // elements of a chunk per workgroup
+constexpr int kSmallLoads = (kMaxRanks * kSmallTile + kBlock - 1) / kBlock;
+
+template <int D, int ALGO, bool RS>
+__global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a) {
+  using S = Storage<D>;
+  using E = typename S::elem;
+  __shared__ float val[kMaxRanks * kSmallTile];                  // [leaf r][element]
+  __shared__ float res[kSmallTile];
+  const int c = blockIdx.y;
+  const int p = a.p;
+  const int tid = threadIdx.x;
+  const int64_t off = c * a.q + (c < a.r ? c : a.r);
+  const int64_t cnt = a.q + (c < a.r ? 1 : 0);
+  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kSmallTile;
+  if (e0 >= cnt) return;                                         // the whole workgroup
+  const int T = cnt - e0 < kSmallTile ? static_cast<int>(cnt - e0) : kSmallTile;
+  E raw[kSmallLoads];
+#pragma unroll
+  for (int j = 0; j < kSmallLoads; ++j) {
+    const int idx = tid + j * kBlock;
+    if (idx < p * T) {
+      const int r = idx / T;
+      raw[j] = static_cast<const E*>(a.leaf[r])[off + e0 + (idx - r * T)];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSmallLoads; ++j) {
+    const int idx = tid + j * kBlock;
+    if (idx < p * T) val[idx] = S::widen1(raw[j]);
+  }
+  __syncthreads();
+  if (tid < T) {
+    float result;
+    if constexpr (ALGO == VCOLL_RING) {
+      const int rot = (c + 1) % p;                               // chunk c's chain starts at rank c+1
+      result = val[rot * T + tid];
+      for (int k = 1; k < p; ++k) result = result + val[((rot + k) % p) * T + tid];
+    } else {
+      float st[kRuntimeDepth][1];
+      for (int k = 0; k < p; ++k) {
+        const float v = val[a.rank[k] * T + tid];
+        rt_push<1>(st, &v);
+        for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
+      }
+      for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
+      result = st[0][0];
+    }
+    res[tid] = result;
+  }
+  __syncthreads();
+  if constexpr (RS) {
+    if (tid < T) static_cast<E*>(a.dst[c])[e0 + tid] = S::narrow1(res[tid]);
+  } else {
+    for (int idx = tid; idx < p * T; idx += kBlock) {
+      const int r = idx / T;
+      const int e = idx - r * T;
+      static_cast<E*>(a.dst[r])[off + e0 + e] = S::narrow1(res[e]);
+    }
+  }
+}
+
+// Largest chunk (elements) that the run-time path stages through LDS: at
+// p = 72 this is 3x faster than the per-thread path up to 256 KiB per rank
+// and slower from 1 MiB, where the per-thread path's 16-byte accesses win.
+constexpr int64_t kSmallMax = 1024;
+
 // 16-byte vectors per thread of the reduce kernel (all are loaded before the
 // first add). Build-time override: -DVCOLL_V_P8=<n> for p = 8.
 #ifndef VCOLL_V_P8
@@ -376,6 +450,10 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
     if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true>, grid, args, stream);
     return launch(reduce_kernel<D, ALGO, P, V, RS, false>, grid, args, stream);
   } else {
+    if (max_chunk <= kSmallMax) {
+      const dim3 small(static_cast<unsigned>((max_chunk + kSmallTile - 1) / kSmallTile), chunks);
+      return launch(reduce_small_kernel<D, ALGO, RS>, small, args, stream);
+    }
     return launch(reduce_kernel<D, ALGO, P, V, RS, false>, grid, args, stream);
   }
 }

@@ -431,3 +431,30 @@ def test_message_size_sweep_large_windows(vc, p, nbytes):
         out = vc.vcoll_allreduce(algo, t)
         sync()
         _window_check(out, x, n, "f32", algo, _sample_windows(n, p, k=8, w=512, seed=p))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p", [3, 12, 72, 128])
+def test_small_chunks_of_the_run_time_program(vc, p, dtype):
+    """p not compiled in, chunks of at most 1024 elements: the LDS-staged
+    path (64-element tiles, the last one ragged) for all-reduce, ring
+    reduce-scatter and reduce to a root."""
+    from oracle import rooted
+    n = p * 1000 + p // 2 + 3
+    x = rand_inputs(p, n, dtype, 300 + p)
+    t = upload(x, dtype)
+    for algo in ALGOS:
+        say(f"small-chunk all-reduce p={p} n={n} {algo} {dtype}")
+        want, _ = oracle.allreduce(x, algo, dtype)
+        got = download(vc.vcoll_allreduce(algo, t), dtype)
+        assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"{algo} p={p}")
+    rs = vc.vcoll_reduce_scatter("ring", t)
+    sync()
+    want, _ = oracle.reduce_scatter(x, "ring", dtype)
+    for c in range(p):
+        assert_bits_equal(download(rs[c], dtype), bits(want[c], dtype), f"rs chunk {c}")
+    root = p // 2
+    red = vc.vcoll_reduce(t, root=root)
+    sync()
+    want, _ = rooted.reduce(x, root, dtype)
+    assert_bits_equal(download(red, dtype), bits(want, dtype), "reduce")
