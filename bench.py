@@ -363,7 +363,7 @@ def extras(vc, torch, h, args):
         "GBps": rate(rows * rb + rows * orb, ms_f), "us": round(ms_f * 1e3, 1),
         "algorithmic_bytes": rows * rb + rows * orb, "payload_bytes_per_row": orb}
     # token-major dispatch: each token row read once, written to its 8 slots
-    slots = vc.vcoll_moe_slots(splits, dst_rows)
+    slots = vc.vcoll_moe_slots(splits, dst_rows, K)
     slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
     recv_rows = splits.sum(axis=0)
     tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)

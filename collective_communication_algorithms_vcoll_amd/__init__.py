@@ -569,13 +569,14 @@ def vcoll_moe_plan(topk_ids: np.ndarray, experts_per_rank: int):
     return splits, src, dst
 
 
-def vcoll_moe_slots(splits, dst_rows) -> np.ndarray:
+def vcoll_moe_slots(splits, dst_rows, topk: int) -> np.ndarray:
     """Token-major view of a vcoll_moe_plan: int32 [p, tokens*topk, 2]
     (destination rank, destination row) per (token, slot)."""
     sp = np.ascontiguousarray(np.asarray(splits, dtype=np.int64))
     dr = np.ascontiguousarray(np.asarray(dst_rows, dtype=np.int32))
     p, rows = dr.shape
-    topk = 1
+    if rows % topk:
+        raise ValueError("vcoll_moe_slots: dst_rows must hold tokens * topk entries per rank")
     slots = np.zeros((p, rows, 2), dtype=np.int32)
     i32 = ctypes.POINTER(ctypes.c_int32)
     _check(_lib().vcoll_moe_slots(p, rows // topk, topk, sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),

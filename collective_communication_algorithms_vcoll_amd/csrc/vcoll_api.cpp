@@ -88,6 +88,19 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
   return from_hip(launch_reduce(a, dtype, algo, scatter, ch.count(0), p, static_cast<hipStream_t>(stream)));
 }
 
+// Workgroup tiles of each launch of at most kA2ABlocks blocks; false when a
+// launch would need more than INT32_MAX of them (checked before any launch,
+// so that an error return still means nothing was enqueued).
+bool block_launch_tiles(const std::vector<A2ABlock>& blocks, int32_t rows_per_tile) {
+  for (size_t b0 = 0; b0 < blocks.size(); b0 += kA2ABlocks) {
+    int64_t tiles = 0;
+    for (size_t k = b0; k < std::min<size_t>(blocks.size(), b0 + kA2ABlocks); ++k)
+      tiles += (blocks[k].rows + rows_per_tile - 1) / rows_per_tile;
+    if (tiles > INT32_MAX) return false;
+  }
+  return true;
+}
+
 // Two-call ledger convention shared by every ledger entry point.
 vcoll_status emit_ledger(const std::vector<vcoll_msg>& out, int32_t steps, int p, vcoll_msg* msgs, int64_t cap,
                          int64_t* n_msgs, int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps) {
@@ -213,6 +226,7 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
       blocks.push_back(b);
       block_vec.push_back(aligned16(b.src) && aligned16(b.dst));
     }
+  if (!block_launch_tiles(blocks, rows_per_tile)) return VCOLL_ERR_UNSUPPORTED;
   for (size_t b0 = 0; b0 < blocks.size(); b0 += kA2ABlocks) {
     A2AArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -547,6 +561,7 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
       b.dst_limit = static_cast<int32_t>(rows);
       blocks.push_back(b);
     }
+  if (!block_launch_tiles(blocks, rows_per_tile)) return VCOLL_ERR_UNSUPPORTED;
   for (size_t b0 = 0; b0 < blocks.size(); b0 += kA2ABlocks) {
     Fp8Args a;
     std::memset(&a, 0, sizeof(a));

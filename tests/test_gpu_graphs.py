@@ -64,7 +64,7 @@ def test_captured_all_to_all_and_moe_dispatch_replay(vc):
     p, T, H, E, K = M["p"], 256, 512, M["experts"], M["topk"]
     topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
     splits, src, dst = vc.vcoll_moe_plan(topk, E // p)
-    slots = vc.vcoll_moe_slots(splits, dst)
+    slots = vc.vcoll_moe_slots(splits, dst, K)
     g = torch.Generator(device="cuda").manual_seed(22)
     toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
     srcg = [torch.from_numpy(s).cuda() for s in src]

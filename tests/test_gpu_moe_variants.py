@@ -172,9 +172,9 @@ def test_fp8_full_workload_sampled_rows(vc):
 
 # --------------------------------------------------------------------------- token-major dispatch
 
-def slots_gpu(vc, splits, dst):
+def slots_gpu(vc, splits, dst, topk):
     import torch
-    s = vc.vcoll_moe_slots(splits, np.stack(dst))
+    s = vc.vcoll_moe_slots(splits, np.stack(dst), topk)
     return [torch.from_numpy(np.ascontiguousarray(s[i])).cuda() for i in range(len(dst))]
 
 
@@ -195,7 +195,7 @@ def test_token_major_dispatch_equals_gather_dispatch(vc, dtype):
     say(f"gather dispatch {dtype}")
     want = vc.vcoll_all_to_all(toks, splits, src_rows=[gpu_i32(s) for s in src])
     say(f"token-major dispatch {dtype}")
-    got = vc.vcoll_moe_dispatch(toks, slots_gpu(vc, splits, dst), splits.sum(axis=0), K)
+    got = vc.vcoll_moe_dispatch(toks, slots_gpu(vc, splits, dst, K), splits.sum(axis=0), K)
     sync()
     iv = torch.int16 if dtype == "bf16" else torch.int32
     for j in range(p):
@@ -209,7 +209,7 @@ def test_token_major_fp8_dispatch_equals_oracle_and_row_major(vc):
     toks = [workloads.rank_window(workloads.TAG_TEST * 1000 + 960, i, 0, T * H, ("normal", 0.0, 1.0),
                                   "bf16").reshape(T, H) for i in range(p)]
     splits, src, dst = vc.vcoll_moe_plan(np.stack(topk), E // p)
-    got = vc.vcoll_moe_dispatch([to_gpu_bf16(t) for t in toks], slots_gpu(vc, splits, dst), splits.sum(axis=0),
+    got = vc.vcoll_moe_dispatch([to_gpu_bf16(t) for t in toks], slots_gpu(vc, splits, dst, K), splits.sum(axis=0),
                                 K, fp8=True)
     sync()
     want, _ = moe.dispatch_fp8(toks, splits, list(src))
@@ -226,7 +226,7 @@ def test_token_major_fp8_full_workload_equals_row_major(vc):
     g = torch.Generator(device="cuda").manual_seed(14)
     toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
     want = vc.vcoll_moe_dispatch_fp8(toks, splits, [gpu_i32(s) for s in src])
-    got = vc.vcoll_moe_dispatch(toks, slots_gpu(vc, splits, dst), splits.sum(axis=0), K, fp8=True)
+    got = vc.vcoll_moe_dispatch(toks, slots_gpu(vc, splits, dst, K), splits.sum(axis=0), K, fp8=True)
     sync()
     for j in range(p):
         assert torch.equal(got[j], want[j])

@@ -205,7 +205,7 @@ def test_slots_invert_the_plan(p, T, K, E):
     block that covers r, at the pair the oracle's plan puts there."""
     topk = small_routing(p, T, K, E, 70 + p)
     splits, src, dst = moe.plan(topk, E // p)
-    slots = vc.vcoll_moe_slots(splits, np.stack(dst))
+    slots = vc.vcoll_moe_slots(splits, np.stack(dst), K)
     assert slots.shape == (p, T * K, 2)
     for j in range(p):
         r = 0
