@@ -212,12 +212,15 @@ def test_guard_bands_and_poison(vc):
 
 # --------------------------------------------------------------------------- reduce-scatter / all-gather
 
+# Rabenseifner's reduce-scatter and recursive doubling's all-gather exist for
+# powers of two only (other p return VCOLL_ERR_UNSUPPORTED, tested below)
+RS_CASES = [("ring", p) for p in (1, 2, 3, 4, 8, 16, 72)] + [("rabenseifner", p) for p in (1, 2, 4, 8, 16)]
+AG_CASES = [("ring", p) for p in (1, 2, 3, 4, 8, 16, 72)] + [("rd", p) for p in (1, 2, 4, 8, 16)]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("p", [1, 2, 3, 4, 8, 16, 72])
-@pytest.mark.parametrize("algo", ["ring", "rabenseifner"])
+@pytest.mark.parametrize("algo,p", RS_CASES)
 def test_reduce_scatter_matches_oracle(vc, algo, p, dtype):
-    if algo == "rabenseifner" and p & (p - 1):
-        pytest.skip("Rabenseifner reduce-scatter needs a power-of-two p")
     for n in (ragged_n(p) if p <= 16 else 72 * 2500 + 41, p * 2048 * 3):   # ragged and aligned chunks
         x = rand_inputs(p, n, dtype, seed=p + 100)
         want, _ = oracle.reduce_scatter(x, algo, dtype)
@@ -229,12 +232,18 @@ def test_reduce_scatter_matches_oracle(vc, algo, p, dtype):
             assert_bits_equal(download(got[c], dtype), bits(want[c], dtype), f"RS {algo} p={p} chunk {c}")
 
 
+def test_non_power_of_two_halving_and_doubling_are_refused(vc):
+    import torch
+    t = torch.zeros(3, 96, device="cuda")
+    with pytest.raises(vc.VcollError, match="unsupported"):
+        vc.vcoll_reduce_scatter("rabenseifner", t)
+    with pytest.raises(vc.VcollError, match="unsupported"):
+        vc.vcoll_all_gather("rd", t)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("p", [1, 2, 3, 4, 8, 16, 72])
-@pytest.mark.parametrize("algo", ["ring", "rd"])
+@pytest.mark.parametrize("algo,p", AG_CASES)
 def test_all_gather_matches_oracle(vc, algo, p, dtype):
-    if algo == "rd" and p & (p - 1):
-        pytest.skip("recursive-doubling all-gather needs a power-of-two p")
     for m in (1, 37, 4096, 5 * 2048 + 8):
         x = rand_inputs(p, m, dtype, seed=m)
         want, _ = oracle.all_gather(x, algo, dtype)
