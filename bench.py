@@ -42,7 +42,7 @@ PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
 # the headline kernel in libvcoll.so: reduce_kernel<f32, ring, p = 8, 2 vectors per thread,
 # all-reduce, large-grid variant>
-HEADLINE_SYMBOL = "reduce_kernelILi0ELi0ELi8ELi2ELb0ELb1EE"
+HEADLINE_SYMBOL = "reduce_kernelILi0ELi0ELi8ELi2ELb0ELb1ELi256EE"
 
 
 def _elf_sections(data: bytes) -> list:
@@ -413,7 +413,7 @@ def _csv_rows(root: str, suffix: str):
     return rows
 
 
-HEADLINE_KERNEL = "reduce_kernel<0, 0, 8, 2, false, true>"
+HEADLINE_KERNEL = "reduce_kernel<0, 0, 8, 2, false, true, 256>"
 COPY_KERNEL = "copy_kernel"
 
 

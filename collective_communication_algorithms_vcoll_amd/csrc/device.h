@@ -121,5 +121,11 @@ hipError_t launch(K kernel, dim3 grid, const Arg& arg, hipStream_t stream) {
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kBlock), args, 0, stream);
 }
 
+template <class K, class Arg>
+hipError_t launch(K kernel, dim3 grid, int block, const Arg& arg, hipStream_t stream) {
+  void* args[] = {const_cast<Arg*>(&arg)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(block), args, 0, stream);
+}
+
 }  // namespace dev
 }  // namespace vcoll
