@@ -60,11 +60,12 @@ struct Fp8Args {
   A2ABlock b[kA2ABlocks];     // src = token table, src_idx = gather map, dst = first row of the block
 };
 
-// Token-major MoE dispatch of one sending rank: token t's row goes to row
-// slots[2(t*topk+k)+1] of rank slots[2(t*topk+k)] for every slot k.
+// Token-major MoE dispatch. Grid: x = tiles of tokens, y = sending rank i:
+// token t of rank i goes to row slots[i][2(t*topk+k)+1] of rank
+// slots[i][2(t*topk+k)] for every slot k.
 struct PushArgs {
-  const void* table;          // the rank's token rows
-  const int32_t* slots;       // [tokens * topk][2]: destination rank, destination row
+  const void* table[kMaxRanks];      // each rank's token rows
+  const int32_t* slots[kMaxRanks];   // each rank's [tokens * topk][2] (destination rank, row)
   void* recv[kMaxRanks];
   int32_t recv_rows[kMaxRanks];
   int64_t tokens;
@@ -75,6 +76,7 @@ struct PushArgs {
   int32_t vec;                // rows and bases 16-byte aligned (copy path)
   int32_t tokens_per_tile;
 };
+static_assert(sizeof(PushArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream);

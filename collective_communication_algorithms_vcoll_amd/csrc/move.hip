@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
 }
 
 // ----------------------------------------------------------------------------
-// token-major MoE dispatch of one sending rank: each token row is read once
+// token-major MoE dispatch: each token row of each sending rank is read once
 // and written to the received-row slot of every (token, chosen expert) pair,
 // copied as it is or quantised to FP8 once for all its copies
 
@@ -276,10 +276,11 @@ constexpr int kPushUnroll = 4;     // 16-byte vectors in flight per thread (a 71
 template <bool FP8>
 __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a) {
   const int tid = threadIdx.x;
+  const int i = blockIdx.y;                                    // sending rank
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * a.tokens_per_tile;
   for (int64_t t = t0; t < t0 + a.tokens_per_tile && t < a.tokens; ++t) {
-    const char* src = static_cast<const char*>(a.table) + t * a.row_bytes;
-    const int32_t* slot = a.slots + 2 * t * a.topk;
+    const char* src = static_cast<const char*>(a.table[i]) + t * a.row_bytes;
+    const int32_t* slot = a.slots[i] + 2 * t * a.topk;
     // destination k of this token (uniform across the workgroup), or null
     auto dest = [&](int k) -> char* {
       const int j = slot[2 * k], r = slot[2 * k + 1];
@@ -399,7 +400,7 @@ hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stre
 hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream) {
   const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
   if (tiles == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(tiles));
+  const dim3 grid(static_cast<unsigned>(tiles), a.p);
   if (fp8) return launch(dispatch_push_kernel<true>, grid, a, stream);
   return launch(dispatch_push_kernel<false>, grid, a, stream);
 }

@@ -44,6 +44,7 @@ struct ReduceArgs {
   uint8_t rank[kMaxRanks];
   uint8_t merges[kMaxRanks];
 };
+static_assert(sizeof(ReduceArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // grid y = chunks: p for all-reduce and reduce-scatter, 1 for a reduce to
 // one root (q = n, r = 0, dst[0] = the root's buffer, scatter = true).

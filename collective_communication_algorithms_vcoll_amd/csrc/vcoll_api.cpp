@@ -500,13 +500,11 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
   a.p = p;
   a.vec = vec;
   a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / rb)));
-  for (int i = 0; i < p; ++i) {       // one launch per sending rank
-    a.table = token_tables[i];
-    a.slots = slots[i];
-    const vcoll_status st = from_hip(launch_dispatch_push(a, fp8 != 0, static_cast<hipStream_t>(stream)));
-    if (st != VCOLL_OK) return st;
+  for (int i = 0; i < p; ++i) {
+    a.table[i] = token_tables[i];
+    a.slots[i] = slots[i];
   }
-  return VCOLL_OK;
+  return from_hip(launch_dispatch_push(a, fp8 != 0, static_cast<hipStream_t>(stream)));
 }
 
 vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank, const int32_t* topk_ids,
