@@ -57,6 +57,8 @@ struct Fp8Args {
   int64_t out_row_bytes;      // hidden + hidden / 32
   int32_t nblocks;
   int32_t rows_per_tile;
+  int32_t vec_out;            // receive rows 16-byte aligned: 16-byte code stores
+  int32_t pad;
   A2ABlock b[kA2ABlocks];     // src = token table, src_idx = gather map, dst = first row of the block
 };
 
@@ -75,6 +77,8 @@ struct PushArgs {
   int32_t topk, p;
   int32_t vec;                // rows and bases 16-byte aligned (copy path)
   int32_t tokens_per_tile;
+  int32_t vec_out;            // FP8: receive rows 16-byte aligned (16-byte code stores)
+  int32_t pad;
 };
 static_assert(sizeof(PushArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 

@@ -201,37 +201,51 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | q;                                     // 0..8 (8 is 2^-6: exponent field 1)
 }
 
-// Quantise 8 bfloat16 values (one 16-byte vector) of a 128-element group
-// spread over 16 consecutive lanes: the group's amax by shuffles within the
-// 16 lanes (all 16 must call this together), its power-of-two scale, and the
-// 8 codes packed little-endian into c0 (elements 0-3) and c1 (4-7).
-__device__ __forceinline__ void quantise8(const u32x4 w, uint32_t& c0, uint32_t& c1, float& scale) {
-  float f[8];
+// Quantise 16 bfloat16 values (two 16-byte vectors) of a 128-element group
+// spread over 8 consecutive lanes: the group's amax by shuffles within the 8
+// lanes (all 8 must call this together), its power-of-two scale, and the 16
+// codes packed little-endian, element k in byte k of the 16-byte result.
+__device__ __forceinline__ void quantise16(const u32x4 w0, const u32x4 w1, u32x4& codes, float& scale) {
+  float f[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    f[2 * i] = __uint_as_float(w0[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w0[i] & 0xFFFF0000u);
+    f[8 + 2 * i] = __uint_as_float(w1[i] << 16);
+    f[8 + 2 * i + 1] = __uint_as_float(w1[i] & 0xFFFF0000u);
   }
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     const float v = fabsf(f[i]);
     m = v <= 3.402823466e38f ? fmaxf(m, v) : m;        // finite values only
   }
-  m = fmaxf(m, __shfl_xor(m, 8, 16));
-  m = fmaxf(m, __shfl_xor(m, 4, 16));
-  m = fmaxf(m, __shfl_xor(m, 2, 16));
-  m = fmaxf(m, __shfl_xor(m, 1, 16));
+  m = fmaxf(m, __shfl_xor(m, 4, 8));
+  m = fmaxf(m, __shfl_xor(m, 2, 8));
+  m = fmaxf(m, __shfl_xor(m, 1, 8));
   const int kx = fp8_group_exponent(m);
   const float inv = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
-  c0 = 0;
-  c1 = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c0 |= e4m3_code(f[i] * inv) << (8 * i);
-    c1 |= e4m3_code(f[4 + i] * inv) << (8 * i);
+  for (int w = 0; w < 4; ++w) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c |= e4m3_code(f[4 * w + i] * inv) << (8 * i);
+    codes[w] = c;
   }
   scale = __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+}
+
+// Store one lane's 16 codes (elements 16y .. 16y+15 of the row) and, from the
+// first lane of each group, the group's scale.
+__device__ __forceinline__ void store_codes(char* row, int64_t hidden, int64_t y, const u32x4 codes, float scale,
+                                            bool vec) {
+  if (vec) {
+    *reinterpret_cast<u32x4*>(row + y * 16) = codes;
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) reinterpret_cast<uint32_t*>(row + y * 16)[w] = codes[w];
+  }
+  if ((y & 7) == 0) *reinterpret_cast<float*>(row + hidden + (y / 8) * 4) = scale;
 }
 
 __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
@@ -253,15 +267,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
     if (sr < 0 || sr >= B.src_limit) continue;
     const char* src = B.src + sr * a.hidden * 2;
     char* dst = B.dst + static_cast<int64_t>(k) * a.out_row_bytes;
-    // nvec and kBlock are multiples of 16, so the 16 lanes of a group are
-    // always active together for the shuffles below
-    for (int64_t x = tid; x < nvec; x += kBlock) {
-      uint32_t c0, c1;
+    // hidden / 16 lane tasks of 16 elements, a multiple of 8, and kBlock a
+    // multiple of 8: the 8 lanes of a group are always active together
+    const int64_t nq = a.hidden / 16;
+    for (int64_t y = tid; y < nq; y += kBlock) {
+      u32x4 codes;
       float scale;
-      quantise8(ld16(src, x * 16), c0, c1, scale);
-      reinterpret_cast<uint32_t*>(dst + x * 8)[0] = c0;
-      reinterpret_cast<uint32_t*>(dst + x * 8)[1] = c1;
-      if ((x & 15) == 0) *reinterpret_cast<float*>(dst + a.hidden + (x / 16) * 4) = scale;
+      quantise16(ld16(src, y * 32), ld16(src, y * 32 + 16), codes, scale);
+      store_codes(dst, a.hidden, y, codes, scale, a.vec_out);
     }
   }
 }
@@ -288,28 +301,26 @@ __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a)
       return static_cast<char*>(a.recv[j]) + static_cast<int64_t>(r) * a.out_row_bytes;
     };
     if constexpr (FP8) {
-      // hidden / 8 vectors, a multiple of 16: each 16-lane group is whole
-      const int64_t nvec = a.hidden / 8;
-      for (int64_t x0 = tid; x0 < nvec; x0 += kPushUnroll * kBlock) {
+      // hidden / 16 lane tasks, a multiple of 8: each 8-lane group is whole
+      const int64_t nq = a.hidden / 16;
+      for (int64_t y0 = tid; y0 < nq; y0 += kPushUnroll / 2 * kBlock) {
         u32x4 w[kPushUnroll];
 #pragma unroll
-        for (int u = 0; u < kPushUnroll; ++u) {
-          const int64_t x = x0 + u * kBlock;
-          w[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
+        for (int u = 0; u < kPushUnroll / 2; ++u) {
+          const int64_t y = y0 + u * kBlock;
+          w[2 * u] = y < nq ? ld16(src, y * 32) : u32x4{0, 0, 0, 0};
+          w[2 * u + 1] = y < nq ? ld16(src, y * 32 + 16) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int u = 0; u < kPushUnroll; ++u) {
-          const int64_t x = x0 + u * kBlock;
-          if (x >= nvec) break;                      // uniform over each 16-lane group
-          uint32_t c0, c1;
+        for (int u = 0; u < kPushUnroll / 2; ++u) {
+          const int64_t y = y0 + u * kBlock;
+          if (y >= nq) break;                        // uniform over each 8-lane group
+          u32x4 codes;
           float scale;
-          quantise8(w[u], c0, c1, scale);
+          quantise16(w[2 * u], w[2 * u + 1], codes, scale);
           for (int k = 0; k < a.topk; ++k) {
             char* d = dest(k);
-            if (!d) continue;
-            reinterpret_cast<uint32_t*>(d + x * 8)[0] = c0;
-            reinterpret_cast<uint32_t*>(d + x * 8)[1] = c1;
-            if ((x & 15) == 0) *reinterpret_cast<float*>(d + a.hidden + (x / 16) * 4) = scale;
+            if (d) store_codes(d, a.hidden, y, codes, scale, a.vec_out);
           }
         }
       }

@@ -499,6 +499,9 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
   a.topk = topk;
   a.p = p;
   a.vec = vec;
+  a.vec_out = orb % 16 == 0;
+  for (int j = 0; j < p; ++j)
+    if (recv_rows[j] > 0) a.vec_out = a.vec_out && aligned16(recv[j]);
   a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / rb)));
   for (int i = 0; i < p; ++i) {
     a.table[i] = token_tables[i];
@@ -544,6 +547,9 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
   std::vector<int64_t> so, ro;
   block_offsets(p, splits, so, ro);
   const int32_t rows_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / (2 * hidden))));
+  bool vec_out = orb % 16 == 0;                 // 16-byte code stores when every receive row is aligned
+  for (int j = 0; j < p; ++j)
+    if (got[j] > 0) vec_out = vec_out && aligned16(recv[j]);
   std::vector<A2ABlock> blocks;
   for (int i = 0; i < p; ++i)
     for (int j = 0; j < p; ++j) {
@@ -566,6 +572,7 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
     a.hidden = hidden;
     a.out_row_bytes = orb;
     a.rows_per_tile = rows_per_tile;
+    a.vec_out = vec_out;
     int64_t tiles = 0;
     const size_t nb = std::min<size_t>(kA2ABlocks, blocks.size() - b0);
     for (size_t k = 0; k < nb; ++k) {
