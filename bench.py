@@ -346,6 +346,16 @@ def extras(vc, torch, h, args):
     _, ms_c = time_launches([comb], 10, 2)
     ok = all(torch.equal(back[i].view(T, K, H).view(torch.int16),
                          toks[i].view(torch.int16).unsqueeze(1).expand(T, K, H)) for i in range(p8))
+    # the plain block transpose on the same splits (send buffers already in
+    # destination-block order, no gather)
+    plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
+                  for i in range(p8)]
+    plain_recv = vc.vcoll_all_to_all(plain_send, splits)
+    a2a = lambda: vc.vcoll_all_to_all(plain_send, splits, recv=plain_recv)               # noqa: E731
+    _, ms_a = time_launches([a2a], 10, 2)
+    ex["moe_all_to_all_plain"] = {"GBps": rate(2 * rows * rb, ms_a), "us": round(ms_a * 1e3, 1),
+                                  "algorithmic_bytes": 2 * rows * rb}
+    del plain_send, plain_recv
     ex["moe_dispatch_fused_gather"] = {"GBps": rate(p8 * T * rb + rows * rb, ms_d), "us": round(ms_d * 1e3, 1),
                                        "algorithmic_bytes": p8 * T * rb + rows * rb,
                                        "rows_to_rank0": float(splits[:, 0].sum() / rows)}
