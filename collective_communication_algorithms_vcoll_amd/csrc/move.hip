@@ -240,12 +240,12 @@ __device__ __forceinline__ void quantise16(const u32x4 w0, const u32x4 w1, u32x4
 __device__ __forceinline__ void store_codes(char* row, int64_t hidden, int64_t y, const u32x4 codes, float scale,
                                             bool vec) {
   if (vec) {
-    *reinterpret_cast<u32x4*>(row + y * 16) = codes;
+    st16(row, y * 16, codes);
   } else {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) reinterpret_cast<uint32_t*>(row + y * 16)[w] = codes[w];
+    for (int w = 0; w < 4; ++w) __builtin_nontemporal_store(codes[w], reinterpret_cast<uint32_t*>(row + y * 16) + w);
   }
-  if ((y & 7) == 0) *reinterpret_cast<float*>(row + hidden + (y / 8) * 4) = scale;
+  if ((y & 7) == 0) __builtin_nontemporal_store(scale, reinterpret_cast<float*>(row + hidden + (y / 8) * 4));
 }
 
 __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
