@@ -502,7 +502,8 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
   a.vec_out = orb % 16 == 0;
   for (int j = 0; j < p; ++j)
     if (recv_rows[j] > 0) a.vec_out = a.vec_out && aligned16(recv[j]);
-  a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / rb)));
+  // up to 16 KiB of token rows per workgroup (one 7168-element bf16 token)
+  a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 16384 / rb)));
   for (int i = 0; i < p; ++i) {
     a.table[i] = token_tables[i];
     a.slots[i] = slots[i];
