@@ -199,13 +199,29 @@ def _span(t):
     return t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()
 
 
-def _no_overlap(a: list, b: list, what: str) -> None:
-    spans_a = [_span(t) for t in a if t is not None and t.numel() > 0]
-    spans_b = [_span(t) for t in b if t is not None and t.numel() > 0]
-    for s0, s1 in spans_a:
-        for d0, d1 in spans_b:
-            if s0 < d1 and d0 < s1:
-                raise ValueError(f"{what}: input and output buffers overlap")
+def _no_overlap(a: list, b: list, what: str, same_index_ok: bool = False) -> None:
+    """Raise if a buffer of `a` overlaps a buffer of `b`. With same_index_ok,
+    a[i] and b[i] may be the very same buffer (in place). Sorted sweep over
+    the spans, so p = 128 rank buffers cost O(p log p), not O(p^2)."""
+    import heapq
+    spans = []
+    for side, ts in ((0, a), (1, b)):
+        for i, t in enumerate(ts):
+            if t is not None and t.numel() > 0:
+                s0, s1 = _span(t)
+                spans.append((s0, s1, side, i))
+    spans.sort()
+    active = []                                   # (end, start, side, index)
+    for s0, s1, side, i in spans:
+        while active and active[0][0] <= s0:
+            heapq.heappop(active)
+        for e1, e0, oside, oi in active:
+            if oside == side:
+                continue
+            if same_index_ok and oi == i and e0 == s0 and e1 == s1:
+                continue
+            raise ValueError(f"{what}: input and output buffers overlap")
+        heapq.heappush(active, (s1, s0, side, i))
 
 
 # -----------------------------------------------------------------------------
@@ -230,10 +246,7 @@ def vcoll_allreduce(algo, send, recv=None):
     _validate(r, "vcoll_allreduce", n)
     if len(r) != len(s) or r[0].dtype != s[0].dtype or r[0].device != s[0].device:
         raise ValueError("vcoll_allreduce: send and recv must match in p, dtype and device")
-    for i, a in enumerate(s):
-        for j, b in enumerate(r):
-            if i != j or a.data_ptr() != b.data_ptr():
-                _no_overlap([a], [b], "vcoll_allreduce")
+    _no_overlap(s, r, "vcoll_allreduce", same_index_ok=True)
     _check(_lib().vcoll_allreduce(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                   _stream(s[0])), "vcoll_allreduce")
     return recv
@@ -252,10 +265,7 @@ def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
         recv = torch.empty_like(send) if isinstance(send, torch.Tensor) else [torch.empty_like(t) for t in s]
     r = _ranks(recv)
     _validate(r, "vcoll_allreduce_stepwise", n)
-    for i, a in enumerate(s):
-        for j, b in enumerate(r):
-            if i != j or a.data_ptr() != b.data_ptr():
-                _no_overlap([a], [b], "vcoll_allreduce_stepwise")
+    _no_overlap(s, r, "vcoll_allreduce_stepwise", same_index_ok=True)
     ws_ptr, ws_bytes = None, 0
     if _dtype_code(s[0]) == BF16:
         if workspace is None:
@@ -373,10 +383,7 @@ def vcoll_allreduce_hierarchical(nodes: int, local: int, send, recv=None):
         recv = torch.empty_like(send) if isinstance(send, torch.Tensor) else [torch.empty_like(t) for t in s]
     r = _ranks(recv)
     _validate(r, "vcoll_allreduce_hierarchical", n)
-    for i, a in enumerate(s):
-        for j, b in enumerate(r):
-            if i != j or a.data_ptr() != b.data_ptr():
-                _no_overlap([a], [b], "vcoll_allreduce_hierarchical")
+    _no_overlap(s, r, "vcoll_allreduce_hierarchical", same_index_ok=True)
     _check(_lib().vcoll_allreduce_hierarchical(nodes, local, n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                                _stream(s[0])), "vcoll_allreduce_hierarchical")
     return recv

@@ -240,3 +240,21 @@ def test_stepwise_validation():
     assert lib.vcoll_allreduce_stepwise(0, 0, 16, 0, P, P, None, 0, None, None) == 1
     assert lib.vcoll_allreduce_stepwise(5, 4, 16, 0, P, P, None, 0, None, None) == 1
     assert lib.vcoll_allreduce_stepwise(0, 4, 0, 0, None, None, None, 0, None, None) == 0
+
+
+def test_overlap_check_allows_in_place_and_rejects_cross_overlap():
+    import torch
+    t = torch.zeros(4, 16)
+    other = torch.zeros(4, 16)
+    rows = [t[r] for r in range(4)]
+    vc._no_overlap(rows, rows, "x", same_index_ok=True)                 # in place
+    vc._no_overlap(rows, [other[r] for r in range(4)], "x")              # disjoint
+    with pytest.raises(ValueError):
+        vc._no_overlap(rows, [t[1], t[0], t[2], t[3]], "x", same_index_ok=True)   # rank 0 writes rank 1's input
+    with pytest.raises(ValueError):
+        vc._no_overlap(rows, rows, "x")                                   # in place not allowed here
+    flat = torch.zeros(64)
+    with pytest.raises(ValueError):
+        vc._no_overlap([flat[0:16]], [flat[8:24]], "x")                   # partial overlap
+    big = [torch.zeros(8) for _ in range(128)]
+    vc._no_overlap(big[:64], big[64:], "x")                               # many disjoint buffers
