@@ -279,3 +279,15 @@ def test_windowed_oracle_equals_full_run(dtype):
         for r in range(12):
             assert part[r].tobytes() == full[r][lo:hi].tobytes()
         assert led_w.sorted() == led.sorted()
+
+
+@pytest.mark.parametrize("nodes,local", [(2, 8), (4, 4), (3, 5), (8, 2)])
+def test_error_bound_against_float64(nodes, local):
+    """p - 1 float32 adds per element: |err| <= 2 (p-1) 2^-24 sum|x|, the
+    bound every all-reduce order meets."""
+    p, n = nodes * local, 4096
+    x = [np.random.default_rng([nodes, local, r]).normal(size=n).astype(np.float32) for r in range(p)]
+    out, _ = oracle.allreduce_hierarchical(x, nodes, local)
+    xs = np.stack(x).astype(np.float64)
+    bound = 2 * (p - 1) * 2.0 ** -24 * np.abs(xs).sum(axis=0)
+    assert np.all(np.abs(out[0].astype(np.float64) - xs.sum(axis=0)) <= bound)

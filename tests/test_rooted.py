@@ -260,3 +260,14 @@ def test_library_rejects_bad_rooted_calls():
         vc.vcoll_ledger("broadcast", "tree", 4, 10)                     # rooted ops have their own ledger
     with pytest.raises(vc.VcollError):
         vc.vcoll_model_chain_optimum(2, 1e6, 1e-6, 1e9)
+
+
+@pytest.mark.parametrize("p", [2, 5, 16, 72])
+def test_reduce_error_bound_against_float64(p):
+    n = 2048
+    x = [np.random.default_rng([p, r]).normal(size=n).astype(np.float32) for r in range(p)]
+    xs = np.stack(x).astype(np.float64)
+    bound = 2 * (p - 1) * 2.0 ** -24 * np.abs(xs).sum(axis=0)
+    for root in (0, p - 1):
+        out, _ = rooted.reduce(x, root)
+        assert np.all(np.abs(out.astype(np.float64) - xs.sum(axis=0)) <= bound)
