@@ -258,3 +258,46 @@ def test_overlap_check_allows_in_place_and_rejects_cross_overlap():
         vc._no_overlap([flat[0:16]], [flat[8:24]], "x")                   # partial overlap
     big = [torch.zeros(8) for _ in range(128)]
     vc._no_overlap(big[:64], big[64:], "x")                               # many disjoint buffers
+
+
+def test_widened_entry_points_validate_before_launching():
+    """Every error below is returned before anything is enqueued (no GPU here)."""
+    lib = _lib()
+    P8 = _ptrs(8)
+    one = ctypes.c_void_p(0x1000)
+    # broadcast: root out of range, bad dtype, missing receive buffer
+    assert lib.vcoll_broadcast(8, 64, 0, 8, one, P8, None) == 1
+    assert lib.vcoll_broadcast(8, 64, 5, 0, one, P8, None) == 1
+    holes = _ptrs(8)
+    holes[3] = None
+    assert lib.vcoll_broadcast(8, 64, 0, 0, one, holes, None) == 1
+    assert lib.vcoll_broadcast(8, 0, 0, 0, None, None, None) == 0                # n = 0: no-op
+    # reduce: only the binomial tree; root range; NULL output
+    assert lib.vcoll_reduce(0, 8, 64, 0, 0, P8, one, None) == 2
+    assert lib.vcoll_reduce(3, 8, 64, 0, 8, P8, one, None) == 1
+    assert lib.vcoll_reduce(3, 8, 64, 0, 0, P8, None, None) == 1
+    assert lib.vcoll_reduce(99, 8, 64, 0, 0, P8, one, None) == 1
+    # hierarchical: shapes
+    assert lib.vcoll_allreduce_hierarchical(0, 8, 64, 0, P8, P8, None) == 1
+    assert lib.vcoll_allreduce_hierarchical(16, 16, 64, 0, _ptrs(256), _ptrs(256), None) == 1
+    assert lib.vcoll_allreduce_hierarchical(2, 4, 64, 2, P8, P8, None) == 1     # U8 is for the all-to-all only
+    # the all-to-all takes raw bytes, the reductions do not
+    assert lib.vcoll_allreduce(0, 8, 64, 2, P8, P8, None) == 1
+    # FP8 dispatch: hidden must be a positive multiple of 128; token tables aligned
+    sp = (ctypes.c_int64 * 4)(1, 0, 0, 1)
+    rows = (ctypes.c_int64 * 2)(4, 4)
+    idx = (ctypes.c_void_p * 2)(0x3000, 0x3000)
+    assert lib.vcoll_moe_dispatch_fp8(2, 100, sp, _ptrs(2), rows, idx, _ptrs(2), None) == 1
+    unaligned = (ctypes.c_void_p * 2)(0x1008, 0x2000)
+    assert lib.vcoll_moe_dispatch_fp8(2, 128, sp, unaligned, rows, idx, _ptrs(2), None) == 1
+    # token-major dispatch: FP8 needs bf16 and hidden % 128 == 0
+    rr = (ctypes.c_int64 * 2)(1, 1)
+    assert lib.vcoll_moe_dispatch(2, 4, 1, 100, 1, 1, _ptrs(2), idx, _ptrs(2), rr, None) == 1
+    assert lib.vcoll_moe_dispatch(2, 4, 1, 128, 0, 1, _ptrs(2), idx, _ptrs(2), rr, None) == 1
+    bad_rows = (ctypes.c_int64 * 2)(-1, 1)
+    assert lib.vcoll_moe_dispatch(2, 4, 1, 128, 1, 0, _ptrs(2), idx, _ptrs(2), bad_rows, None) == 1
+    # models
+    t = ctypes.c_double()
+    assert lib.vcoll_model_chain_optimum(2, 1e6, 1e-6, 1e9, ctypes.byref(t), ctypes.byref(t)) == 1
+    assert lib.vcoll_model_broadcast_formula(6, 8, 1e6, 0, 1e-6, 1e9, ctypes.byref(t)) == 1   # chain, 0 blocks
+    assert lib.vcoll_model_clock(None, 3, 8, 8, 1e-6, 1e9, 1e-6, 1e9, ctypes.byref(t)) == 1
