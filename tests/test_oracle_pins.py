@@ -461,3 +461,24 @@ def test_moe_routing_draws_follow_the_zipf_weights():
     # top-k draws are distinct and sorted
     ids8 = workloads.moe_topk(1, 1000, E, 8)
     assert np.all(np.diff(ids8, axis=1) > 0)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("p", [2, 3, 5, 8, 12, 16])
+def test_every_rank_holds_the_same_bits(algo, p):
+    """An all-reduce leaves one value per element, the same bits on every
+    rank ([NCC] 4.1); a schedule that sums in a rank-dependent order (for
+    example a dissemination pattern) fails this on random inputs."""
+    x = [np.random.default_rng([p, r, 5]).normal(size=3 * p + 1).astype(np.float32) for r in range(p)]
+    out, _ = oracle.allreduce(x, algo)
+    assert all(v.tobytes() == out[0].tobytes() for v in out)
+
+
+@pytest.mark.parametrize("p", [2, 4, 8, 16])
+def test_recursive_doubling_exchanges_with_xor_partners(p):
+    """[NCC] 5.2: in step k, ranks i and i xor 2^k exchange their vectors."""
+    _, led = oracle.allreduce([np.zeros(p, np.float32)] * p, "rd")
+    pairs = {(m.step, m.src, m.dst) for m in led.msgs}
+    assert len(pairs) == p * (p.bit_length() - 1)
+    for s, a, b in pairs:
+        assert b == a ^ (1 << s) and (s, b, a) in pairs
