@@ -165,3 +165,132 @@ def test_planted_mistake_is_caught(tmp_path, idx):
     o = load_copy(tmp_path, f"oracle_mutant_{idx}", (fname, old, new), FOLLOW_UPS.get(name))
     fails = battery(o)
     assert fails, f"planted mistake not caught: {name}"
+
+
+# ---------------------------------------------------------------- the widened rows' oracles
+
+WIDE_MUTANTS = [
+    ("hierarchical cross-node ring runs backwards", "collectives.py",
+     "    same = [[g * L + l for g in range(N)] for l in range(L)]",
+     "    same = [[g * L + l for g in reversed(range(N))] for l in range(L)]"),
+    ("hierarchical in-node reduce-scatter owner shifted", "collectives.py",
+     "        step = together(step, [(grp, cpieces, ADD, 1) for grp in groups])",
+     "        step = together(step, [(grp, cpieces, ADD, 2) for grp in groups])"),
+    ("reduce relabels ranks the other way round", "rooted.py",
+     "        cl.step(step, [Send((v + root) % p, (v - m + root) % p, 0, 0, n, ADD)",
+     "        cl.step(step, [Send((root - v) % p, (root - v + m) % p, 0, 0, n, ADD)"),
+    ("binomial broadcast with masks ascending", "rooted.py",
+     "        for step, m in enumerate(reversed(_masks(p))):",
+     "        for step, m in enumerate(_masks(p)):"),
+    ("E4M3 rounds half up", "fp8.py",
+     "    q = np.rint(np.ldexp(a[nor], -(e[nor] - 3))).astype(np.int64)",
+     "    q = np.floor(np.ldexp(a[nor], -(e[nor] - 3)) + 0.5).astype(np.int64)"),
+    ("FP8 scale aims at 480 instead of 448", "fp8.py", "MAX_E4M3 = 448.0", "MAX_E4M3 = 480.0"),
+    ("deduplicated blocks in descending token order", "moe.py",
+     "                           if int(ids[t, k]) // experts_per_rank == j})",
+     "                           if int(ids[t, k]) // experts_per_rank == j}, reverse=True)"),
+]
+
+
+def wide_battery(o) -> list:
+    from oracle import fp8 as _unused  # noqa: F401  (the real module stays importable)
+    fails = []
+
+    def check(name, fn):
+        try:
+            if not fn():
+                fails.append(name)
+        except Exception:                        # noqa: BLE001
+            fails.append(name)
+
+    big = 2.0 ** 24
+    # hierarchical: the hand-worked probes of the inner and the outer chain
+    check("hierarchical inner probe", lambda: o.allreduce_hierarchical(
+        [np.full(6, v, np.float32) for v in (big, 1.0, -big, 0.0, 0.0, 0.0)], 2, 3)[0][0].tolist() == [1, 1, 1, 1, 0, 0])
+    check("hierarchical outer probe", lambda: o.allreduce_hierarchical(
+        [np.full(6, v, np.float32) for v in (big, 0.0, 1.0, 0.0, -big, 0.0)], 3, 2)[0][0].tolist() == [1, 1, 0, 1, 1, 0])
+
+    def hier_ledger_cross_node_bytes():
+        _, led = o.allreduce_hierarchical([np.zeros(1, np.float32)] * 16, 2, 8, n=16 * 64, lo=0)
+        cross = [m for m in led.msgs if m.src // 8 != m.dst // 8]
+        return sum(m.bytes for m in cross) == 16 * 2 * (128 // 2) * 4 and all(m.dst == m.src ^ 8 for m in cross)
+    check("hierarchical cross-node ring", hier_ledger_cross_node_bytes)
+    # rooted: the reduce probe by root, broadcast delivery and causality
+    x3 = [np.full(3, v, np.float32) for v in (big, 1.0, -big)]
+    check("reduce probe", lambda: [o.rooted.reduce(x3, r)[0].tolist()[0] for r in range(3)] == [0.0, 1.0, 1.0])
+
+    def broadcast_causal():
+        for p in (5, 8):
+            for root in (0, 3):
+                led = o.rooted.broadcast(np.zeros(9, np.float32), p, "tree", root)[1]
+                have = {root}
+                for s in range(led.n_steps):
+                    msgs = [m for m in led.msgs if m.step == s]
+                    if any(m.src not in have for m in msgs):
+                        return False
+                    have |= {m.dst for m in msgs}
+                if have != set(range(p)) or led.n_steps != (p - 1).bit_length():
+                    return False
+        return True
+    check("broadcast causality", broadcast_causal)
+
+    # FP8: codes against torch's float8_e4m3fn, and the scale's binade
+    def e4m3_vs_torch():
+        import torch
+        v = np.random.default_rng(1).uniform(-448, 448, 50_000).astype(np.float32)
+        v = np.concatenate([v, np.float32([1.0625, 1.1875, 2 ** -10, 1.5 * 2 ** -10])])
+        return np.array_equal(o.fp8.e4m3_encode(v),
+                              torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    check("E4M3 vs torch", e4m3_vs_torch)
+
+    def scale_binade():
+        x = np.random.default_rng(2).normal(size=(4, 256)).astype(np.float32)
+        x[0, 7] = 460 * 2.0 ** -7                 # amax between 448 and 480 times a power of two
+        b = o.fp8.quantize_rows(x)
+        s = np.ascontiguousarray(b[:, 256:]).view(np.float32)
+        amax = np.abs(x).reshape(4, 2, 128).max(axis=2)
+        return bool(np.all(amax / s <= 448) and np.all(amax / s > 224))
+    check("FP8 scale", scale_binade)
+
+    # deduplicated dispatch: expansion equals the plain dispatch; blocks by token
+    def dedup():
+        topk = [np.stack([np.sort(np.random.default_rng([7, i, t]).choice(16, 3, replace=False))
+                          for t in range(20)]).astype(np.int32) for i in range(4)]
+        toks = [workloads.tagged_rows(np.zeros((20, 8), np.uint16), i, np.arange(20)) for i in range(4)]
+        splits, src, _ = o.moe_plan(topk, 4)
+        plain, _, _ = o.moe_dispatch(toks, splits, src)
+        expanded, _, _ = o.moe.dispatch_dedup(toks, topk, 4)
+        su, src_u, _ = o.moe.plan_dedup(topk, 4)
+        ordered = all(np.all(np.diff(src_u[i][int(su[i, :j].sum()):int(su[i, :j + 1].sum())]) > 0)
+                      for i in range(4) for j in range(4))
+        return ordered and all(np.array_equal(a, b) for a, b in zip(plain, expanded))
+    check("dedup dispatch", dedup)
+    return fails
+
+
+def load_wide(tmp_path, name, patch=None):
+    o = load_copy(tmp_path, name, patch)
+    for sub in ("rooted", "fp8", "moe"):
+        setattr(o, sub, importlib.import_module(f"{name}.{sub}"))
+    return o
+
+
+@pytest.mark.timeout(120)
+def test_unmodified_widened_oracles_pass_their_battery(tmp_path):
+    sys.path.insert(0, str(tmp_path))
+    try:
+        assert wide_battery(load_wide(tmp_path, "oracle_wide_copy")) == []
+    finally:
+        sys.path.remove(str(tmp_path))
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("idx", range(len(WIDE_MUTANTS)), ids=[m[0] for m in WIDE_MUTANTS])
+def test_planted_mistake_in_a_widened_oracle_is_caught(tmp_path, idx):
+    name, fname, old, new = WIDE_MUTANTS[idx]
+    sys.path.insert(0, str(tmp_path))
+    try:
+        o = load_wide(tmp_path, f"oracle_wide_mutant_{idx}", (fname, old, new))
+        assert wide_battery(o), f"planted mistake not caught: {name}"
+    finally:
+        sys.path.remove(str(tmp_path))
