@@ -171,36 +171,6 @@ __device__ __forceinline__ int fp8_group_exponent(float amax) {
   return k < -126 ? -126 : (k > 126 ? 126 : k);
 }
 
-// |y| <= 448 (or non-finite) -> E4M3 code, round to nearest, ties to even,
-// done on the float32 bit pattern.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t b = __float_as_uint(y);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t u = b & 0x7FFFFFFFu;
-  if (u >= 0x7F800000u) return 0x7Fu;                 // infinity or NaN
-  const int E = static_cast<int>(u >> 23);
-  if (E == 0) return sign;                             // zero, or a float32 subnormal (< 2^-126)
-  const int e = E - 127;
-  const uint32_t mant = (u & 0x7FFFFFu) | 0x800000u;   // 1.f times 2^23
-  // normal results keep 1 + 3 fraction bits; below 2^-6 the grid is 2^-9:
-  // y * 2^9 = mant * 2^(e - 14)
-  const int shift = e >= -6 ? 20 : 14 - e;
-  if (shift > 24) return sign;                         // below 2^-10: rounds to zero
-  uint32_t q = mant >> shift;
-  const uint32_t rem = mant & ((1u << shift) - 1u);
-  const uint32_t half = 1u << (shift - 1);
-  if (rem > half || (rem == half && (q & 1u))) ++q;
-  if (e >= -6) {
-    int ee = e;
-    if (q == 16u) {
-      q = 8u;
-      ++ee;
-    }
-    return sign | (static_cast<uint32_t>(ee + 7) << 3) | (q - 8u);
-  }
-  return sign | q;                                     // 0..8 (8 is 2^-6: exponent field 1)
-}
-
 // Quantise 16 bfloat16 values (two 16-byte vectors) of a 128-element group
 // spread over 8 consecutive lanes: the group's amax by shuffles within the 8
 // lanes (all 8 must call this together), its power-of-two scale, and the 16
@@ -225,12 +195,25 @@ __device__ __forceinline__ void quantise16(const u32x4 w0, const u32x4 w1, u32x4
   m = fmaxf(m, __shfl_xor(m, 1, 8));
   const int kx = fp8_group_exponent(m);
   const float inv = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
+  // Every scaled value is exact and |x * 2^-k| <= 448, so gfx950's fp32 ->
+  // E4M3 pack (OCP format, round to nearest even under the default mode)
+  // gives the code directly. It writes NaN with the input's sign (0xFF for
+  // a negative NaN or -inf), so lanes holding a non-finite value rewrite
+  // those bytes as 0x7F.
+  bool nonfinite = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nonfinite |= !(fabsf(f[i]) <= 3.402823466e38f);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t c = 0;
+    const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w] * inv, f[4 * w + 1] * inv, 0, false);
+    codes[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w + 2] * inv, f[4 * w + 3] * inv, lo, true);
+  }
+  if (nonfinite) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c |= e4m3_code(f[4 * w + i] * inv) << (8 * i);
-    codes[w] = c;
+    for (int i = 0; i < 16; ++i) {
+      if (!(fabsf(f[i]) <= 3.402823466e38f))
+        codes[i / 4] = (codes[i / 4] & ~(0xFFu << (8 * (i % 4)))) | (0x7Fu << (8 * (i % 4)));
+    }
   }
   scale = __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
 }

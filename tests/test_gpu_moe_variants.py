@@ -79,12 +79,52 @@ def test_fp8_dispatch_special_values(vc):
     rows[3] = np.ldexp(rng.normal(0, 1, H), 100)
     rows[4] = np.ldexp(rng.normal(0, 1, H), -100)
     rows[5, :128] = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -10, 1.5 * 2.0 ** -10, 448.0] + [0.0] * 122)
-    rows[6, :4] = [np.nan, np.inf, -np.inf, 1.0]
+    rows[6, :5] = [np.nan, np.inf, -np.inf, 1.0, -np.nan]
     rows[7] = rng.uniform(-1, 1, H)
     bf = oracle.f32_to_bf16(rows)
     toks = [bf, bf[::-1].copy()]
     topk = [np.array([[0], [1], [0], [1], [0], [1], [0], [1]], np.int32)] * p
     check_fp8(vc, toks, topk, 1, "special values")
+
+
+def every_bf16_pattern_rows():
+    """bfloat16 rows of 128 (one scale group each) that hold every bit
+    pattern: (a) each in-domain pattern (finite, |x| <= 448) in a group led
+    by 448, so the group's scale is 2^0 and the encoder sees the pattern
+    itself; (b) every non-finite pattern, also behind 448; (c) all 65536
+    patterns in plain order, 128 consecutive patterns being one binade of
+    one sign, so every group exponent from -126 to 126 and the clamps
+    occur."""
+    pats = np.arange(65536, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    anchor = np.uint16(0x43E0)                           # 448.0
+    assert (np.uint32(anchor) << 16).view(np.float32) == 448.0
+    rows = []
+    for sel in (np.isfinite(vals) & (np.abs(vals) <= 448.0), ~np.isfinite(vals)):
+        body = pats[sel].astype(np.uint16)
+        pad = (-len(body)) % 127
+        body = np.concatenate([body, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        rows.append(np.concatenate([np.full((body.shape[0], 1), anchor, np.uint16), body], axis=1))
+    rows.append(pats.astype(np.uint16).reshape(-1, 128))
+    return np.concatenate(rows)
+
+
+def test_fp8_dispatch_every_bf16_pattern(vc):
+    """Both FP8 dispatch forms (row-major gather and token-major push)
+    against the oracle's quantiser on every bfloat16 bit pattern."""
+    import torch
+    rows = every_bf16_pattern_rows()
+    T, H, p = rows.shape[0], 128, 2
+    toks = [rows, rows[::-1].copy()]
+    topk = [(np.arange(T) % 2).astype(np.int32).reshape(T, 1)] * p
+    check_fp8(vc, toks, topk, 1, "every bf16 pattern")
+    splits, src, dst = vc.vcoll_moe_plan(np.stack(topk), 1)
+    got = vc.vcoll_moe_dispatch([to_gpu_bf16(t) for t in toks], slots_gpu(vc, splits, dst, 1), splits.sum(axis=0),
+                                1, fp8=True)
+    sync()
+    want, _ = moe.dispatch_fp8(toks, splits, list(src))
+    for j in range(p):
+        assert np.array_equal(got[j].cpu().numpy(), want[j]), f"token-major, rank {j}"
 
 
 def test_fp8_dispatch_skips_out_of_range_rows(vc):
