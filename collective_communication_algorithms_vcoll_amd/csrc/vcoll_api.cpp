@@ -39,6 +39,17 @@ bool valid_algo(int a) { return a >= VCOLL_RING && a <= VCOLL_BINARY_TREE; }
 
 bool valid_p(int p) { return p >= 1 && p <= kMaxRanks; }
 
+// Element counts up to 2^48: far beyond any buffer, and small enough that
+// every byte offset (count x 4 bytes x up to 128 ranks) fits in int64.
+constexpr int64_t kMaxCount = int64_t(1) << 48;
+
+bool valid_count(int64_t n) { return n >= 0 && n <= kMaxCount; }
+
+// A buffer of `rows` rows of `row_bytes` bytes stays within 2^56 bytes.
+bool fits(int64_t rows, int64_t row_bytes) {
+  return row_bytes <= 0 || rows <= (int64_t(1) << 56) / row_bytes;
+}
+
 bool all_set(int p, const void* const* ptrs) {
   if (!ptrs) return false;
   for (int r = 0; r < p; ++r)
@@ -54,7 +65,7 @@ bool all_aligned(int p, const void* const* ptrs) {
 
 vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                            const void* const* send, void* const* recv, void* stream, bool scatter) {
-  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
   const vcoll_status combo =
       check_combination(scatter ? VCOLL_OP_REDUCE_SCATTER : VCOLL_OP_ALLREDUCE, algo, p);
   if (combo != VCOLL_OK) return combo;
@@ -139,7 +150,7 @@ const char* vcoll_status_str(vcoll_status status) {
 }
 
 vcoll_status vcoll_chunk(int p, int64_t n, int c, int64_t* off, int64_t* count) {
-  if (!valid_p(p) || n < 0 || c < 0 || c >= p || !off || !count) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(n) || c < 0 || c >= p || !off || !count) return VCOLL_ERR_INVALID_ARG;
   const Chunks ch(n, p);
   *off = ch.off(c);
   *count = ch.count(c);
@@ -158,7 +169,7 @@ vcoll_status vcoll_reduce_scatter(vcoll_algo algo, int p, int64_t n, vcoll_dtype
 
 vcoll_status vcoll_all_gather(vcoll_algo algo, int p, int64_t m, vcoll_dtype dtype,
                               const void* const* send, void* const* recv, void* stream) {
-  if (!valid_p(p) || m < 0 || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(m) || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
   const vcoll_status combo = check_combination(VCOLL_OP_ALL_GATHER, algo, p);
   if (combo != VCOLL_OK) return combo;
   if (m == 0) return VCOLL_OK;
@@ -181,7 +192,7 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
                               const int32_t* const* src_rows, const int64_t* src_table_rows,
                               const int32_t* const* dst_rows, const int64_t* dst_table_rows,
                               void* stream) {
-  if (!valid_p(p) || row_elems < 0 || !valid_a2a_dtype(dtype) || !splits) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(row_elems) || !valid_a2a_dtype(dtype) || !splits) return VCOLL_ERR_INVALID_ARG;
   const int64_t rb = row_elems * elem_bytes(dtype);
   std::vector<int64_t> sent(p, 0), got(p, 0);
   for (int i = 0; i < p; ++i)
@@ -195,11 +206,14 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
   auto gathers = [&](int i) { return src_rows && src_rows[i]; };
   auto scatters = [&](int j) { return dst_rows && dst_rows[j]; };
   for (int i = 0; i < p; ++i) {
+    if (!fits(sent[i], rb) || !fits(got[i], rb)) return VCOLL_ERR_INVALID_ARG;
     if (sent[i] > 0 && rb > 0 && (!send || !send[i])) return VCOLL_ERR_INVALID_ARG;
     if (got[i] > 0 && rb > 0 && (!recv || !recv[i])) return VCOLL_ERR_INVALID_ARG;
-    if (gathers(i) && (!src_table_rows || src_table_rows[i] < 0 || src_table_rows[i] > INT32_MAX))
+    if (gathers(i) && (!src_table_rows || src_table_rows[i] < 0 || src_table_rows[i] > INT32_MAX ||
+                       !fits(src_table_rows[i], rb)))
       return VCOLL_ERR_INVALID_ARG;
-    if (scatters(i) && (!dst_table_rows || dst_table_rows[i] < 0 || dst_table_rows[i] > INT32_MAX))
+    if (scatters(i) && (!dst_table_rows || dst_table_rows[i] < 0 || dst_table_rows[i] > INT32_MAX ||
+                        !fits(dst_table_rows[i], rb)))
       return VCOLL_ERR_INVALID_ARG;
   }
   if (rb == 0) return VCOLL_OK;
@@ -257,11 +271,11 @@ vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_
   if (op < VCOLL_OP_ALLREDUCE || op > VCOLL_OP_ALL_TO_ALL) return VCOLL_ERR_INVALID_ARG;
   if (!(op == VCOLL_OP_ALL_TO_ALL ? valid_a2a_dtype(dtype) : valid_dtype(dtype))) return VCOLL_ERR_INVALID_ARG;
   if (op == VCOLL_OP_ALL_TO_ALL) {
-    if (!splits || row_elems < 0) return VCOLL_ERR_INVALID_ARG;
+    if (!splits || !valid_count(row_elems)) return VCOLL_ERR_INVALID_ARG;
     for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
       if (splits[k] < 0) return VCOLL_ERR_INVALID_ARG;
   } else {
-    if (n < 0 || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+    if (!valid_count(n) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
     const vcoll_status combo = check_combination(op, algo, p);
     if (combo != VCOLL_OK) return combo;
   }
@@ -274,7 +288,7 @@ vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_
 vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
                                  int64_t blocks, vcoll_msg* msgs, int64_t cap, int64_t* n_msgs,
                                  int64_t* sent_bytes, int64_t* recv_bytes, int32_t* n_steps) {
-  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || !n_msgs || root < 0 || root >= p)
+  if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || !n_msgs || root < 0 || root >= p)
     return VCOLL_ERR_INVALID_ARG;
   if (op != VCOLL_OP_BROADCAST && op != VCOLL_OP_REDUCE) return VCOLL_ERR_INVALID_ARG;
   std::vector<vcoll_msg> out;
@@ -286,7 +300,7 @@ vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n,
 
 vcoll_status vcoll_broadcast(int p, int64_t n, vcoll_dtype dtype, int root, const void* send, void* const* recv,
                              void* stream) {
-  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
   if (n == 0) return VCOLL_OK;
   if (!send || !recv) return VCOLL_ERR_INVALID_ARG;
   BcastArgs a;
@@ -305,7 +319,7 @@ vcoll_status vcoll_broadcast(int p, int64_t n, vcoll_dtype dtype, int root, cons
 
 vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root,
                           const void* const* send, void* recv, void* stream) {
-  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
   if (algo != VCOLL_BINARY_TREE)
     return (algo >= VCOLL_RING && algo <= VCOLL_PIPELINED_CHAIN) ? VCOLL_ERR_UNSUPPORTED : VCOLL_ERR_INVALID_ARG;
   if (n == 0) return VCOLL_OK;
@@ -335,7 +349,7 @@ vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, 
 vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_rank,
                             const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
                             int32_t* dst_rows) {
-  if (!valid_p(p) || tokens < 0 || topk < 1 || experts_per_rank < 1) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(tokens) || topk < 1 || experts_per_rank < 1) return VCOLL_ERR_INVALID_ARG;
   if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
   if (!splits || (tokens > 0 && (!topk_ids || !src_rows || !dst_rows))) return VCOLL_ERR_INVALID_ARG;
   return moe_plan(p, tokens, topk, experts_per_rank, topk_ids, splits, src_rows, dst_rows);
@@ -370,7 +384,7 @@ vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_d
                                       const void* const* send, void* const* recv, void* workspace,
                                       int64_t workspace_bytes, int32_t* n_launches, void* stream) {
   if (n_launches) *n_launches = 0;
-  if (!valid_p(p) || n < 0 || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
+  if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
   if (n == 0) return VCOLL_OK;
   if (!all_set(p, send) || !all_set(p, const_cast<const void* const*>(recv))) return VCOLL_ERR_INVALID_ARG;
   const bool bf16 = dtype == VCOLL_BF16;
@@ -421,7 +435,7 @@ vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_d
 
 vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype,
                                           const void* const* send, void* const* recv, void* stream) {
-  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || n < 0 || !valid_dtype(dtype))
+  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || !valid_count(n) || !valid_dtype(dtype))
     return VCOLL_ERR_INVALID_ARG;
   if (n == 0) return VCOLL_OK;
   const int p = nodes * local;
@@ -444,7 +458,7 @@ vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll
 vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype, vcoll_msg* msgs,
                                        int64_t cap, int64_t* n_msgs, int64_t* sent_bytes,
                                        int64_t* recv_bytes, int32_t* n_steps) {
-  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || n < 0 || !valid_dtype(dtype) || !n_msgs)
+  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || !valid_count(n) || !valid_dtype(dtype) || !n_msgs)
     return VCOLL_ERR_INVALID_ARG;
   const int p = nodes * local;
   std::vector<vcoll_msg> out;
@@ -455,7 +469,7 @@ vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dt
 
 vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
                              int32_t* slots) {
-  if (!valid_p(p) || tokens < 0 || topk < 1 || !splits || (tokens > 0 && (!dst_rows || !slots)))
+  if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !splits || (tokens > 0 && (!dst_rows || !slots)))
     return VCOLL_ERR_INVALID_ARG;
   if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
   for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
@@ -466,7 +480,7 @@ vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* spl
 vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden, vcoll_dtype dtype, int fp8,
                                 const void* const* token_tables, const int32_t* const* slots,
                                 void* const* recv, const int64_t* recv_rows, void* stream) {
-  if (!valid_p(p) || tokens < 0 || topk < 1 || hidden < 0 || !valid_dtype(dtype) || !recv_rows)
+  if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !valid_count(hidden) || !valid_dtype(dtype) || !recv_rows)
     return VCOLL_ERR_INVALID_ARG;
   if (fp8 && (dtype != VCOLL_BF16 || hidden % 128 != 0)) return VCOLL_ERR_INVALID_ARG;
   if (tokens * topk > INT32_MAX || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
@@ -474,9 +488,10 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
   if (!token_tables || !slots || !recv) return VCOLL_ERR_INVALID_ARG;
   const int64_t rb = hidden * elem_bytes(dtype);
   const int64_t orb = fp8 ? hidden + hidden / 32 : rb;
+  if (!fits(tokens, rb)) return VCOLL_ERR_INVALID_ARG;
   bool vec = rb % 16 == 0;
   for (int j = 0; j < p; ++j) {
-    if (recv_rows[j] < 0 || recv_rows[j] > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+    if (recv_rows[j] < 0 || recv_rows[j] > INT32_MAX || !fits(recv_rows[j], orb)) return VCOLL_ERR_INVALID_ARG;
     if (recv_rows[j] > 0 && !recv[j]) return VCOLL_ERR_INVALID_ARG;
     if (recv_rows[j] > 0 && fp8 && (reinterpret_cast<uintptr_t>(recv[j]) & 3u) != 0) return VCOLL_ERR_INVALID_ARG;
     if (recv_rows[j] > 0) vec = vec && aligned16(recv[j]);
@@ -514,7 +529,7 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
 vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank, const int32_t* topk_ids,
                                   int64_t* splits_unique, int32_t* src_unique, int32_t* expand,
                                   int64_t* expand_count) {
-  if (!valid_p(p) || tokens < 0 || topk < 1 || experts_per_rank < 1 || !topk_ids || !splits_unique ||
+  if (!valid_p(p) || !valid_count(tokens) || topk < 1 || experts_per_rank < 1 || !topk_ids || !splits_unique ||
       !src_unique || !expand || !expand_count)
     return VCOLL_ERR_INVALID_ARG;
   if (tokens * topk > INT32_MAX || static_cast<int64_t>(p) * tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
@@ -525,7 +540,8 @@ vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_p
 vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits, const void* const* tokens,
                                     const int64_t* token_rows, const int32_t* const* src_rows,
                                     void* const* recv, void* stream) {
-  if (!valid_p(p) || hidden <= 0 || hidden % 128 != 0 || !splits || !token_rows || !src_rows)
+  if (!valid_p(p) || hidden <= 0 || hidden % 128 != 0 || hidden > INT32_MAX / 2 || !splits || !token_rows ||
+      !src_rows)
     return VCOLL_ERR_INVALID_ARG;
   std::vector<int64_t> sent(p, 0), got(p, 0);
   for (int i = 0; i < p; ++i)
@@ -543,7 +559,6 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
     if (got[i] > 0 && (!recv || !recv[i] || (reinterpret_cast<uintptr_t>(recv[i]) & 3u) != 0))
       return VCOLL_ERR_INVALID_ARG;
   }
-  if (hidden * 2 > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
   const int64_t orb = hidden + hidden / 32;
   std::vector<int64_t> so, ro;
   block_offsets(p, splits, so, ro);

@@ -18,8 +18,14 @@
  *
  * Common conventions
  *   - Every function returns a vcoll_status; nothing throws across the ABI.
- *   - All arguments are validated before anything is enqueued: an error
- *     return means no work was launched.
+ *   - All arguments are validated before anything is enqueued: a return
+ *     other than VCOLL_ERR_HIP means no work was launched. (Calls that
+ *     enqueue several launches -- the stepwise all-reduce, all-to-alls and
+ *     FP8 dispatches of more than 64 non-empty blocks -- may have enqueued
+ *     earlier launches when a later one returns VCOLL_ERR_HIP.)
+ *   - Sizes: element counts (n, m, row_elems, tokens, hidden) above 2^48,
+ *     and any buffer the arguments describe above 2^56 bytes, are refused
+ *     with VCOLL_ERR_INVALID_ARG, so every byte offset fits in int64.
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
  *     stream) and the call returns before it completes. The library never
  *     synchronizes, never allocates device memory, and keeps no state

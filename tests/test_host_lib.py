@@ -301,3 +301,35 @@ def test_widened_entry_points_validate_before_launching():
     assert lib.vcoll_model_chain_optimum(2, 1e6, 1e-6, 1e9, ctypes.byref(t), ctypes.byref(t)) == 1
     assert lib.vcoll_model_broadcast_formula(6, 8, 1e6, 0, 1e-6, 1e9, ctypes.byref(t)) == 1   # chain, 0 blocks
     assert lib.vcoll_model_clock(None, 3, 8, 8, 1e-6, 1e9, 1e-6, 1e9, ctypes.byref(t)) == 1
+
+
+def test_oversized_counts_and_buffers_are_refused():
+    """Element counts above 2^48 and buffers above 2^56 bytes are refused
+    before anything is enqueued, so no byte offset can overflow int64."""
+    lib = _lib()
+    P8 = _ptrs(8)
+    one = ctypes.c_void_p(0x1000)
+    big = (1 << 48) + 1
+    assert lib.vcoll_allreduce(0, 8, big, 0, P8, P8, None) == 1
+    assert lib.vcoll_reduce_scatter(0, 8, big, 0, P8, P8, None) == 1
+    assert lib.vcoll_all_gather(0, 8, big, 0, P8, P8, None) == 1
+    assert lib.vcoll_broadcast(8, big, 0, 0, one, P8, None) == 1
+    assert lib.vcoll_reduce(3, 8, big, 0, 0, P8, one, None) == 1
+    assert lib.vcoll_allreduce_hierarchical(2, 4, big, 0, P8, P8, None) == 1
+    ws = ctypes.c_void_p(0x4000)
+    assert lib.vcoll_allreduce_stepwise(0, 8, big, 1, P8, P8, ws, ctypes.c_int64(1 << 62), None, None) == 1
+    n = ctypes.c_int64()
+    assert lib.vcoll_ledger(0, 0, 8, big, 0, None, 0, None, 0, ctypes.byref(n), None, None, None) == 1
+    # all-to-all: rows x row bytes above 2^56 (each factor within its own bound)
+    sp = (ctypes.c_int64 * 4)(1 << 21, 0, 0, 1)
+    P2 = _ptrs(2)
+    assert lib.vcoll_all_to_all(2, 1 << 35, 1, sp, P2, P2, None, None, None, None, None) == 1
+    assert lib.vcoll_all_to_all(2, big, 2, sp, P2, P2, None, None, None, None, None) == 1
+    # token-major dispatch: tokens x row bytes above 2^56
+    idx = (ctypes.c_void_p * 2)(0x3000, 0x3000)
+    rr = (ctypes.c_int64 * 2)(1, 1)
+    assert lib.vcoll_moe_dispatch(2, 1 << 30, 1, 1 << 26, 0, 0, P2, idx, P2, rr, None) == 1
+    # FP8 dispatch: hidden beyond the row bound
+    rows = (ctypes.c_int64 * 2)(4, 4)
+    sp1 = (ctypes.c_int64 * 4)(1, 0, 0, 1)
+    assert lib.vcoll_moe_dispatch_fp8(2, 1 << 40, sp1, P2, rows, idx, P2, None) == 1
