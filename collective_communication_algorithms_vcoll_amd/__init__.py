@@ -167,10 +167,32 @@ def _ranks(bufs) -> list:
     return list(bufs)
 
 
+def _on_current_gpu(t) -> None:
+    """The library launches on the calling thread's current device, so every
+    buffer whose address it receives must live there (a host or other-device
+    address would fault inside a kernel)."""
+    import torch
+    if t.device.type != "cuda":
+        raise ValueError(f"vcoll: buffer on {t.device}; every buffer must be a GPU tensor")
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"vcoll: buffer on {t.device}, but kernels run on the current device cuda:{cur}")
+
+
+def _dptr(t) -> int:
+    """Device address of a tensor on the current GPU."""
+    _on_current_gpu(t)
+    return t.data_ptr()
+
+
 def _ptrs(ts: Sequence) -> ctypes.Array:
     arr = (ctypes.c_void_p * len(ts))()
     for i, t in enumerate(ts):
-        arr[i] = t.data_ptr() if t is not None and t.numel() > 0 else None
+        if t is not None and t.numel() > 0:
+            _on_current_gpu(t)
+            arr[i] = t.data_ptr()
+        else:
+            arr[i] = None
     return arr
 
 
@@ -273,7 +295,7 @@ def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
         if workspace.dtype != torch.float32 or workspace.numel() < len(s) * n:
             raise ValueError("vcoll_allreduce_stepwise: workspace must hold p*n float32")
         _no_overlap([workspace], s + r, "vcoll_allreduce_stepwise")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * 4
+        ws_ptr, ws_bytes = _dptr(workspace), workspace.numel() * 4
     launches = ctypes.c_int32()
     _check(_lib().vcoll_allreduce_stepwise(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                            ws_ptr, ws_bytes, ctypes.byref(launches), _stream(s[0])),
@@ -297,7 +319,7 @@ def vcoll_broadcast(send, recv, root: int = 0):
     _no_overlap([send], targets, "vcoll_broadcast")
     for i, a in enumerate(targets):
         _no_overlap([a], targets[i + 1:], "vcoll_broadcast")
-    _check(_lib().vcoll_broadcast(len(r), n, _dtype_code(send), root, send.data_ptr() if n else None, _ptrs(r),
+    _check(_lib().vcoll_broadcast(len(r), n, _dtype_code(send), root, _dptr(send) if n else None, _ptrs(r),
                                   _stream(send)), "vcoll_broadcast")
     return recv
 
@@ -320,7 +342,7 @@ def vcoll_reduce(send, recv=None, root: int = 0, algo="tree"):
     others = [t for i, t in enumerate(s) if not (i == root and t.data_ptr() == recv.data_ptr())]
     _no_overlap(others, [recv], "vcoll_reduce")
     _check(_lib().vcoll_reduce(_algo(algo), len(s), n, _dtype_code(s[0]), root, _ptrs(s),
-                               recv.data_ptr() if n else None, _stream(s[0])), "vcoll_reduce")
+                               _dptr(recv) if n else None, _stream(s[0])), "vcoll_reduce")
     return recv
 
 
@@ -693,7 +715,7 @@ def vcoll_bench_copy(dst, src) -> None:
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("vcoll_bench_copy: size mismatch")
-    _check(_lib().vcoll_bench_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(src)),
+    _check(_lib().vcoll_bench_copy(_dptr(dst), _dptr(src), nbytes, _stream(src)),
            "vcoll_bench_copy")
 
 

@@ -333,3 +333,24 @@ def test_oversized_counts_and_buffers_are_refused():
     rows = (ctypes.c_int64 * 2)(4, 4)
     sp1 = (ctypes.c_int64 * 4)(1, 0, 0, 1)
     assert lib.vcoll_moe_dispatch_fp8(2, 1 << 40, sp1, P2, rows, idx, P2, None) == 1
+
+
+def test_binding_refuses_host_tensors_before_calling_the_library():
+    """Host (CPU) tensors never reach a kernel: every entry point that takes
+    device buffers refuses them, including the MoE paths whose tensors are
+    only compared with one another."""
+    import torch
+    toks = [torch.zeros((4, 128), dtype=torch.bfloat16) for _ in range(2)]
+    splits = np.array([[2, 2], [2, 2]])
+    idx = [torch.zeros(4, dtype=torch.int32) for _ in range(2)]
+    with pytest.raises(ValueError):
+        vc.vcoll_all_to_all(toks, splits)
+    with pytest.raises(ValueError):
+        vc.vcoll_moe_dispatch_fp8(toks, splits, idx)
+    slots = [torch.zeros((4, 2), dtype=torch.int32) for _ in range(2)]
+    with pytest.raises(ValueError):
+        vc.vcoll_moe_dispatch(toks, slots, [4, 4], 1)
+    with pytest.raises(ValueError):
+        vc.vcoll_allreduce("ring", torch.zeros((2, 64)))
+    with pytest.raises(ValueError):
+        vc.vcoll_bench_copy(torch.zeros(16), torch.zeros(16))
