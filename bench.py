@@ -376,6 +376,14 @@ def extras(vc, torch, h, args):
     slots = vc.vcoll_moe_slots(splits, dst_rows, K)
     slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
     recv_rows = splits.sum(axis=0)
+    # token-major combine: each (token, slot) row pulled from its expert output
+    tc = vc.vcoll_moe_combine(recv, slots_g, T, K)
+    tc_ok = all(torch.equal(tc[i].view(torch.int16), back[i].view(torch.int16)) for i in range(p8))
+    pull = lambda: vc.vcoll_moe_combine(recv, slots_g, T, K, out=tc)                        # noqa: E731
+    _, ms_tc = time_launches([pull], 10, 2)
+    ex["moe_combine_token_major"] = {"GBps": rate(2 * rows * rb, ms_tc), "us": round(ms_tc * 1e3, 1),
+                                     "algorithmic_bytes": 2 * rows * rb, "equals_scatter_combine": bool(tc_ok)}
+    del tc
     tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
     tm_ok = all(torch.equal(tm[j].view(torch.int16), recv[j].view(torch.int16)) for j in range(p8))
     tm8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)

@@ -111,6 +111,8 @@ def _lib():
         lib.vcoll_moe_slots.restype = I
         lib.vcoll_moe_dispatch.argtypes = [I, I64, I, I64, I, I, P(VP), P(VP), P(VP), P(I64), VP]
         lib.vcoll_moe_dispatch.restype = I
+        lib.vcoll_moe_combine.argtypes = [I, I64, I, I64, I, P(VP), P(I64), P(VP), P(VP), VP]
+        lib.vcoll_moe_combine.restype = I
         lib.vcoll_moe_plan_dedup.argtypes = [I, I64, I, I, P(ctypes.c_int32), P(I64), P(ctypes.c_int32),
                                              P(ctypes.c_int32), P(I64)]
         lib.vcoll_moe_plan_dedup.restype = I
@@ -646,6 +648,43 @@ def vcoll_moe_dispatch(tokens, slots, recv_rows, topk: int, fp8: bool = False, r
     _check(_lib().vcoll_moe_dispatch(p, T, topk, H, _dtype_code(t[0]), int(bool(fp8)), _ptrs(t), _ptrs(s),
                                      _ptrs(r), rows, _stream(t[0])), "vcoll_moe_dispatch")
     return recv
+
+
+def vcoll_moe_combine(expert_out, slots, tokens: int, topk: int, out=None):
+    """Token-major combine (see vcoll.h): expert_out p tensors [rows_j,
+    hidden] in dispatch receive order; slots the dispatch's p int32 GPU
+    tensors [tokens*topk, 2]. Returns out (p tensors [tokens*topk, hidden]),
+    row t*topk + k of rank i being the expert output of token t's slot k."""
+    import torch
+    e = list(expert_out)
+    p = len(e)
+    H = e[0].shape[1]
+    dev, dt = e[0].device, e[0].dtype
+    for x in e:
+        if x.dim() != 2 or x.shape[1] != H or x.dtype != dt or x.device != dev or not x.is_contiguous():
+            raise ValueError("vcoll_moe_combine: expert outputs must be contiguous [rows, hidden] of one dtype")
+    T = int(tokens)
+    if out is None:
+        out = [torch.empty((T * topk, H), dtype=dt, device=dev) for _ in range(p)]
+    o = list(out)
+    if len(o) != p:
+        raise ValueError("vcoll_moe_combine: need p output buffers")
+    for x in o:
+        if x.dtype != dt or not x.is_contiguous() or x.numel() < T * topk * H:
+            raise ValueError(f"vcoll_moe_combine: every output must hold {T * topk} rows of {H} {dt}")
+    s = list(slots)
+    if len(s) != p:
+        raise ValueError("vcoll_moe_combine: need p slot tables")
+    for x in s:
+        if x.dtype != torch.int32 or x.device != dev or not x.is_contiguous() or x.numel() < 2 * T * topk:
+            raise ValueError("vcoll_moe_combine: slots must be contiguous int32 GPU tensors of tokens*topk pairs")
+    _no_overlap(e, o, "vcoll_moe_combine")
+    for i, a in enumerate(o):
+        _no_overlap([a], o[i + 1:], "vcoll_moe_combine")
+    rows = (ctypes.c_int64 * p)(*[x.shape[0] for x in e])
+    _check(_lib().vcoll_moe_combine(p, T, topk, H, _dtype_code(e[0]), _ptrs(e), rows, _ptrs(s), _ptrs(o),
+                                    _stream(e[0])), "vcoll_moe_combine")
+    return out
 
 
 def vcoll_moe_plan_dedup(topk_ids: np.ndarray, experts_per_rank: int):

@@ -82,11 +82,27 @@ struct PushArgs {
 };
 static_assert(sizeof(PushArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
+// Token-major MoE combine: rank i's row t*topk + k is pulled from row r of
+// expert-output buffer j, (j, r) = slots[i][t*topk + k] (the dispatch's slot).
+struct CombineArgs {
+  const void* src[kMaxRanks];        // each rank's expert-output rows (dispatch receive layout)
+  void* out[kMaxRanks];              // each rank's [tokens * topk] combined rows
+  const int32_t* slots[kMaxRanks];   // each rank's [tokens * topk][2] (source rank, row)
+  int32_t src_rows[kMaxRanks];
+  int64_t tokens;
+  int64_t row_bytes;
+  int32_t topk, p;
+  int32_t vec;                       // rows and bases 16-byte aligned
+  int32_t tokens_per_tile;
+};
+static_assert(sizeof(CombineArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
 hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 }  // namespace vcoll

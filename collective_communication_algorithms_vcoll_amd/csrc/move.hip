@@ -342,6 +342,64 @@ __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a)
 }
 
 // ----------------------------------------------------------------------------
+// token-major MoE combine: the reverse all-to-all of the dispatch, written in
+// (token, slot) order. Each output row pulls its expert-output row, so the
+// writes stream through each rank's output while the reads gather; the
+// scattering form of the same permutation writes rows in send order instead.
+
+constexpr int kCombineRows = 2;    // output rows whose loads are in flight together
+
+__global__ __launch_bounds__(kBlock) void combine_pull_kernel(const CombineArgs a) {
+  const int tid = threadIdx.x;
+  const int i = blockIdx.y;                                    // rank that owns the tokens
+  const int64_t total = a.tokens * a.topk;
+  const int64_t x_begin = static_cast<int64_t>(blockIdx.x) * a.tokens_per_tile * a.topk;
+  const int64_t x_end = x_begin + static_cast<int64_t>(a.tokens_per_tile) * a.topk < total
+                            ? x_begin + static_cast<int64_t>(a.tokens_per_tile) * a.topk
+                            : total;
+  const int32_t* slot = a.slots[i];
+  char* out = static_cast<char*>(a.out[i]);
+  // the expert-output row of output row x (uniform across the workgroup), or null
+  auto source = [&](int64_t x) -> const char* {
+    const int j = slot[2 * x], r = slot[2 * x + 1];
+    if (j < 0 || j >= a.p || r < 0 || r >= a.src_rows[j]) return nullptr;
+    return static_cast<const char*>(a.src[j]) + static_cast<int64_t>(r) * a.row_bytes;
+  };
+  for (int64_t x = x_begin; x < x_end; x += kCombineRows) {
+    const char* src[kCombineRows];
+#pragma unroll
+    for (int q = 0; q < kCombineRows; ++q) src[q] = x + q < x_end ? source(x + q) : nullptr;
+    if (a.vec) {
+      const int64_t nvec = a.row_bytes / 16;
+      for (int64_t v0 = tid; v0 < nvec; v0 += kPushUnroll * kBlock) {
+        u32x4 w[kCombineRows][kPushUnroll];
+#pragma unroll
+        for (int q = 0; q < kCombineRows; ++q)
+#pragma unroll
+          for (int u = 0; u < kPushUnroll; ++u) {
+            const int64_t v = v0 + u * kBlock;
+            w[q][u] = src[q] && v < nvec ? ld16(src[q], v * 16) : u32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+        for (int q = 0; q < kCombineRows; ++q)
+#pragma unroll
+          for (int u = 0; u < kPushUnroll; ++u) {
+            const int64_t v = v0 + u * kBlock;
+            if (src[q] && v < nvec) st16(out + (x + q) * a.row_bytes, v * 16, w[q][u]);
+          }
+      }
+    } else {
+      for (int64_t e = tid; e < a.row_bytes / 2; e += kBlock) {
+#pragma unroll
+        for (int q = 0; q < kCombineRows; ++q)
+          if (src[q])
+            reinterpret_cast<uint16_t*>(out + (x + q) * a.row_bytes)[e] = reinterpret_cast<const uint16_t*>(src[q])[e];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // plain copy: the streaming ceiling the collectives are measured against
 
 __global__ __launch_bounds__(kBlock) void copy_kernel(const void* src, void* dst, int64_t nvec) {
@@ -400,6 +458,12 @@ hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream)
   const dim3 grid(static_cast<unsigned>(tiles), a.p);
   if (fp8) return launch(dispatch_push_kernel<true>, grid, a, stream);
   return launch(dispatch_push_kernel<false>, grid, a, stream);
+}
+
+hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream) {
+  const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
+  if (tiles == 0) return hipSuccess;
+  return launch(combine_pull_kernel, dim3(static_cast<unsigned>(tiles), a.p), a, stream);
 }
 
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {

@@ -526,6 +526,45 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
   return from_hip(launch_dispatch_push(a, fp8 != 0, static_cast<hipStream_t>(stream)));
 }
 
+vcoll_status vcoll_moe_combine(int p, int64_t tokens, int topk, int64_t hidden, vcoll_dtype dtype,
+                               const void* const* expert_out, const int64_t* expert_rows,
+                               const int32_t* const* slots, void* const* out, void* stream) {
+  if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !valid_count(hidden) || !valid_dtype(dtype) ||
+      !expert_rows)
+    return VCOLL_ERR_INVALID_ARG;
+  if (tokens * topk > INT32_MAX || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
+  const int64_t rb = hidden * elem_bytes(dtype);
+  if (!fits(tokens * topk, rb)) return VCOLL_ERR_INVALID_ARG;
+  if (tokens == 0 || hidden == 0) return VCOLL_OK;
+  if (!expert_out || !slots || !out) return VCOLL_ERR_INVALID_ARG;
+  bool vec = rb % 16 == 0;
+  for (int j = 0; j < p; ++j) {
+    if (expert_rows[j] < 0 || expert_rows[j] > INT32_MAX || !fits(expert_rows[j], rb)) return VCOLL_ERR_INVALID_ARG;
+    if (expert_rows[j] > 0 && !expert_out[j]) return VCOLL_ERR_INVALID_ARG;
+    if (expert_rows[j] > 0) vec = vec && aligned16(expert_out[j]);
+  }
+  for (int i = 0; i < p; ++i) {
+    if (!slots[i] || !out[i]) return VCOLL_ERR_INVALID_ARG;
+    vec = vec && aligned16(out[i]);
+  }
+  CombineArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < p; ++r) {
+    a.src[r] = expert_out[r];
+    a.src_rows[r] = static_cast<int32_t>(expert_rows[r]);
+    a.out[r] = out[r];
+    a.slots[r] = slots[r];
+  }
+  a.tokens = tokens;
+  a.row_bytes = rb;
+  a.topk = topk;
+  a.p = p;
+  a.vec = vec;
+  // up to 128 KiB of output rows per workgroup (one token's 8 rows of 7168 bf16)
+  a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 131072 / (topk * rb))));
+  return from_hip(launch_combine_pull(a, static_cast<hipStream_t>(stream)));
+}
+
 vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_rank, const int32_t* topk_ids,
                                   int64_t* splits_unique, int32_t* src_unique, int32_t* expand,
                                   int64_t* expand_count) {

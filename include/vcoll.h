@@ -218,6 +218,27 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
                                 void* const* recv, const int64_t* recv_rows, void* stream);
 
 /*
+ * Token-major MoE combine ([NCC] 7.4: combine is the all-to-all that returns
+ * every expert output to the rank and position of its token; 4.2: applied
+ * after the dispatch it restores the original layout). For every rank i,
+ * token t < tokens and slot k < topk:
+ *   out[i][t*topk + k] = expert_out[j][r],  (j, r) = slots[i][t*topk + k],
+ * rows of hidden elements of dtype. slots are the dispatch's, from
+ * vcoll_moe_slots ([tokens*topk][2] int32 per rank), and expert_out[j] holds
+ * rank j's expert outputs in its dispatch receive order (expert_rows[j]
+ * rows). The result equals the reverse vcoll_all_to_all (splits transposed)
+ * scattered by dst_rows, bit for bit; here each output row pulls its source
+ * row, so each rank's output is written in order. A slot outside
+ * [0, p) x [0, expert_rows[j]) leaves its output row untouched. out[i]
+ * holds tokens*topk rows; buffers must not overlap. Rows move as 16-byte
+ * vectors when every buffer is 16-byte aligned and a row is a multiple of
+ * 16 bytes, else as 2-byte words.
+ */
+vcoll_status vcoll_moe_combine(int p, int64_t tokens, int topk, int64_t hidden, vcoll_dtype dtype,
+                               const void* const* expert_out, const int64_t* expert_rows,
+                               const int32_t* const* slots, void* const* out, void* stream);
+
+/*
  * Deduplicated MoE dispatch plan ([NCC] 7.4 and exercise 10: a token goes
  * once to each place that needs it and is then copied locally). Host only,
  * integers only; topk_ids and expert placement as vcoll_moe_plan. Rank i

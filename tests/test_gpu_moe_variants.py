@@ -284,3 +284,69 @@ def test_token_major_dispatch_skips_bad_slots(vc):
     sync()
     assert torch.equal(recv[1][0], toks[0][0]) and torch.equal(recv[0][0], toks[0][1])
     assert torch.equal(recv[0][1], toks[0][2]) and torch.equal(recv[1][1], toks[0][2])
+
+
+# --------------------------------------------------------------------------- token-major combine
+
+@pytest.mark.parametrize("dtype,H", [("bf16", 384), ("f32", 133)])
+def test_token_major_combine_matches_oracle(vc, dtype, H):
+    """Pulling every (token, slot) row from the expert outputs equals the
+    oracle's combine (reverse all-to-all, then the scatter to (token, slot)
+    positions); f32 rows of 532 bytes take the 2-byte path."""
+    import torch
+    p, T, K, E = 4, 64, 3, 16
+    topk = small_routing(p, T, K, E, 21)
+    splits, _, dst = vc.vcoll_moe_plan(np.stack(topk), E // p)
+    rows = splits.sum(axis=0)
+    eo = [workloads.rank_window(workloads.TAG_TEST * 1000 + 970, j, 0, int(rows[j]) * H, ("normal", 0.0, 1.0),
+                                dtype).reshape(-1, H) for j in range(p)]
+    if dtype == "bf16":
+        teo = [to_gpu_bf16(x) for x in eo]
+    else:
+        teo = [torch.from_numpy(x).cuda() for x in eo]
+    say(f"vcoll_moe_combine {dtype} H={H}")
+    got = vc.vcoll_moe_combine(teo, slots_gpu(vc, splits, dst, K), T, K)
+    sync()
+    want, _ = moe.combine(eo, splits, list(dst), K, T, dtype)
+    for i in range(p):
+        g = got[i].cpu()
+        g = g.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else g.numpy()
+        assert np.array_equal(g.view(np.uint8), want[i].view(np.uint8)), f"rank {i}"
+
+
+def test_token_major_combine_full_workload(vc):
+    """Full MoE workload: the token-major combine equals the scattering
+    combine bit for bit, and combine(dispatch(x)) puts token t in every one
+    of its topk rows."""
+    import torch
+    M = workloads.MOE
+    p, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    splits, src, dst = vc.vcoll_moe_plan(topk, E // p)
+    g = torch.Generator(device="cuda").manual_seed(15)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
+    say("dispatch (gather)")
+    recv = vc.vcoll_all_to_all(toks, splits, src_rows=[gpu_i32(s) for s in src])
+    say("combine (scatter)")
+    want = vc.vcoll_all_to_all(recv, splits.T, dst_rows=[gpu_i32(d) for d in dst], dst_table_rows=[T * K] * p)
+    say("combine (token-major)")
+    got = vc.vcoll_moe_combine(recv, slots_gpu(vc, splits, dst, K), T, K)
+    sync()
+    for i in range(p):
+        assert torch.equal(got[i].view(torch.int16), want[i].view(torch.int16)), f"rank {i}"
+        assert torch.equal(got[i].view(T, K, H).view(torch.int16),
+                           toks[i].view(torch.int16).unsqueeze(1).expand(T, K, H)), f"identity, rank {i}"
+
+
+def test_token_major_combine_skips_bad_slots(vc):
+    import torch
+    p, T, H, K = 2, 2, 64, 2
+    eo = [torch.arange(3 * H, device="cuda", dtype=torch.float32).reshape(3, H) + 1000 * j for j in range(p)]
+    # rank 0: (t0,k0) <- (1, 2); (t0,k1) <- rank 5 (no such rank); (t1,k0) <- (0, 3) (row too big); (t1,k1) <- (0, 0)
+    s0 = torch.tensor([[1, 2], [5, 0], [0, 3], [0, 0]], dtype=torch.int32, device="cuda")
+    s1 = torch.full((T * K, 2), -1, dtype=torch.int32, device="cuda")
+    out = [torch.full((T * K, H), -7.0, device="cuda") for _ in range(p)]
+    vc.vcoll_moe_combine(eo, [s0, s1], T, K, out=out)
+    sync()
+    assert torch.equal(out[0][0], eo[1][2]) and torch.equal(out[0][3], eo[0][0])
+    assert torch.all(out[0][1] == -7.0) and torch.all(out[0][2] == -7.0) and torch.all(out[1] == -7.0)

@@ -354,3 +354,21 @@ def test_binding_refuses_host_tensors_before_calling_the_library():
         vc.vcoll_allreduce("ring", torch.zeros((2, 64)))
     with pytest.raises(ValueError):
         vc.vcoll_bench_copy(torch.zeros(16), torch.zeros(16))
+
+
+def test_combine_validates_before_launching():
+    lib = _lib()
+    P2 = _ptrs(2)
+    rows = (ctypes.c_int64 * 2)(4, 4)
+    idx = (ctypes.c_void_p * 2)(0x3000, 0x3000)
+    assert lib.vcoll_moe_combine(2, 4, 1, 64, 7, P2, rows, idx, P2, None) == 1          # bad dtype
+    assert lib.vcoll_moe_combine(2, 4, 0, 64, 0, P2, rows, idx, P2, None) == 1          # topk 0
+    assert lib.vcoll_moe_combine(2, 4, 1, 64, 0, P2, None, idx, P2, None) == 1          # no row counts
+    bad = (ctypes.c_int64 * 2)(-1, 4)
+    assert lib.vcoll_moe_combine(2, 4, 1, 64, 0, P2, bad, idx, P2, None) == 1
+    holes = _ptrs(2)
+    holes[1] = None
+    assert lib.vcoll_moe_combine(2, 4, 1, 64, 0, holes, rows, idx, P2, None) == 1     # missing expert buffer
+    assert lib.vcoll_moe_combine(2, 4, 1, 64, 0, P2, rows, idx, holes, None) == 1     # missing output
+    assert lib.vcoll_moe_combine(2, 1 << 30, 1, 1 << 26, 0, P2, rows, idx, P2, None) == 1  # > 2^56 bytes
+    assert lib.vcoll_moe_combine(2, 0, 1, 64, 0, None, rows, None, None, None) == 0   # no tokens: no-op
