@@ -140,6 +140,13 @@ def time_launches(calls, steps, warmup):
     return wall, start.elapsed_time(end) / steps
 
 
+def device_info(torch) -> dict:
+    """The GPU the numbers were taken on."""
+    prop = torch.cuda.get_device_properties(0)
+    return {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
+            "compute_units": prop.multi_processor_count, "memory_bytes": prop.total_memory}
+
+
 def rate(nbytes, ms):
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
@@ -465,6 +472,19 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
                       f"roofline.achieved {run['roofline']['achieved']} GB/s by events, "
                       f"{419430400 / (rocprof_avg * 1e-6) / 1e9:.1f} GB/s by rocprofv3."]
 
+    trace = [r for r in _csv_rows(trace_dir, "kernel_trace.csv") if HEADLINE_KERNEL in r.get("Kernel_Name", "")]
+    if trace:
+        d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace)
+
+        def pct(q):
+            return d[min(len(d) - 1, int(q * (len(d) - 1) + 0.5))]
+        r0 = trace[0]
+        lines += ["", f"Headline launches in the kernel trace: {len(d)} (warm-up included); duration "
+                      f"p10 {pct(0.1):.2f} us, median {pct(0.5):.2f} us, p90 {pct(0.9):.2f} us. Per dispatch: "
+                      f"{r0.get('VGPR_Count')} VGPRs, {r0.get('SGPR_Count')} SGPRs, {r0.get('LDS_Block_Size')} B LDS, "
+                      f"{r0.get('Scratch_Size')} B scratch, workgroup {r0.get('Workgroup_Size_X')} work-items, "
+                      f"grid {r0.get('Grid_Size_X')} x {r0.get('Grid_Size_Y')} work-items."]
+
     def per_dispatch(root, counter):
         out = {}
         for r in _csv_rows(root, "counter_collection.csv"):
@@ -652,6 +672,7 @@ def main() -> int:
             "p": h["p"], "elements_per_rank": h["n"], "algorithm": "ring",
             "algorithmic_bytes_per_step": h["nbytes"], "buffer_sets_cycled": h["sets"],
         },
+        "device": device_info(torch),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
