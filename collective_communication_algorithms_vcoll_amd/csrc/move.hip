@@ -11,8 +11,12 @@ namespace {
 using namespace dev;
 
 // ----------------------------------------------------------------------------
-// fan-out store of the all-gather and the broadcast: streaming (non-temporal)
-// or cached; which one, and the workgroup shape, the host picks by size
+// store of a fan-out (one load, several copies stored): streaming
+// (non-temporal) or cached. Measured on MI355X, the large fan-outs write
+// faster through L2 with cached stores: the all-gather and broadcast beyond
+// 1 GiB written (4-6%) and the bf16 token-major MoE dispatch, 8 copies of
+// each token row (3%). One-to-one movers (all-to-all, combine, FP8 codes)
+// lost 1-8% with cached stores and keep streaming ones.
 
 template <bool NT>
 __device__ __forceinline__ void fan_st16(void* base, int64_t byte_off, u32x4 v) {
@@ -113,7 +117,8 @@ __global__ __launch_bounds__(BS) void broadcast_kernel(const BcastArgs a) {
 // ----------------------------------------------------------------------------
 // all-to-all: workgroup t moves rows_per_tile rows of one (i -> j) block
 
-__global__ __launch_bounds__(kBlock) void all_to_all_kernel(const A2AArgs a) {
+template <int BS>
+__global__ __launch_bounds__(BS) void all_to_all_kernel(const A2AArgs a) {
   const int t = blockIdx.x;
   // the block this workgroup belongs to: last one whose first tile <= t
   int lo = 0, hi = a.nblocks - 1;
@@ -136,27 +141,27 @@ __global__ __launch_bounds__(kBlock) void all_to_all_kernel(const A2AArgs a) {
     if (a.vec) {
       const int64_t nvec = a.row_bytes / 16;
       constexpr int U = 4;
-      for (int64_t x0 = tid; x0 < nvec; x0 += U * kBlock) {
+      for (int64_t x0 = tid; x0 < nvec; x0 += U * BS) {
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t x = x0 + u * kBlock;
+          const int64_t x = x0 + u * BS;
           v[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t x = x0 + u * kBlock;
+          const int64_t x = x0 + u * BS;
           if (x < nvec) st16(dst, x * 16, v[u]);
         }
       }
     } else if (a.esize == 4) {
-      for (int64_t x = tid; x < a.row_bytes / 4; x += kBlock)
+      for (int64_t x = tid; x < a.row_bytes / 4; x += BS)
         reinterpret_cast<uint32_t*>(dst)[x] = reinterpret_cast<const uint32_t*>(src)[x];
     } else if (a.esize == 2) {
-      for (int64_t x = tid; x < a.row_bytes / 2; x += kBlock)
+      for (int64_t x = tid; x < a.row_bytes / 2; x += BS)
         reinterpret_cast<uint16_t*>(dst)[x] = reinterpret_cast<const uint16_t*>(src)[x];
     } else {
-      for (int64_t x = tid; x < a.row_bytes; x += kBlock)
+      for (int64_t x = tid; x < a.row_bytes; x += BS)
         reinterpret_cast<uint8_t*>(dst)[x] = reinterpret_cast<const uint8_t*>(src)[x];
     }
   }
@@ -281,8 +286,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
 
 constexpr int kPushUnroll = 4;     // 16-byte vectors in flight per thread (a 7168 bf16 row is 3.5)
 
-template <bool FP8>
-__global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a) {
+template <bool FP8, int BS>
+__global__ __launch_bounds__(BS) void dispatch_push_kernel(const PushArgs a) {
   const int tid = threadIdx.x;
   const int i = blockIdx.y;                                    // sending rank
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * a.tokens_per_tile;
@@ -298,17 +303,17 @@ __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a)
     if constexpr (FP8) {
       // hidden / 16 lane tasks, a multiple of 8: each 8-lane group is whole
       const int64_t nq = a.hidden / 16;
-      for (int64_t y0 = tid; y0 < nq; y0 += kPushUnroll / 2 * kBlock) {
+      for (int64_t y0 = tid; y0 < nq; y0 += kPushUnroll / 2 * BS) {
         u32x4 w[kPushUnroll];
 #pragma unroll
         for (int u = 0; u < kPushUnroll / 2; ++u) {
-          const int64_t y = y0 + u * kBlock;
+          const int64_t y = y0 + u * BS;
           w[2 * u] = y < nq ? ld16(src, y * 32) : u32x4{0, 0, 0, 0};
           w[2 * u + 1] = y < nq ? ld16(src, y * 32 + 16) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < kPushUnroll / 2; ++u) {
-          const int64_t y = y0 + u * kBlock;
+          const int64_t y = y0 + u * BS;
           if (y >= nq) break;                        // uniform over each 8-lane group
           u32x4 codes;
           float scale;
@@ -321,11 +326,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a)
       }
     } else if (a.vec) {
       const int64_t nvec = a.row_bytes / 16;
-      for (int64_t x0 = tid; x0 < nvec; x0 += kPushUnroll * kBlock) {
+      for (int64_t x0 = tid; x0 < nvec; x0 += kPushUnroll * BS) {
         u32x4 v[kPushUnroll];
 #pragma unroll
         for (int u = 0; u < kPushUnroll; ++u) {
-          const int64_t x = x0 + u * kBlock;
+          const int64_t x = x0 + u * BS;
           v[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
         }
         for (int k = 0; k < a.topk; ++k) {
@@ -333,13 +338,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a)
           if (!d) continue;
 #pragma unroll
           for (int u = 0; u < kPushUnroll; ++u) {
-            const int64_t x = x0 + u * kBlock;
-            if (x < nvec) st16(d, x * 16, v[u]);
+            const int64_t x = x0 + u * BS;
+            if (x < nvec) fan_st16<false>(d, x * 16, v[u]);
           }
         }
       }
     } else {
-      for (int64_t x = tid; x < a.row_bytes / 2; x += kBlock) {
+      for (int64_t x = tid; x < a.row_bytes / 2; x += BS) {
         const uint16_t v = reinterpret_cast<const uint16_t*>(src)[x];
         for (int k = 0; k < a.topk; ++k) {
           char* d = dest(k);
@@ -358,7 +363,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_push_kernel(const PushArgs a)
 
 constexpr int kCombineRows = 2;    // output rows whose loads are in flight together
 
-__global__ __launch_bounds__(kBlock) void combine_pull_kernel(const CombineArgs a) {
+template <int BS>
+__global__ __launch_bounds__(BS) void combine_pull_kernel(const CombineArgs a) {
   const int tid = threadIdx.x;
   const int i = blockIdx.y;                                    // rank that owns the tokens
   const int64_t total = a.tokens * a.topk;
@@ -380,25 +386,25 @@ __global__ __launch_bounds__(kBlock) void combine_pull_kernel(const CombineArgs 
     for (int q = 0; q < kCombineRows; ++q) src[q] = x + q < x_end ? source(x + q) : nullptr;
     if (a.vec) {
       const int64_t nvec = a.row_bytes / 16;
-      for (int64_t v0 = tid; v0 < nvec; v0 += kPushUnroll * kBlock) {
+      for (int64_t v0 = tid; v0 < nvec; v0 += kPushUnroll * BS) {
         u32x4 w[kCombineRows][kPushUnroll];
 #pragma unroll
         for (int q = 0; q < kCombineRows; ++q)
 #pragma unroll
           for (int u = 0; u < kPushUnroll; ++u) {
-            const int64_t v = v0 + u * kBlock;
+            const int64_t v = v0 + u * BS;
             w[q][u] = src[q] && v < nvec ? ld16(src[q], v * 16) : u32x4{0, 0, 0, 0};
           }
 #pragma unroll
         for (int q = 0; q < kCombineRows; ++q)
 #pragma unroll
           for (int u = 0; u < kPushUnroll; ++u) {
-            const int64_t v = v0 + u * kBlock;
+            const int64_t v = v0 + u * BS;
             if (src[q] && v < nvec) st16(out + (x + q) * a.row_bytes, v * 16, w[q][u]);
           }
       }
     } else {
-      for (int64_t e = tid; e < a.row_bytes / 2; e += kBlock) {
+      for (int64_t e = tid; e < a.row_bytes / 2; e += BS) {
 #pragma unroll
         for (int q = 0; q < kCombineRows; ++q)
           if (src[q])
@@ -481,19 +487,19 @@ hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream)
   const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
   if (tiles == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(tiles), a.p);
-  if (fp8) return launch(dispatch_push_kernel<true>, grid, a, stream);
-  return launch(dispatch_push_kernel<false>, grid, a, stream);
+  if (fp8) return launch(dispatch_push_kernel<true, kBlock>, grid, kBlock, a, stream);
+  return launch(dispatch_push_kernel<false, kBlock>, grid, kBlock, a, stream);
 }
 
 hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream) {
   const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
   if (tiles == 0) return hipSuccess;
-  return launch(combine_pull_kernel, dim3(static_cast<unsigned>(tiles), a.p), a, stream);
+  return launch(combine_pull_kernel<kBlock>, dim3(static_cast<unsigned>(tiles), a.p), kBlock, a, stream);
 }
 
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
-  return launch(all_to_all_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
+  return launch(all_to_all_kernel<kBlock>, dim3(static_cast<unsigned>(tiles)), kBlock, a, stream);
 }
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
