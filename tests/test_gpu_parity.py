@@ -254,6 +254,30 @@ def test_all_gather_matches_oracle(vc, algo, p, dtype):
         assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"AG {algo} p={p} m={m}")
 
 
+@pytest.mark.parametrize("m_extra", [4, 1])
+def test_all_gather_beyond_1gib_written(vc, m_extra):
+    """The all-gather's shape for launches that write more than 1 GiB (one
+    vector per thread, cached stores): p = 8 float32 blocks of 2^22 + m_extra
+    elements, 16-byte multiples (vector path, last tile partial) and an odd
+    count (element path). Every output block of every rank is compared with
+    its source block at both ends and at random windows."""
+    p, m = 8, (1 << 22) + m_extra
+    assert p * p * m * 4 > 1 << 30
+    x = rand_inputs(p, m, "f32", seed=90 + m_extra)
+    t = upload(x, "f32")
+    say(f"vcoll_all_gather ring p={p} m={m} f32 (more than 1 GiB written)")
+    out = vc.vcoll_all_gather("ring", t)
+    sync()
+    rng = np.random.default_rng(7)
+    w = 4099
+    for r in range(p):
+        for b in range(p):
+            for lo in (0, m - w, *rng.integers(0, m - w, size=3)):
+                lo = int(lo)
+                got = out[r, b * m + lo: b * m + lo + w].cpu().numpy().view(np.uint32)
+                assert_bits_equal(got, bits(x[b][lo:lo + w], "f32"), f"AG rank {r} block {b} at {lo}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("p", [4, 8, 16])
 def test_allreduce_is_reduce_scatter_then_all_gather_on_gpu(vc, p, dtype):

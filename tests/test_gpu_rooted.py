@@ -94,6 +94,28 @@ def test_broadcast_unaligned_uses_element_path(vc):
         assert out[r, 0].item() == 0
 
 
+@pytest.mark.parametrize("offset", [0, 1])
+def test_broadcast_beyond_1gib_written(vc, offset):
+    """The broadcast's shape for launches that write more than 1 GiB (one
+    vector per thread, cached stores): 2^26 + 8 bfloat16 elements to 16
+    buffers, 16-byte aligned (vector path) and shifted by one element
+    (element path)."""
+    import torch
+    p, n = 16, (1 << 26) + 8
+    assert p * n * 2 > 1 << 30
+    x = rand_inputs(1, n, "bf16", 3)[0]
+    big = upload([np.concatenate([np.zeros(offset, np.uint16), x]).astype(np.uint16)], "bf16")[0]
+    src = big[offset:]
+    out = torch.zeros((p, n + offset), dtype=torch.bfloat16, device=big.device)
+    say(f"vcoll_broadcast p={p} n={n} bf16 offset={offset} (more than 1 GiB written)")
+    vc.vcoll_broadcast(src, [out[r, offset:] for r in range(p)], 4)
+    sync()
+    for r in range(p):
+        assert torch.equal(out[r, offset:].view(torch.int16), src.view(torch.int16)), f"rank {r}"
+        if offset:
+            assert out[r, 0].item() == 0
+
+
 def test_broadcast_rejects_overlap(vc):
     import torch
     t = torch.zeros(4, 64, device="cuda")
