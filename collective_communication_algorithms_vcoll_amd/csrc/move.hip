@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const void* src, void* dst
 constexpr int kFanBlock = 64;
 constexpr int64_t kFanLargeBytes = int64_t(1) << 30;
 
-template <int ES, int V, bool NT, class Args, class Kernel>
+template <int ES, int V, class Args, class Kernel>
 hipError_t launch_fan(Kernel kernel, int64_t elems, unsigned blocks_y, const Args& a, hipStream_t stream) {
   const int64_t per_tile = static_cast<int64_t>(V) * kFanBlock * (16 / ES);
   const int64_t tiles = (elems + per_tile - 1) / per_tile;
@@ -456,15 +456,15 @@ hipError_t launch_fan(Kernel kernel, int64_t elems, unsigned blocks_y, const Arg
 template <int ES>
 hipError_t launch_broadcast_es(const BcastArgs& a, hipStream_t stream) {
   if (a.n * ES > kFanLargeBytes / a.q)                     // bytes written, without overflow
-    return launch_fan<ES, 1, false>(broadcast_kernel<ES, 1, kFanBlock, false>, a.n, 1, a, stream);
-  return launch_fan<ES, 4, true>(broadcast_kernel<ES, 4, kFanBlock, true>, a.n, 1, a, stream);
+    return launch_fan<ES, 1>(broadcast_kernel<ES, 1, kFanBlock, false>, a.n, 1, a, stream);
+  return launch_fan<ES, 4>(broadcast_kernel<ES, 4, kFanBlock, true>, a.n, 1, a, stream);
 }
 
 template <int ES>
 hipError_t launch_all_gather_es(const GatherArgs& a, hipStream_t stream) {
   if (a.m * ES * a.p > kFanLargeBytes / a.p)
-    return launch_fan<ES, 1, false>(all_gather_kernel<ES, 1, kFanBlock, false>, a.m, a.p, a, stream);
-  return launch_fan<ES, 4, true>(all_gather_kernel<ES, 4, kFanBlock, true>, a.m, a.p, a, stream);
+    return launch_fan<ES, 1>(all_gather_kernel<ES, 1, kFanBlock, false>, a.m, a.p, a, stream);
+  return launch_fan<ES, 4>(all_gather_kernel<ES, 4, kFanBlock, true>, a.m, a.p, a, stream);
 }
 
 }  // namespace
