@@ -422,6 +422,24 @@ def extras(vc, torch, h, args):
         "all_to_all_us": round(ms_u * 1e3, 1), "expand_us": round(ms_x * 1e3, 1),
         "message_bytes_bf16": offrank(su) * rb, "message_bytes_fp8": offrank(su) * orb,
         "message_bytes_plain_bf16": offrank(splits) * rb}
+
+    # the host rows: partition + step schedule + ledger of a collective (the
+    # record-free ledger call builds every message and sums it per rank) and
+    # the MoE routing plan, through the Python binding, median of repeated calls
+    def host_us(fn, reps):
+        t = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+        return round(float(np.median(t)) * 1e6, 1)
+    n8 = workloads.DDP_BUCKET["n"]
+    host = {"ledger_ring_p8_ddp_bucket_us": host_us(lambda: vc.vcoll_ledger_summary("allreduce", "ring", 8, n8), 200)}
+    for algo in ("ring", "rd", "rabenseifner", "tree"):
+        host[f"ledger_{algo}_p72_us"] = host_us(lambda: vc.vcoll_ledger_summary("allreduce", algo, 72, 72 << 20), 50)
+    host["ledger_ring_p72_messages"] = vc.vcoll_ledger_summary("allreduce", "ring", 72, 72 << 20)[0]
+    host["moe_plan_8x4096x8_us"] = host_us(lambda: vc.vcoll_moe_plan(topk, E // p8), 20)
+    ex["host_schedule_and_ledger"] = host
     return ex
 
 

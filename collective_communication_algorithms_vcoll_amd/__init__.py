@@ -561,6 +561,26 @@ def vcoll_ledger(op, algo, p: int, n: int, dtype: str = "f32", splits=None, row_
     return out, list(sent), list(got), steps.value
 
 
+def vcoll_ledger_summary(op, algo, p: int, n: int, dtype: str = "f32", splits=None, row_elems: int = 0):
+    """Totals of a collective's ledger without its records: (message count,
+    sent bytes per rank, received bytes per rank, step count). One call of
+    vcoll_ledger with no record buffer."""
+    lib = _lib()
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    dtc = {"f32": F32, "bf16": BF16, "u8": U8}[dtype] if isinstance(dtype, str) else int(dtype)
+    sp = None
+    if splits is not None:
+        sp_arr = np.ascontiguousarray(np.asarray(splits, dtype=np.int64).reshape(p, p))
+        sp = sp_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    count = ctypes.c_int64()
+    sent = (ctypes.c_int64 * p)()
+    got = (ctypes.c_int64 * p)()
+    steps = ctypes.c_int32()
+    _check(lib.vcoll_ledger(opc, _algo(algo), p, n, dtc, sp, row_elems, None, 0, ctypes.byref(count),
+                            sent, got, ctypes.byref(steps)), "vcoll_ledger")
+    return count.value, list(sent), list(got), steps.value
+
+
 def vcoll_model_formula(algo, p: int, nbytes: float, alpha: float, beta: float) -> float:
     """Closed-form alpha-beta all-reduce time in seconds (see vcoll.h)."""
     t = ctypes.c_double()

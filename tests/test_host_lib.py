@@ -103,6 +103,15 @@ def test_headline_ledger_closed_form():
     assert sent == [377_487_360] * 16 and steps == 30
 
 
+@pytest.mark.parametrize("op,algo,p", [("allreduce", "ring", 8), ("allreduce", "rabenseifner", 72),
+                                       ("allreduce", "tree", 5), ("reduce_scatter", "ring", 16),
+                                       ("all_gather", "rd", 4)])
+def test_ledger_summary_equals_the_records(op, algo, p):
+    """The record-free ledger call gives the totals of the full ledger."""
+    n = 1000 * p + 7
+    msgs, sent, got, steps = vc.vcoll_ledger(op, algo, p, n)
+    assert vc.vcoll_ledger_summary(op, algo, p, n) == (len(msgs), sent, got, steps)
+
 @pytest.mark.parametrize("p,n", [(1, 0), (1, 5), (4, 3), (8, 6_553_600), (72, 1000), (128, 129)])
 def test_chunk_bounds_match_oracle(p, n):
     offs = oracle.chunk_bounds(n, p)
