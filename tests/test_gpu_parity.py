@@ -467,6 +467,32 @@ def test_message_size_sweep_large_windows(vc, p, nbytes):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_max_p_with_vector_chunks(vc, dtype):
+    """p = 128, the largest p, with chunks of about 5000 elements: the
+    run-time order program's 16-byte vector path (chunk heads and tails
+    ragged), every algorithm, and the reduce-scatter and all-gather."""
+    p = 128
+    n = p * 5000 + 77
+    x = rand_inputs(p, n, dtype, 400)
+    t = upload(x, dtype)
+    for algo in ALGOS:
+        say(f"vcoll_allreduce p={p} n={n} {algo} {dtype}")
+        want, _ = oracle.allreduce(x, algo, dtype)
+        got = download(vc.vcoll_allreduce(algo, t), dtype)
+        assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"{algo} p={p}")
+    rs = vc.vcoll_reduce_scatter("ring", t)
+    sync()
+    want, _ = oracle.reduce_scatter(x, "ring", dtype)
+    for c in range(p):
+        assert_bits_equal(download(rs[c], dtype), bits(want[c], dtype), f"rs chunk {c}")
+    m = 4099
+    y = rand_inputs(p, m, dtype, 401)
+    want, _ = oracle.all_gather(y, "ring", dtype)
+    got = download(vc.vcoll_all_gather("ring", upload(y, dtype)), dtype)
+    assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"AG p={p} m={m}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("p", [3, 12, 72, 128])
 def test_small_chunks_of_the_run_time_program(vc, p, dtype):
     """p not compiled in, chunks of at most 1024 elements: the LDS-staged
