@@ -543,6 +543,136 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
     return 0
 
 
+# kernel (a substring of its rocprofv3 name) -> (workload, algorithmic bytes per launch), for the
+# counter-traffic pass: each workload below uses its own kernel instantiation
+TRAFFIC_SET = {
+    "reduce_kernel<0, 0, 8, 2, false, true, 256>": ("fused ring all-reduce, p=8 x 25 MiB f32", 419_430_400),
+    "hier_kernel<0, 2, 4, true>": ("hierarchical 2x4 all-reduce, p=8 x 25 MiB f32", 419_430_400),
+    "reduce_kernel<0, 3, 8, 2, true, false, 256>": ("tree reduce to one root, p=8 x 25 MiB f32", 235_929_600),
+    "broadcast_kernel<4, 4, 64, true>": ("broadcast of 25 MiB f32 to 8 buffers", 235_929_600),
+    "reduce_kernel<1, 0, 16, 1, false, true, 64>": ("fused ring all-reduce, p=16 x 192 MiB bf16", 6_442_450_944),
+    "reduce_kernel<1, 0, 16, 1, true, false, 64>": ("ring reduce-scatter, p=16 x 192 MiB bf16", 3_422_552_064),
+    "all_gather_kernel<2, 1, 64, false>": ("all-gather of 12 MiB bf16 blocks, p=16", 3_422_552_064),
+    "all_to_all_kernel<256>": ("variable-split all-to-all of the MoE splits (plain)", None),
+    "dispatch_push_kernel<false, 256>": ("token-major MoE dispatch, bf16", None),
+    "dispatch_push_kernel<true, 256>": ("token-major MoE dispatch, FP8", None),
+    "combine_pull_kernel<256>": ("token-major MoE combine", None),
+    "dispatch_fp8_kernel": ("row-major FP8 dispatch (gather + quantise)", None),
+    "copy_kernel": ("plain copy, 200 MiB read + 200 MiB written (counter scale)", 419_430_400),
+}
+
+
+def traffic_set(vc, torch, launches: int) -> int:
+    """Launch each kernel of TRAFFIC_SET `launches` times (after one warm-up),
+    for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs. Prints the MoE
+    kernels' algorithmic bytes (they depend on the routing) as one JSON line."""
+    import numpy as np
+    import workloads
+
+    def run(call):
+        for _ in range(launches + 1):
+            call()
+        torch.cuda.synchronize()
+
+    out = {}
+    p, n = 8, workloads.DDP_BUCKET["n"]
+    g = torch.Generator(device="cuda").manual_seed(9)
+    t = torch.randn((p, n), device="cuda", generator=g) * 1e-3
+    o = torch.empty_like(t)
+    run(vc.prepare_allreduce("ring", t, o))
+    run(vc.prepare_allreduce_hierarchical(2, 4, t, o))
+    root_out = torch.empty(n, device="cuda")
+    run(vc.prepare_reduce(t, root_out, 0))
+    run(vc.prepare_broadcast(t[0].clone(), o, 0))
+    src, dst = torch.empty(p * n, device="cuda"), torch.empty(p * n, device="cuda")
+    run(vc.prepare_bench_copy(dst, src))
+    del t, o, root_out, src, dst
+    torch.cuda.empty_cache()
+    P16, N16 = 16, 100_663_296
+    t16 = (torch.rand((P16, N16), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
+    o16 = torch.empty_like(t16)
+    run(vc.prepare_allreduce("ring", t16, o16))
+    rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
+    run(vc.prepare_reduce_scatter("ring", t16, rs16))
+    run(vc.prepare_all_gather("ring", rs16, o16))
+    del t16, o16, rs16
+    torch.cuda.empty_cache()
+    M = workloads.MOE
+    p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
+    splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
+    rb, orb, rows = 2 * H, H + H // 32, int(splits.sum())
+    plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
+                  for i in range(p8)]
+    plain_recv = vc.vcoll_all_to_all(plain_send, splits)
+    run(lambda: vc.vcoll_all_to_all(plain_send, splits, recv=plain_recv))
+    del plain_send
+    slots = vc.vcoll_moe_slots(splits, dst_rows, K)
+    slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
+    recv_rows = splits.sum(axis=0)
+    tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
+    run(lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=tm))
+    tm8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
+    run(lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=tm8))
+    tc = vc.vcoll_moe_combine(tm, slots_g, T, K)
+    run(lambda: vc.vcoll_moe_combine(tm, slots_g, T, K, out=tc))
+    src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
+    f8 = vc.vcoll_moe_dispatch_fp8(toks, splits, src_g)
+    run(lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, f8))
+    out["all_to_all_kernel<256>"] = 2 * rows * rb
+    out["dispatch_push_kernel<false, 256>"] = p8 * T * rb + rows * rb
+    out["dispatch_push_kernel<true, 256>"] = p8 * T * rb + rows * orb
+    out["combine_pull_kernel<256>"] = 2 * rows * rb
+    out["dispatch_fp8_kernel"] = rows * rb + rows * orb
+    print(json.dumps({"moe_algorithmic_bytes": out}), flush=True)
+    return 0
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, moe_json: str, command: str) -> int:
+    """Per-kernel HBM bytes per launch from the two counter runs of
+    --traffic-set, scaled by copy_kernel's readings, against each kernel's
+    algorithmic bytes: profiles/traffic_hot_kernels.md."""
+    with open(moe_json) as f:
+        moe = json.loads([ln for ln in f.read().splitlines() if "moe_algorithmic_bytes" in ln][-1])
+    algo_bytes = {k: (v[1] if v[1] is not None else moe["moe_algorithmic_bytes"][k]) for k, v in TRAFFIC_SET.items()}
+
+    def per_kernel(root, counter):
+        vals = {}
+        for r in _csv_rows(root, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            for key in TRAFFIC_SET:
+                if key in name:
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, nw = per_kernel(write_dir, "WRITE_SIZE")
+    half = 209_715_200                          # copy_kernel reads, and writes, this many bytes
+    f_scale, w_scale = half / fetch["copy_kernel"], half / write["copy_kernel"]
+    lines = ["# HBM traffic per launch from rocprofv3 counters: the hot kernels", "",
+             f"Command: `{command}`", "",
+             f"FETCH_SIZE and WRITE_SIZE per dispatch, averaged over each kernel's dispatches (warm-up "
+             f"included), scaled by copy_kernel's readings for a copy of {half} B: {f_scale:.2f} B per "
+             f"FETCH_SIZE unit, {w_scale:.2f} B per WRITE_SIZE unit. Algorithmic bytes are the bytes "
+             f"each operation must move (inputs read once, outputs written once).", "",
+             "| kernel | workload | dispatches | read B | written B | traffic / algorithmic |",
+             "|---|---|---|---|---|---|"]
+    for key, (label, _) in TRAFFIC_SET.items():
+        if key not in fetch or key not in write:
+            lines.append(f"| {key} | {label} | 0 | - | - | - |")
+            continue
+        rd, wr = fetch[key] * f_scale, write[key] * w_scale
+        lines.append(f"| {key} | {label} | {nf[key]} | {rd:,.0f} | {wr:,.0f} | "
+                     f"{(rd + wr) / algo_bytes[key]:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "traffic_hot_kernels.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def sweep(vc, torch, out_path: str, max_bytes: int) -> int:
     """Message-size sweep of the fused all-reduce: every p in SWEEP_P, every
     per-rank size in SWEEP_BYTES up to max_bytes, every algorithm. Each point
@@ -646,6 +776,10 @@ def main() -> int:
     ap.add_argument("--sweep", metavar="OUT_JSONL", help="run the message-size sweep instead, one JSON line per "
                     "(p, size, algorithm) point written to OUT_JSONL, and exit")
     ap.add_argument("--sweep-max-bytes", type=int, default=2 ** 30, help="largest per-rank size of the sweep")
+    ap.add_argument("--traffic-set", type=int, default=0, metavar="K",
+                    help="launch each hot kernel K times (plus a warm-up) for counter runs, then exit")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRAFFIC_SET_LOG"),
+                    help="turn the counter runs of --traffic-set into a table in profiles/ and exit")
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", help="turn a sweep's JSON lines into a table in "
                     "profiles/ and exit")
     args = ap.parse_args()
@@ -653,6 +787,8 @@ def main() -> int:
         return summarize_profile(*args.summarize_profile, args.profile_command)
     if args.summarize_sweep:
         return summarize_sweep(args.summarize_sweep, args.profile_command)
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic, args.profile_command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -666,6 +802,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.sweep:
         return sweep(vc, torch, args.sweep, args.sweep_max_bytes)
+    if args.traffic_set:
+        return traffic_set(vc, torch, args.traffic_set)
     h = headline(vc, torch, args)
     value = h["nbytes"] * args.steps / h["wall"] / 1e9
     achieved = h["nbytes"] / (h["mean_ms"] * 1e-3) / 1e9
