@@ -509,6 +509,8 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
             if r.get("Counter_Name") != counter:
                 continue
             name = r.get("Kernel_Name", "")
+            if "vcoll::" not in name:               # torch's own kernels (direct_copy_kernel_cuda, ...)
+                continue
             key = "headline" if HEADLINE_KERNEL in name else ("copy" if COPY_KERNEL in name else None)
             if key:
                 out.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -643,6 +645,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, moe_json: str, command: st
             if r.get("Counter_Name") != counter:
                 continue
             name = r.get("Kernel_Name", "")
+            if "vcoll::" not in name:               # torch's own kernels (direct_copy_kernel_cuda, ...)
+                continue
             for key in TRAFFIC_SET:
                 if key in name:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))
