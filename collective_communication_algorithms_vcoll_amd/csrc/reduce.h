@@ -31,8 +31,10 @@ constexpr bool has_fixed_kernel(int p) { return p == 2 || p == 4 || p == 8 || p 
 // For has_fixed_kernel(p), leaf[c * kFixedMax + k] is the buffer of the k-th input
 // in chunk c's summation order (the host resolves the ring's per-chunk
 // rotation and the trees' leaf order), so a workgroup fetches its p source
-// pointers with one wide scalar load. For any other p, leaf[r] = send[r] and
-// the kernel resolves the order itself.
+// pointers with one wide scalar load. For any other p, the ring has
+// leaf[r] = send[r] and the kernel rotates it per chunk; the trees have
+// leaf[k] = the k-th leaf of the program (send[rank[k]]), so no leaf costs
+// a lookup of rank[] on the device.
 struct ReduceArgs {
   const void* leaf[kFixedMax * kFixedMax];
   void* dst[kMaxRanks];

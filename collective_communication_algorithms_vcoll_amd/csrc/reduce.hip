@@ -141,7 +141,7 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
 #pragma unroll
       for (int b = 0; b < kOneBatch; ++b)
         if (k0 + b < p) {
-          const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : a.rank[k0 + b];
+          const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : k0 + b;
           raw[b] = static_cast<const E*>(a.leaf[rank])[e];
         }
 #pragma unroll
@@ -245,7 +245,7 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       if (k0 + b < p) {
-        const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : a.rank[k0 + b];
+        const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : k0 + b;
         raw[b] = valid ? ld16(a.leaf[rank], boff) : u32x4{0, 0, 0, 0};
       }
     }
@@ -405,8 +405,9 @@ __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a
       }
     } else {
       float st[kRuntimeDepth][1];
+#pragma unroll 4
       for (int k = 0; k < p; ++k) {
-        const float v = val[a.rank[k] * T + tid];
+        const float v = val[k * T + tid];
         rt_push<1>(st, &v);
         for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
       }

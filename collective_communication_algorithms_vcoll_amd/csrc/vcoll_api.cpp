@@ -89,7 +89,7 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
       for (int k = 0; k < p; ++k)
         a.leaf[c * kFixedMax + k] = send[algo == VCOLL_RING ? (c + 1 + k) % p : prog.rank[k]];
   } else {
-    for (int r = 0; r < p; ++r) a.leaf[r] = send[r];
+    for (int k = 0; k < p; ++k) a.leaf[k] = send[algo == VCOLL_RING ? k : prog.rank[k]];
   }
   for (int k = 0; k < p; ++k) {
     a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
@@ -333,11 +333,7 @@ vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, 
   a.vec = all_aligned(p, send) && aligned16(recv);
   // the tree runs on ranks relative to the root: leaf v is rank (v + root) mod p
   const OrderProgram prog = order_program(VCOLL_BINARY_TREE, p);
-  if (has_fixed_kernel(p)) {
-    for (int k = 0; k < p; ++k) a.leaf[k] = send[(prog.rank[k] + root) % p];
-  } else {
-    for (int v = 0; v < p; ++v) a.leaf[v] = send[(v + root) % p];
-  }
+  for (int k = 0; k < p; ++k) a.leaf[k] = send[(prog.rank[k] + root) % p];   // leaves in program order
   for (int k = 0; k < p; ++k) {
     a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
     a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
