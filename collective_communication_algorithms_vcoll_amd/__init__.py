@@ -248,6 +248,15 @@ def _no_overlap(a: list, b: list, what: str, same_index_ok: bool = False) -> Non
         heapq.heappush(active, (s1, s0, side, i))
 
 
+def _disjoint(ts: list, what: str) -> None:
+    """Raise if two of the buffers overlap: every output of a collective gets
+    its own data, so two outputs sharing bytes would race."""
+    spans = sorted(_span(t) for t in ts if t is not None and t.numel() > 0)
+    for (_, e0), (s1, _) in zip(spans, spans[1:]):
+        if s1 < e0:
+            raise ValueError(f"{what}: output buffers overlap")
+
+
 # -----------------------------------------------------------------------------
 
 
@@ -271,6 +280,7 @@ def vcoll_allreduce(algo, send, recv=None):
     if len(r) != len(s) or r[0].dtype != s[0].dtype or r[0].device != s[0].device:
         raise ValueError("vcoll_allreduce: send and recv must match in p, dtype and device")
     _no_overlap(s, r, "vcoll_allreduce", same_index_ok=True)
+    _disjoint(r, "vcoll_allreduce")
     _check(_lib().vcoll_allreduce(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                   _stream(s[0])), "vcoll_allreduce")
     return recv
@@ -290,6 +300,7 @@ def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
     r = _ranks(recv)
     _validate(r, "vcoll_allreduce_stepwise", n)
     _no_overlap(s, r, "vcoll_allreduce_stepwise", same_index_ok=True)
+    _disjoint(r, "vcoll_allreduce_stepwise")
     ws_ptr, ws_bytes = None, 0
     if _dtype_code(s[0]) == BF16:
         if workspace is None:
@@ -408,6 +419,7 @@ def vcoll_allreduce_hierarchical(nodes: int, local: int, send, recv=None):
     r = _ranks(recv)
     _validate(r, "vcoll_allreduce_hierarchical", n)
     _no_overlap(s, r, "vcoll_allreduce_hierarchical", same_index_ok=True)
+    _disjoint(r, "vcoll_allreduce_hierarchical")
     _check(_lib().vcoll_allreduce_hierarchical(nodes, local, n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                                _stream(s[0])), "vcoll_allreduce_hierarchical")
     return recv
@@ -458,6 +470,7 @@ def vcoll_reduce_scatter(algo, send, recv=None):
         if r[c].numel() != vcoll_chunk(p, n, c)[1] or r[c].dtype != s[0].dtype or not r[c].is_contiguous():
             raise ValueError(f"vcoll_reduce_scatter: output {c} must hold chunk {c}")
     _no_overlap(s, r, "vcoll_reduce_scatter")
+    _disjoint(r, "vcoll_reduce_scatter")
     _check(_lib().vcoll_reduce_scatter(_algo(algo), p, n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                        _stream(s[0])), "vcoll_reduce_scatter")
     return recv
@@ -476,6 +489,7 @@ def vcoll_all_gather(algo, send, recv=None):
     r = _ranks(recv)
     _validate(r, "vcoll_all_gather", p * m)
     _no_overlap(s, r, "vcoll_all_gather")
+    _disjoint(r, "vcoll_all_gather")
     _check(_lib().vcoll_all_gather(_algo(algo), p, m, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                    _stream(s[0])), "vcoll_all_gather")
     return recv
@@ -526,6 +540,7 @@ def vcoll_all_to_all(send, splits, recv=None, src_rows=None, dst_rows=None, dst_
         if scat[i] is not None and scat[i].numel() < int(sp[:, i].sum()):
             raise ValueError(f"vcoll_all_to_all: dst_rows[{i}] is shorter than the rows rank {i} receives")
     _no_overlap(s, r, "vcoll_all_to_all")
+    _disjoint(r, "vcoll_all_to_all")
     src_tab = (ctypes.c_int64 * p)(*[t.shape[0] if t.dim() == 2 else t.numel() for t in s])
     dst_tab = (ctypes.c_int64 * p)(*[t.shape[0] if t.dim() == 2 else t.numel() for t in r])
     for idx in gath + scat:
@@ -664,6 +679,7 @@ def vcoll_moe_dispatch(tokens, slots, recv_rows, topk: int, fp8: bool = False, r
         if x.dtype != torch.int32 or x.device != dev or x.numel() < 2 * T * topk:
             raise ValueError("vcoll_moe_dispatch: slots must be int32 GPU tensors of T*topk pairs")
     _no_overlap(t, r, "vcoll_moe_dispatch")
+    _disjoint(r, "vcoll_moe_dispatch")
     rows = (ctypes.c_int64 * p)(*rr)
     _check(_lib().vcoll_moe_dispatch(p, T, topk, H, _dtype_code(t[0]), int(bool(fp8)), _ptrs(t), _ptrs(s),
                                      _ptrs(r), rows, _stream(t[0])), "vcoll_moe_dispatch")
@@ -763,6 +779,7 @@ def vcoll_moe_dispatch_fp8(tokens, splits, src_rows, recv=None):
         if g[i].dtype != torch.int32 or g[i].device != dev or g[i].numel() < int(sp[i].sum()):
             raise ValueError(f"vcoll_moe_dispatch_fp8: src_rows[{i}] must be int32 on the GPU, one per sent row")
     _no_overlap(t, r, "vcoll_moe_dispatch_fp8")
+    _disjoint(r, "vcoll_moe_dispatch_fp8")
     rows = (ctypes.c_int64 * p)(*[x.shape[0] for x in t])
     _check(_lib().vcoll_moe_dispatch_fp8(p, H, sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptrs(t), rows,
                                          _ptrs(g), _ptrs(r), _stream(t[0])), "vcoll_moe_dispatch_fp8")

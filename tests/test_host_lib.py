@@ -269,6 +269,19 @@ def test_overlap_check_allows_in_place_and_rejects_cross_overlap():
     vc._no_overlap(big[:64], big[64:], "x")                               # many disjoint buffers
 
 
+def test_outputs_must_not_overlap_each_other():
+    import torch
+    t = torch.zeros(4, 16)
+    vc._disjoint([t[r] for r in range(4)], "x")                          # rows of one tensor
+    vc._disjoint([t[0], torch.zeros(0), t[1]], "x")                      # empty buffers are ignored
+    with pytest.raises(ValueError, match="output buffers overlap"):
+        vc._disjoint([t[0], t[1], t[0]], "x")                             # one buffer twice
+    flat = torch.zeros(64)
+    with pytest.raises(ValueError, match="output buffers overlap"):
+        vc._disjoint([flat[0:16], flat[32:48], flat[15:20]], "x")         # one element shared
+    vc._disjoint([flat[0:16], flat[16:32]], "x")                          # adjacent, not shared
+
+
 def test_widened_entry_points_validate_before_launching():
     """Every error below is returned before anything is enqueued (no GPU here)."""
     lib = _lib()
