@@ -130,6 +130,29 @@ __global__ __launch_bounds__(BS) void all_to_all_kernel(const A2AArgs a) {
   const A2ABlock& B = a.b[lo];
   const int r0 = (t - B.tile_start) * a.rows_per_tile;
   const int tid = threadIdx.x;
+  if (a.vec && !B.src_idx && !B.dst_idx) {
+    // rows contiguous on both sides: the tile's rows are one run of bytes,
+    // copied with every load of a round in flight before its stores
+    const int k1 = r0 + a.rows_per_tile < B.rows ? r0 + a.rows_per_tile : B.rows;
+    const char* src = B.src + static_cast<int64_t>(r0) * a.row_bytes;
+    char* dst = B.dst + static_cast<int64_t>(r0) * a.row_bytes;
+    const int64_t nvec = static_cast<int64_t>(k1 - r0) * a.row_bytes / 16;
+    constexpr int U = 8;
+    for (int64_t x0 = tid; x0 < nvec; x0 += U * BS) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t x = x0 + u * BS;
+        v[u] = x < nvec ? ld16(src, x * 16) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t x = x0 + u * BS;
+        if (x < nvec) st16(dst, x * 16, v[u]);
+      }
+    }
+    return;
+  }
   for (int rr = 0; rr < a.rows_per_tile; ++rr) {
     const int k = r0 + rr;
     if (k >= B.rows) break;
