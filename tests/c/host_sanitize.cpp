@@ -1,0 +1,235 @@
+// The host half of libvcoll under AddressSanitizer and UndefinedBehavior-
+// Sanitizer: argument validation, schedules, ledgers, the alpha-beta model
+// and the MoE plans, with the kernel launchers replaced by stubs that record
+// each launch and return success (fake, never dereferenced device
+// addresses). Built with g++ and run by tests/test_host_sanitize.py; exits
+// non-zero on the first failed check (the sanitizers abort on their own).
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "hier.h"
+#include "move.h"
+#include "reduce.h"
+#include "schedule.h"
+#include "step.h"
+#include "vcoll.h"
+
+static long g_launches = 0;
+using vcoll::kMaxRanks;
+using vcoll::kA2ABlocks;
+
+extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
+
+namespace vcoll {
+hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype, vcoll_algo, bool, int64_t max_chunk, int chunks,
+                         hipStream_t) {
+  if (a.p < 1 || a.p > kMaxRanks || chunks < 1 || max_chunk < 0) std::abort();
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_hierarchical(const HierArgs&, vcoll_dtype, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype, hipStream_t) {
+  if (a.p < 1 || a.m < 0) std::abort();
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype, hipStream_t) {
+  if (a.q < 0 || a.q > kMaxRanks) std::abort();
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t) {
+  if (a.nblocks < 1 || a.nblocks > kA2ABlocks || tiles < 1) std::abort();
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_dispatch_fp8(const Fp8Args&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_dispatch_push(const PushArgs&, bool, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_combine_pull(const CombineArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_copy(void*, const void*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_step(const StepArgs&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
+}  // namespace vcoll
+
+#define CHECK(cond)                                                             \
+  do {                                                                          \
+    if (!(cond)) {                                                              \
+      std::fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #cond); \
+      std::exit(1);                                                             \
+    }                                                                           \
+  } while (0)
+
+static void* fake(int r) { return reinterpret_cast<void*>(uintptr_t(0x10000000) + uintptr_t(r) * 0x1000000); }
+
+static void ledgers(std::mt19937_64& rng) {
+  const int ps[] = {1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16, 17, 24, 31, 32, 33, 64, 72, 100, 127, 128};
+  const vcoll_algo algos[] = {VCOLL_RING, VCOLL_RECURSIVE_DOUBLING, VCOLL_RABENSEIFNER, VCOLL_BINARY_TREE};
+  for (int p : ps) {
+    const int64_t ns[] = {0, 1, p - 1 > 0 ? p - 1 : 1, p, p + 1, 1000, int64_t(1) << 20};
+    for (int64_t n : ns)
+      for (vcoll_op op : {VCOLL_OP_ALLREDUCE, VCOLL_OP_REDUCE_SCATTER, VCOLL_OP_ALL_GATHER})
+        for (vcoll_algo algo : algos) {
+          int64_t count = -1;
+          vcoll_status st = vcoll_ledger(op, algo, p, n, VCOLL_F32, nullptr, 0, nullptr, 0, &count, nullptr, nullptr,
+                                         nullptr);
+          if (st == VCOLL_ERR_UNSUPPORTED) continue;
+          CHECK(st == VCOLL_OK && count >= 0);
+          std::vector<vcoll_msg> msgs(count + 1);
+          std::vector<int64_t> sent(p), got(p);
+          int32_t steps = -1;
+          if (count > 0) {
+            CHECK(vcoll_ledger(op, algo, p, n, VCOLL_F32, nullptr, 0, msgs.data(), count - 1, &count, nullptr,
+                               nullptr, nullptr) == VCOLL_ERR_BUFFER_TOO_SMALL);
+          }
+          CHECK(vcoll_ledger(op, algo, p, n, VCOLL_BF16, nullptr, 0, msgs.data(), count, &count, sent.data(),
+                             got.data(), &steps) == VCOLL_OK);
+          int64_t s = 0, g = 0;
+          for (int r = 0; r < p; ++r) {
+            s += sent[r];
+            g += got[r];
+          }
+          CHECK(s == g && steps >= 0);
+          if (op == VCOLL_OP_ALLREDUCE && (algo == VCOLL_RING || algo == VCOLL_RABENSEIFNER) && n % p == 0 &&
+              (p & (p - 1)) == 0)
+            for (int r = 0; r < p; ++r) CHECK(sent[r] == 2 * (p - 1) * (n / p) * 2);
+        }
+    // all-to-all with random splits
+    std::vector<int64_t> splits(size_t(p) * p);
+    for (auto& v : splits) v = int64_t(rng() % 5);
+    int64_t count = 0;
+    CHECK(vcoll_ledger(VCOLL_OP_ALL_TO_ALL, VCOLL_RING, p, 0, VCOLL_BF16, splits.data(), 33, nullptr, 0, &count,
+                       nullptr, nullptr, nullptr) == VCOLL_OK);
+    std::vector<vcoll_msg> msgs(count + 1);
+    CHECK(vcoll_ledger(VCOLL_OP_ALL_TO_ALL, VCOLL_RING, p, 0, VCOLL_BF16, splits.data(), 33, msgs.data(), count,
+                       &count, nullptr, nullptr, nullptr) == VCOLL_OK);
+  }
+  // hierarchical and rooted ledgers
+  const int shapes[][2] = {{1, 1}, {2, 4}, {4, 2}, {2, 8}, {4, 4}, {3, 5}, {8, 8}, {16, 8}};
+  for (const auto& sh : shapes)
+    for (int64_t n : {int64_t(0), int64_t(7), int64_t(4096), int64_t(1000003)}) {
+      int64_t count = 0;
+      int32_t steps = 0;
+      CHECK(vcoll_ledger_hierarchical(sh[0], sh[1], n, VCOLL_F32, nullptr, 0, &count, nullptr, nullptr, &steps) ==
+            VCOLL_OK);
+      std::vector<vcoll_msg> msgs(count + 1);
+      CHECK(vcoll_ledger_hierarchical(sh[0], sh[1], n, VCOLL_BF16, msgs.data(), count, &count, nullptr, nullptr,
+                                      &steps) == VCOLL_OK);
+    }
+  for (int p : {1, 2, 3, 8, 13, 72, 128})
+    for (int root : {0, p / 2, p - 1})
+      for (vcoll_algo algo : {VCOLL_BINARY_TREE, VCOLL_NAIVE, VCOLL_SCATTER_ALLGATHER, VCOLL_PIPELINED_CHAIN})
+        for (int64_t blocks : {int64_t(1), int64_t(3), int64_t(64)}) {
+          int64_t count = 0;
+          const vcoll_status st = vcoll_ledger_rooted(VCOLL_OP_BROADCAST, algo, p, 100003, VCOLL_F32, root, blocks,
+                                                      nullptr, 0, &count, nullptr, nullptr, nullptr);
+          if (st != VCOLL_OK) continue;
+          std::vector<vcoll_msg> msgs(count + 1);
+          std::vector<int64_t> sent(p), got(p);
+          CHECK(vcoll_ledger_rooted(VCOLL_OP_BROADCAST, algo, p, 100003, VCOLL_F32, root, blocks, msgs.data(), count,
+                                    &count, sent.data(), got.data(), nullptr) == VCOLL_OK);
+          double t = 0;
+          CHECK(vcoll_model_clock(msgs.data(), count, p, p, 2e-6, 450e9, 2e-6, 450e9, &t) == VCOLL_OK && t >= 0);
+        }
+}
+
+static void model() {
+  for (vcoll_algo algo : {VCOLL_RING, VCOLL_RECURSIVE_DOUBLING, VCOLL_RABENSEIFNER, VCOLL_BINARY_TREE})
+    for (int p : {1, 2, 5, 8, 16, 72, 128}) {
+      double t = -1;
+      CHECK(vcoll_model_formula(algo, p, 1e6, 2e-6, 450e9, &t) == VCOLL_OK && t >= 0);
+      int32_t steps = 0;
+      CHECK(vcoll_model_ledger_time(VCOLL_OP_ALLREDUCE, algo, p, 4096, VCOLL_F32, nullptr, 0, 2e-6, 450e9, &t,
+                                    &steps) == VCOLL_OK);
+    }
+  double blocks = 0, t = 0;
+  CHECK(vcoll_model_chain_optimum(8, 1e8, 2e-6, 450e9, &blocks, &t) == VCOLL_OK && blocks >= 1);
+}
+
+static void moe(std::mt19937_64& rng) {
+  const int p = 8, tokens = 512, topk = 8, epr = 32;
+  std::vector<int32_t> ids(size_t(p) * tokens * topk);
+  for (int i = 0; i < p; ++i)
+    for (int t = 0; t < tokens; ++t) {
+      std::vector<int> chosen;
+      while (int(chosen.size()) < topk) {
+        const int e = int(rng() % (p * epr));
+        bool dup = false;
+        for (int c : chosen) dup = dup || c == e;
+        if (!dup) chosen.push_back(e);
+      }
+      for (int k = 0; k < topk; ++k) ids[(size_t(i) * tokens + t) * topk + k] = chosen[k];
+    }
+  std::vector<int64_t> splits(p * p);
+  std::vector<int32_t> src(size_t(p) * tokens * topk), dst(size_t(p) * tokens * topk);
+  CHECK(vcoll_moe_plan(p, tokens, topk, epr, ids.data(), splits.data(), src.data(), dst.data()) == VCOLL_OK);
+  int64_t total = 0;
+  for (auto v : splits) total += v;
+  CHECK(total == int64_t(p) * tokens * topk);
+  std::vector<int32_t> slots(size_t(p) * tokens * topk * 2);
+  CHECK(vcoll_moe_slots(p, tokens, topk, splits.data(), dst.data(), slots.data()) == VCOLL_OK);
+  std::vector<int64_t> su(p * p);
+  std::vector<int32_t> srcu(size_t(p) * tokens * topk), expand(size_t(p) * p * tokens * topk);   // [p][p*tokens*topk]
+  std::vector<int64_t> expand_count(p);
+  CHECK(vcoll_moe_plan_dedup(p, tokens, topk, epr, ids.data(), su.data(), srcu.data(), expand.data(),
+                             expand_count.data()) == VCOLL_OK);
+  ids[5] = p * epr;                                         // an expert id out of range is refused
+  CHECK(vcoll_moe_plan(p, tokens, topk, epr, ids.data(), splits.data(), src.data(), dst.data()) ==
+        VCOLL_ERR_INVALID_ARG);
+}
+
+static void launches(std::mt19937_64& rng) {
+  void* send[kMaxRanks];
+  void* recv[kMaxRanks];
+  for (int r = 0; r < kMaxRanks; ++r) {
+    send[r] = fake(r);
+    recv[r] = fake(r + kMaxRanks);
+  }
+  const vcoll_algo algos[] = {VCOLL_RING, VCOLL_RECURSIVE_DOUBLING, VCOLL_RABENSEIFNER, VCOLL_BINARY_TREE};
+  for (int p : {1, 2, 3, 8, 16, 24, 72, 128})
+    for (int64_t n : {int64_t(1), int64_t(1000), int64_t(6553600)})
+      for (vcoll_algo algo : algos) {
+        CHECK(vcoll_allreduce(algo, p, n, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+        const vcoll_status rs = vcoll_reduce_scatter(algo, p, n, VCOLL_BF16, send, recv, nullptr);
+        CHECK(rs == VCOLL_OK || rs == VCOLL_ERR_UNSUPPORTED);
+        const vcoll_status ag = vcoll_all_gather(algo, p, n, VCOLL_F32, send, recv, nullptr);
+        CHECK(ag == VCOLL_OK || ag == VCOLL_ERR_UNSUPPORTED);
+      }
+  for (int p : {1, 4, 72, 128}) {
+    CHECK(vcoll_broadcast(p, 12345, VCOLL_F32, p - 1, send[0], recv, nullptr) == VCOLL_OK);
+    CHECK(vcoll_reduce(VCOLL_BINARY_TREE, p, 12345, VCOLL_BF16, p / 2, send, recv[0], nullptr) == VCOLL_OK);
+    std::vector<int64_t> splits(size_t(p) * p);
+    for (auto& v : splits) v = int64_t(rng() % 7);
+    CHECK(vcoll_all_to_all(p, 7168, VCOLL_BF16, splits.data(), send, recv, nullptr, nullptr, nullptr, nullptr,
+                           nullptr) == VCOLL_OK);
+  }
+  for (int nodes : {2, 4})
+    CHECK(vcoll_allreduce_hierarchical(nodes, 4, 100000, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+  // error paths: nothing is launched
+  const long before = g_launches;
+  CHECK(vcoll_allreduce(VCOLL_RING, 0, 10, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+  CHECK(vcoll_allreduce(VCOLL_RING, 129, 10, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+  CHECK(vcoll_allreduce(VCOLL_RING, 4, -1, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+  CHECK(vcoll_allreduce(VCOLL_RING, 4, 10, VCOLL_F32, nullptr, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+  CHECK(vcoll_allreduce(VCOLL_RING, 4, int64_t(1) << 50, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+  CHECK(vcoll_reduce_scatter(VCOLL_RECURSIVE_DOUBLING, 4, 10, VCOLL_F32, send, recv, nullptr) ==
+        VCOLL_ERR_UNSUPPORTED);
+  CHECK(vcoll_reduce_scatter(VCOLL_RABENSEIFNER, 6, 10, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_UNSUPPORTED);
+  std::vector<int64_t> bad = {1, -1, 0, 2};
+  CHECK(vcoll_all_to_all(2, 16, VCOLL_F32, bad.data(), send, recv, nullptr, nullptr, nullptr, nullptr, nullptr) ==
+        VCOLL_ERR_INVALID_ARG);
+  CHECK(g_launches == before);
+}
+
+int main() {
+  std::mt19937_64 rng(7);
+  ledgers(rng);
+  model();
+  moe(rng);
+  launches(rng);
+  CHECK(g_launches > 0);
+  std::printf("OK %ld launches recorded\n", g_launches);
+  return 0;
+}
