@@ -9,6 +9,8 @@ has not been built this module raises on import.
 Rank buffers are given either as one 2-D tensor [p, n] (row r is rank r) or
 as a sequence of p 1-D tensors, all on the same GPU, contiguous, same dtype
 (torch.float32 or torch.bfloat16).
+
+Environment: VCOLL_DEBUG=1 synchronizes after every call (see _check).
 """
 from __future__ import annotations
 
@@ -136,9 +138,22 @@ def _lib():
 _lib()
 
 
+# VCOLL_DEBUG=1: wait for the device after every successful call, so that a
+# fault in a kernel surfaces at the call that launched it rather than at a
+# later synchronization (slow; for debugging only)
+_DEBUG = os.environ.get("VCOLL_DEBUG", "") not in ("", "0")
+
+
 def _check(status: int, what: str) -> None:
     if status != 0:
         raise VcollError(status, what)
+    if _DEBUG:
+        import torch
+        if torch.cuda.is_initialized():
+            try:
+                torch.cuda.synchronize()
+            except RuntimeError as e:
+                raise RuntimeError(f"{what}: the device reported an error after this call: {e}") from e
 
 
 def _algo(algo) -> int:

@@ -282,6 +282,18 @@ def test_outputs_must_not_overlap_each_other():
     vc._disjoint([flat[0:16], flat[16:32]], "x")                          # adjacent, not shared
 
 
+def test_debug_flag_is_read_from_the_environment():
+    """VCOLL_DEBUG=1 turns on a device synchronization after every call; a
+    host-only call in a process that never touched the GPU must still work."""
+    import subprocess
+    import sys
+    code = ("import collective_communication_algorithms_vcoll_amd as vc; assert vc._DEBUG; "
+            "assert vc.vcoll_chunk(4, 10, 1) == (3, 3); print('ok')")
+    env = dict(os.environ, VCOLL_DEBUG="1", PYTHONPATH=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stderr[-2000:]
+
+
 def test_widened_entry_points_validate_before_launching():
     """Every error below is returned before anything is enqueued (no GPU here)."""
     lib = _lib()
