@@ -757,6 +757,30 @@ def summarize_sweep(jsonl: str, command: str) -> int:
                     cells.append(f"{r[0]['GBps']:.0f}")
             lines.append(f"| {p} | " + " | ".join(cells) + " |")
         lines.append("")
+    # the virtual cluster read through the pages' alpha-beta model (T = alpha
+    # + bytes / beta, half-performance length n_1/2 = alpha * beta): alpha is
+    # the fastest point moving under 1 MiB in all (the launch floor), beta the
+    # least-squares slope over the points moving at least 512 MiB (out of the
+    # Infinity Cache); bytes are the algorithmic 2*p*S
+    import numpy as np
+    lines += ["## alpha-beta reading", "",
+              "T = alpha + 2pS / beta: alpha = fastest point moving < 1 MiB in all (launch floor), beta = "
+              "least-squares slope of time against 2pS over the points moving >= 512 MiB; "
+              "n_1/2 = alpha * beta, the per-call bytes at which half of beta is reached.", "",
+              "| algorithm | p | alpha (us) | beta (TB/s) | n_1/2 (MiB moved) |", "|---|---|---|---|---|"]
+    for algo in ("ring", "rd", "rabenseifner", "tree"):
+        for p in sorted({r["p"] for r in recs}):
+            pts = [r for r in recs if r["p"] == p and r["algo"] == algo]
+            small = [r["us"] for r in pts if 2 * p * r["bytes_per_rank"] < 2 ** 20]
+            big = [(2 * p * r["bytes_per_rank"], r["us"]) for r in pts if 2 * p * r["bytes_per_rank"] >= 2 ** 29]
+            if not small or len(big) < 2:
+                continue
+            alpha = min(small)
+            slope = float(np.polyfit([b for b, _ in big], [t for _, t in big], 1)[0])      # us per byte
+            beta = 1e6 / slope                                                             # bytes per second
+            lines.append(f"| {algo} | {p} | {alpha:.1f} | {beta / 1e12:.2f} | "
+                         f"{alpha * 1e-6 * beta / 2 ** 20:.0f} |")
+    lines.append("")
     with open(os.path.join(ROOT, "profiles", "reduce_kernel_sweep_p2-72_1KiB-1GiB.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
