@@ -416,10 +416,19 @@ def extras(vc, torch, h, args):
     d2 = lambda: vc.vcoll_moe_expand(ru, exp_g, ex_out)                           # noqa: E731
     _, ms_u = time_launches([d1], 10, 2)
     _, ms_x = time_launches([d2], 10, 2)
+    # token-major expansion: each received unique row read once, pushed to its copies
+    xslots = [torch.from_numpy(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)).cuda()
+              for j in range(p8)]
+    xcounts = [len(e) for e in expand]
+    ex_tm = vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K)
+    tm_x_ok = all(torch.equal(ex_tm[j].view(torch.int16), ex_out[j].view(torch.int16)) for j in range(p8))
+    d3 = lambda: vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K, out=ex_tm)  # noqa: E731
+    _, ms_xt = time_launches([d3], 10, 2)
     offrank = lambda sp: int(sp.sum() - np.trace(sp))                              # noqa: E731
     ex["moe_dispatch_dedup"] = {
         "rows": rows_u, "rows_plain": rows, "offrank_rows": offrank(su), "offrank_rows_plain": offrank(splits),
         "all_to_all_us": round(ms_u * 1e3, 1), "expand_us": round(ms_x * 1e3, 1),
+        "expand_token_major_us": round(ms_xt * 1e3, 1), "expand_token_major_equal": bool(tm_x_ok),
         "message_bytes_bf16": offrank(su) * rb, "message_bytes_fp8": offrank(su) * orb,
         "message_bytes_plain_bf16": offrank(splits) * rb}
 

@@ -111,6 +111,8 @@ def _lib():
         lib.vcoll_model_clock.restype = I
         lib.vcoll_moe_slots.argtypes = [I, I64, I, P(I64), P(ctypes.c_int32), P(ctypes.c_int32)]
         lib.vcoll_moe_slots.restype = I
+        lib.vcoll_moe_expand_slots.argtypes = [I64, I, P(ctypes.c_int32), I64, P(ctypes.c_int32)]
+        lib.vcoll_moe_expand_slots.restype = I
         lib.vcoll_moe_dispatch.argtypes = [I, I64, I, I64, I, I, P(VP), P(VP), P(VP), P(I64), VP]
         lib.vcoll_moe_dispatch.restype = I
         lib.vcoll_moe_combine.argtypes = [I, I64, I, I64, I, P(VP), P(I64), P(VP), P(VP), VP]
@@ -764,6 +766,44 @@ def vcoll_moe_expand(recv_unique, expand, out=None):
     p = len(recv_unique)
     counts = [int(e.numel()) for e in expand]
     return vcoll_all_to_all(recv_unique, np.diag(counts).astype(np.int64), recv=out, src_rows=expand)
+
+
+def vcoll_moe_expand_slots(unique_rows: int, expand: np.ndarray, topk: int) -> np.ndarray:
+    """Token-major form of one rank's expansion (see vcoll.h): int32
+    [unique_rows*topk, 2], the plain rows copying each unique row as (0, x)."""
+    e = np.ascontiguousarray(np.asarray(expand, dtype=np.int32))
+    slots = np.zeros((max(1, unique_rows * topk), 2), dtype=np.int32)
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    _check(_lib().vcoll_moe_expand_slots(unique_rows, topk, e.ctypes.data_as(i32), e.size,
+                                         slots.ctypes.data_as(i32)), "vcoll_moe_expand_slots")
+    return slots[:unique_rows * topk]
+
+
+def vcoll_moe_expand_token_major(recv_unique, slots, counts, topk: int, out=None):
+    """The expansion of vcoll_moe_expand, reading each unique row once:
+    rank j's received unique rows are the token table of a one-rank
+    vcoll_moe_dispatch whose slots come from vcoll_moe_expand_slots (int32
+    GPU tensors [unique_rows*topk, 2]); counts[j] plain rows are written.
+    Equal to vcoll_moe_expand bit for bit."""
+    import torch
+    u = list(recv_unique)
+    p = len(u)
+    if out is None:
+        out = [torch.empty((int(counts[j]), u[j].shape[1]), dtype=u[j].dtype, device=u[j].device) for j in range(p)]
+    _disjoint(list(out), "vcoll_moe_expand_token_major")
+
+    def words(t):
+        # byte rows (FP8 payloads) move as 2-byte words: the copy is bitwise
+        if t.dtype != torch.uint8:
+            return t
+        if t.dim() != 2 or t.shape[1] % 2:
+            raise ValueError("vcoll_moe_expand_token_major: byte rows must be [rows, even width]")
+        return t.view(torch.bfloat16)
+    for j in range(p):
+        if u[j].shape[0] == 0 or int(counts[j]) == 0:
+            continue
+        vcoll_moe_dispatch([words(u[j])], [slots[j]], [int(counts[j])], topk, recv=[words(out[j])])
+    return out
 
 
 def vcoll_moe_dispatch_fp8(tokens, splits, src_rows, recv=None):

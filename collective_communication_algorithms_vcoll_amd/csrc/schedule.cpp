@@ -459,4 +459,18 @@ vcoll_status moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, c
   return VCOLL_OK;
 }
 
+vcoll_status moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
+                              int32_t* slots) {
+  std::fill(slots, slots + 2 * unique_rows * topk, -1);
+  std::vector<int32_t> used(static_cast<size_t>(unique_rows), 0);
+  for (int64_t x = 0; x < expand_count; ++x) {
+    const int32_t u = expand[x];
+    if (u < 0 || u >= unique_rows || used[static_cast<size_t>(u)] >= topk) return VCOLL_ERR_INVALID_ARG;
+    const int64_t k = used[static_cast<size_t>(u)]++;
+    slots[2 * (u * topk + k)] = 0;
+    slots[2 * (u * topk + k) + 1] = static_cast<int32_t>(x);
+  }
+  return VCOLL_OK;
+}
+
 }  // namespace vcoll

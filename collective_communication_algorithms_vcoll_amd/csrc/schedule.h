@@ -83,4 +83,10 @@ vcoll_status moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_ran
 vcoll_status moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
                        int32_t* slots);
 
+// Token-major form of one rank's deduplicated-dispatch expansion: for each
+// unique row u, the plain rows x with expand[x] == u as (0, x) pairs in
+// ascending x, padded with (-1, -1) to topk; see vcoll.h.
+vcoll_status moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
+                              int32_t* slots);
+
 }  // namespace vcoll

@@ -473,6 +473,14 @@ vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* spl
   return moe_slots(p, tokens, topk, splits, dst_rows, slots);
 }
 
+vcoll_status vcoll_moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
+                                    int32_t* slots) {
+  if (!valid_count(unique_rows) || topk < 1 || !valid_count(expand_count)) return VCOLL_ERR_INVALID_ARG;
+  if (unique_rows * topk > INT32_MAX || expand_count > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if ((expand_count > 0 && !expand) || (unique_rows > 0 && !slots)) return VCOLL_ERR_INVALID_ARG;
+  return moe_expand_slots(unique_rows, topk, expand, expand_count, slots);
+}
+
 vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden, vcoll_dtype dtype, int fp8,
                                 const void* const* token_tables, const int32_t* const* slots,
                                 void* const* recv, const int64_t* recv_rows, void* stream) {

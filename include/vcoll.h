@@ -218,6 +218,25 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
                                 void* const* recv, const int64_t* recv_rows, void* stream);
 
 /*
+ * Token-major form of one rank's deduplicated-dispatch expansion ([NCC] 7.4
+ * and exercise 10: a token arrives once per rank and is then copied to
+ * every (token, expert) row of that rank that needs it), for
+ * vcoll_moe_dispatch with p = 1. Host only. expand (expand_count entries)
+ * is rank j's expansion map from vcoll_moe_plan_dedup (plain row x copies
+ * unique row expand[x]); unique_rows is the number of rows rank j received
+ * in the deduplicated all-to-all. Fills slots [unique_rows*topk][2] int32:
+ * for unique row u, the plain rows copying it as (0, x) pairs in ascending
+ * x, then (-1, -1). vcoll_moe_dispatch(1, unique_rows, topk, ...) with the
+ * received unique rows as the token table and recv_rows = expand_count then
+ * writes the plain layout, reading each unique row once; the result equals
+ * the gathering expansion (vcoll_all_to_all with src_rows = expand) bit for
+ * bit. An expand entry outside [0, unique_rows), or a unique row copied
+ * more than topk times, is VCOLL_ERR_INVALID_ARG.
+ */
+vcoll_status vcoll_moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
+                                    int32_t* slots);
+
+/*
  * Token-major MoE combine ([NCC] 7.4: combine is the all-to-all that returns
  * every expert output to the rank and position of its token; 4.2: applied
  * after the dispatch it restores the original layout). For every rank i,

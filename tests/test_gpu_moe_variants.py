@@ -158,9 +158,13 @@ def test_dedup_dispatch_and_expand_equal_plain(vc):
     say("deduplicated dispatch + expansion")
     recv_u = vc.vcoll_all_to_all(toks, su, src_rows=[gpu_i32(s) for s in src_u])
     out = vc.vcoll_moe_expand(recv_u, [gpu_i32(e) for e in expand])
+    say("token-major expansion")
+    slots = [gpu_i32(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)) for j in range(p)]
+    out_tm = vc.vcoll_moe_expand_token_major(recv_u, slots, [len(e) for e in expand], K)
     sync()
     for j in range(p):
         assert torch.equal(out[j].view(torch.int16), plain[j].view(torch.int16))
+        assert torch.equal(out_tm[j].view(torch.int16), plain[j].view(torch.int16))
     assert int(su.sum()) < int(splits.sum())
 
 
@@ -177,9 +181,12 @@ def test_fp8_dedup_combination(vc):
     plain = vc.vcoll_moe_dispatch_fp8(toks, splits, [gpu_i32(s) for s in src])
     recv_u = vc.vcoll_moe_dispatch_fp8(toks, su, [gpu_i32(s) for s in src_u])
     out = vc.vcoll_moe_expand(recv_u, [gpu_i32(e) for e in expand])
+    slots = [gpu_i32(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)) for j in range(p)]
+    out_tm = vc.vcoll_moe_expand_token_major(recv_u, slots, [len(e) for e in expand], K)
     sync()
     for j in range(p):
         assert torch.equal(out[j], plain[j])
+        assert torch.equal(out_tm[j], plain[j])
 
 
 def test_fp8_full_workload_sampled_rows(vc):

@@ -217,3 +217,35 @@ def test_slots_invert_the_plan(p, T, K, E):
                 assert pair // K == int(src[i][s0 + q])    # the token it carries
                 r += 1
     assert np.all(slots[:, :, 0] >= 0)                      # every pair has a destination
+
+
+# --------------------------------------------------------------------------- token-major expansion map
+
+@pytest.mark.parametrize("p,T,K,E", [(2, 9, 2, 4), (4, 40, 3, 16), (8, 64, 8, 256), (3, 11, 2, 3)])
+def test_expand_slots_invert_the_oracle_expansion(p, T, K, E):
+    """For each rank, the token-major expansion map lists, for unique row u,
+    exactly the plain rows x whose oracle expansion entry is u, ascending,
+    padded with (-1, -1); so pushing each unique row to its slots writes the
+    same plain layout as gathering through the oracle's map."""
+    topk = small_routing(p, T, K, E, 90 + p)
+    su, _, expand = moe.plan_dedup(topk, E // p)
+    for j in range(p):
+        U = int(su[:, j].sum())
+        slots = vc.vcoll_moe_expand_slots(U, expand[j], K)
+        assert slots.shape == (U * K, 2)
+        seen = []
+        for u in range(U):
+            row = slots[u * K:(u + 1) * K]
+            xs = [int(x) for d, x in row if d >= 0]
+            assert all(d == 0 for d, _ in row[:len(xs)]) and all(d == -1 and x == -1 for d, x in row[len(xs):])
+            assert xs == sorted(xs) and all(int(expand[j][x]) == u for x in xs)
+            seen += xs
+        assert sorted(seen) == list(range(len(expand[j])))           # every plain row exactly once
+
+
+def test_expand_slots_reject_bad_maps():
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_moe_expand_slots(2, np.array([0, 2], np.int32), 4)       # unique row 2 does not exist
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_moe_expand_slots(1, np.zeros(3, np.int32), 2)            # three copies of one row, topk 2
+    assert vc.vcoll_moe_expand_slots(0, np.zeros(0, np.int32), 8).shape == (0, 2)
