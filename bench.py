@@ -424,11 +424,29 @@ def extras(vc, torch, h, args):
     tm_x_ok = all(torch.equal(ex_tm[j].view(torch.int16), ex_out[j].view(torch.int16)) for j in range(p8))
     d3 = lambda: vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K, out=ex_tm)  # noqa: E731
     _, ms_xt = time_launches([d3], 10, 2)
+    # token-major deduplicated dispatch: each token read once (and quantised
+    # once for FP8), written once per destination rank
+    dsl = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
+    dsl_g = [torch.from_numpy(np.ascontiguousarray(dsl[i])).cuda() for i in range(p8)]
+    urows = su.sum(axis=0)
+    ru_tm = vc.vcoll_moe_dispatch(toks, dsl_g, urows, K)
+    ru8 = vc.vcoll_moe_dispatch_fp8(toks, su, src_ug)
+    ru8_tm = vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, fp8=True)
+    dd_ok = all(torch.equal(ru_tm[j].view(torch.int16), ru[j].view(torch.int16)) and torch.equal(ru8_tm[j], ru8[j])
+                for j in range(p8))
+    d4 = lambda: vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, recv=ru_tm)            # noqa: E731
+    d5 = lambda: vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, fp8=True, recv=ru8_tm)  # noqa: E731
+    d6 = lambda: vc.vcoll_moe_dispatch_fp8(toks, su, src_ug, ru8)                    # noqa: E731
+    _, ms_dt = time_launches([d4], 10, 2)
+    _, ms_d8t = time_launches([d5], 10, 2)
+    _, ms_d8 = time_launches([d6], 10, 2)
     offrank = lambda sp: int(sp.sum() - np.trace(sp))                              # noqa: E731
     ex["moe_dispatch_dedup"] = {
         "rows": rows_u, "rows_plain": rows, "offrank_rows": offrank(su), "offrank_rows_plain": offrank(splits),
         "all_to_all_us": round(ms_u * 1e3, 1), "expand_us": round(ms_x * 1e3, 1),
         "expand_token_major_us": round(ms_xt * 1e3, 1), "expand_token_major_equal": bool(tm_x_ok),
+        "all_to_all_token_major_us": round(ms_dt * 1e3, 1), "fp8_row_major_us": round(ms_d8 * 1e3, 1),
+        "fp8_token_major_us": round(ms_d8t * 1e3, 1), "token_major_equal": bool(dd_ok),
         "message_bytes_bf16": offrank(su) * rb, "message_bytes_fp8": offrank(su) * orb,
         "message_bytes_plain_bf16": offrank(splits) * rb}
 

@@ -113,6 +113,8 @@ def _lib():
         lib.vcoll_moe_slots.restype = I
         lib.vcoll_moe_expand_slots.argtypes = [I64, I, P(ctypes.c_int32), I64, P(ctypes.c_int32)]
         lib.vcoll_moe_expand_slots.restype = I
+        lib.vcoll_moe_dedup_slots.argtypes = [I, I64, I, P(I64), P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.vcoll_moe_dedup_slots.restype = I
         lib.vcoll_moe_dispatch.argtypes = [I, I64, I, I64, I, I, P(VP), P(VP), P(VP), P(I64), VP]
         lib.vcoll_moe_dispatch.restype = I
         lib.vcoll_moe_combine.argtypes = [I, I64, I, I64, I, P(VP), P(I64), P(VP), P(VP), VP]
@@ -766,6 +768,25 @@ def vcoll_moe_expand(recv_unique, expand, out=None):
     p = len(recv_unique)
     counts = [int(e.numel()) for e in expand]
     return vcoll_all_to_all(recv_unique, np.diag(counts).astype(np.int64), recv=out, src_rows=expand)
+
+
+def vcoll_moe_dedup_slots(splits_unique, src_unique, tokens: int, topk: int) -> np.ndarray:
+    """Token-major form of a deduplicated plan (see vcoll.h): int32
+    [p, tokens*topk, 2] for vcoll_moe_dispatch. src_unique: the p arrays of
+    vcoll_moe_plan_dedup (each rank's sent rows' tokens)."""
+    su = np.ascontiguousarray(np.asarray(splits_unique, dtype=np.int64))
+    p = su.shape[0]
+    src = np.zeros((p, tokens * topk), dtype=np.int32)
+    for i in range(p):
+        a = np.asarray(src_unique[i], dtype=np.int32)
+        if a.size > tokens * topk:
+            raise ValueError("vcoll_moe_dedup_slots: more sent rows than tokens*topk")
+        src[i, :a.size] = a
+    slots = np.zeros((p, max(1, tokens * topk), 2), dtype=np.int32)
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    _check(_lib().vcoll_moe_dedup_slots(p, tokens, topk, su.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                        src.ctypes.data_as(i32), slots.ctypes.data_as(i32)), "vcoll_moe_dedup_slots")
+    return slots[:, :tokens * topk]
 
 
 def vcoll_moe_expand_slots(unique_rows: int, expand: np.ndarray, topk: int) -> np.ndarray:

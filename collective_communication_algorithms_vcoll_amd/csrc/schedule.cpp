@@ -473,4 +473,26 @@ vcoll_status moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expa
   return VCOLL_OK;
 }
 
+vcoll_status moe_dedup_slots(int p, int64_t tokens, int width, const int64_t* splits_unique,
+                             const int32_t* src_unique, int32_t* slots) {
+  std::vector<int64_t> so, ro;
+  block_offsets(p, splits_unique, so, ro);
+  std::vector<int32_t> used(static_cast<size_t>(tokens));
+  for (int i = 0; i < p; ++i) {
+    int32_t* out = slots + 2 * static_cast<int64_t>(i) * tokens * width;
+    std::fill(out, out + 2 * tokens * width, -1);
+    std::fill(used.begin(), used.end(), 0);
+    int64_t pos = 0;
+    for (int j = 0; j < p; ++j)
+      for (int64_t q = 0; q < splits_unique[static_cast<size_t>(i) * p + j]; ++q, ++pos) {
+        const int32_t t = src_unique[static_cast<int64_t>(i) * tokens * width + pos];
+        if (t < 0 || t >= tokens || used[static_cast<size_t>(t)] >= width) return VCOLL_ERR_INVALID_ARG;
+        const int64_t k = used[static_cast<size_t>(t)]++;
+        out[2 * (t * width + k)] = j;
+        out[2 * (t * width + k) + 1] = static_cast<int32_t>(ro[static_cast<size_t>(i) * p + j] + q);
+      }
+  }
+  return VCOLL_OK;
+}
+
 }  // namespace vcoll

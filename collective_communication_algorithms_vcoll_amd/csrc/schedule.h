@@ -89,4 +89,11 @@ vcoll_status moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, c
 vcoll_status moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
                               int32_t* slots);
 
+// Token-major form of a deduplicated dispatch plan: for rank i's token t,
+// the (destination rank, row of its deduplicated receive buffer) of each
+// copy, in ascending destination order, padded with (-1, -1) to `width`;
+// see vcoll.h.
+vcoll_status moe_dedup_slots(int p, int64_t tokens, int width, const int64_t* splits_unique,
+                             const int32_t* src_unique, int32_t* slots);
+
 }  // namespace vcoll

@@ -473,6 +473,23 @@ vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* spl
   return moe_slots(p, tokens, topk, splits, dst_rows, slots);
 }
 
+vcoll_status vcoll_moe_dedup_slots(int p, int64_t tokens, int topk, const int64_t* splits_unique,
+                                   const int32_t* src_unique, int32_t* slots) {
+  if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !splits_unique) return VCOLL_ERR_INVALID_ARG;
+  if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (tokens > 0 && (!src_unique || !slots)) return VCOLL_ERR_INVALID_ARG;
+  for (int i = 0; i < p; ++i) {
+    int64_t sent = 0;
+    for (int j = 0; j < p; ++j) {
+      const int64_t v = splits_unique[static_cast<size_t>(i) * p + j];
+      if (v < 0) return VCOLL_ERR_INVALID_ARG;
+      sent += v;
+    }
+    if (sent > tokens * topk) return VCOLL_ERR_INVALID_ARG;      // src_unique holds tokens*topk entries per rank
+  }
+  return moe_dedup_slots(p, tokens, topk, splits_unique, src_unique, slots);
+}
+
 vcoll_status vcoll_moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
                                     int32_t* slots) {
   if (!valid_count(unique_rows) || topk < 1 || !valid_count(expand_count)) return VCOLL_ERR_INVALID_ARG;

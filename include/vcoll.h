@@ -218,6 +218,23 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
                                 void* const* recv, const int64_t* recv_rows, void* stream);
 
 /*
+ * Token-major form of a deduplicated dispatch plan ([NCC] 7.4 and exercise
+ * 10), for vcoll_moe_dispatch. Host only. From splits_unique [p*p] and
+ * src_unique [p][tokens*topk] of vcoll_moe_plan_dedup it fills slots
+ * [p][tokens*topk][2] int32: for rank i's token t, the destination ranks it
+ * is sent to, ascending, each with the row of that rank's deduplicated
+ * receive buffer it lands in, then (-1, -1). vcoll_moe_dispatch with these
+ * slots (recv_rows[j] = sum_i splits_unique[i][j]) reads each token once
+ * and writes the receive buffers of the deduplicated all-to-all
+ * (vcoll_all_to_all(splits_unique, src_rows = src_unique)) bit for bit, or,
+ * with fp8, those of vcoll_moe_dispatch_fp8 over the same plan. A token id
+ * outside [0, tokens), or more than topk copies of one token, is
+ * VCOLL_ERR_INVALID_ARG.
+ */
+vcoll_status vcoll_moe_dedup_slots(int p, int64_t tokens, int topk, const int64_t* splits_unique,
+                                   const int32_t* src_unique, int32_t* slots);
+
+/*
  * Token-major form of one rank's deduplicated-dispatch expansion ([NCC] 7.4
  * and exercise 10: a token arrives once per rank and is then copied to
  * every (token, expert) row of that rank that needs it), for

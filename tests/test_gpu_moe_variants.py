@@ -161,10 +161,14 @@ def test_dedup_dispatch_and_expand_equal_plain(vc):
     say("token-major expansion")
     slots = [gpu_i32(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)) for j in range(p)]
     out_tm = vc.vcoll_moe_expand_token_major(recv_u, slots, [len(e) for e in expand], K)
+    say("token-major deduplicated dispatch")
+    dslots = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
+    recv_tm = vc.vcoll_moe_dispatch(toks, [gpu_i32(dslots[i]) for i in range(p)], su.sum(axis=0), K)
     sync()
     for j in range(p):
         assert torch.equal(out[j].view(torch.int16), plain[j].view(torch.int16))
         assert torch.equal(out_tm[j].view(torch.int16), plain[j].view(torch.int16))
+        assert torch.equal(recv_tm[j].view(torch.int16), recv_u[j].view(torch.int16))
     assert int(su.sum()) < int(splits.sum())
 
 
@@ -183,10 +187,13 @@ def test_fp8_dedup_combination(vc):
     out = vc.vcoll_moe_expand(recv_u, [gpu_i32(e) for e in expand])
     slots = [gpu_i32(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)) for j in range(p)]
     out_tm = vc.vcoll_moe_expand_token_major(recv_u, slots, [len(e) for e in expand], K)
+    dslots = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
+    recv_tm = vc.vcoll_moe_dispatch(toks, [gpu_i32(dslots[i]) for i in range(p)], su.sum(axis=0), K, fp8=True)
     sync()
     for j in range(p):
         assert torch.equal(out[j], plain[j])
         assert torch.equal(out_tm[j], plain[j])
+        assert torch.equal(recv_tm[j], recv_u[j])                   # FP8 quantised once per token
 
 
 def test_fp8_full_workload_sampled_rows(vc):

@@ -249,3 +249,37 @@ def test_expand_slots_reject_bad_maps():
     with pytest.raises(vc.VcollError):
         vc.vcoll_moe_expand_slots(1, np.zeros(3, np.int32), 2)            # three copies of one row, topk 2
     assert vc.vcoll_moe_expand_slots(0, np.zeros(0, np.int32), 8).shape == (0, 2)
+
+
+@pytest.mark.parametrize("p,T,K,E", [(2, 9, 2, 4), (4, 40, 3, 16), (8, 64, 8, 256), (3, 11, 2, 3)])
+def test_dedup_slots_invert_the_oracle_plan(p, T, K, E):
+    """The token-major form of the deduplicated plan sends token t of rank i
+    to each rank holding one of its experts, ascending, at the row where the
+    oracle's deduplicated all-to-all puts it (blocks by source rank, tokens
+    in order), and nowhere else."""
+    topk = small_routing(p, T, K, E, 110 + p)
+    su, src_u, _ = moe.plan_dedup(topk, E // p)
+    slots = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
+    assert slots.shape == (p, T * K, 2)
+    for i in range(p):
+        where = {}
+        pos = 0
+        for j in range(p):
+            r0 = int(su[:i, j].sum())
+            for q in range(int(su[i, j])):
+                where[(int(src_u[i][pos]), j)] = r0 + q
+                pos += 1
+        for t in range(T):
+            dests = sorted({int(e) // (E // p) for e in topk[i][t]})
+            row = slots[i, t * K:(t + 1) * K].tolist()
+            assert row[:len(dests)] == [[j, where[(t, j)]] for j in dests]
+            assert row[len(dests):] == [[-1, -1]] * (K - len(dests))
+
+
+def test_dedup_slots_reject_bad_plans():
+    su = np.array([[2, 0], [0, 0]], np.int64)
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_moe_dedup_slots(su, [np.array([0, 5], np.int32), np.zeros(0, np.int32)], 3, 2)   # token 5 of 3
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_moe_dedup_slots(np.array([[3, 0], [0, 0]], np.int64),
+                                 [np.array([1, 1, 1], np.int32), np.zeros(0, np.int32)], 2, 2)      # 3 copies, topk 2
