@@ -487,6 +487,11 @@ vcoll_status vcoll_moe_dedup_slots(int p, int64_t tokens, int topk, const int64_
     }
     if (sent > tokens * topk) return VCOLL_ERR_INVALID_ARG;      // src_unique holds tokens*topk entries per rank
   }
+  for (int j = 0; j < p; ++j) {                                  // receive rows are int32 in the slots
+    int64_t got = 0;
+    for (int i = 0; i < p; ++i) got += splits_unique[static_cast<size_t>(i) * p + j];
+    if (got > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  }
   return moe_dedup_slots(p, tokens, topk, splits_unique, src_unique, slots);
 }
 

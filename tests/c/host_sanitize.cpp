@@ -175,6 +175,19 @@ static void moe(std::mt19937_64& rng) {
   std::vector<int64_t> expand_count(p);
   CHECK(vcoll_moe_plan_dedup(p, tokens, topk, epr, ids.data(), su.data(), srcu.data(), expand.data(),
                              expand_count.data()) == VCOLL_OK);
+  // token-major forms of the deduplicated plan: send slots and per-rank expansion slots
+  std::vector<int32_t> dslots(size_t(p) * tokens * topk * 2);
+  CHECK(vcoll_moe_dedup_slots(p, tokens, topk, su.data(), srcu.data(), dslots.data()) == VCOLL_OK);
+  const int64_t cap = int64_t(p) * tokens * topk;
+  for (int j = 0; j < p; ++j) {
+    int64_t unique_rows = 0;
+    for (int i = 0; i < p; ++i) unique_rows += su[size_t(i) * p + j];
+    std::vector<int32_t> xs(size_t(unique_rows) * topk * 2 + 2);
+    CHECK(vcoll_moe_expand_slots(unique_rows, topk, expand.data() + j * cap, expand_count[j], xs.data()) == VCOLL_OK);
+    if (unique_rows > 0)                                    // one unique row too few: an entry out of range
+      CHECK(vcoll_moe_expand_slots(unique_rows - 1, topk, expand.data() + j * cap, expand_count[j], xs.data()) ==
+            VCOLL_ERR_INVALID_ARG || expand_count[j] == 0);
+  }
   ids[5] = p * epr;                                         // an expert id out of range is refused
   CHECK(vcoll_moe_plan(p, tokens, topk, epr, ids.data(), splits.data(), src.data(), dst.data()) ==
         VCOLL_ERR_INVALID_ARG);
