@@ -585,7 +585,7 @@ TRAFFIC_SET = {
     "all_to_all_kernel<256>": ("variable-split all-to-all of the MoE splits (plain)", None),
     "dispatch_push_kernel<false, 256>": ("token-major MoE dispatch, bf16", None),
     "dispatch_push_kernel<true, 512>": ("token-major MoE dispatch, FP8", None),
-    "combine_pull_kernel<256>": ("token-major MoE combine", None),
+    "combine_pull_kernel<512>": ("token-major MoE combine", None),
     "dispatch_fp8_kernel": ("row-major FP8 dispatch (gather + quantise)", None),
     "copy_kernel": ("plain copy, 200 MiB read + 200 MiB written (counter scale)", 419_430_400),
 }
@@ -652,7 +652,7 @@ def traffic_set(vc, torch, launches: int) -> int:
     out["all_to_all_kernel<256>"] = 2 * rows * rb
     out["dispatch_push_kernel<false, 256>"] = p8 * T * rb + rows * rb
     out["dispatch_push_kernel<true, 512>"] = p8 * T * rb + rows * orb
-    out["combine_pull_kernel<256>"] = 2 * rows * rb
+    out["combine_pull_kernel<512>"] = 2 * rows * rb
     out["dispatch_fp8_kernel"] = rows * rb + rows * orb
     print(json.dumps({"moe_algorithmic_bytes": out}), flush=True)
     return 0

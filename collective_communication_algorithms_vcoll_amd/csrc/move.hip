@@ -523,7 +523,10 @@ hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream)
 hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream) {
   const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
   if (tiles == 0) return hipSuccess;
-  return launch(combine_pull_kernel<kBlock>, dim3(static_cast<unsigned>(tiles), a.p), kBlock, a, stream);
+  // 512 threads per token's output rows: 2% faster than 256 on the MoE
+  // workload (1024: 1% slower)
+  constexpr int kPullBlock = 512;
+  return launch(combine_pull_kernel<kPullBlock>, dim3(static_cast<unsigned>(tiles), a.p), kPullBlock, a, stream);
 }
 
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {
