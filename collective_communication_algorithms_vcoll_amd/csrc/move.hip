@@ -531,6 +531,13 @@ hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream) {
 
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
+  // a launch whose blocks all copy contiguous rows (no gather or scatter
+  // index) runs the run-of-bytes path in 1024-thread workgroups, fewer of
+  // them resident per CU: 3% faster on the MoE splits, where the indexed
+  // forms lost 5-11% with them and keep 256
+  bool flat = a.vec != 0;
+  for (int k = 0; flat && k < a.nblocks; ++k) flat = !a.b[k].src_idx && !a.b[k].dst_idx;
+  if (flat) return launch(all_to_all_kernel<1024>, dim3(static_cast<unsigned>(tiles)), 1024, a, stream);
   return launch(all_to_all_kernel<kBlock>, dim3(static_cast<unsigned>(tiles)), kBlock, a, stream);
 }
 
