@@ -582,7 +582,7 @@ TRAFFIC_SET = {
     "reduce_kernel<1, 0, 16, 1, false, true, 64>": ("fused ring all-reduce, p=16 x 192 MiB bf16", 6_442_450_944),
     "reduce_kernel<1, 0, 16, 1, true, false, 64>": ("ring reduce-scatter, p=16 x 192 MiB bf16", 3_422_552_064),
     "all_gather_kernel<2, 1, 64, false>": ("all-gather of 12 MiB bf16 blocks, p=16", 3_422_552_064),
-    "all_to_all_kernel<256>": ("variable-split all-to-all of the MoE splits (plain)", None),
+    "all_to_all_kernel<1024>": ("variable-split all-to-all of the MoE splits (plain)", None),
     "dispatch_push_kernel<false, 256>": ("token-major MoE dispatch, bf16", None),
     "dispatch_push_kernel<true, 512>": ("token-major MoE dispatch, FP8", None),
     "combine_pull_kernel<512>": ("token-major MoE combine", None),
@@ -649,7 +649,7 @@ def traffic_set(vc, torch, launches: int) -> int:
     src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
     f8 = vc.vcoll_moe_dispatch_fp8(toks, splits, src_g)
     run(lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, f8))
-    out["all_to_all_kernel<256>"] = 2 * rows * rb
+    out["all_to_all_kernel<1024>"] = 2 * rows * rb
     out["dispatch_push_kernel<false, 256>"] = p8 * T * rb + rows * rb
     out["dispatch_push_kernel<true, 512>"] = p8 * T * rb + rows * orb
     out["combine_pull_kernel<512>"] = 2 * rows * rb
