@@ -91,3 +91,51 @@ def test_captured_all_to_all_and_moe_dispatch_replay(vc):
         torch.cuda.synchronize()
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+
+
+def test_captured_plain_all_to_all_combine_and_dedup_replay(vc):
+    """The index-free all-to-all (1024-thread path), the token-major combine,
+    the token-major deduplicated dispatch (bf16 and FP8) and the token-major
+    expansion (one launch per rank), captured once and replayed three times
+    with the outputs cleared in between: every replay equals the eager run."""
+    import torch
+    M = workloads.MOE
+    p, T, H, E, K = M["p"], 256, 512, M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p)])
+    splits, src, dst = vc.vcoll_moe_plan(topk, E // p)
+    slots = vc.vcoll_moe_slots(splits, dst, K)
+    su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p)
+    g = torch.Generator(device="cuda").manual_seed(23)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p)]
+    plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
+                  for i in range(p)]
+    slg = [torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in slots]
+    dsl = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
+    dslg = [torch.from_numpy(np.ascontiguousarray(dsl[i])).cuda() for i in range(p)]
+    urows = su.sum(axis=0)
+    xsl = [torch.from_numpy(vc.vcoll_moe_expand_slots(int(urows[j]), expand[j], K)).cuda() for j in range(p)]
+    counts = [len(e) for e in expand]
+    plain = vc.vcoll_all_to_all(plain_send, splits)
+    push = vc.vcoll_moe_dispatch(toks, slg, splits.sum(axis=0), K)
+    comb = vc.vcoll_moe_combine(push, slg, T, K)
+    du = vc.vcoll_moe_dispatch(toks, dslg, urows, K)
+    du8 = vc.vcoll_moe_dispatch(toks, dslg, urows, K, fp8=True)
+    ex = vc.vcoll_moe_expand_token_major(du, xsl, counts, K)
+    want = [t.clone() for t in plain + comb + du + du8 + ex]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vc.vcoll_all_to_all(plain_send, splits, recv=plain)
+        vc.vcoll_moe_combine(push, slg, T, K, out=comb)
+        vc.vcoll_moe_dispatch(toks, dslg, urows, K, recv=du)
+        vc.vcoll_moe_dispatch(toks, dslg, urows, K, fp8=True, recv=du8)
+        vc.vcoll_moe_expand_token_major(du, xsl, counts, K, out=ex)
+    got = plain + comb + du + du8 + ex
+    for rep in range(3):
+        for t in got:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
