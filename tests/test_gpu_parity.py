@@ -97,6 +97,29 @@ def test_allreduce_matches_oracle(vc, algo, p, dtype):
         assert_bits_equal(got[r], bits(want[r], dtype), f"{algo} p={p} rank {r}")
 
 
+@pytest.mark.parametrize("p", [9, 10, 11, 13, 15, 17, 24, 31, 33, 63, 100, 127])
+def test_allreduce_run_time_programs_over_many_p(vc, p):
+    """p without a compiled program, chosen so that the fold of recursive
+    doubling and Rabenseifner pairs 1, 2, 3, 5, 7, 8, 15, 17, 31, 36 and 63
+    ranks (p - 2^floor(log2 p)); chunks of about 1500 elements (the vector
+    path, heads and tails ragged) and of about 300 (the LDS-staged path);
+    float32 and bfloat16; every algorithm and the ring reduce-scatter."""
+    for n in (p * 1500 + 13, p * 300 + 5):
+        for dtype in ("f32", "bf16"):
+            x = rand_inputs(p, n, dtype, seed=600 + p)
+            t = upload(x, dtype)
+            for algo in ALGOS:
+                say(f"vcoll_allreduce p={p} n={n} {algo} {dtype}")
+                want, _ = oracle.allreduce(x, algo, dtype)
+                got = download(vc.vcoll_allreduce(algo, t), dtype)
+                assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"{algo} p={p} n={n} {dtype}")
+            rs = vc.vcoll_reduce_scatter("ring", t)
+            sync()
+            want, _ = oracle.reduce_scatter(x, "ring", dtype)
+            for c in range(p):
+                assert_bits_equal(download(rs[c], dtype), bits(want[c], dtype), f"rs p={p} chunk {c}")
+
+
 @pytest.mark.parametrize("p,n", [(8, 1), (8, 7), (8, 8), (16, 9), (72, 5), (3, 2), (128, 300)])
 def test_allreduce_tiny_and_max_p(vc, p, n):
     for dtype in ("f32", "bf16"):
