@@ -126,7 +126,8 @@ vcoll_status vcoll_model_ledger_time_nodes(int hierarchical, vcoll_algo algo, in
                                            int32_t* n_steps) {
   if (!(alpha_in >= 0) || !(beta_in > 0) || !(alpha_out >= 0) || !(beta_out > 0) || !seconds)
     return VCOLL_ERR_INVALID_ARG;
-  if (nodes < 1 || local < 1) return VCOLL_ERR_INVALID_ARG;
+  // each factor is bounded before the product is formed (no int overflow)
+  if (nodes < 1 || local < 1 || nodes > VCOLL_MAX_RANKS || local > VCOLL_MAX_RANKS) return VCOLL_ERR_INVALID_ARG;
   const int p = nodes * local;
   int64_t count = 0;
   vcoll_status st = hierarchical

@@ -412,14 +412,13 @@ vcoll_status moe_plan_dedup(int p, int64_t tokens, int topk, int experts_per_ran
       splits_unique[static_cast<int64_t>(i) * p + j] = n;
     }
   };
-  for (int i = 0; i < p; ++i) dedup_rank(i);
   // rank j's plain layout holds the blocks of ranks 0..p-1, each in the
   // sender's (expert, token) order; its deduplicated buffer the same blocks,
   // each in token order
   const int64_t cap = static_cast<int64_t>(p) * rows;
   std::vector<int64_t> xoff(p, 0), uoff(p, 0);
   for (int i = 0; i < p; ++i) {
-    dedup_rank(i);
+    dedup_rank(i);                        // rank i's unique rows, splits_unique row i and `where`
     int64_t s0 = 0;                       // offset of block (i -> j) in rank i's plain send order
     for (int j = 0; j < p; ++j) {
       const int64_t nij = splits[static_cast<size_t>(i) * p + j];

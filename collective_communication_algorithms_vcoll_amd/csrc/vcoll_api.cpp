@@ -39,6 +39,16 @@ bool valid_algo(int a) { return a >= VCOLL_RING && a <= VCOLL_BINARY_TREE; }
 
 bool valid_p(int p) { return p >= 1 && p <= kMaxRanks; }
 
+// nodes x local ranks: each factor is bounded before the product is formed,
+// so the product cannot overflow int
+bool valid_grid(int nodes, int local) {
+  return nodes >= 1 && local >= 1 && nodes <= kMaxRanks && local <= kMaxRanks && valid_p(nodes * local);
+}
+
+// rows x topk within int32 (the row indices of the MoE maps), tested by
+// division so that the product is only formed once it is known to fit
+bool pairs_fit(int64_t rows, int topk) { return topk >= 1 && rows >= 0 && rows <= INT32_MAX / topk; }
+
 // Element counts up to 2^48: far beyond any buffer, and small enough that
 // every byte offset (count x 4 bytes x up to 128 ranks) fits in int64.
 constexpr int64_t kMaxCount = int64_t(1) << 48;
@@ -346,7 +356,7 @@ vcoll_status vcoll_moe_plan(int p, int64_t tokens, int topk, int experts_per_ran
                             const int32_t* topk_ids, int64_t* splits, int32_t* src_rows,
                             int32_t* dst_rows) {
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || experts_per_rank < 1) return VCOLL_ERR_INVALID_ARG;
-  if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(tokens, topk)) return VCOLL_ERR_INVALID_ARG;
   if (!splits || (tokens > 0 && (!topk_ids || !src_rows || !dst_rows))) return VCOLL_ERR_INVALID_ARG;
   return moe_plan(p, tokens, topk, experts_per_rank, topk_ids, splits, src_rows, dst_rows);
 }
@@ -431,7 +441,7 @@ vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_d
 
 vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype,
                                           const void* const* send, void* const* recv, void* stream) {
-  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || !valid_count(n) || !valid_dtype(dtype))
+  if (!valid_grid(nodes, local) || !valid_count(n) || !valid_dtype(dtype))
     return VCOLL_ERR_INVALID_ARG;
   if (n == 0) return VCOLL_OK;
   const int p = nodes * local;
@@ -454,7 +464,7 @@ vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll
 vcoll_status vcoll_ledger_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype, vcoll_msg* msgs,
                                        int64_t cap, int64_t* n_msgs, int64_t* sent_bytes,
                                        int64_t* recv_bytes, int32_t* n_steps) {
-  if (nodes < 1 || local < 1 || !valid_p(nodes * local) || !valid_count(n) || !valid_dtype(dtype) || !n_msgs)
+  if (!valid_grid(nodes, local) || !valid_count(n) || !valid_dtype(dtype) || !n_msgs)
     return VCOLL_ERR_INVALID_ARG;
   const int p = nodes * local;
   std::vector<vcoll_msg> out;
@@ -467,7 +477,7 @@ vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* spl
                              int32_t* slots) {
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !splits || (tokens > 0 && (!dst_rows || !slots)))
     return VCOLL_ERR_INVALID_ARG;
-  if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(tokens, topk)) return VCOLL_ERR_INVALID_ARG;
   for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
     if (splits[k] < 0) return VCOLL_ERR_INVALID_ARG;
   return moe_slots(p, tokens, topk, splits, dst_rows, slots);
@@ -476,7 +486,7 @@ vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* spl
 vcoll_status vcoll_moe_dedup_slots(int p, int64_t tokens, int topk, const int64_t* splits_unique,
                                    const int32_t* src_unique, int32_t* slots) {
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !splits_unique) return VCOLL_ERR_INVALID_ARG;
-  if (tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(tokens, topk)) return VCOLL_ERR_INVALID_ARG;
   if (tokens > 0 && (!src_unique || !slots)) return VCOLL_ERR_INVALID_ARG;
   for (int i = 0; i < p; ++i) {
     int64_t sent = 0;
@@ -498,7 +508,7 @@ vcoll_status vcoll_moe_dedup_slots(int p, int64_t tokens, int topk, const int64_
 vcoll_status vcoll_moe_expand_slots(int64_t unique_rows, int topk, const int32_t* expand, int64_t expand_count,
                                     int32_t* slots) {
   if (!valid_count(unique_rows) || topk < 1 || !valid_count(expand_count)) return VCOLL_ERR_INVALID_ARG;
-  if (unique_rows * topk > INT32_MAX || expand_count > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(unique_rows, topk) || expand_count > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
   if ((expand_count > 0 && !expand) || (unique_rows > 0 && !slots)) return VCOLL_ERR_INVALID_ARG;
   return moe_expand_slots(unique_rows, topk, expand, expand_count, slots);
 }
@@ -509,7 +519,7 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !valid_count(hidden) || !valid_dtype(dtype) || !recv_rows)
     return VCOLL_ERR_INVALID_ARG;
   if (fp8 && (dtype != VCOLL_BF16 || hidden % 128 != 0)) return VCOLL_ERR_INVALID_ARG;
-  if (tokens * topk > INT32_MAX || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(tokens, topk) || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
   if (tokens == 0 || hidden == 0) return VCOLL_OK;
   if (!token_tables || !slots || !recv) return VCOLL_ERR_INVALID_ARG;
   const int64_t rb = hidden * elem_bytes(dtype);
@@ -558,7 +568,7 @@ vcoll_status vcoll_moe_combine(int p, int64_t tokens, int topk, int64_t hidden, 
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !valid_count(hidden) || !valid_dtype(dtype) ||
       !expert_rows)
     return VCOLL_ERR_INVALID_ARG;
-  if (tokens * topk > INT32_MAX || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(tokens, topk) || hidden > INT32_MAX / 4) return VCOLL_ERR_INVALID_ARG;
   const int64_t rb = hidden * elem_bytes(dtype);
   if (!fits(tokens * topk, rb)) return VCOLL_ERR_INVALID_ARG;
   if (tokens == 0 || hidden == 0) return VCOLL_OK;
@@ -597,7 +607,7 @@ vcoll_status vcoll_moe_plan_dedup(int p, int64_t tokens, int topk, int experts_p
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || experts_per_rank < 1 || !topk_ids || !splits_unique ||
       !src_unique || !expand || !expand_count)
     return VCOLL_ERR_INVALID_ARG;
-  if (tokens * topk > INT32_MAX || static_cast<int64_t>(p) * tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
+  if (!pairs_fit(tokens, topk) || static_cast<int64_t>(p) * tokens * topk > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
   return moe_plan_dedup(p, tokens, topk, experts_per_rank, topk_ids, splits_unique, src_unique, expand,
                         expand_count);
 }

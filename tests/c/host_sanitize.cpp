@@ -227,6 +227,26 @@ static void launches(std::mt19937_64& rng) {
   CHECK(vcoll_allreduce(VCOLL_RING, 4, -1, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
   CHECK(vcoll_allreduce(VCOLL_RING, 4, 10, VCOLL_F32, nullptr, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
   CHECK(vcoll_allreduce(VCOLL_RING, 4, int64_t(1) << 50, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+  // rank grids whose product wraps around int, and token x topk products
+  // beyond int64, are refused before the product is formed (UBSan would flag it)
+  {
+    int64_t cnt = 0;
+    double secs = 0;
+    const int grids[3][2] = {{4, (1 << 30) + 1}, {65536, 65536}, {(1 << 30) + 1, 4}};
+    for (const auto& g : grids) {
+      CHECK(vcoll_allreduce_hierarchical(g[0], g[1], 64, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
+      CHECK(vcoll_ledger_hierarchical(g[0], g[1], 64, VCOLL_F32, nullptr, 0, &cnt, nullptr, nullptr, nullptr) ==
+            VCOLL_ERR_INVALID_ARG);
+      CHECK(vcoll_model_ledger_time_nodes(1, VCOLL_RING, g[0], g[1], 64, VCOLL_F32, 1e-6, 1e9, 1e-6, 1e9, &secs,
+                                          nullptr) == VCOLL_ERR_INVALID_ARG);
+    }
+    int32_t ids[8] = {};
+    int64_t sp[4] = {};
+    int32_t rows[8] = {};
+    CHECK(vcoll_moe_plan(2, int64_t(1) << 48, INT32_MAX, 4, ids, sp, rows, rows) == VCOLL_ERR_INVALID_ARG);
+    CHECK(vcoll_moe_slots(2, int64_t(1) << 48, INT32_MAX, sp, rows, rows) == VCOLL_ERR_INVALID_ARG);
+    CHECK(vcoll_moe_expand_slots(int64_t(1) << 48, INT32_MAX, rows, 1, rows) == VCOLL_ERR_INVALID_ARG);
+  }
   CHECK(vcoll_reduce_scatter(VCOLL_RECURSIVE_DOUBLING, 4, 10, VCOLL_F32, send, recv, nullptr) ==
         VCOLL_ERR_UNSUPPORTED);
   CHECK(vcoll_reduce_scatter(VCOLL_RABENSEIFNER, 6, 10, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_UNSUPPORTED);

@@ -315,6 +315,21 @@ def test_widened_entry_points_validate_before_launching():
     assert lib.vcoll_allreduce_hierarchical(0, 8, 64, 0, P8, P8, None) == 1
     assert lib.vcoll_allreduce_hierarchical(16, 16, 64, 0, _ptrs(256), _ptrs(256), None) == 1
     assert lib.vcoll_allreduce_hierarchical(2, 4, 64, 2, P8, P8, None) == 1     # U8 is for the all-to-all only
+    # nodes x local would wrap around int: each factor is bounded on its own
+    n = ctypes.c_int64()
+    for nodes, local in ((4, 2 ** 30 + 1), (65536, 65536), (2 ** 30 + 1, 4)):
+        assert lib.vcoll_allreduce_hierarchical(nodes, local, 64, 0, P8, P8, None) == 1
+        assert lib.vcoll_ledger_hierarchical(nodes, local, 64, 0, None, 0, ctypes.byref(n), None, None, None) == 1
+        t = ctypes.c_double()
+        assert lib.vcoll_model_ledger_time_nodes(1, 0, nodes, local, 64, 0, 1e-6, 1e9, 1e-6, 1e9,
+                                                 ctypes.byref(t), None) == 1
+    # tokens x topk would overflow int64: refused by division, before the product
+    ids = (ctypes.c_int32 * 8)()
+    out64 = (ctypes.c_int64 * 4)()
+    out32 = (ctypes.c_int32 * 8)()
+    assert lib.vcoll_moe_plan(2, 1 << 48, 2 ** 31 - 1, 4, ids, out64, out32, out32) == 1
+    assert lib.vcoll_moe_slots(2, 1 << 48, 2 ** 31 - 1, out64, out32, out32) == 1
+    assert lib.vcoll_moe_expand_slots(1 << 48, 2 ** 31 - 1, out32, 1, out32) == 1
     # the all-to-all takes raw bytes, the reductions do not
     assert lib.vcoll_allreduce(0, 8, 64, 2, P8, P8, None) == 1
     # FP8 dispatch: hidden must be a positive multiple of 128; token tables aligned

@@ -189,6 +189,13 @@ WIDE_MUTANTS = [
     ("deduplicated blocks in descending token order", "moe.py",
      "                           if int(ids[t, k]) // experts_per_rank == j})",
      "                           if int(ids[t, k]) // experts_per_rank == j}, reverse=True)"),
+    ("plan blocks ordered by (destination, token, expert)", "moe.py",
+     "        pairs.sort()\n", "        pairs.sort(key=lambda x: (x[0], x[2], x[1], x[3]))\n"),
+    ("plan blocks with experts descending", "moe.py",
+     "        pairs.sort()\n", "        pairs.sort(key=lambda x: (x[0], -x[1], x[2], x[3]))\n"),
+    ("plan combine slot index transposed", "moe.py",
+     "dst_rows.append(np.array([t * K + k for _, _, t, k in pairs], dtype=np.int32))",
+     "dst_rows.append(np.array([k * T + t for _, _, t, k in pairs], dtype=np.int32))"),
 ]
 
 
@@ -265,6 +272,15 @@ def wide_battery(o) -> list:
                       for i in range(4) for j in range(4))
         return ordered and all(np.array_equal(a, b) for a, b in zip(plain, expanded))
     check("dedup dispatch", dedup)
+
+    # the plan's row order inside each block, worked by hand
+    def plan_order():
+        g = json.load(open(os.path.join(ROOT, "tests", "golden", "moe_plan_order.json")))
+        topk = [np.array(t, dtype=np.int32) for t in g["topk_ids"]]
+        splits, src, dst = o.moe_plan(topk, g["experts_per_rank"])
+        return (splits.tolist() == g["splits"] and [x.tolist() for x in src] == g["src_rows"]
+                and [x.tolist() for x in dst] == g["dst_rows"])
+    check("MoE plan row order", plan_order)
     return fails
 
 

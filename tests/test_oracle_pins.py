@@ -433,6 +433,47 @@ def test_moe_plan_dispatch_combine_round_trip():
         assert np.array_equal(outs[i], np.repeat(toks[i], K, axis=0))
 
 
+def test_moe_plan_row_order_hand_worked():
+    """The plan's row order inside each (i -> j) block, worked by hand
+    (tests/golden/moe_plan_order.json): by expert, then token, then slot."""
+    g = json.load(open(os.path.join(GOLDEN, "moe_plan_order.json")))
+    topk = [np.array(t, dtype=np.int32) for t in g["topk_ids"]]
+    splits, src_rows, dst_rows = oracle.moe_plan(topk, g["experts_per_rank"])
+    assert splits.tolist() == g["splits"]
+    assert [s.tolist() for s in src_rows] == g["src_rows"]
+    assert [d.tolist() for d in dst_rows] == g["dst_rows"]
+    # the expert of each row rank j receives (source blocks in order), from
+    # the sender's (token, slot) of that row
+    for j in range(g["p"]):
+        exp = []
+        for i in range(g["p"]):
+            s0 = int(splits[i, :j].sum())
+            for q in range(int(splits[i, j])):
+                t, k = divmod(int(dst_rows[i][s0 + q]), g["topk"])
+                exp.append(int(topk[i][t, k]))
+        assert exp == g["received_expert_per_row"][j]
+
+
+def test_moe_plan_blocks_are_expert_major_on_the_full_workload():
+    """On the cfg-sized routing (8 ranks x 4096 tokens, top-8 of 256): inside
+    every block the (expert, token) keys of the rows strictly increase, and
+    every row's expert lives on the block's destination."""
+    p, T, E, K = 8, 4096, 256, 8
+    epr = E // p
+    topk = [workloads.moe_topk(r, T, E, K) for r in range(p)]
+    splits, src_rows, dst_rows = oracle.moe_plan(topk, epr)
+    for i in range(p):
+        t, k = np.divmod(dst_rows[i].astype(np.int64), K)
+        assert np.array_equal(t, src_rows[i])
+        e = topk[i][t, k].astype(np.int64)
+        bounds = np.concatenate([[0], np.cumsum(splits[i])])
+        for j in range(p):
+            eb, tb = e[bounds[j]:bounds[j + 1]], t[bounds[j]:bounds[j + 1]]
+            assert np.all(eb // epr == j)
+            key = eb * T + tb
+            assert np.all(np.diff(key) > 0)
+
+
 def test_moe_workload_skew_and_conservation():
     p, T, E, K = 8, 4096, 256, 8
     topk = [workloads.moe_topk(r, T, E, K) for r in range(p)]
