@@ -125,6 +125,8 @@ def _lib():
         lib.vcoll_moe_dispatch_fp8.argtypes = [I, I64, P(I64), P(VP), P(I64), P(VP), P(VP), VP]
         lib.vcoll_moe_dispatch_fp8.restype = I
         lib.vcoll_allreduce_stepwise.argtypes = [I, I, I64, I, P(VP), P(VP), VP, I64, P(ctypes.c_int32), VP]
+        lib.vcoll_allreduce_stepwise_static.restype = I
+        lib.vcoll_allreduce_stepwise_static.argtypes = [I, I, I64, I, P(VP), P(VP), P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise.restype = I
         D = ctypes.c_double
         lib.vcoll_model_formula.argtypes = [I, I, D, D, D, P(D)]
@@ -332,6 +334,32 @@ def vcoll_allreduce_stepwise(algo, send, recv=None, workspace=None):
     _check(_lib().vcoll_allreduce_stepwise(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
                                            ws_ptr, ws_bytes, ctypes.byref(launches), _stream(s[0])),
            "vcoll_allreduce_stepwise")
+    return recv, launches.value
+
+
+STEP_SCRATCH_BYTES = 64 * 1024 * 1024     # VCOLL_STEP_SCRATCH_BYTES
+
+
+def vcoll_allreduce_stepwise_static(algo, send, recv=None):
+    """vcoll_allreduce_stepwise without a workspace: bf16 partial sums live
+    in the library's own per-GPU scratch array (p*n*4 bytes at most
+    STEP_SCRATCH_BYTES). Returns (recv, launches). Calls on one GPU that
+    are not ordered on one stream race on that array."""
+    import torch
+    s = _ranks(send)
+    _validate(s, "vcoll_allreduce_stepwise_static")
+    n = s[0].numel()
+    _validate(s, "vcoll_allreduce_stepwise_static", n)
+    if recv is None:
+        recv = torch.empty_like(send) if isinstance(send, torch.Tensor) else [torch.empty_like(t) for t in s]
+    r = _ranks(recv)
+    _validate(r, "vcoll_allreduce_stepwise_static", n)
+    _no_overlap(s, r, "vcoll_allreduce_stepwise_static", same_index_ok=True)
+    _disjoint(r, "vcoll_allreduce_stepwise_static")
+    launches = ctypes.c_int32()
+    _check(_lib().vcoll_allreduce_stepwise_static(_algo(algo), len(s), n, _dtype_code(s[0]), _ptrs(s), _ptrs(r),
+                                                  ctypes.byref(launches), _stream(s[0])),
+           "vcoll_allreduce_stepwise_static")
     return recv, launches.value
 
 

@@ -34,4 +34,10 @@ struct StepArgs {
 
 hipError_t launch_step(const StepArgs& a, int32_t tiles, hipStream_t stream);
 
+// Device address, on the current device, of the library's own float32 scratch
+// array (VCOLL_STEP_SCRATCH_BYTES, one copy per GPU, alive until the process
+// ends) for the allocation-free stepwise all-reduce. The address is looked up
+// once per device and cached.
+hipError_t step_scratch(void** ptr);
+
 }  // namespace vcoll

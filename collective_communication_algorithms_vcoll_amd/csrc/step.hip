@@ -1,4 +1,6 @@
 // The stepwise (one launch per algorithm step) all-reduce kernel of libvcoll.
+#include <mutex>
+
 #include "device.h"
 #include "step.h"
 
@@ -92,11 +94,40 @@ __global__ __launch_bounds__(kBlock) void step_kernel(const StepArgs a) {
   if (tail < e1) step_apply1(o, tail);
 }
 
+// Float32 partial sums of the allocation-free stepwise all-reduce (bf16
+// inputs): one copy per GPU, owned by the library. Host code never passes
+// this name to a kernel (on the host it is only a stand-in for the symbol);
+// it uses the device address that step_scratch() looks up.
+static __device__ __align__(256) float scratch[VCOLL_STEP_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kScratchDevices = 64;
+
 }  // namespace
 
 hipError_t launch_step(const StepArgs& a, int32_t tiles, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   return launch(step_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
+}
+
+hipError_t step_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kScratchDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    // each GPU holds its own copy of the array at its own address: look it
+    // up with this device current, once
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!addr) return hipErrorInvalidSymbol;
+    per_device[dev] = addr;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 }  // namespace vcoll

@@ -155,6 +155,7 @@ const char* vcoll_status_str(vcoll_status status) {
     case VCOLL_ERR_UNSUPPORTED: return "unsupported operation/algorithm/p combination";
     case VCOLL_ERR_BUFFER_TOO_SMALL: return "ledger buffer too small";
     case VCOLL_ERR_HIP: return "HIP launch failed";
+    case VCOLL_ERR_SCRATCH_LIMIT: return "size exceeds the library's static scratch array (VCOLL_STEP_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -386,18 +387,22 @@ vcoll_status run_step_ops(const std::vector<StepLaunchOp>& ops, hipStream_t stre
 
 }  // namespace
 
-vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
-                                      const void* const* send, void* const* recv, void* workspace,
-                                      int64_t workspace_bytes, int32_t* n_launches, void* stream) {
-  if (n_launches) *n_launches = 0;
+namespace {
+
+// Arguments of a stepwise all-reduce, before any workspace question.
+vcoll_status stepwise_args(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, const void* const* send,
+                           void* const* recv) {
   if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
   if (n == 0) return VCOLL_OK;
   if (!all_set(p, send) || !all_set(p, const_cast<const void* const*>(recv))) return VCOLL_ERR_INVALID_ARG;
+  return VCOLL_OK;
+}
+
+// The stepwise all-reduce on validated arguments; for bf16, `workspace`
+// holds at least p*n float32.
+vcoll_status stepwise_run(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, const void* const* send,
+                          void* const* recv, void* workspace, int32_t* n_launches, void* stream) {
   const bool bf16 = dtype == VCOLL_BF16;
-  if (bf16) {
-    if (!workspace) return VCOLL_ERR_INVALID_ARG;
-    if (workspace_bytes < static_cast<int64_t>(p) * n * 4) return VCOLL_ERR_BUFFER_TOO_SMALL;
-  }
   // working buffers: recv itself for float32, the float32 workspace for bf16
   std::vector<float*> W(p);
   for (int r = 0; r < p; ++r)
@@ -437,6 +442,37 @@ vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_d
     st = run_step_ops(ops, s, n_launches);
   }
   return st;
+}
+
+}  // namespace
+
+vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                      const void* const* send, void* const* recv, void* workspace,
+                                      int64_t workspace_bytes, int32_t* n_launches, void* stream) {
+  if (n_launches) *n_launches = 0;
+  const vcoll_status st = stepwise_args(algo, p, n, dtype, send, recv);
+  if (st != VCOLL_OK || n == 0) return st;
+  if (dtype == VCOLL_BF16) {
+    if (!workspace) return VCOLL_ERR_INVALID_ARG;
+    if (workspace_bytes < static_cast<int64_t>(p) * n * 4) return VCOLL_ERR_BUFFER_TOO_SMALL;
+  }
+  return stepwise_run(algo, p, n, dtype, send, recv, workspace, n_launches, stream);
+}
+
+vcoll_status vcoll_allreduce_stepwise_static(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                             const void* const* send, void* const* recv,
+                                             int32_t* n_launches, void* stream) {
+  if (n_launches) *n_launches = 0;
+  const vcoll_status st = stepwise_args(algo, p, n, dtype, send, recv);
+  if (st != VCOLL_OK || n == 0) return st;
+  void* workspace = nullptr;
+  if (dtype == VCOLL_BF16) {
+    // p <= 128 and n <= 2^48, so the product fits in int64
+    if (static_cast<int64_t>(p) * n * 4 > VCOLL_STEP_SCRATCH_BYTES) return VCOLL_ERR_SCRATCH_LIMIT;
+    const hipError_t e = step_scratch(&workspace);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return stepwise_run(algo, p, n, dtype, send, recv, workspace, n_launches, stream);
 }
 
 vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype,

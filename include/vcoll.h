@@ -55,13 +55,17 @@ extern "C" {
 
 #define VCOLL_ABI_VERSION 1
 #define VCOLL_MAX_RANKS 128
+/* Size of the library's own scratch array (one per GPU) behind
+ * vcoll_allreduce_stepwise_static: 64 MiB of float32 partial sums. */
+#define VCOLL_STEP_SCRATCH_BYTES (64 * 1024 * 1024)
 
 typedef enum {
   VCOLL_OK = 0,
   VCOLL_ERR_INVALID_ARG = 1,     /* out-of-range p, n, dtype, algo, NULL pointer, bad split */
   VCOLL_ERR_UNSUPPORTED = 2,     /* the (operation, algorithm, p) combination does not exist */
   VCOLL_ERR_BUFFER_TOO_SMALL = 3,/* ledger capacity below the number of messages */
-  VCOLL_ERR_HIP = 4              /* the HIP runtime refused a launch */
+  VCOLL_ERR_HIP = 4,             /* the HIP runtime refused a launch */
+  VCOLL_ERR_SCRATCH_LIMIT = 5    /* the call needs more than the library's static scratch array */
 } vcoll_status;
 
 typedef enum {
@@ -150,6 +154,30 @@ vcoll_status vcoll_allreduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtyp
 vcoll_status vcoll_allreduce_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                                       const void* const* send, void* const* recv, void* workspace,
                                       int64_t workspace_bytes, int32_t* n_launches, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as vcoll_allreduce_stepwise, bit for bit and launch for launch,
+ * with the bfloat16 float32 partial sums in a scratch array the library
+ * owns instead of a caller workspace. The array is a file-scope device
+ * variable of VCOLL_STEP_SCRATCH_BYTES: every GPU the library runs on holds
+ * its own copy until the process ends, and the call uses the copy of the
+ * current device (the stream must belong to it). The call allocates no
+ * device memory. Its first use on a device looks the array's address up once
+ * (a HIP symbol query, before anything is enqueued; a failure returns
+ * VCOLL_ERR_HIP).
+ * bfloat16 needs p*n*4 <= VCOLL_STEP_SCRATCH_BYTES, else
+ * VCOLL_ERR_SCRATCH_LIMIT (nothing enqueued); float32 works in recv and uses
+ * no scratch, at any size. Nothing in the array has to start at zero: every
+ * call first writes the partial sums it later reads. All calls on one GPU
+ * share the array, so calls that overlap on one GPU (different streams
+ * without ordering between them) race and give undefined results; calls
+ * ordered on one stream are safe.
+ */
+vcoll_status vcoll_allreduce_stepwise_static(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
+                                             const void* const* send, void* const* recv,
+                                             int32_t* n_launches, void* stream);
 
 /*
  * Broadcast ([NCC] 4.1): every rank's buffer receives the root's n elements,

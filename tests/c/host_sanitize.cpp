@@ -52,6 +52,13 @@ hipError_t launch_dispatch_push(const PushArgs&, bool, hipStream_t) { ++g_launch
 hipError_t launch_combine_pull(const CombineArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_copy(void*, const void*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_step(const StepArgs&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
+// the scratch lookup of the allocation-free stepwise mode: a host stand-in
+// address (the stubbed launches never dereference it)
+hipError_t step_scratch(void** ptr) {
+  static float stand_in[4];
+  *ptr = stand_in;
+  return hipSuccess;
+}
 }  // namespace vcoll
 
 #define CHECK(cond)                                                             \
@@ -220,8 +227,29 @@ static void launches(std::mt19937_64& rng) {
   }
   for (int nodes : {2, 4})
     CHECK(vcoll_allreduce_hierarchical(nodes, 4, 100000, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+  // the allocation-free stepwise mode: same launches as with a workspace
+  for (int p : {2, 8, 72}) {
+    int32_t with_ws = 0, without = 0;
+    std::vector<float> ws(size_t(p) * 1000);
+    CHECK(vcoll_allreduce_stepwise(VCOLL_RABENSEIFNER, p, 1000, VCOLL_BF16, send, recv, ws.data(),
+                                   int64_t(ws.size()) * 4, &with_ws, nullptr) == VCOLL_OK);
+    CHECK(vcoll_allreduce_stepwise_static(VCOLL_RABENSEIFNER, p, 1000, VCOLL_BF16, send, recv, &without,
+                                          nullptr) == VCOLL_OK);
+    CHECK(with_ws == without && without > 0);
+  }
   // error paths: nothing is launched
   const long before = g_launches;
+  {
+    int32_t launched = -1;
+    // 8 x 2^21 float32 partial sums = 64 MiB fits; one more element does not
+    CHECK(vcoll_allreduce_stepwise_static(VCOLL_RING, 8, (int64_t(1) << 21) + 1, VCOLL_BF16, send, recv, &launched,
+                                          nullptr) == VCOLL_ERR_SCRATCH_LIMIT);
+    CHECK(launched == 0);
+    CHECK(vcoll_allreduce_stepwise_static(VCOLL_RING, 8, int64_t(1) << 48, VCOLL_BF16, send, recv, &launched,
+                                          nullptr) == VCOLL_ERR_SCRATCH_LIMIT);
+    CHECK(vcoll_allreduce_stepwise_static(VCOLL_RING, 0, 10, VCOLL_BF16, send, recv, &launched, nullptr) ==
+          VCOLL_ERR_INVALID_ARG);
+  }
   CHECK(vcoll_allreduce(VCOLL_RING, 0, 10, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
   CHECK(vcoll_allreduce(VCOLL_RING, 129, 10, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);
   CHECK(vcoll_allreduce(VCOLL_RING, 4, -1, VCOLL_F32, send, recv, nullptr) == VCOLL_ERR_INVALID_ARG);

@@ -352,6 +352,22 @@ def test_widened_entry_points_validate_before_launching():
     assert lib.vcoll_model_clock(None, 3, 8, 8, 1e-6, 1e9, 1e-6, 1e9, ctypes.byref(t)) == 1
 
 
+def test_static_stepwise_refuses_sizes_beyond_its_scratch_array():
+    """vcoll_allreduce_stepwise_static keeps bf16 partial sums in the
+    library's own 64 MiB array: a call needing more is refused before any
+    HIP call (so this runs without a GPU), and n = 0 is a no-op."""
+    lib = _lib()
+    P8 = _ptrs(8)
+    launches = ctypes.c_int32(-1)
+    over = (64 * 2 ** 20) // (8 * 4) + 1
+    assert lib.vcoll_allreduce_stepwise_static(0, 8, over, 1, P8, P8, ctypes.byref(launches), None) == 5
+    assert launches.value == 0
+    assert lib.vcoll_allreduce_stepwise_static(0, 8, 1 << 48, 1, P8, P8, None, None) == 5
+    assert lib.vcoll_allreduce_stepwise_static(0, 8, 0, 1, None, None, None, None) == 0
+    assert lib.vcoll_allreduce_stepwise_static(0, 129, 10, 1, P8, P8, None, None) == 1
+    assert b"static scratch" in lib.vcoll_status_str(5)
+
+
 def test_oversized_counts_and_buffers_are_refused():
     """Element counts above 2^48 and buffers above 2^56 bytes are refused
     before anything is enqueued, so no byte offset can overflow int64."""
