@@ -14,16 +14,29 @@ the previous one left in cache.
 
 roofline.achieved: the same algorithmic bytes / the kernel's mean launch
 duration: HIP events on the launch stream around the timed region, divided
-by the number of launches. roofline.traffic: HBM bytes per launch from rocprofv3 counters
-(profiles/ summary of the same kernel source), or null.
+by the number of launches; roofline.launch_us: median, p10 and p90 of 60
+launches timed one by one, each after a 1 GiB copy that evicts the
+Infinity Cache. roofline.traffic: HBM bytes per launch from rocprofv3
+counters (profiles/traffic.json, valid while the kernel's machine code is
+unchanged), or null.
 
 cpu_baseline: the CPU oracle (step-by-step numpy ring with its message
-ledger) on the same workload, on this host, one thread.
+ledger) on the same workload, on this host, one thread; its result is
+compared with the GPU's bit for bit (parity_vs_oracle).
 
-Extras (not the headline): other algorithms and the unfused reduce-scatter +
-all-gather pair on the same bucket, the plain-copy ceiling, the p = 16 x
-192 MiB bfloat16 workload, MoE dispatch/combine, and decode/prefill-sized
-messages.
+Extras (not the headline), each kernel with algorithmic bytes, microseconds
+and fraction of 8 TB/s, each configuration with its oracle baseline and
+parity check:
+  ceilings -- read-only, write-only and copy streams of this GPU;
+  cfg1 -- the pages' 4-device worked example and p = 8 x 262,144 float32;
+  other algorithms, hierarchical orders, broadcast, reduce and the unfused
+  reduce-scatter + all-gather on the bucket; stepwise execution;
+  decode-like 10 KiB and prefill-like 80 MiB messages (and from a HIP graph);
+  cfg3 -- p = 16 x 192 MiB bfloat16, ring and Rabenseifner;
+  cfg4 -- MoE dispatch/combine (p = 8, 4096 tokens, hidden 7168, top-8);
+  moe_variants -- row-major, FP8 and deduplicated dispatch forms;
+  cfg5 -- the sweep's p in {2, 4, 8, 16, 72} at 64 MiB and 1 KiB per rank;
+  host_schedule_and_ledger -- the host rows.
 """
 from __future__ import annotations
 
@@ -40,9 +53,8 @@ sys.path.insert(0, ROOT)
 METRIC = "all-reduce effective HBM GB/s (p=8, 25 MB/rank fp32) + % of HBM roofline"
 PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
-# the headline kernel in libvcoll.so: reduce_kernel<f32, ring, p = 8, 2 vectors per thread,
-# all-reduce, large-grid variant>
-HEADLINE_SYMBOL = "reduce_kernelILi0ELi0ELi8ELi2ELb0ELb1ELi256EE"
+# the headline kernel in libvcoll.so: the two-phase ring all-reduce, float32, 25 vectors per thread
+HEADLINE_SYMBOL = "burst_ring_kernelILi0ELi25EE"
 
 
 def _elf_sections(data: bytes) -> list:
@@ -171,8 +183,10 @@ def headline(vc, torch, args):
     calls = [vc.prepare_allreduce("ring", ins[i], outs[i]) for i in range(R)]
     wall, mean_ms = time_launches(calls, args.steps, args.warmup)
     result = outs[(args.steps - 1) % R].cpu().numpy()       # written by the last timed launch
+    scrub = Scrub(vc, torch)
+    dist = launch_distribution(torch, calls, scrub)
     return dict(x=x, p=p, n=n, S=S, nbytes=nbytes, sets=R, wall=wall, mean_ms=mean_ms,
-                result=result, base=base)
+                result=result, base=base, scrub=scrub, dist=dist)
 
 
 def cpu_baseline(h, seconds):
@@ -194,13 +208,361 @@ def cpu_baseline(h, seconds):
     }, parity
 
 
+def roof(kernel: str, nbytes: int, ms: float, **more) -> dict:
+    """Roofline record of one kernel: algorithmic bytes per launch over its
+    mean launch duration, against MI355X's 8 TB/s."""
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    rec = {"kernel": kernel, "algorithmic_bytes": int(nbytes), "us": round(ms * 1e3, 2),
+           "achieved_GBps": round(gbps, 1), "peak_GBps": PEAK_GBPS, "frac": round(gbps / PEAK_GBPS, 4)}
+    rec.update(more)
+    return rec
+
+
+class Scrub:
+    """A 1 GiB streaming copy that evicts the 256 MB Infinity Cache between
+    timed launches (run outside the timed events)."""
+
+    def __init__(self, vc, torch):
+        half = 512 * 2 ** 20
+        self.src = torch.empty(half // 4, device="cuda")
+        self.dst = torch.empty(half // 4, device="cuda")
+        self.call = vc.prepare_bench_stream("copy", self.dst, self.src)
+
+    def __call__(self):
+        self.call()
+
+
+def launch_distribution(torch, calls, scrub, iters: int = 60) -> dict:
+    """Per-launch durations: for each of `iters` launches, scrub the cache,
+    then time the launch alone between two HIP events on its stream;
+    median, p10 and p90 in microseconds (each includes one event pair's own
+    cost, reported once as event_pair_floor_us)."""
+    import numpy as np
+    ts = []
+    for k in range(iters + 3):
+        scrub()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        calls[k % len(calls)]()
+        e.record()
+        e.synchronize()
+        if k >= 3:
+            ts.append(s.elapsed_time(e) * 1e3)
+    q = np.percentile(ts, [10, 50, 90])
+    return {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2), "p90": round(float(q[2]), 2),
+            "iterations": iters, "cache_scrubbed": True}
+
+
+def event_pair_floor(vc, torch) -> float:
+    """Median time between two HIP events around a 16-byte copy: the floor
+    every per-launch event measurement includes."""
+    import numpy as np
+    a, b = torch.zeros(4, device="cuda"), torch.zeros(4, device="cuda")
+    call = vc.prepare_bench_stream("copy", b, a)
+    ts = []
+    for _ in range(53):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        call()
+        e.record()
+        e.synchronize()
+        ts.append(s.elapsed_time(e) * 1e3)
+    return round(float(np.median(ts[3:])), 2)
+
+
+def oracle_seconds(fn, seconds: float):
+    """Run fn repeatedly for about `seconds` (at least once); returns
+    (result of the last run, runs, elapsed seconds)."""
+    reps, t0, out = 0, time.perf_counter(), None
+    while True:
+        out = fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return out, reps, el
+
+
+def host_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def ceilings(vc, torch, nbytes: int) -> dict:
+    """Streaming ceilings of this GPU measured in the same run: read-only,
+    write-only, the fastest copy shape and the earlier plain copy, each over
+    `nbytes` read and/or written per launch, cycled through buffer sets that
+    exceed the Infinity Cache."""
+    R = sets_for(2 * nbytes)
+    src = [torch.empty(nbytes // 4, device="cuda") for _ in range(R)]
+    dst = [torch.empty(nbytes // 4, device="cuda") for _ in range(R)]
+    sink = torch.zeros(4, device="cuda")
+    out = {}
+    for kind, moved, mk in (
+            ("read", nbytes, lambda i: vc.prepare_bench_stream("read", sink, src[i])),
+            ("write", nbytes, lambda i: vc.prepare_bench_stream("write", dst[i])),
+            ("copy", 2 * nbytes, lambda i: vc.prepare_bench_stream("copy", dst[i], src[i])),
+            ("copy_plain", 2 * nbytes, lambda i: vc.prepare_bench_stream("copy_plain", dst[i], src[i]))):
+        calls = [mk(i) for i in range(R)]
+        _, ms = time_launches(calls, 60, 5)
+        out[kind] = roof({"read": "read_kernel<4, 256>", "write": "write_kernel<4, 64>",
+                          "copy": "copy_kernel<2, 64, sc0 sc1 nt>", "copy_plain": "copy_kernel<4, 256, nt>"}[kind],
+                         moved, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def cfg1(vc, torch, scrub, cpu_seconds, cpu_leg: bool) -> dict:
+    """The pages' 4-device worked example, then p = 8 x 262,144 float32
+    (uniform[-1, 1]): ring all-reduce, reduce-scatter + all-gather identity,
+    ledger, latency."""
+    import numpy as np
+    import workloads
+    res = {"workload": "worked example p=4 x 4 (device d holds 10d..10d+3); ring all-reduce p=8 x 262,144 fp32"}
+    x4 = workloads.worked_example()
+    t4 = torch.from_numpy(np.stack(x4)).cuda()
+    ar4 = {a: vc.vcoll_allreduce(a, t4).cpu().numpy() for a in ("ring", "rd", "rabenseifner", "tree")}
+    rs4 = vc.vcoll_reduce_scatter("ring", t4)
+    ag4 = vc.vcoll_all_gather("ring", rs4).cpu().numpy()
+    res["worked_example_allreduce"] = ar4["ring"][0].tolist()
+    res["worked_example_rs_then_ag_equals_allreduce"] = bool(np.array_equal(ag4, ar4["ring"]))
+    msgs, sent, _, steps = vc.vcoll_ledger("allreduce", "ring", 4, 4, "f32")
+    res["worked_example_ledger"] = {"steps": steps, "messages": len(msgs), "sent_bytes_per_rank": sent}
+
+    cfg = workloads.RING_SMALL
+    p, n = cfg["p"], cfg["n"]
+    x = workloads.rank_buffers(cfg["tag"], p, n, cfg["dist"], cfg["dtype"])
+    base = torch.from_numpy(np.stack(x)).cuda()
+    S = n * 4
+    R = sets_for(2 * p * S)
+    ins = [base.clone() for _ in range(R)]
+    outs = [torch.empty_like(base) for _ in range(R)]
+    calls = [vc.prepare_allreduce("ring", ins[i], outs[i]) for i in range(R)]
+    _, ms = time_launches(calls, 200, 20)
+    res["roofline"] = roof("reduce_kernel<f32, ring, p=8, 4 vectors per thread>", 2 * p * S, ms,
+                           bound="latency (16 MiB moved per call)",
+                           launch_us=launch_distribution(torch, calls, scrub))
+    rs = vc.vcoll_reduce_scatter("ring", base)
+    ag = vc.vcoll_all_gather("ring", rs)
+    ar = vc.vcoll_allreduce("ring", base)
+    torch.cuda.synchronize()
+    res["rs_then_ag_equals_allreduce"] = bool(torch.equal(ag.view(torch.int32), ar.view(torch.int32)))
+    msgs, sent, _, steps = vc.vcoll_ledger("allreduce", "ring", p, n, "f32")
+    res["ledger"] = {"steps": steps, "messages": len(msgs), "bytes_per_message": sorted({m[6] for m in msgs}),
+                     "sent_bytes_per_rank": sorted(set(sent)),
+                     "closed_form_2(p-1)/p*S": 2 * (p - 1) * S // p}
+    if cpu_leg:
+        import oracle
+        got = ar.cpu().numpy().view(np.uint32)
+        (want, _), reps, el = oracle_seconds(lambda: oracle.allreduce(x, "ring", "f32"), cpu_seconds)
+        ok4 = all(np.array_equal(ar4[a], np.stack(oracle.allreduce(x4, a, "f32")[0]))
+                  for a in ("ring", "rd", "rabenseifner", "tree"))
+        res["parity_vs_oracle"] = "bit-exact" if (np.array_equal(got, np.stack(want).view(np.uint32)) and ok4) \
+            else "MISMATCH"
+        res["cpu_baseline"] = {"value": round(2 * p * S * reps / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} full ring all-reduces of p=8 x 262,144 fp32, {el:.1f} s, numpy "
+                                         f"single thread, host has {host_cores()} cores; worked example all four "
+                                         f"algorithms"}
+    del ins, outs, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def cfg3(vc, torch, scrub, cpu_leg: bool) -> dict:
+    """p = 16 x 192 MiB bf16 per rank, float32 accumulation: fused ring and
+    Rabenseifner all-reduces, their reduce-scatter and all-gather halves,
+    and the 2 x 8 / 4 x 4 hierarchical orders."""
+    import numpy as np
+    P16, N16 = 16, 100_663_296
+    S16 = N16 * 2
+    res = {"workload": "p=16 x 192 MiB bf16 per rank (100,663,296 elements), uniform[-1,1], fp32 accumulation, "
+                       "bf16 output; inputs drawn on the GPU (seeded torch generator)"}
+    g = torch.Generator(device="cuda").manual_seed(3)
+    t16 = (torch.rand((P16, N16), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
+    o16 = {a: torch.empty_like(t16) for a in ("ring", "rabenseifner")}
+    for algo in ("ring", "rabenseifner"):
+        call = vc.prepare_allreduce(algo, t16, o16[algo])
+        _, ms = time_launches([call], 30, 5)
+        res[f"{algo}_allreduce"] = roof(f"reduce_kernel<bf16, {algo}, p=16, 1 vector per thread, 64 threads>",
+                                        2 * P16 * S16, ms, launch_us=launch_distribution(torch, [call], scrub, 50))
+    tmp = torch.empty_like(t16)
+    for nodes, local in ((2, 8), (4, 4)):
+        call = vc.prepare_allreduce_hierarchical(nodes, local, t16, tmp)
+        _, ms = time_launches([call], 30, 5)
+        res[f"hierarchical_{nodes}x{local}_allreduce"] = roof(f"hier_kernel<bf16, {nodes}, {local}>", 2 * P16 * S16, ms)
+    rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
+    for algo, ag_algo in (("ring", "ring"), ("rabenseifner", "rd")):
+        call = vc.prepare_reduce_scatter(algo, t16, rs16)
+        _, ms = time_launches([call], 30, 5)
+        res[f"{algo}_reduce_scatter"] = roof(f"reduce_kernel<bf16, {algo}, p=16, reduce-scatter>",
+                                             P16 * S16 + S16, ms)
+        call = vc.prepare_all_gather(ag_algo, rs16, tmp)
+        _, ms = time_launches([call], 30, 5)
+        res[f"{ag_algo}_all_gather"] = roof("all_gather_kernel<bf16, 1 vector per thread, 64 threads>",
+                                            S16 + P16 * S16, ms)
+    del tmp, rs16
+    if cpu_leg:
+        import oracle
+        w = 1 << 20
+        lo = N16 // P16 - w // 2                     # straddles the chunk 0 / chunk 1 boundary
+        xw = [t16[r, lo:lo + w].view(torch.int16).cpu().numpy().view(np.uint16) for r in range(P16)]
+        ok, reps, t_or = True, 0, 0.0
+        for algo in ("ring", "rabenseifner"):
+            (want, _), k, el = oracle_seconds(lambda: oracle.allreduce(xw, algo, "bf16", n=N16, lo=lo), 1.5)
+            t_or += el
+            reps += k
+            got = o16[algo][:, lo:lo + w].view(torch.int16).cpu().numpy().view(np.uint16)
+            ok = ok and np.array_equal(got, np.stack(want))
+        res["parity_vs_oracle"] = "bit-exact" if ok else "MISMATCH"
+        res["parity_fraction"] = round(w / N16, 6)
+        res["cpu_baseline"] = {"value": round(2 * P16 * w * 2 * reps / t_or / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"windowed oracle, ring and Rabenseifner, elements [{lo}, {lo + w}) of all "
+                                         f"16 ranks ({100 * w / N16:.2f} % of the vector), {t_or:.1f} s, numpy single "
+                                         f"thread, host has {host_cores()} cores; every element of the full vector is "
+                                         f"compared with the oracle by the GPU tests"}
+    del t16, o16
+    torch.cuda.empty_cache()
+    return res
+
+
+def cfg4(vc, torch, cpu_leg: bool) -> dict:
+    """MoE dispatch/combine: p = 8, 4096 tokens per rank, hidden 7168 bf16,
+    top-8 of 256 Zipf(1.1) experts."""
+    import numpy as np
+    import workloads
+    M = workloads.MOE
+    p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
+    splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
+    rb, orb = H * 2, H + H // 32
+    rows = int(splits.sum())
+    res = {"workload": "MoE dispatch/combine p=8, 4096 tokens/rank, hidden 7168 bf16, top-8 of 256 experts "
+                       "(32/rank), Zipf(1.1) popularity; tokens normal(0,1) drawn on the GPU",
+           "rows": rows, "rows_to_rank0": round(float(splits[:, 0].sum() / rows), 4)}
+    g = torch.Generator(device="cuda").manual_seed(4)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
+    slots = vc.vcoll_moe_slots(splits, dst_rows, K)
+    slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
+    recv_rows = splits.sum(axis=0)
+    # dispatch: token-major (each token row read once, written to each of its slots)
+    recv = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
+    push = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=recv)          # noqa: E731
+    _, ms = time_launches([push], 10, 2)
+    res["dispatch"] = roof("dispatch_push_kernel<bf16, 256>", p8 * T * rb + rows * rb, ms)
+    # combine: token-major (each (token, slot) row pulled from its expert output)
+    back = vc.vcoll_moe_combine(recv, slots_g, T, K)
+    pull = lambda: vc.vcoll_moe_combine(recv, slots_g, T, K, out=back)                    # noqa: E731
+    _, ms = time_launches([pull], 10, 2)
+    res["combine"] = roof("combine_pull_kernel<512>", 2 * rows * rb, ms)
+    torch.cuda.synchronize()
+    res["combine_of_dispatch_is_identity"] = all(
+        torch.equal(back[i].view(T, K, H).view(torch.int16), toks[i].view(torch.int16).unsqueeze(1).expand(T, K, H))
+        for i in range(p8))
+    # FP8 payload, token-major
+    f8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
+    push8 = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=f8)  # noqa: E731
+    _, ms = time_launches([push8], 10, 2)
+    res["dispatch_fp8"] = roof("dispatch_push_kernel<fp8, 512>", p8 * T * rb + rows * orb, ms)
+    del f8
+    # the plain block transpose on the same splits (send buffers already in
+    # destination-block order)
+    plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
+                  for i in range(p8)]
+    plain_recv = vc.vcoll_all_to_all(plain_send, splits)
+    a2a = lambda: vc.vcoll_all_to_all(plain_send, splits, recv=plain_recv)                # noqa: E731
+    _, ms = time_launches([a2a], 10, 2)
+    res["all_to_all_plain"] = roof("all_to_all_kernel<1024>", 2 * rows * rb, ms)
+    del plain_send, plain_recv
+    torch.cuda.empty_cache()
+    if cpu_leg:
+        import oracle
+        t_h = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in toks]
+        o_splits, o_src, o_dst = oracle.moe_plan(list(topk), E // p8)
+        t0 = time.perf_counter()
+        want_recv, _, _ = oracle.moe_dispatch(t_h, o_splits, o_src)
+        t_d = time.perf_counter() - t0
+        ok = all(np.array_equal(recv[j].view(torch.int16).cpu().numpy().view(np.uint16), want_recv[j])
+                 for j in range(p8))
+        t0 = time.perf_counter()
+        want_back, _ = oracle.moe_combine(want_recv, o_splits, o_dst, K, T)
+        t_c = time.perf_counter() - t0
+        ok = ok and np.array_equal(o_splits, splits)
+        ok = ok and all(np.array_equal(back[i].view(torch.int16).cpu().numpy().view(np.uint16), want_back[i])
+                        for i in range(p8))
+        del want_recv, want_back, t_h
+        moved = (p8 * T * rb + rows * rb) + 2 * rows * rb
+        res["parity_vs_oracle"] = "bit-exact" if ok else "MISMATCH"
+        res["cpu_baseline"] = {"value": round(moved / (t_d + t_c) / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one full dispatch ({t_d:.1f} s) and combine ({t_c:.1f} s) of the workload "
+                                         f"(262,144 rows of 14,336 B each way), numpy single thread, host has "
+                                         f"{host_cores()} cores; bytes as the GPU figures (dispatch: tokens read "
+                                         f"once + rows written; combine: rows read + written)"}
+    del toks, recv, back
+    torch.cuda.empty_cache()
+    return res
+
+
+def cfg5(vc, torch, cpu_leg: bool) -> dict:
+    """The message-size sweep in the driver's run: every p at 64 MiB per rank
+    (the largest oracle-timed size) for all four algorithms, and at 1 KiB per
+    rank (latency). The full 260-point sweep is `bench.py --sweep`."""
+    import numpy as np
+    import workloads
+    res = {"workload": "p in {2,4,8,16,72}, fp32 normal(0,1) drawn on the GPU; 64 MiB and 1 KiB per rank"}
+    for p in workloads.SWEEP_P:
+        for nbytes in (2 ** 10, 64 * 2 ** 20):
+            n = nbytes // 4
+            g = torch.Generator(device="cuda").manual_seed(workloads.TAG_SWEEP * 10 ** 6 + p * 1000 + nbytes % 997)
+            t = torch.randn((p, n), device="cuda", generator=g)
+            sets = 1 if 2 * p * nbytes > 4 * MALL_BYTES else min(64, sets_for(2 * p * nbytes))
+            ins = [t] + [t.clone() for _ in range(sets - 1)]
+            outs = [torch.empty_like(t) for _ in range(sets)]
+            for algo in ("ring", "rd", "rabenseifner", "tree"):
+                calls = [vc.prepare_allreduce(algo, ins[i], outs[i]) for i in range(sets)]
+                K = 200 if nbytes < 2 ** 20 else 15
+                _, ms = time_launches(calls, K, 3)
+                key = f"p{p}_{'1KiB' if nbytes < 2 ** 20 else '64MiB'}_{algo}"
+                res[key] = roof(f"reduce_kernel<f32, {algo}, p={p}>", 2 * p * nbytes, ms)
+            if cpu_leg and nbytes > 2 ** 20:
+                import oracle
+                w = min(n, 1 << 18)
+                offs = [c * (n // p) + min(c, n % p) for c in range(p + 1)]
+                lo = max(0, offs[1] - w // 2)
+                xw = [t[r, lo:lo + w].cpu().numpy() for r in range(p)]
+                ok, t_or, reps = True, 0.0, 0
+                for algo in ("ring", "rd", "rabenseifner", "tree"):
+                    vc.vcoll_allreduce(algo, t, outs[0])
+                    (want, _), k, el = oracle_seconds(lambda: oracle.allreduce(xw, algo, "f32", n=n, lo=lo), 0.3)
+                    t_or += el
+                    reps += k
+                    ok = ok and np.array_equal(outs[0][:, lo:lo + w].cpu().numpy().view(np.uint32),
+                                               np.stack(want).view(np.uint32))
+                res[f"p{p}_64MiB_parity_vs_oracle"] = "bit-exact" if ok else "MISMATCH"
+                res[f"p{p}_64MiB_cpu_baseline"] = {
+                    "value": round(reps * 2 * p * w * 4 / t_or / 1e9, 3), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle",
+                    "sample": f"windowed oracle, all four algorithms, {reps} runs over elements [{lo}, {lo + w}) "
+                              f"of all {p} ranks ({100 * w / n:.2f} % of the vector), {t_or:.1f} s, numpy single "
+                              f"thread"}
+            del t, ins, outs
+            torch.cuda.empty_cache()
+    return res
+
+
 def extras(vc, torch, h, args):
     import numpy as np
     import workloads
+    cpu_leg = not args.no_cpu_baseline
     ex = {}
     p, n, S = h["p"], h["n"], h["S"]
     base = h["base"]
     steps, warm = max(20, args.steps // 4), 5
+    scrub = h["scrub"]
+    ex["event_pair_floor_us"] = event_pair_floor(vc, torch)
+    ex["ceilings"] = ceilings(vc, torch, p * S)
+    ex["cfg1"] = cfg1(vc, torch, scrub, min(3.0, args.cpu_seconds), cpu_leg)
 
     # other algorithms on the same bucket (fused, one pass each)
     R = sets_for(2 * p * S)
@@ -209,44 +571,38 @@ def extras(vc, torch, h, args):
     for algo in ("rd", "rabenseifner", "tree"):
         calls = [vc.prepare_allreduce(algo, ins[i], outs[i]) for i in range(R)]
         _, mean_ms = time_launches(calls, steps, warm)
-        ex[f"ddp_bucket_{algo}_fused"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+        ex[f"ddp_bucket_{algo}_fused"] = roof(f"reduce_kernel<f32, {algo}, p=8>", 2 * p * S, mean_ms)
     # hierarchical (2 groups of 4, and 4 of 2) on the same bucket
     for nodes, local in ((2, 4), (4, 2)):
         calls = [vc.prepare_allreduce_hierarchical(nodes, local, ins[i], outs[i]) for i in range(R)]
         _, mean_ms = time_launches(calls, steps, warm)
-        ex[f"ddp_bucket_hierarchical_{nodes}x{local}_fused"] = {"GBps": rate(2 * p * S, mean_ms),
-                                                               "us": round(mean_ms * 1e3, 1)}
+        ex[f"ddp_bucket_hierarchical_{nodes}x{local}_fused"] = roof(f"hier_kernel<f32, {nodes}, {local}>",
+                                                                   2 * p * S, mean_ms)
     # rooted collectives on the same bucket: broadcast of one rank's 25 MiB to
     # 8 receive buffers (S read + 8 S written), reduce to rank 0 (8 S + S)
     bsrc = [base[i % p].clone() for i in range(R)]
     calls = [vc.prepare_broadcast(bsrc[i], outs[i], 0) for i in range(R)]
     _, mean_ms = time_launches(calls, steps, warm)
-    ex["ddp_bucket_broadcast_p8"] = {"GBps": rate((p + 1) * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    ex["ddp_bucket_broadcast_p8"] = roof("broadcast_kernel<f32, 4 vectors per thread, 64 threads>", (p + 1) * S,
+                                         mean_ms)
     rout = [torch.empty(n, device="cuda") for _ in range(R)]
     calls = [vc.prepare_reduce(ins[i], rout[i], 0) for i in range(R)]
     _, mean_ms = time_launches(calls, steps, warm)
-    ex["ddp_bucket_reduce_tree_p8"] = {"GBps": rate((p + 1) * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    ex["ddp_bucket_reduce_tree_p8"] = roof("reduce_kernel<f32, tree, p=8, reduce>", (p + 1) * S, mean_ms)
     del bsrc, rout
     # warm: one set reused back to back (partly served by the Infinity Cache)
     call = vc.prepare_allreduce("ring", ins[0], outs[0])
     _, mean_ms = time_launches([call], steps, warm)
-    ex["ddp_bucket_ring_fused_warm_cache"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
+    ex["ddp_bucket_ring_fused_warm_cache"] = roof("ring all-reduce, one buffer set (warm)", 2 * p * S, mean_ms)
     # unfused ring: reduce-scatter kernel then all-gather kernel
     rs_out = [[torch.empty(n // p, device="cuda") for _ in range(p)] for _ in range(R)]
     rs = [vc.prepare_reduce_scatter("ring", ins[i], rs_out[i]) for i in range(R)]
     ag = [vc.prepare_all_gather("ring", rs_out[i], outs[i]) for i in range(R)]
     pair = [lambda i=i: (rs[i](), ag[i]()) for i in range(R)]
     _, mean_ms = time_launches(pair, steps, warm)
-    ex["ddp_bucket_ring_unfused_rs_then_ag"] = {"GBps": rate(2 * p * S + 2 * S, mean_ms),
-                                                "us": round(mean_ms * 1e3, 1),
-                                                "algorithmic_bytes": 2 * p * S + 2 * S}
-    # plain copy ceiling over the same bytes (p*S read, p*S written)
-    src = [torch.empty(p * n, device="cuda") for _ in range(R)]
-    dst = [torch.empty(p * n, device="cuda") for _ in range(R)]
-    copies = [vc.prepare_bench_copy(dst[i], src[i]) for i in range(R)]
-    _, mean_ms = time_launches(copies, steps, warm)
-    ex["copy_ceiling_same_bytes"] = {"GBps": rate(2 * p * S, mean_ms), "us": round(mean_ms * 1e3, 1)}
-    del ins, outs, rs_out, src, dst
+    ex["ddp_bucket_ring_unfused_rs_then_ag"] = roof("reduce-scatter kernel + all-gather kernel",
+                                                    2 * p * S + 2 * S, mean_ms)
+    del ins, outs, rs_out
     torch.cuda.empty_cache()
 
     # stepwise execution (one launch per algorithm step, messages through
@@ -256,7 +612,7 @@ def extras(vc, torch, h, args):
         m = nbytes // 4
         g = torch.Generator(device="cuda").manual_seed(6)
         t = torch.randn((8, m), device="cuda", generator=g)
-        R2 = sets_for(2 * 8 * nbytes)
+        R2 = min(64, sets_for(2 * 8 * nbytes))
         ts = [t.clone() for _ in range(R2)]
         os_ = [torch.empty_like(t) for _ in range(R2)]
         for algo in ("ring", "rd", "rabenseifner", "tree"):
@@ -277,13 +633,13 @@ def extras(vc, torch, h, args):
         m = nbytes // 4
         g = torch.Generator(device="cuda").manual_seed(5)
         t = torch.randn((8, m), device="cuda", generator=g)
-        R2 = sets_for(2 * 8 * nbytes)
+        R2 = min(64, sets_for(2 * 8 * nbytes))
         ts = [t.clone() for _ in range(R2)]
         os_ = [torch.empty_like(t) for _ in range(R2)]
         for algo in ("ring", "rd", "rabenseifner", "tree"):
             calls = [vc.prepare_allreduce(algo, ts[i], os_[i]) for i in range(R2)]
             _, mean_ms = time_launches(calls, steps, warm)
-            ex[f"p8_{label}_{algo}"] = {"GBps": rate(2 * 8 * nbytes, mean_ms), "us": round(mean_ms * 1e3, 2)}
+            ex[f"p8_{label}_{algo}"] = roof(f"reduce_kernel<f32, {algo}, p=8>", 2 * 8 * nbytes, mean_ms)
         del t, ts, os_
     torch.cuda.empty_cache()
 
@@ -308,147 +664,10 @@ def extras(vc, torch, h, args):
     del t, o
     torch.cuda.empty_cache()
 
-    # p = 16, 192 MiB bf16 per rank, float32 accumulation
-    P16, N16 = 16, 100_663_296
-    g = torch.Generator(device="cuda").manual_seed(3)
-    t16 = (torch.rand((P16, N16), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
-    o16 = torch.empty_like(t16)
-    S16 = N16 * 2
-    for algo in ("ring", "rabenseifner"):
-        call = vc.prepare_allreduce(algo, t16, o16)
-        _, mean_ms = time_launches([call], 30, 5)
-        ex[f"hier16_bf16_{algo}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms), "us": round(mean_ms * 1e3, 1)}
-    for nodes, local in ((2, 8), (4, 4)):
-        call = vc.prepare_allreduce_hierarchical(nodes, local, t16, o16)
-        _, mean_ms = time_launches([call], 30, 5)
-        ex[f"hier16_bf16_hierarchical_{nodes}x{local}_fused"] = {"GBps": rate(2 * P16 * S16, mean_ms),
-                                                                "us": round(mean_ms * 1e3, 1)}
-    rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
-    for algo, ag_algo in (("ring", "ring"), ("rabenseifner", "rd")):
-        call = vc.prepare_reduce_scatter(algo, t16, rs16)
-        _, ms_rs = time_launches([call], 30, 5)
-        call = vc.prepare_all_gather(ag_algo, rs16, o16)
-        _, ms_ag = time_launches([call], 30, 5)
-        ex[f"hier16_bf16_{algo}_reduce_scatter"] = {"GBps": rate(P16 * S16 + S16, ms_rs), "us": round(ms_rs * 1e3, 1)}
-        ex[f"hier16_bf16_{ag_algo}_all_gather"] = {"GBps": rate(S16 + P16 * S16, ms_ag), "us": round(ms_ag * 1e3, 1)}
-    del t16, o16, rs16
-    torch.cuda.empty_cache()
-
-    # MoE dispatch (fused gather) and combine (fused scatter), p = 8
-    M = workloads.MOE
-    p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
-    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
-    splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
-    g = torch.Generator(device="cuda").manual_seed(4)
-    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
-    srcs = [torch.from_numpy(src_rows[i]).cuda() for i in range(p8)]
-    dsts = [torch.from_numpy(dst_rows[i]).cuda() for i in range(p8)]
-    rb = H * 2
-    rows = int(splits.sum())
-    recv = vc.vcoll_all_to_all(toks, splits, src_rows=srcs)
-    back = vc.vcoll_all_to_all(recv, splits.T, dst_rows=dsts, dst_table_rows=[T * K] * p8)
-    disp = lambda: vc.vcoll_all_to_all(toks, splits, recv=recv, src_rows=srcs)          # noqa: E731
-    comb = lambda: vc.vcoll_all_to_all(recv, splits.T, recv=back, dst_rows=dsts)         # noqa: E731
-    _, ms_d = time_launches([disp], 10, 2)
-    _, ms_c = time_launches([comb], 10, 2)
-    ok = all(torch.equal(back[i].view(T, K, H).view(torch.int16),
-                         toks[i].view(torch.int16).unsqueeze(1).expand(T, K, H)) for i in range(p8))
-    # the plain block transpose on the same splits (send buffers already in
-    # destination-block order, no gather)
-    plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
-                  for i in range(p8)]
-    plain_recv = vc.vcoll_all_to_all(plain_send, splits)
-    a2a = lambda: vc.vcoll_all_to_all(plain_send, splits, recv=plain_recv)               # noqa: E731
-    _, ms_a = time_launches([a2a], 10, 2)
-    ex["moe_all_to_all_plain"] = {"GBps": rate(2 * rows * rb, ms_a), "us": round(ms_a * 1e3, 1),
-                                  "algorithmic_bytes": 2 * rows * rb}
-    del plain_send, plain_recv
-    ex["moe_dispatch_fused_gather"] = {"GBps": rate(p8 * T * rb + rows * rb, ms_d), "us": round(ms_d * 1e3, 1),
-                                       "algorithmic_bytes": p8 * T * rb + rows * rb,
-                                       "rows_to_rank0": float(splits[:, 0].sum() / rows)}
-    ex["moe_combine_fused_scatter"] = {"GBps": rate(2 * rows * rb, ms_c), "us": round(ms_c * 1e3, 1),
-                                       "algorithmic_bytes": 2 * rows * rb,
-                                       "combine_of_dispatch_is_identity": bool(ok)}
-    # dispatch variants: FP8 payload (quantised at the sender) and
-    # per-destination deduplication (unique rows + local expansion)
-    src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
-    f8 = vc.vcoll_moe_dispatch_fp8(toks, splits, src_g)
-    fp8_call = lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, f8)        # noqa: E731
-    _, ms_f = time_launches([fp8_call], 10, 2)
-    orb = H + H // 32
-    ex["moe_dispatch_fp8_fused_gather_quantise"] = {
-        "GBps": rate(rows * rb + rows * orb, ms_f), "us": round(ms_f * 1e3, 1),
-        "algorithmic_bytes": rows * rb + rows * orb, "payload_bytes_per_row": orb}
-    # token-major dispatch: each token row read once, written to its 8 slots
-    slots = vc.vcoll_moe_slots(splits, dst_rows, K)
-    slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
-    recv_rows = splits.sum(axis=0)
-    # token-major combine: each (token, slot) row pulled from its expert output
-    tc = vc.vcoll_moe_combine(recv, slots_g, T, K)
-    tc_ok = all(torch.equal(tc[i].view(torch.int16), back[i].view(torch.int16)) for i in range(p8))
-    pull = lambda: vc.vcoll_moe_combine(recv, slots_g, T, K, out=tc)                        # noqa: E731
-    _, ms_tc = time_launches([pull], 10, 2)
-    ex["moe_combine_token_major"] = {"GBps": rate(2 * rows * rb, ms_tc), "us": round(ms_tc * 1e3, 1),
-                                     "algorithmic_bytes": 2 * rows * rb, "equals_scatter_combine": bool(tc_ok)}
-    del tc
-    tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
-    tm_ok = all(torch.equal(tm[j].view(torch.int16), recv[j].view(torch.int16)) for j in range(p8))
-    tm8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
-    tm8_ok = all(torch.equal(tm8[j], f8[j]) for j in range(p8))
-    push = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=tm)              # noqa: E731
-    push8 = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=tm8)  # noqa: E731
-    _, ms_p = time_launches([push], 10, 2)
-    _, ms_p8 = time_launches([push8], 10, 2)
-    ex["moe_dispatch_token_major"] = {"GBps": rate(p8 * T * rb + rows * rb, ms_p), "us": round(ms_p * 1e3, 1),
-                                      "algorithmic_bytes": p8 * T * rb + rows * rb,
-                                      "equals_gather_dispatch": bool(tm_ok)}
-    ex["moe_dispatch_token_major_fp8"] = {"GBps": rate(p8 * T * rb + rows * orb, ms_p8),
-                                          "us": round(ms_p8 * 1e3, 1),
-                                          "algorithmic_bytes": p8 * T * rb + rows * orb,
-                                          "equals_row_major_fp8": bool(tm8_ok)}
-    su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p8)
-    src_ug = [torch.from_numpy(x).cuda() for x in src_u]
-    exp_g = [torch.from_numpy(x).cuda() for x in expand]
-    ru = vc.vcoll_all_to_all(toks, su, src_rows=src_ug)
-    ex_out = vc.vcoll_moe_expand(ru, exp_g)
-    rows_u = int(su.sum())
-    d1 = lambda: vc.vcoll_all_to_all(toks, su, recv=ru, src_rows=src_ug)         # noqa: E731
-    d2 = lambda: vc.vcoll_moe_expand(ru, exp_g, ex_out)                           # noqa: E731
-    _, ms_u = time_launches([d1], 10, 2)
-    _, ms_x = time_launches([d2], 10, 2)
-    # token-major expansion: each received unique row read once, pushed to its copies
-    xslots = [torch.from_numpy(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)).cuda()
-              for j in range(p8)]
-    xcounts = [len(e) for e in expand]
-    ex_tm = vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K)
-    tm_x_ok = all(torch.equal(ex_tm[j].view(torch.int16), ex_out[j].view(torch.int16)) for j in range(p8))
-    d3 = lambda: vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K, out=ex_tm)  # noqa: E731
-    _, ms_xt = time_launches([d3], 10, 2)
-    # token-major deduplicated dispatch: each token read once (and quantised
-    # once for FP8), written once per destination rank
-    dsl = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
-    dsl_g = [torch.from_numpy(np.ascontiguousarray(dsl[i])).cuda() for i in range(p8)]
-    urows = su.sum(axis=0)
-    ru_tm = vc.vcoll_moe_dispatch(toks, dsl_g, urows, K)
-    ru8 = vc.vcoll_moe_dispatch_fp8(toks, su, src_ug)
-    ru8_tm = vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, fp8=True)
-    dd_ok = all(torch.equal(ru_tm[j].view(torch.int16), ru[j].view(torch.int16)) and torch.equal(ru8_tm[j], ru8[j])
-                for j in range(p8))
-    d4 = lambda: vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, recv=ru_tm)            # noqa: E731
-    d5 = lambda: vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, fp8=True, recv=ru8_tm)  # noqa: E731
-    d6 = lambda: vc.vcoll_moe_dispatch_fp8(toks, su, src_ug, ru8)                    # noqa: E731
-    _, ms_dt = time_launches([d4], 10, 2)
-    _, ms_d8t = time_launches([d5], 10, 2)
-    _, ms_d8 = time_launches([d6], 10, 2)
-    offrank = lambda sp: int(sp.sum() - np.trace(sp))                              # noqa: E731
-    ex["moe_dispatch_dedup"] = {
-        "rows": rows_u, "rows_plain": rows, "offrank_rows": offrank(su), "offrank_rows_plain": offrank(splits),
-        "all_to_all_us": round(ms_u * 1e3, 1), "expand_us": round(ms_x * 1e3, 1),
-        "expand_token_major_us": round(ms_xt * 1e3, 1), "expand_token_major_equal": bool(tm_x_ok),
-        "all_to_all_token_major_us": round(ms_dt * 1e3, 1), "fp8_row_major_us": round(ms_d8 * 1e3, 1),
-        "fp8_token_major_us": round(ms_d8t * 1e3, 1), "token_major_equal": bool(dd_ok),
-        "message_bytes_bf16": offrank(su) * rb, "message_bytes_fp8": offrank(su) * orb,
-        "message_bytes_plain_bf16": offrank(splits) * rb}
+    ex["cfg3"] = cfg3(vc, torch, scrub, cpu_leg)
+    ex["cfg4"] = cfg4(vc, torch, cpu_leg)
+    ex["moe_variants"] = moe_variants(vc, torch)
+    ex["cfg5"] = cfg5(vc, torch, cpu_leg)
 
     # the host rows: partition + step schedule + ledger of a collective (the
     # record-free ledger call builds every message and sums it per rank) and
@@ -460,14 +679,98 @@ def extras(vc, torch, h, args):
             fn()
             t.append(time.perf_counter() - t0)
         return round(float(np.median(t)) * 1e6, 1)
+    M = workloads.MOE
+    topk = np.stack([workloads.moe_topk(r, M["tokens"], M["experts"], M["topk"]) for r in range(M["p"])])
     n8 = workloads.DDP_BUCKET["n"]
     host = {"ledger_ring_p8_ddp_bucket_us": host_us(lambda: vc.vcoll_ledger_summary("allreduce", "ring", 8, n8), 200)}
     for algo in ("ring", "rd", "rabenseifner", "tree"):
         host[f"ledger_{algo}_p72_us"] = host_us(lambda: vc.vcoll_ledger_summary("allreduce", algo, 72, 72 << 20), 50)
     host["ledger_ring_p72_messages"] = vc.vcoll_ledger_summary("allreduce", "ring", 72, 72 << 20)[0]
-    host["moe_plan_8x4096x8_us"] = host_us(lambda: vc.vcoll_moe_plan(topk, E // p8), 20)
+    host["moe_plan_8x4096x8_us"] = host_us(lambda: vc.vcoll_moe_plan(topk, M["experts"] // M["p"]), 20)
     ex["host_schedule_and_ledger"] = host
     return ex
+
+
+def moe_variants(vc, torch) -> dict:
+    """The other MoE dispatch/combine forms on the same workload: the
+    row-major gathering dispatch and scattering combine (generic all-to-all
+    with index maps), the row-major FP8 dispatch, and the per-destination
+    deduplicated dispatch with its local expansion."""
+    import numpy as np
+    import workloads
+    M = workloads.MOE
+    p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
+    splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
+    srcs = [torch.from_numpy(src_rows[i]).cuda() for i in range(p8)]
+    dsts = [torch.from_numpy(dst_rows[i]).cuda() for i in range(p8)]
+    rb, orb = H * 2, H + H // 32
+    rows = int(splits.sum())
+    uniq = p8 * T * rb                              # every token row once: the algorithmic read of a dispatch
+    res = {}
+    recv = vc.vcoll_all_to_all(toks, splits, src_rows=srcs)
+    back = vc.vcoll_all_to_all(recv, splits.T, dst_rows=dsts, dst_table_rows=[T * K] * p8)
+    disp = lambda: vc.vcoll_all_to_all(toks, splits, recv=recv, src_rows=srcs)          # noqa: E731
+    comb = lambda: vc.vcoll_all_to_all(recv, splits.T, recv=back, dst_rows=dsts)         # noqa: E731
+    _, ms = time_launches([disp], 10, 2)
+    res["dispatch_row_major_gather"] = roof("all_to_all_kernel<256> with gather map", uniq + rows * rb, ms,
+                                            note="reads each token row once per (token, expert) pair: 8x the "
+                                                 "unique token bytes")
+    _, ms = time_launches([comb], 10, 2)
+    res["combine_row_major_scatter"] = roof("all_to_all_kernel<256> with scatter map", 2 * rows * rb, ms)
+    src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
+    f8 = vc.vcoll_moe_dispatch_fp8(toks, splits, src_g)
+    fp8_call = lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, f8)               # noqa: E731
+    _, ms = time_launches([fp8_call], 10, 2)
+    res["dispatch_fp8_row_major_gather"] = roof("dispatch_fp8_kernel", uniq + rows * orb, ms,
+                                                note="reads each token row once per (token, expert) pair")
+    del f8, recv, back
+    su, src_u, expand = vc.vcoll_moe_plan_dedup(topk, E // p8)
+    src_ug = [torch.from_numpy(x).cuda() for x in src_u]
+    exp_g = [torch.from_numpy(x).cuda() for x in expand]
+    ru = vc.vcoll_all_to_all(toks, su, src_rows=src_ug)
+    ex_out = vc.vcoll_moe_expand(ru, exp_g)
+    rows_u = int(su.sum())
+    d1 = lambda: vc.vcoll_all_to_all(toks, su, recv=ru, src_rows=src_ug)         # noqa: E731
+    d2 = lambda: vc.vcoll_moe_expand(ru, exp_g, ex_out)                           # noqa: E731
+    _, ms_u = time_launches([d1], 10, 2)
+    _, ms_x = time_launches([d2], 10, 2)
+    xslots = [torch.from_numpy(vc.vcoll_moe_expand_slots(int(su[:, j].sum()), expand[j], K)).cuda()
+              for j in range(p8)]
+    xcounts = [len(e) for e in expand]
+    ex_tm = vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K)
+    tm_x_ok = all(torch.equal(ex_tm[j].view(torch.int16), ex_out[j].view(torch.int16)) for j in range(p8))
+    d3 = lambda: vc.vcoll_moe_expand_token_major(ru, xslots, xcounts, K, out=ex_tm)  # noqa: E731
+    _, ms_xt = time_launches([d3], 10, 2)
+    dsl = vc.vcoll_moe_dedup_slots(su, src_u, T, K)
+    dsl_g = [torch.from_numpy(np.ascontiguousarray(dsl[i])).cuda() for i in range(p8)]
+    urows = su.sum(axis=0)
+    ru_tm = vc.vcoll_moe_dispatch(toks, dsl_g, urows, K)
+    ru8 = vc.vcoll_moe_dispatch_fp8(toks, su, src_ug)
+    ru8_tm = vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, fp8=True)
+    dd_ok = all(torch.equal(ru_tm[j].view(torch.int16), ru[j].view(torch.int16)) and torch.equal(ru8_tm[j], ru8[j])
+                for j in range(p8))
+    d4 = lambda: vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, recv=ru_tm)            # noqa: E731
+    d5 = lambda: vc.vcoll_moe_dispatch(toks, dsl_g, urows, K, fp8=True, recv=ru8_tm)  # noqa: E731
+    _, ms_dt = time_launches([d4], 10, 2)
+    _, ms_d8t = time_launches([d5], 10, 2)
+    offrank = lambda sp: int(sp.sum() - np.trace(sp))                              # noqa: E731
+    res["dispatch_dedup_token_major"] = roof("dispatch_push_kernel<bf16, 256>, deduplicated plan",
+                                             uniq + rows_u * rb, ms_dt)
+    res["dispatch_dedup_token_major_fp8"] = roof("dispatch_push_kernel<fp8, 512>, deduplicated plan",
+                                                 uniq + rows_u * orb, ms_d8t)
+    res["dedup"] = {
+        "rows": rows_u, "rows_plain": rows, "offrank_rows": offrank(su), "offrank_rows_plain": offrank(splits),
+        "all_to_all_gather_us": round(ms_u * 1e3, 1), "expand_us": round(ms_x * 1e3, 1),
+        "expand_token_major_us": round(ms_xt * 1e3, 1), "expand_token_major_equal": bool(tm_x_ok),
+        "token_major_equal_row_major": bool(dd_ok),
+        "message_bytes_bf16": offrank(su) * rb, "message_bytes_fp8": offrank(su) * orb,
+        "message_bytes_plain_bf16": offrank(splits) * rb}
+    del toks, ru, ex_out, ex_tm, ru_tm, ru8, ru8_tm
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -483,8 +786,8 @@ def _csv_rows(root: str, suffix: str):
     return rows
 
 
-HEADLINE_KERNEL = "reduce_kernel<0, 0, 8, 2, false, true, 256>"
-COPY_KERNEL = "copy_kernel"
+HEADLINE_KERNEL = "burst_ring_kernel<0, 25>"
+COPY_KERNEL = "copy_kernel<2, 64"
 
 
 def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: str) -> int:
@@ -572,133 +875,201 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
     return 0
 
 
-# kernel (a substring of its rocprofv3 name) -> (workload, algorithmic bytes per launch), for the
-# counter-traffic pass: each workload below uses its own kernel instantiation
-TRAFFIC_SET = {
-    "reduce_kernel<0, 0, 8, 2, false, true, 256>": ("fused ring all-reduce, p=8 x 25 MiB f32", 419_430_400),
-    "hier_kernel<0, 2, 4, true>": ("hierarchical 2x4 all-reduce, p=8 x 25 MiB f32", 419_430_400),
-    "reduce_kernel<0, 3, 8, 2, true, false, 256>": ("tree reduce to one root, p=8 x 25 MiB f32", 235_929_600),
-    "broadcast_kernel<4, 4, 64, true>": ("broadcast of 25 MiB f32 to 8 buffers", 235_929_600),
-    "reduce_kernel<1, 0, 16, 1, false, true, 64>": ("fused ring all-reduce, p=16 x 192 MiB bf16", 6_442_450_944),
-    "reduce_kernel<1, 0, 16, 1, true, false, 64>": ("ring reduce-scatter, p=16 x 192 MiB bf16", 3_422_552_064),
-    "all_gather_kernel<2, 1, 64, false>": ("all-gather of 12 MiB bf16 blocks, p=16", 3_422_552_064),
-    "all_to_all_kernel<1024>": ("variable-split all-to-all of the MoE splits (plain)", None),
-    "dispatch_push_kernel<false, 256>": ("token-major MoE dispatch, bf16", None),
-    "dispatch_push_kernel<true, 512>": ("token-major MoE dispatch, FP8", None),
-    "combine_pull_kernel<512>": ("token-major MoE combine", None),
-    "dispatch_fp8_kernel": ("row-major FP8 dispatch (gather + quantise)", None),
-    "copy_kernel": ("plain copy, 200 MiB read + 200 MiB written (counter scale)", 419_430_400),
+# Counter-traffic workloads, in launch order. Each entry: (label, kernel
+# name substring as rocprofv3 prints it, algorithmic bytes per launch or
+# None when the routing decides them, printed by the run). A one-workgroup
+# marker launch separates consecutive workloads in the counter records.
+TRAFFIC_GROUPS = {
+    "hot": [
+        ("two-phase ring all-reduce, p=8 x 25 MiB f32 (headline)", "burst_ring_kernel<0, 25>", 419_430_400),
+        ("hierarchical 2x4 all-reduce, p=8 x 25 MiB f32", "hier_kernel<0, 2, 4, true>", 419_430_400),
+        ("tree reduce to one root, p=8 x 25 MiB f32", "reduce_kernel<0, 3, 8, 2, true, false, 256>", 235_929_600),
+        ("broadcast of 25 MiB f32 to 8 buffers", "broadcast_kernel<4, 4, 64, true>", 235_929_600),
+        ("copy, 200 MiB read + 200 MiB written (counter scale)", "copy_kernel<2, 64", 419_430_400),
+        ("fused ring all-reduce, p=16 x 192 MiB bf16", "reduce_kernel<1, 0, 16, 1, false, true, 64>", 6_442_450_944),
+        ("ring reduce-scatter, p=16 x 192 MiB bf16", "reduce_kernel<1, 0, 16, 1, true, false, 64>", 3_422_552_064),
+        ("all-gather of 12 MiB bf16 blocks, p=16", "all_gather_kernel<2, 1, 64, false>", 3_422_552_064),
+        ("variable-split all-to-all of the MoE splits (plain)", "all_to_all_kernel<1024>", None),
+        ("token-major MoE dispatch, bf16", "dispatch_push_kernel<false, 256>", None),
+        ("token-major MoE dispatch, FP8", "dispatch_push_kernel<true, 512>", None),
+        ("token-major MoE combine", "combine_pull_kernel<512>", None),
+        ("row-major MoE dispatch, gather map (all-to-all)", "all_to_all_kernel<256>", None),
+        ("row-major FP8 dispatch (gather + quantise)", "dispatch_fp8_kernel", None),
+    ],
+    "sweep": [
+        ("copy, 200 MiB read + 200 MiB written (counter scale)", "copy_kernel<2, 64", 419_430_400),
+        ("ring all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 0, 0, 1, false, false, 256>",
+         2 * 72 * 16 * 2 ** 20),
+        ("tree all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
+         2 * 72 * 16 * 2 ** 20),
+        ("ring all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 0, 0, 1, false, false, 256>",
+         2 * 72 * 256 * 2 ** 20),
+        ("tree all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
+         2 * 72 * 256 * 2 ** 20),
+        ("ring reduce-scatter, p=72 x 64 MiB f32 (unaligned chunk starts)",
+         "reduce_kernel<0, 0, 0, 1, true, false, 256>", 73 * 64 * 2 ** 20),
+        ("ring all-reduce, p=16 x 16 MiB f32", "burst_ring_kernel<0, 25>", 2 * 16 * 16 * 2 ** 20),
+        ("ring all-reduce, p=16 x 64 MiB f32", "reduce_kernel<0, 0, 16, 1, false, true, 64>", 2 * 16 * 64 * 2 ** 20),
+        ("ring all-reduce, p=8 x 1 GiB f32", "reduce_kernel<0, 0, 8, 2, false, true, 256>", 2 * 8 * 2 ** 30),
+    ],
 }
 
 
-def traffic_set(vc, torch, launches: int) -> int:
-    """Launch each kernel of TRAFFIC_SET `launches` times (after one warm-up),
-    for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs. Prints the MoE
-    kernels' algorithmic bytes (they depend on the routing) as one JSON line."""
+def traffic_set(vc, torch, launches: int, group: str) -> int:
+    """Launch each workload of TRAFFIC_GROUPS[group] `launches` times (after
+    one warm-up), a marker launch before each, for rocprofv3 --pmc
+    FETCH_SIZE / WRITE_SIZE runs. Prints the group's manifest (labels,
+    kernels, algorithmic bytes, the routing-dependent ones filled in) as one
+    JSON line."""
     import numpy as np
     import workloads
 
+    marker_buf = torch.empty(4 * 64, device="cuda")
+    marker = vc.prepare_bench_stream("write", marker_buf)          # one workgroup of 64
+
     def run(call):
+        torch.cuda.synchronize()
+        marker()
         for _ in range(launches + 1):
             call()
         torch.cuda.synchronize()
 
-    out = {}
-    p, n = 8, workloads.DDP_BUCKET["n"]
+    def copy_ref():
+        src, dst = torch.empty(8 * 6_553_600, device="cuda"), torch.empty(8 * 6_553_600, device="cuda")
+        run(vc.prepare_bench_stream("copy", dst, src))
+
+    filled = {}
     g = torch.Generator(device="cuda").manual_seed(9)
-    t = torch.randn((p, n), device="cuda", generator=g) * 1e-3
-    o = torch.empty_like(t)
-    run(vc.prepare_allreduce("ring", t, o))
-    run(vc.prepare_allreduce_hierarchical(2, 4, t, o))
-    root_out = torch.empty(n, device="cuda")
-    run(vc.prepare_reduce(t, root_out, 0))
-    run(vc.prepare_broadcast(t[0].clone(), o, 0))
-    src, dst = torch.empty(p * n, device="cuda"), torch.empty(p * n, device="cuda")
-    run(vc.prepare_bench_copy(dst, src))
-    del t, o, root_out, src, dst
-    torch.cuda.empty_cache()
-    P16, N16 = 16, 100_663_296
-    t16 = (torch.rand((P16, N16), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
-    o16 = torch.empty_like(t16)
-    run(vc.prepare_allreduce("ring", t16, o16))
-    rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
-    run(vc.prepare_reduce_scatter("ring", t16, rs16))
-    run(vc.prepare_all_gather("ring", rs16, o16))
-    del t16, o16, rs16
-    torch.cuda.empty_cache()
-    M = workloads.MOE
-    p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
-    topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
-    splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
-    toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
-    rb, orb, rows = 2 * H, H + H // 32, int(splits.sum())
-    plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
-                  for i in range(p8)]
-    plain_recv = vc.vcoll_all_to_all(plain_send, splits)
-    run(lambda: vc.vcoll_all_to_all(plain_send, splits, recv=plain_recv))
-    del plain_send
-    slots = vc.vcoll_moe_slots(splits, dst_rows, K)
-    slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
-    recv_rows = splits.sum(axis=0)
-    tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
-    run(lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=tm))
-    tm8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
-    run(lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=tm8))
-    tc = vc.vcoll_moe_combine(tm, slots_g, T, K)
-    run(lambda: vc.vcoll_moe_combine(tm, slots_g, T, K, out=tc))
-    src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
-    f8 = vc.vcoll_moe_dispatch_fp8(toks, splits, src_g)
-    run(lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, f8))
-    out["all_to_all_kernel<1024>"] = 2 * rows * rb
-    out["dispatch_push_kernel<false, 256>"] = p8 * T * rb + rows * rb
-    out["dispatch_push_kernel<true, 512>"] = p8 * T * rb + rows * orb
-    out["combine_pull_kernel<512>"] = 2 * rows * rb
-    out["dispatch_fp8_kernel"] = rows * rb + rows * orb
-    print(json.dumps({"moe_algorithmic_bytes": out}), flush=True)
+    if group == "hot":
+        p, n = 8, workloads.DDP_BUCKET["n"]
+        t = torch.randn((p, n), device="cuda", generator=g) * 1e-3
+        o = torch.empty_like(t)
+        run(vc.prepare_allreduce("ring", t, o))
+        run(vc.prepare_allreduce_hierarchical(2, 4, t, o))
+        root_out = torch.empty(n, device="cuda")
+        run(vc.prepare_reduce(t, root_out, 0))
+        run(vc.prepare_broadcast(t[0].clone(), o, 0))
+        copy_ref()
+        del t, o, root_out
+        torch.cuda.empty_cache()
+        P16, N16 = 16, 100_663_296
+        t16 = (torch.rand((P16, N16), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
+        o16 = torch.empty_like(t16)
+        run(vc.prepare_allreduce("ring", t16, o16))
+        rs16 = [torch.empty(N16 // P16, dtype=torch.bfloat16, device="cuda") for _ in range(P16)]
+        run(vc.prepare_reduce_scatter("ring", t16, rs16))
+        run(vc.prepare_all_gather("ring", rs16, o16))
+        del t16, o16, rs16
+        torch.cuda.empty_cache()
+        M = workloads.MOE
+        p8, T, H, E, K = M["p"], M["tokens"], M["hidden"], M["experts"], M["topk"]
+        topk = np.stack([workloads.moe_topk(r, T, E, K) for r in range(p8)])
+        splits, src_rows, dst_rows = vc.vcoll_moe_plan(topk, E // p8)
+        toks = [torch.randn((T, H), device="cuda", generator=g).to(torch.bfloat16) for _ in range(p8)]
+        rb, orb, rows = 2 * H, H + H // 32, int(splits.sum())
+        plain_send = [torch.randn((int(splits[i].sum()), H), device="cuda", generator=g).to(torch.bfloat16)
+                      for i in range(p8)]
+        plain_recv = vc.vcoll_all_to_all(plain_send, splits)
+        run(lambda: vc.vcoll_all_to_all(plain_send, splits, recv=plain_recv))
+        del plain_send, plain_recv
+        slots = vc.vcoll_moe_slots(splits, dst_rows, K)
+        slots_g = [torch.from_numpy(np.ascontiguousarray(slots[i])).cuda() for i in range(p8)]
+        recv_rows = splits.sum(axis=0)
+        tm = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
+        run(lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=tm))
+        tm8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
+        run(lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=tm8))
+        tc = vc.vcoll_moe_combine(tm, slots_g, T, K)
+        run(lambda: vc.vcoll_moe_combine(tm, slots_g, T, K, out=tc))
+        srcs = [torch.from_numpy(src_rows[i]).cuda() for i in range(p8)]
+        run(lambda: vc.vcoll_all_to_all(toks, splits, recv=tm, src_rows=srcs))
+        src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
+        run(lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, tm8))
+        uniq = p8 * T * rb                          # every token row once
+        filled = {"all_to_all_kernel<1024>": 2 * rows * rb, "dispatch_push_kernel<false, 256>": uniq + rows * rb,
+                  "dispatch_push_kernel<true, 512>": uniq + rows * orb, "combine_pull_kernel<512>": 2 * rows * rb,
+                  "all_to_all_kernel<256>": uniq + rows * rb, "dispatch_fp8_kernel": uniq + rows * orb}
+    else:
+        copy_ref()
+        for p, mib, algos in ((72, 16, ("ring", "tree")), (72, 256, ("ring", "tree"))):
+            n = mib * 2 ** 18
+            t = torch.randn((p, n), device="cuda", generator=g)
+            o = torch.empty_like(t)
+            for algo in algos:
+                run(vc.prepare_allreduce(algo, t, o))
+            del t, o
+            torch.cuda.empty_cache()
+        n = 64 * 2 ** 18
+        t = torch.randn((72, n), device="cuda", generator=g)
+        rs = vc.vcoll_reduce_scatter("ring", t)
+        run(vc.prepare_reduce_scatter("ring", t, rs))
+        del t, rs
+        torch.cuda.empty_cache()
+        for p, mib in ((16, 16), (16, 64), (8, 1024)):
+            n = mib * 2 ** 18
+            t = torch.randn((p, n), device="cuda", generator=g)
+            o = torch.empty_like(t)
+            run(vc.prepare_allreduce("ring", t, o))
+            del t, o
+            torch.cuda.empty_cache()
+    manifest = [{"label": lab, "kernel": k, "algorithmic_bytes": b if b is not None else filled[k]}
+                for lab, k, b in TRAFFIC_GROUPS[group]]
+    print(json.dumps({"traffic_manifest": manifest, "group": group}), flush=True)
     return 0
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str, moe_json: str, command: str) -> int:
-    """Per-kernel HBM bytes per launch from the two counter runs of
-    --traffic-set, scaled by copy_kernel's readings, against each kernel's
-    algorithmic bytes: profiles/traffic_hot_kernels.md."""
-    with open(moe_json) as f:
-        moe = json.loads([ln for ln in f.read().splitlines() if "moe_algorithmic_bytes" in ln][-1])
-    algo_bytes = {k: (v[1] if v[1] is not None else moe["moe_algorithmic_bytes"][k]) for k, v in TRAFFIC_SET.items()}
+def summarize_traffic(fetch_dir: str, write_dir: str, manifest_log: str, command: str) -> int:
+    """Per-workload HBM bytes per launch from the two counter runs of
+    --traffic-set (FETCH_SIZE, WRITE_SIZE), scaled by the copy's readings,
+    against each workload's algorithmic bytes: a table in profiles/. The
+    counter records are cut into workloads at the marker launches."""
+    with open(manifest_log) as f:
+        info = json.loads([ln for ln in f.read().splitlines() if "traffic_manifest" in ln][-1])
+    manifest, group = info["traffic_manifest"], info["group"]
 
-    def per_kernel(root, counter):
-        vals = {}
-        for r in _csv_rows(root, "counter_collection.csv"):
-            if r.get("Counter_Name") != counter:
-                continue
-            name = r.get("Kernel_Name", "")
-            if "vcoll::" not in name:               # torch's own kernels (direct_copy_kernel_cuda, ...)
-                continue
-            for key in TRAFFIC_SET:
-                if key in name:
-                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+    def segments(root, counter):
+        recs = [r for r in _csv_rows(root, "counter_collection.csv")
+                if r.get("Counter_Name") == counter and "vcoll::" in r.get("Kernel_Name", "")]
+        recs.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        segs, cur = [], None
+        for r in recs:
+            name = r["Kernel_Name"]
+            if "write_kernel<4, 64>" in name and int(r.get("Grid_Size", 0)) == 64:
+                cur = []
+                segs.append(cur)
+            elif cur is not None:
+                cur.append(r)
+        out = []
+        for seg, m in zip(segs, manifest):
+            vals = [float(r["Counter_Value"]) for r in seg if m["kernel"] in r["Kernel_Name"]]
+            out.append((sum(vals) / len(vals), len(vals)) if vals else (None, 0))
+        return out
 
-    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
-    write, nw = per_kernel(write_dir, "WRITE_SIZE")
-    half = 209_715_200                          # copy_kernel reads, and writes, this many bytes
-    f_scale, w_scale = half / fetch["copy_kernel"], half / write["copy_kernel"]
-    lines = ["# HBM traffic per launch from rocprofv3 counters: the hot kernels", "",
+    fetch = segments(fetch_dir, "FETCH_SIZE")
+    write = segments(write_dir, "WRITE_SIZE")
+    ci = next(i for i, m in enumerate(manifest) if m["kernel"].startswith("copy_kernel"))
+    half = manifest[ci]["algorithmic_bytes"] // 2
+    f_scale, w_scale = half / fetch[ci][0], half / write[ci][0]
+    lines = [f"# HBM traffic per launch from rocprofv3 counters: {group} kernels", "",
              f"Command: `{command}`", "",
-             f"FETCH_SIZE and WRITE_SIZE per dispatch, averaged over each kernel's dispatches (warm-up "
-             f"included), scaled by copy_kernel's readings for a copy of {half} B: {f_scale:.2f} B per "
-             f"FETCH_SIZE unit, {w_scale:.2f} B per WRITE_SIZE unit. Algorithmic bytes are the bytes "
-             f"each operation must move (inputs read once, outputs written once).", "",
-             "| kernel | workload | dispatches | read B | written B | traffic / algorithmic |",
-             "|---|---|---|---|---|---|"]
-    for key, (label, _) in TRAFFIC_SET.items():
-        if key not in fetch or key not in write:
-            lines.append(f"| {key} | {label} | 0 | - | - | - |")
+             f"FETCH_SIZE and WRITE_SIZE per dispatch, averaged over each workload's dispatches (warm-up "
+             f"included), scaled by the copy's readings for {half} B read and written: {f_scale:.2f} B per "
+             f"FETCH_SIZE unit, {w_scale:.2f} B per WRITE_SIZE unit. Algorithmic bytes are the bytes each "
+             f"operation must move (inputs read once, outputs written once).", "",
+             "| workload | kernel | dispatches | read B | written B | algorithmic B | traffic / algorithmic |",
+             "|---|---|---|---|---|---|---|"]
+    out = {}
+    for m, (fv, nf), (wv, _) in zip(manifest, fetch, write):
+        if fv is None or wv is None:
+            lines.append(f"| {m['label']} | {m['kernel']} | 0 | - | - | {m['algorithmic_bytes']:,} | - |")
             continue
-        rd, wr = fetch[key] * f_scale, write[key] * w_scale
-        lines.append(f"| {key} | {label} | {nf[key]} | {rd:,.0f} | {wr:,.0f} | "
-                     f"{(rd + wr) / algo_bytes[key]:.3f} |")
-    with open(os.path.join(ROOT, "profiles", "traffic_hot_kernels.md"), "w") as f:
+        rd, wr = fv * f_scale, wv * w_scale
+        ratio = (rd + wr) / m["algorithmic_bytes"]
+        out[m["label"]] = {"read": round(rd), "written": round(wr), "ratio": round(ratio, 4)}
+        lines.append(f"| {m['label']} | {m['kernel']} | {nf} | {rd:,.0f} | {wr:,.0f} | "
+                     f"{m['algorithmic_bytes']:,} | {ratio:.3f} |")
+    name = "traffic_hot_kernels.md" if group == "hot" else "traffic_sweep_kernels.md"
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     return 0
@@ -831,6 +1202,8 @@ def main() -> int:
     ap.add_argument("--sweep", metavar="OUT_JSONL", help="run the message-size sweep instead, one JSON line per "
                     "(p, size, algorithm) point written to OUT_JSONL, and exit")
     ap.add_argument("--sweep-max-bytes", type=int, default=2 ** 30, help="largest per-rank size of the sweep")
+    ap.add_argument("--traffic-group", default="hot", choices=sorted(TRAFFIC_GROUPS),
+                    help="which workloads --traffic-set launches")
     ap.add_argument("--traffic-set", type=int, default=0, metavar="K",
                     help="launch each hot kernel K times (plus a warm-up) for counter runs, then exit")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRAFFIC_SET_LOG"),
@@ -858,7 +1231,7 @@ def main() -> int:
     if args.sweep:
         return sweep(vc, torch, args.sweep, args.sweep_max_bytes)
     if args.traffic_set:
-        return traffic_set(vc, torch, args.traffic_set)
+        return traffic_set(vc, torch, args.traffic_set, args.traffic_group)
     h = headline(vc, torch, args)
     value = h["nbytes"] * args.steps / h["wall"] / 1e9
     achieved = h["nbytes"] / (h["mean_ms"] * 1e-3) / 1e9
@@ -887,7 +1260,8 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": "reduce_kernel<f32, ring, p=8>", "mean_launch_us": round(h["mean_ms"] * 1e3, 2),
+            "kernel": "burst_ring_kernel<f32, 25 vectors per thread> (two-phase ring, 256 workgroups)",
+            "mean_launch_us": round(h["mean_ms"] * 1e3, 2), "launch_us": h["dist"],
             "kernel_code": kernel_code_hash(),
         },
     }

@@ -135,6 +135,8 @@ def _lib():
         lib.vcoll_model_ledger_time.restype = I
         lib.vcoll_bench_copy.argtypes = [VP, VP, I64, VP]
         lib.vcoll_bench_copy.restype = I
+        lib.vcoll_bench_stream.argtypes = [I, VP, VP, I64, VP]
+        lib.vcoll_bench_stream.restype = I
         if lib.vcoll_abi_version() != 1:
             raise ImportError("libvcoll ABI version mismatch")
         _LIB = lib
@@ -890,13 +892,34 @@ def vcoll_moe_dispatch_fp8(tokens, splits, src_rows, recv=None):
     return recv
 
 
+BENCH_KINDS = {"copy": 0, "read": 1, "write": 2, "copy_plain": 3}
+
+
 def vcoll_bench_copy(dst, src) -> None:
-    """Plain streaming copy of src into dst (equal byte sizes, 16-byte multiple)."""
+    """Streaming copy of src into dst (equal byte sizes, 16-byte multiple)."""
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("vcoll_bench_copy: size mismatch")
     _check(_lib().vcoll_bench_copy(_dptr(dst), _dptr(src), nbytes, _stream(src)),
            "vcoll_bench_copy")
+
+
+def _bench_stream_args(kind: str, dst, src):
+    if kind not in BENCH_KINDS:
+        raise ValueError(f"vcoll_bench_stream: unknown kind {kind!r}")
+    ref = src if kind != "write" else dst
+    nbytes = ref.numel() * ref.element_size()
+    if kind in ("copy", "copy_plain") and dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("vcoll_bench_stream: size mismatch")
+    if kind in ("copy", "copy_plain"):
+        _no_overlap([dst], [src], "vcoll_bench_stream")
+    return (BENCH_KINDS[kind], _dptr(dst), _dptr(src) if src is not None else None, nbytes, _stream(ref))
+
+
+def vcoll_bench_stream(kind: str, dst, src=None) -> None:
+    """One streaming pass: 'copy' / 'copy_plain' src -> dst, 'read' src (dst:
+    a small sink tensor), 'write' dst."""
+    _check(_lib().vcoll_bench_stream(*_bench_stream_args(kind, dst, src)), "vcoll_bench_stream")
 
 
 class PreparedCall:
@@ -963,6 +986,12 @@ def prepare_bench_copy(dst, src) -> PreparedCall:
     vcoll_bench_copy(dst, src)
     args = (dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), _stream(src))
     return PreparedCall("vcoll_bench_copy", _lib().vcoll_bench_copy, args, (dst, src))
+
+
+def prepare_bench_stream(kind: str, dst, src=None) -> PreparedCall:
+    vcoll_bench_stream(kind, dst, src)
+    return PreparedCall("vcoll_bench_stream", _lib().vcoll_bench_stream, _bench_stream_args(kind, dst, src),
+                        (dst, src))
 
 
 def prepare_allreduce_stepwise(algo, send, recv, workspace=None) -> PreparedCall:

@@ -32,7 +32,8 @@ FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-SOURCES = ["reduce.hip", "hier.hip", "move.hip", "step.hip", "vcoll_api.cpp", "schedule.cpp", "model.cpp"]
+SOURCES = ["reduce.hip", "hier.hip", "move.hip", "step.hip", "bench.hip", "vcoll_api.cpp", "schedule.cpp",
+           "model.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -103,6 +103,5 @@ hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream
 hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream);
-hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 }  // namespace vcoll

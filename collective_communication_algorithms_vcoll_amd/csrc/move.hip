@@ -1,7 +1,7 @@
 // Data-movement kernels of libvcoll for gfx950: all-gather fan-out,
-// broadcast, variable-split all-to-all, FP8 MoE dispatch and the plain copy
-// the collectives are measured against. Nothing here adds; every byte is
-// read once and written to its destinations.
+// broadcast, variable-split all-to-all and the FP8 and token-major MoE
+// dispatches and combine. Nothing here adds; every byte is read once and
+// written to its destinations.
 #include "device.h"
 #include "move.h"
 
@@ -438,25 +438,6 @@ __global__ __launch_bounds__(BS) void combine_pull_kernel(const CombineArgs a) {
   }
 }
 
-// ----------------------------------------------------------------------------
-// plain copy: the streaming ceiling the collectives are measured against
-
-__global__ __launch_bounds__(kBlock) void copy_kernel(const void* src, void* dst, int64_t nvec) {
-  constexpr int V = 4;
-  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * kBlock) + threadIdx.x;
-  u32x4 x[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int64_t v = v0 + j * kBlock;
-    x[j] = v < nvec ? ld16(src, v * 16) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int64_t v = v0 + j * kBlock;
-    if (v < nvec) st16(dst, v * 16, x[j]);
-  }
-}
-
 // Fan-out shape of the all-gather and the broadcast, chosen by the bytes a
 // launch writes; both use one-wave workgroups. Measured on MI355X against
 // four-wave workgroups with two streaming-stored vectors per thread: up to
@@ -539,16 +520,6 @@ hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream
   for (int k = 0; flat && k < a.nblocks; ++k) flat = !a.b[k].src_idx && !a.b[k].dst_idx;
   if (flat) return launch(all_to_all_kernel<1024>, dim3(static_cast<unsigned>(tiles)), 1024, a, stream);
   return launch(all_to_all_kernel<kBlock>, dim3(static_cast<unsigned>(tiles)), kBlock, a, stream);
-}
-
-hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
-  const int64_t nvec = bytes / 16;
-  const int64_t per_tile = 4LL * kBlock;
-  const int64_t tiles = (nvec + per_tile - 1) / per_tile;
-  if (tiles == 0) return hipSuccess;
-  void* args[] = {const_cast<const void**>(&src), &dst, const_cast<int64_t*>(&nvec)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel), dim3(static_cast<unsigned>(tiles)),
-                         dim3(kBlock), args, 0, stream);
 }
 
 }  // namespace vcoll

@@ -53,4 +53,24 @@ static_assert(sizeof(ReduceArgs) <= 4096, "kernel arguments are limited to 4 KiB
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
                          int64_t max_chunk, int chunks, hipStream_t stream);
 
+// Ring all-reduce in two chip-wide phases, for vectors whose sums fit in the
+// register files of one workgroup per compute unit: every workgroup reads
+// its tile of all p ranks (chain order, the next rank's loads in flight while
+// the current one is added), then writes the tile to all p outputs. Grid:
+// x = tiles of a chunk, y = chunk. Requires 16-byte aligned buffers and
+// chunks of a whole number of 16-byte vectors (n a multiple of p * 16 / s).
+struct BurstArgs {
+  const void* src[kMaxRanks];
+  void* dst[kMaxRanks];
+  int64_t q;                  // chunk length in elements
+  int32_t p;
+  int32_t tv;                 // 16-byte vectors per tile (at most burst_tile_max)
+};
+static_assert(sizeof(BurstArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
+// Largest tile (16-byte vectors) one workgroup of the burst kernel holds.
+int64_t burst_tile_max(vcoll_dtype dtype);
+
+hipError_t launch_burst_ring(const BurstArgs& a, vcoll_dtype dtype, int tiles, hipStream_t stream);
+
 }  // namespace vcoll

@@ -4,8 +4,10 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
+#include "bench.h"
 #include "hier.h"
 #include "move.h"
 #include "reduce.h"
@@ -73,6 +75,42 @@ bool all_aligned(int p, const void* const* ptrs) {
   return true;
 }
 
+// Compute units of the current device, read once per device (0 when no
+// device can be queried, which turns the burst kernel off).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Smallest tile (16-byte vectors) for which the two-phase ring kernel beats
+// the one-pass kernel: 16 vectors per thread (16 MiB of float32 per rank at
+// p = 8) gained 9 %, 4 vectors (4 MiB) lost 2.3x, on MI355X.
+constexpr int64_t kBurstMinTile = 3072;
+
+// Tiles per chunk for the two-phase ring all-reduce, or 0 when the one-pass
+// kernel is the better choice: the whole vector must fit in one generation
+// of workgroups (one per compute unit) at between kBurstMinTile and
+// burst_tile_max vectors each, with chunks of whole 16-byte vectors.
+int burst_tiles(int p, int64_t n, vcoll_dtype dtype, int64_t* tv) {
+  const int64_t ve = 16 / elem_bytes(dtype);
+  if (n % (static_cast<int64_t>(p) * ve) != 0) return 0;
+  const int per_chunk = device_cus() / p;
+  if (per_chunk < 1) return 0;
+  const int64_t cv = n / p / ve;
+  const int64_t t = (cv + per_chunk - 1) / per_chunk;
+  if (t < kBurstMinTile || t > burst_tile_max(dtype)) return 0;
+  *tv = t;
+  return static_cast<int>((cv + t - 1) / t);
+}
+
 vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                            const void* const* send, void* const* recv, void* stream, bool scatter) {
   if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
@@ -90,6 +128,20 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
   a.r = ch.r;
   a.p = p;
   a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv));
+  int64_t tv = 0;
+  const int tiles = (!scatter && algo == VCOLL_RING && a.vec) ? burst_tiles(p, n, dtype, &tv) : 0;
+  if (tiles > 0) {
+    BurstArgs b;
+    std::memset(&b, 0, sizeof(b));
+    for (int r = 0; r < p; ++r) {
+      b.src[r] = send[r];
+      b.dst[r] = recv[r];
+    }
+    b.q = ch.q;
+    b.p = p;
+    b.tv = static_cast<int32_t>(tv);
+    return from_hip(launch_burst_ring(b, dtype, tiles, static_cast<hipStream_t>(stream)));
+  }
   const OrderProgram prog = order_program(algo, p);
   if (has_fixed_kernel(p)) {
     // leaf pointers in summation order: ring rotated per chunk (chunk c's
@@ -715,11 +767,19 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
   return VCOLL_OK;
 }
 
-vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+vcoll_status vcoll_bench_stream(vcoll_bench_kind kind, void* dst, const void* src, int64_t bytes, void* stream) {
+  if (kind < VCOLL_BENCH_COPY || kind > VCOLL_BENCH_COPY_PLAIN) return VCOLL_ERR_INVALID_ARG;
   if (bytes < 0 || (bytes % 16) != 0) return VCOLL_ERR_INVALID_ARG;
   if (bytes == 0) return VCOLL_OK;
-  if (!dst || !src || !aligned16(dst) || !aligned16(src)) return VCOLL_ERR_INVALID_ARG;
-  return from_hip(launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+  const bool uses_src = kind != VCOLL_BENCH_WRITE;
+  if (!dst || (uses_src && (!src || !aligned16(src)))) return VCOLL_ERR_INVALID_ARG;
+  if (kind == VCOLL_BENCH_READ ? (reinterpret_cast<uintptr_t>(dst) & 3u) != 0 : !aligned16(dst))
+    return VCOLL_ERR_INVALID_ARG;
+  return from_hip(launch_stream(kind, dst, src, bytes, static_cast<hipStream_t>(stream)));
+}
+
+vcoll_status vcoll_bench_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  return vcoll_bench_stream(VCOLL_BENCH_COPY, dst, src, bytes, stream);
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@
 #include <random>
 #include <vector>
 
+#include "bench.h"
 #include "hier.h"
 #include "move.h"
 #include "reduce.h"
@@ -23,6 +24,9 @@ using vcoll::kMaxRanks;
 using vcoll::kA2ABlocks;
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
+// a 256-compute-unit device 0, so that the size-selected kernels are exercised
+extern "C" hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+extern "C" hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }
 
 namespace vcoll {
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype, vcoll_algo, bool, int64_t max_chunk, int chunks,
@@ -50,8 +54,23 @@ hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t) {
 hipError_t launch_dispatch_fp8(const Fp8Args&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_dispatch_push(const PushArgs&, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_combine_pull(const CombineArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_copy(void*, const void*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_stream(vcoll_bench_kind, void*, const void*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_step(const StepArgs&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
+int64_t burst_tile_max(vcoll_dtype dtype) { return dtype == VCOLL_F32 ? 25 * 256 : 16 * 256; }
+}  // namespace vcoll
+static long g_burst = 0;
+namespace vcoll {
+hipError_t launch_burst_ring(const BurstArgs& a, vcoll_dtype dtype, int tiles, hipStream_t) {
+  // every tile starts inside its chunk, and the tiles cover the chunk
+  const int64_t cv = a.q / (dtype == VCOLL_F32 ? 4 : 8);
+  if (!(a.tv >= 1 && a.tv <= burst_tile_max(dtype) && int64_t(tiles - 1) * a.tv < cv && int64_t(tiles) * a.tv >= cv)) {
+    std::fprintf(stderr, "burst tiling does not cover the chunk\n");
+    std::abort();
+  }
+  ++g_launches;
+  ++g_burst;
+  return hipSuccess;
+}
 // the scratch lookup of the allocation-free stepwise mode: a host stand-in
 // address (the stubbed launches never dereference it)
 hipError_t step_scratch(void** ptr) {
@@ -291,6 +310,22 @@ int main() {
   moe(rng);
   launches(rng);
   CHECK(g_launches > 0);
+  {
+    // the DDP bucket (p = 8 x 6,553,600 float32) takes the two-phase ring kernel
+    void* send[8];
+    void* recv[8];
+    for (int r = 0; r < 8; ++r) {
+      send[r] = reinterpret_cast<void*>(uintptr_t(0x100000) * (r + 1));
+      recv[r] = reinterpret_cast<void*>(uintptr_t(0x100000) * (r + 9));
+    }
+    const long before = g_burst;
+    CHECK(vcoll_allreduce(VCOLL_RING, 8, 6553600, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(g_burst == before + 1);
+    CHECK(vcoll_allreduce(VCOLL_RABENSEIFNER, 8, 6553600, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(vcoll_allreduce(VCOLL_RING, 8, 6553600 + 8, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(vcoll_allreduce(VCOLL_RING, 8, 1 << 20, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(g_burst == before + 1);
+  }
   std::printf("OK %ld launches recorded\n", g_launches);
   return 0;
 }

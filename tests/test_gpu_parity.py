@@ -255,6 +255,27 @@ def test_reduce_scatter_matches_oracle(vc, algo, p, dtype):
             assert_bits_equal(download(got[c], dtype), bits(want[c], dtype), f"RS {algo} p={p} chunk {c}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p", [3, 5, 12, 24, 72, 128])
+def test_reduce_scatter_with_unaligned_chunk_starts(vc, p, dtype):
+    """Ring reduce-scatter at a p without a compiled program where chunk
+    starts are not 16-byte aligned: the vector path realigns every rank's
+    loads to the output (every shift of 1..VE-1 elements occurs across the
+    chunks), the last vectors and the ragged end go through the element path."""
+    ve = 4 if dtype == "f32" else 8
+    for n in (p * (3 * 1024 + 5) + 3, p * 777 + p - 1, p * 2 * ve + 1):
+        x = rand_inputs(p, n, dtype, seed=p + 500 + n % 97)
+        want, _ = oracle.reduce_scatter(x, "ring", dtype)
+        offs = oracle.chunk_bounds(n, p)
+        assert {o % ve for o in offs[:-1]} - {0}, "no unaligned chunk start"
+        t = upload(x, dtype)
+        say(f"vcoll_reduce_scatter ring p={p} n={n} dtype={dtype} (unaligned chunk starts)")
+        got = vc.vcoll_reduce_scatter("ring", t)
+        sync()
+        for c in range(p):
+            assert_bits_equal(download(got[c], dtype), bits(want[c], dtype), f"RS ring p={p} n={n} chunk {c}")
+
+
 def test_non_power_of_two_halving_and_doubling_are_refused(vc):
     import torch
     t = torch.zeros(3, 96, device="cuda")
@@ -411,49 +432,47 @@ def test_ddp_bucket_headline_workload(vc):
     assert led.sent_bytes() == [45_875_200] * 8
 
 
-def _window_check(out, x, n, dtype, algo, windows):
-    """Compare element windows of the GPU result with the oracle run in
-    windowed mode on the same windows of the host inputs x."""
-    for lo, hi in windows:
-        want, _ = oracle.allreduce([v[lo:hi] for v in x], algo, dtype, n=n, lo=lo)
-        got = download(out[:, lo:hi], dtype)
-        assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"{algo} window [{lo},{hi})")
-
-
-def _sample_windows(n, p, k=24, w=1000, seed=0):
-    offs = oracle.chunk_bounds(n, p)
-    rng = np.random.default_rng(seed)
-    wins = [(0, w), (n - w, n)]
-    for c in range(1, p):                   # straddle every chunk boundary
-        wins.append((offs[c] - w // 2, offs[c] + w // 2))
-    for s in rng.integers(0, n - w, size=k):
-        wins.append((int(s), int(s) + w))
-    return wins
-
-
-@pytest.mark.parametrize("algo", ["ring", "rabenseifner"])
-def test_hierarchy_bf16_workload(vc, algo):
-    """p=16, 192 MiB bf16 per rank: sampled windows against the windowed oracle,
-    every rank bitwise equal, and reduce-scatter + all-gather equal to the
-    fused all-reduce at full size."""
+def test_hierarchy_bf16_workload_every_element(vc):
+    """p=16, 192 MiB bf16 per rank (100,663,296 elements), ring and
+    Rabenseifner: every element of every rank compared with the oracle,
+    streamed over consecutive windows by a pool of CPU workers; and
+    reduce-scatter + all-gather equal to the fused all-reduce at full size."""
     import torch
+    from tests import oracle_pool
     cfg = workloads.HIER_BF16
-    p, n = cfg["p"], cfg["n"]
-    say(f"generating {p} x {n} bf16 inputs")
-    x = workloads.rank_buffers(cfg["tag"], p, n, cfg["dist"], "bf16")
-    t = upload(x, "bf16")
-    say(f"vcoll_allreduce {algo} p=16 n={n} bf16")
-    out = vc.vcoll_allreduce(algo, t)
-    sync()
-    _window_check(out, x, n, "bf16", algo, _sample_windows(n, p, seed=3))
-    for r in range(1, p):
-        assert torch.equal(out[r].view(torch.int16), out[0].view(torch.int16))
-    say(f"vcoll_reduce_scatter {algo} + vcoll_all_gather at full size")
-    rs = vc.vcoll_reduce_scatter(algo, t)
-    ag_out = torch.empty_like(t)
-    vc.vcoll_all_gather("ring" if algo == "ring" else "rd", rs, ag_out)
-    sync()
-    assert torch.equal(ag_out.view(torch.int16), out.view(torch.int16))
+    p, n, tag, dist = cfg["p"], cfg["n"], cfg["tag"], cfg["dist"]
+    algos = ("ring", "rabenseifner")
+    wins = oracle_pool.windows(n, oracle_pool.window_len(p))
+    t = torch.empty((p, n), dtype=torch.bfloat16, device="cuda")
+    with oracle_pool.pool() as pool:
+        say(f"generating {p} x {n} bf16 inputs in {len(wins)} windows")
+        for lo, hi, xw in pool.imap(oracle_pool.gen_window, [(tag, p, lo, hi, dist, "bf16") for lo, hi in wins]):
+            t[:, lo:hi].copy_(torch.from_numpy(xw.view(np.int16)).view(torch.bfloat16))
+        outs = {}
+        for algo in algos:
+            say(f"vcoll_allreduce {algo} p=16 n={n} bf16")
+            outs[algo] = vc.vcoll_allreduce(algo, t)
+        sync()
+        checked = {a: 0 for a in algos}
+        jobs = [(tag, p, n, lo, hi, dist, "bf16", algos) for lo, hi in wins]
+        for lo, hi, want in pool.imap(oracle_pool.oracle_window, jobs):
+            for algo in algos:
+                got = download(outs[algo][:, lo:hi], "bf16")
+                assert_bits_equal(got, want[algo], f"{algo} window [{lo},{hi})")
+                checked[algo] += p * (hi - lo)
+    for algo in algos:
+        assert checked[algo] == p * n
+        say(f"cfg3 {algo}: 100 % of {n:,} elements x {p} ranks equal to the oracle")
+    for algo, ag_algo in (("ring", "ring"), ("rabenseifner", "rd")):
+        say(f"vcoll_reduce_scatter {algo} + vcoll_all_gather {ag_algo} at full size")
+        rs = vc.vcoll_reduce_scatter(algo, t)
+        ag_out = torch.empty_like(t)
+        vc.vcoll_all_gather(ag_algo, rs, ag_out)
+        sync()
+        assert torch.equal(ag_out.view(torch.int16), outs[algo].view(torch.int16))
+        del rs, ag_out
+    del t, outs
+    torch.cuda.empty_cache()
 
 
 def test_moe_full_workload(vc):
@@ -474,20 +493,6 @@ def test_message_size_sweep(vc, p):
             say(f"sweep p={p} bytes={nbytes} {algo}")
             got = download(vc.vcoll_allreduce(algo, t), "f32")
             assert_bits_equal(got, np.stack([bits(w, "f32") for w in want]), f"sweep p={p} {nbytes}B {algo}")
-
-
-@pytest.mark.parametrize("p,nbytes", [(8, 80 * 1024 * 1024), (72, 16 * 1024 * 1024), (2, 256 * 1024 * 1024)])
-def test_message_size_sweep_large_windows(vc, p, nbytes):
-    n = nbytes // 4
-    dist = workloads.SWEEP_DIST
-    say(f"generating sweep p={p} n={n}")
-    x = [workloads.rank_window(workloads.TAG_SWEEP, r, 0, n, dist, "f32") for r in range(p)]
-    t = upload(x, "f32")
-    for algo in ALGOS:
-        say(f"sweep large p={p} bytes={nbytes} {algo}")
-        out = vc.vcoll_allreduce(algo, t)
-        sync()
-        _window_check(out, x, n, "f32", algo, _sample_windows(n, p, k=8, w=512, seed=p))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
