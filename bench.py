@@ -220,13 +220,15 @@ def roof(kernel: str, nbytes: int, ms: float, **more) -> dict:
 
 class Scrub:
     """A 1 GiB streaming copy that evicts the 256 MB Infinity Cache between
-    timed launches (run outside the timed events)."""
+    timed launches (run outside the timed events). It uses the plain copy
+    shape, so that the fast copy stays the only kernel of its kind in a run
+    (its counter readings scale the other kernels')."""
 
     def __init__(self, vc, torch):
         half = 512 * 2 ** 20
         self.src = torch.empty(half // 4, device="cuda")
         self.dst = torch.empty(half // 4, device="cuda")
-        self.call = vc.prepare_bench_stream("copy", self.dst, self.src)
+        self.call = vc.prepare_bench_stream("copy_plain", self.dst, self.src)
 
     def __call__(self):
         self.call()
@@ -551,19 +553,51 @@ def cfg5(vc, torch, cpu_leg: bool) -> dict:
     return res
 
 
+EXTRA_SECTIONS = ("ceilings", "cfg1", "bucket", "stepwise", "decode_prefill", "graphs", "cfg3", "cfg4",
+                  "moe_variants", "cfg5", "host")
+
+
 def extras(vc, torch, h, args):
     import numpy as np
     import workloads
     cpu_leg = not args.no_cpu_baseline
+    only = set(args.only.split(",")) if args.only else set(EXTRA_SECTIONS)
     ex = {}
     p, n, S = h["p"], h["n"], h["S"]
     base = h["base"]
     steps, warm = max(20, args.steps // 4), 5
     scrub = h["scrub"]
     ex["event_pair_floor_us"] = event_pair_floor(vc, torch)
-    ex["ceilings"] = ceilings(vc, torch, p * S)
-    ex["cfg1"] = cfg1(vc, torch, scrub, min(3.0, args.cpu_seconds), cpu_leg)
+    if "ceilings" in only:
+        ex["ceilings"] = ceilings(vc, torch, p * S)
+    if "cfg1" in only:
+        ex["cfg1"] = cfg1(vc, torch, scrub, min(3.0, args.cpu_seconds), cpu_leg)
+    if "bucket" in only:
+        bucket_extras(vc, torch, h, ex, steps, warm)
+    if "stepwise" in only:
+        stepwise_extras(vc, torch, ex, steps, warm)
+    if "decode_prefill" in only:
+        decode_prefill_extras(vc, torch, ex, steps, warm)
+    if "graphs" in only:
+        graph_extras(vc, torch, ex)
+    if "cfg3" in only:
+        ex["cfg3"] = cfg3(vc, torch, scrub, cpu_leg)
+    if "cfg4" in only:
+        ex["cfg4"] = cfg4(vc, torch, cpu_leg)
+    if "moe_variants" in only:
+        ex["moe_variants"] = moe_variants(vc, torch)
+    if "cfg5" in only:
+        ex["cfg5"] = cfg5(vc, torch, cpu_leg)
+    if "host" in only:
+        ex["host_schedule_and_ledger"] = host_rows(vc)
+    return ex
 
+
+def bucket_extras(vc, torch, h, ex, steps, warm):
+    """Other algorithms, hierarchical orders, broadcast, reduce, the warm
+    cache and the unfused pair on the DDP bucket."""
+    p, n, S = h["p"], h["n"], h["S"]
+    base = h["base"]
     # other algorithms on the same bucket (fused, one pass each)
     R = sets_for(2 * p * S)
     ins = [base.clone() for _ in range(R)]
@@ -605,9 +639,11 @@ def extras(vc, torch, h, args):
     del ins, outs, rs_out
     torch.cuda.empty_cache()
 
-    # stepwise execution (one launch per algorithm step, messages through
-    # memory) against the fused kernels: the per-step latency and the memory
-    # round trips that fusion removes
+
+def stepwise_extras(vc, torch, ex, steps, warm):
+    """Stepwise execution (one launch per algorithm step, messages through
+    memory) against the fused kernels: the per-step latency and the memory
+    round trips that fusion removes."""
     for label, nbytes in (("10KiB", 10 * 1024), ("25MiB", 25 * 2 ** 20)):
         m = nbytes // 4
         g = torch.Generator(device="cuda").manual_seed(6)
@@ -628,7 +664,9 @@ def extras(vc, torch, h, args):
         del t, ts, os_
     torch.cuda.empty_cache()
 
-    # decode-like (10 KiB) and prefill-like (80 MiB) messages, p = 8
+
+def decode_prefill_extras(vc, torch, ex, steps, warm):
+    """Decode-like (10 KiB) and prefill-like (80 MiB) messages, p = 8."""
     for label, nbytes in (("decode_10KiB", 10 * 1024), ("prefill_80MiB", 80 * 2 ** 20)):
         m = nbytes // 4
         g = torch.Generator(device="cuda").manual_seed(5)
@@ -643,8 +681,10 @@ def extras(vc, torch, h, args):
         del t, ts, os_
     torch.cuda.empty_cache()
 
-    # decode-sized all-reduces replayed from a HIP graph: the per-call cost
-    # without the host's launch path (100 captured calls per replay)
+
+def graph_extras(vc, torch, ex):
+    """Decode-sized all-reduces replayed from a HIP graph: the per-call cost
+    without the host's launch path (100 captured calls per replay)."""
     g = torch.Generator(device="cuda").manual_seed(7)
     t = torch.randn((8, 2560), device="cuda", generator=g)
     o = torch.empty_like(t)
@@ -664,14 +704,14 @@ def extras(vc, torch, h, args):
     del t, o
     torch.cuda.empty_cache()
 
-    ex["cfg3"] = cfg3(vc, torch, scrub, cpu_leg)
-    ex["cfg4"] = cfg4(vc, torch, cpu_leg)
-    ex["moe_variants"] = moe_variants(vc, torch)
-    ex["cfg5"] = cfg5(vc, torch, cpu_leg)
 
-    # the host rows: partition + step schedule + ledger of a collective (the
-    # record-free ledger call builds every message and sums it per rank) and
-    # the MoE routing plan, through the Python binding, median of repeated calls
+def host_rows(vc) -> dict:
+    """The host rows: partition + step schedule + ledger of a collective (the
+    record-free ledger call builds every message and sums it per rank) and
+    the MoE routing plan, through the Python binding, median of repeated calls."""
+    import numpy as np
+    import workloads
+
     def host_us(fn, reps):
         t = []
         for _ in range(reps):
@@ -687,8 +727,7 @@ def extras(vc, torch, h, args):
         host[f"ledger_{algo}_p72_us"] = host_us(lambda: vc.vcoll_ledger_summary("allreduce", algo, 72, 72 << 20), 50)
     host["ledger_ring_p72_messages"] = vc.vcoll_ledger_summary("allreduce", "ring", 72, 72 << 20)[0]
     host["moe_plan_8x4096x8_us"] = host_us(lambda: vc.vcoll_moe_plan(topk, M["experts"] // M["p"]), 20)
-    ex["host_schedule_and_ledger"] = host
-    return ex
+    return host
 
 
 def moe_variants(vc, torch) -> dict:
@@ -875,6 +914,36 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str, command: s
     return 0
 
 
+def summarize_stats(trace_dir: str, name: str, title: str, command: str) -> int:
+    """rocprofv3 --kernel-trace --stats output as a table in profiles/<name>.md:
+    one row per libvcoll kernel instantiation (calls, average, min and max
+    duration), plus p10 / median / p90 of each from the kernel trace."""
+    stats = [r for r in _csv_rows(trace_dir, "kernel_stats.csv") if "vcoll::" in r.get("Name", r.get("KernelName", ""))]
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    lines = [f"# rocprofv3 kernel statistics: {title}", "", f"Command: `{command}`", "",
+             "Template arguments of reduce_kernel: dtype (0 f32, 1 bf16), algorithm (0 ring, 1 recursive doubling, "
+             "2 Rabenseifner, 3 tree), p (0: read at run time), vectors per thread, reduce-scatter, large-grid "
+             "variant, workgroup size; of burst_ring_kernel: dtype, vectors per thread.", "",
+             "| kernel | calls | average us | min us | max us | p10 us | median us | p90 us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
+        full = r.get("Name", r.get("KernelName", "?"))
+        short = full.replace("vcoll::(anonymous namespace)::", "")
+        short = short.split("(vcoll::")[0].split("(")[0] if short.startswith(("reduce", "burst", "hier")) else short
+        d = sorted((int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3
+                   for t in trace if t.get("Kernel_Name") == full)
+
+        def pct(q):
+            return d[min(len(d) - 1, int(q * (len(d) - 1) + 0.5))] if d else float("nan")
+        lines.append(f"| {short[:100]} | {r.get('Calls')} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {pct(0.1):.2f} | "
+                     f"{pct(0.5):.2f} | {pct(0.9):.2f} |")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 # Counter-traffic workloads, in launch order. Each entry: (label, kernel
 # name substring as rocprofv3 prints it, algorithmic bytes per launch or
 # None when the routing decides them, printed by the run). A one-workgroup
@@ -1012,8 +1081,8 @@ def traffic_set(vc, torch, launches: int, group: str) -> int:
             run(vc.prepare_allreduce("ring", t, o))
             del t, o
             torch.cuda.empty_cache()
-    manifest = [{"label": lab, "kernel": k, "algorithmic_bytes": b if b is not None else filled[k]}
-                for lab, k, b in TRAFFIC_GROUPS[group]]
+    manifest = [{"label": lab, "kernel": k, "algorithmic_bytes": b if b is not None else filled[k],
+                 "dispatches": launches + 1} for lab, k, b in TRAFFIC_GROUPS[group]]
     print(json.dumps({"traffic_manifest": manifest, "group": group}), flush=True)
     return 0
 
@@ -1039,9 +1108,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, manifest_log: str, command
                 segs.append(cur)
             elif cur is not None:
                 cur.append(r)
+        # the marker launch made while preparing the markers opens an extra
+        # first segment; a workload's own preparation call runs before its
+        # marker, so it ends the previous segment: take the first `dispatches`
+        # matching records of each of the last len(manifest) segments
         out = []
-        for seg, m in zip(segs, manifest):
-            vals = [float(r["Counter_Value"]) for r in seg if m["kernel"] in r["Kernel_Name"]]
+        for seg, m in zip(segs[-len(manifest):], manifest):
+            vals = [float(r["Counter_Value"]) for r in seg if m["kernel"] in r["Kernel_Name"]][:m["dispatches"]]
             out.append((sum(vals) / len(vals), len(vals)) if vals else (None, 0))
         return out
 
@@ -1193,6 +1266,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only", default="", help="comma-separated extras sections to run (default all): "
+                    + ", ".join(EXTRA_SECTIONS))
     ap.add_argument("--copy-reference", type=int, default=0, metavar="K",
                     help="after the headline, launch the plain copy K times over the headline's "
                          "bytes (a known-size kernel to scale hardware counter readings)")
@@ -1208,11 +1283,15 @@ def main() -> int:
                     help="launch each hot kernel K times (plus a warm-up) for counter runs, then exit")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRAFFIC_SET_LOG"),
                     help="turn the counter runs of --traffic-set into a table in profiles/ and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("TRACE_DIR", "NAME", "TITLE"),
+                    help="turn a rocprofv3 --kernel-trace --stats directory into profiles/NAME.md and exit")
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", help="turn a sweep's JSON lines into a table in "
                     "profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_profile:
         return summarize_profile(*args.summarize_profile, args.profile_command)
+    if args.summarize_stats:
+        return summarize_stats(*args.summarize_stats, args.profile_command)
     if args.summarize_sweep:
         return summarize_sweep(args.summarize_sweep, args.profile_command)
     if args.summarize_traffic:

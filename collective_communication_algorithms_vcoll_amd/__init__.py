@@ -126,6 +126,8 @@ def _lib():
         lib.vcoll_moe_dispatch_fp8.restype = I
         lib.vcoll_allreduce_stepwise.argtypes = [I, I, I64, I, P(VP), P(VP), VP, I64, P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise_static.restype = I
+        lib.vcoll_broadcast_stepwise.restype = I
+        lib.vcoll_broadcast_stepwise.argtypes = [I, I, I64, I, I, I64, VP, P(VP), P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise_static.argtypes = [I, I, I64, I, P(VP), P(VP), P(ctypes.c_int32), VP]
         lib.vcoll_allreduce_stepwise.restype = I
         D = ctypes.c_double
@@ -384,6 +386,39 @@ def vcoll_broadcast(send, recv, root: int = 0):
     _check(_lib().vcoll_broadcast(len(r), n, _dtype_code(send), root, _dptr(send) if n else None, _ptrs(r),
                                   _stream(send)), "vcoll_broadcast")
     return recv
+
+
+def vcoll_broadcast_stepwise(algo, send, recv, root: int = 0, blocks: int = 1):
+    """vcoll_broadcast executed one launch per step of the algorithm's
+    schedule ('naive', 'tree', 'scatter_allgather', 'chain' with `blocks`
+    blocks). Returns (recv, launches)."""
+    r = _ranks(recv)
+    _validate(r, "vcoll_broadcast_stepwise")
+    n = r[0].numel()
+    _validate(r, "vcoll_broadcast_stepwise", n)
+    if not 0 <= root < len(r):
+        raise ValueError("vcoll_broadcast_stepwise: root out of range")
+    _validate([send], "vcoll_broadcast_stepwise", n)
+    if send.dtype != r[0].dtype or send.device != r[0].device:
+        raise ValueError("vcoll_broadcast_stepwise: send and recv differ in dtype or device")
+    targets = [t for i, t in enumerate(r) if not (i == root and t.data_ptr() == send.data_ptr())]
+    _no_overlap([send], targets, "vcoll_broadcast_stepwise")
+    for i, a in enumerate(targets):
+        _no_overlap([a], targets[i + 1:], "vcoll_broadcast_stepwise")
+    launches = ctypes.c_int32()
+    _check(_lib().vcoll_broadcast_stepwise(_algo(algo), len(r), n, _dtype_code(send), root, blocks,
+                                           _dptr(send) if n else None, _ptrs(r), ctypes.byref(launches),
+                                           _stream(send)), "vcoll_broadcast_stepwise")
+    return recv, launches.value
+
+
+def prepare_broadcast_stepwise(algo, send, recv, root: int = 0, blocks: int = 1) -> PreparedCall:
+    r = _ranks(recv)
+    vcoll_broadcast_stepwise(algo, send, recv, root, blocks)
+    rp = _ptrs(r)
+    args = (_algo(algo), len(r), r[0].numel(), _dtype_code(send), root, blocks, send.data_ptr(), rp, None,
+            _stream(send))
+    return PreparedCall("vcoll_broadcast_stepwise", _lib().vcoll_broadcast_stepwise, args, (send, recv, rp))
 
 
 def vcoll_reduce(send, recv=None, root: int = 0, algo="tree"):

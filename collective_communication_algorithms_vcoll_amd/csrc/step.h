@@ -17,7 +17,8 @@ namespace vcoll {
 constexpr int kStepOps = 64;
 constexpr int kStepTile = 4096;      // elements per workgroup
 enum StepLaunchKind : int32_t {
-  SK_ADD = 0, SK_COPY = 1, SK_XADD = 2, SK_NARROW = 3, SK_WIDEN_BF16 = 4, SK_STORE_BF16 = 5
+  SK_ADD = 0, SK_COPY = 1, SK_XADD = 2, SK_NARROW = 3, SK_WIDEN_BF16 = 4, SK_STORE_BF16 = 5,
+  SK_COPY16 = 6              // raw copy of 16-bit elements (bf16 messages of the stepwise broadcast)
 };
 struct StepLaunchOp {
   const void* src;

@@ -45,6 +45,15 @@ __device__ __forceinline__ void step_apply4(const StepLaunchOp& o, int64_t e, bo
       if (vec) st16(o.dst, e * 4, ld16(o.src, e * 4));
       else for (int i = 0; i < 4; ++i) d[e + i] = sf[e + i];
       break;
+    case SK_COPY16: {
+      // four 16-bit elements: one 8-byte access when both ends allow it
+      if (vec) {
+        static_cast<uint64_t*>(o.dst)[e / 4] = static_cast<const uint64_t*>(o.src)[e / 4];
+      } else {
+        for (int i = 0; i < 4; ++i) static_cast<uint16_t*>(o.dst)[e + i] = static_cast<const uint16_t*>(o.src)[e + i];
+      }
+      break;
+    }
     case SK_NARROW:
       for (int i = 0; i < 4; ++i) d[e + i] = round_bf16(d[e + i]);
       break;
@@ -68,6 +77,7 @@ __device__ __forceinline__ void step_apply1(const StepLaunchOp& o, int64_t e) {
     case SK_ADD: d[e] = d[e] + sf[e]; break;
     case SK_XADD: { const float v = d[e] + sf[e]; d[e] = v; const_cast<float*>(sf)[e] = v; break; }
     case SK_COPY: d[e] = sf[e]; break;
+    case SK_COPY16: static_cast<uint16_t*>(o.dst)[e] = static_cast<const uint16_t*>(o.src)[e]; break;
     case SK_NARROW: d[e] = round_bf16(d[e]); break;
     case SK_WIDEN_BF16: d[e] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(o.src)[e]) << 16); break;
     default: static_cast<uint16_t*>(o.dst)[e] = static_cast<uint16_t>(bf16_rne(sf[e])); break;
@@ -85,9 +95,12 @@ __global__ __launch_bounds__(kBlock) void step_kernel(const StepArgs a) {
   const StepLaunchOp& o = a.op[lo];
   const int64_t e0 = static_cast<int64_t>(t - o.tile_start) * kStepTile;
   const int64_t e1 = o.count < e0 + kStepTile ? o.count : e0 + kStepTile;
-  // float32 sides move as 16-byte vectors when both ends are aligned
-  const bool vec = (o.kind == SK_ADD || o.kind == SK_XADD || o.kind == SK_COPY) &&
-                   ((reinterpret_cast<uintptr_t>(o.src) | reinterpret_cast<uintptr_t>(o.dst)) & 15u) == 0;
+  // float32 sides move as 16-byte vectors when both ends are aligned, 16-bit
+  // copies as 8-byte words when both ends are 8-byte aligned (e is a
+  // multiple of 4 elements in every group)
+  const uintptr_t ends = reinterpret_cast<uintptr_t>(o.src) | reinterpret_cast<uintptr_t>(o.dst);
+  const bool vec = o.kind == SK_COPY16 ? (ends & 7u) == 0
+                                       : (o.kind == SK_ADD || o.kind == SK_XADD || o.kind == SK_COPY) && (ends & 15u) == 0;
   const int64_t groups = (e1 - e0) / 4;
   for (int64_t g = threadIdx.x; g < groups; g += kBlock) step_apply4(o, e0 + 4 * g, vec);
   const int64_t tail = e0 + 4 * groups + threadIdx.x;

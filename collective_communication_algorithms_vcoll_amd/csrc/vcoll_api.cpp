@@ -527,6 +527,64 @@ vcoll_status vcoll_allreduce_stepwise_static(vcoll_algo algo, int p, int64_t n, 
   return stepwise_run(algo, p, n, dtype, send, recv, workspace, n_launches, stream);
 }
 
+// Blocks of a stepwise pipelined chain: each block adds one launch.
+constexpr int64_t kMaxChainBlocks = 65536;
+
+vcoll_status vcoll_broadcast_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root, int64_t blocks,
+                                      const void* send, void* const* recv, int32_t* n_launches, void* stream) {
+  if (n_launches) *n_launches = 0;
+  if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || root < 0 || root >= p) return VCOLL_ERR_INVALID_ARG;
+  if (algo == VCOLL_PIPELINED_CHAIN && blocks > kMaxChainBlocks) return VCOLL_ERR_INVALID_ARG;
+  std::vector<vcoll_msg> msgs;
+  int32_t n_steps = 0;
+  const vcoll_status led = build_ledger_rooted(VCOLL_OP_BROADCAST, algo, p, n, elem_bytes(dtype), root,
+                                               blocks, msgs, &n_steps);
+  if (led != VCOLL_OK) return led;
+  if (n == 0) return VCOLL_OK;
+  if (!send || !recv) return VCOLL_ERR_INVALID_ARG;
+  for (int r = 0; r < p; ++r)
+    if (r != root && !recv[r]) return VCOLL_ERR_INVALID_ARG;
+  // the root's messages leave from `send`; its own receive buffer (if any,
+  // and not `send` itself) gets a local copy first, which is no message, and
+  // receives the messages addressed to the root (the scatter + all-gather
+  // ring sends the root chunks it already holds; with no separate buffer
+  // they are dropped, `send` is never written)
+  const int64_t es = elem_bytes(dtype);
+  const int32_t kind = dtype == VCOLL_F32 ? SK_COPY : SK_COPY16;
+  char* const root_out = (recv[root] && recv[root] != send) ? static_cast<char*>(recv[root]) : nullptr;
+  auto src_buf = [&](int r) -> const char* {
+    return static_cast<const char*>(r == root ? send : recv[r]);
+  };
+  auto dst_buf = [&](int r) -> char* { return r == root ? root_out : static_cast<char*>(recv[r]); };
+  auto op = [&](const void* src, void* dst, int64_t count) {
+    StepLaunchOp o{};
+    o.src = src;
+    o.dst = dst;
+    o.count = count;
+    o.kind = kind;
+    return o;
+  };
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<StepLaunchOp> ops;
+  if (root_out) {
+    ops.push_back(op(send, root_out, n));
+    const vcoll_status st = run_step_ops(ops, s, n_launches);
+    if (st != VCOLL_OK) return st;
+  }
+  size_t k = 0;
+  for (int32_t step = 0; step < n_steps; ++step) {
+    ops.clear();
+    for (; k < msgs.size() && msgs[k].step == step; ++k) {
+      const vcoll_msg& m = msgs[k];
+      if (m.count > 0 && dst_buf(m.dst))
+        ops.push_back(op(src_buf(m.src) + m.src_off * es, dst_buf(m.dst) + m.dst_off * es, m.count));
+    }
+    const vcoll_status st = run_step_ops(ops, s, n_launches);
+    if (st != VCOLL_OK) return st;
+  }
+  return VCOLL_OK;
+}
+
 vcoll_status vcoll_allreduce_hierarchical(int nodes, int local, int64_t n, vcoll_dtype dtype,
                                           const void* const* send, void* const* recv, void* stream) {
   if (!valid_grid(nodes, local) || !valid_count(n) || !valid_dtype(dtype))

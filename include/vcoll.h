@@ -193,6 +193,23 @@ vcoll_status vcoll_broadcast(int p, int64_t n, vcoll_dtype dtype, int root, cons
                              void* stream);
 
 /*
+ * Stepwise broadcast: the same bytes as vcoll_broadcast, but executed the way
+ * the algorithm runs on a network, one launch per step of the schedule
+ * vcoll_ledger_rooted lists for (algo, root, blocks), each copying that
+ * step's messages between the rank buffers -- [NCC] 5.5 naive (p-1 steps),
+ * binomial tree (ceil(log2 p)), 4.2 scatter + all-gather (1 + (p-1)),
+ * pipelined chain of `blocks` blocks (p-2+blocks; 1 <= blocks <= 65536).
+ * It measures what the one-pass broadcast hides: per-step launch latency and
+ * the bytes each step moves. The root's messages are read from `send`;
+ * recv[root], when it is neither NULL nor `send`, first gets a local copy
+ * (one extra launch) and receives whatever the schedule sends to the root;
+ * `send` is never written. Steps whose messages are all empty launch
+ * nothing. *n_launches (may be NULL) receives the launches enqueued.
+ */
+vcoll_status vcoll_broadcast_stepwise(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, int root, int64_t blocks,
+                                      const void* send, void* const* recv, int32_t* n_launches, void* stream);
+
+/*
  * Reduce to a root ([NCC] 4.1: elementwise sum, result on the root only) by
  * the binomial tree of [NCC] 5.2 on ranks relative to the root,
  * v = (r - root) mod p: masks 1, 2, 4, ..; the relative rank whose lowest

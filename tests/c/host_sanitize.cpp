@@ -256,6 +256,16 @@ static void launches(std::mt19937_64& rng) {
                                           nullptr) == VCOLL_OK);
     CHECK(with_ws == without && without > 0);
   }
+  // the stepwise broadcast: every algorithm, roots, launch counts from the ledger
+  for (int p : {1, 2, 7, 64, 65, 128}) {
+    for (vcoll_algo algo : {VCOLL_NAIVE, VCOLL_BINARY_TREE, VCOLL_SCATTER_ALLGATHER, VCOLL_PIPELINED_CHAIN}) {
+      int32_t launched = 0;
+      const long at = g_launches;
+      CHECK(vcoll_broadcast_stepwise(algo, p, 10007, VCOLL_BF16, p / 3, 5, send[p / 3], recv, &launched, nullptr) ==
+            VCOLL_OK);
+      CHECK(launched == g_launches - at);
+    }
+  }
   // error paths: nothing is launched
   const long before = g_launches;
   {

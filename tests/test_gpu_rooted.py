@@ -227,3 +227,71 @@ def test_reduce_sixteen_rank_bf16_windows(vc):
     for lo, hi in wins:
         want, _ = rooted.reduce([v[lo:hi] for v in x], 7, "bf16", n=n, lo=lo)
         assert_bits_equal(download(out[lo:hi], "bf16"), bits(want, "bf16"), f"window [{lo},{hi})")
+
+
+# --------------------------------------------------------------------------- stepwise broadcast
+
+STEPWISE_BCAST = [("naive", 1), ("tree", 1), ("scatter_allgather", 1), ("chain", 1), ("chain", 3), ("chain", 8)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p", [1, 2, 3, 5, 8, 16, 72])
+def test_stepwise_broadcast_equals_oracle_and_one_pass(vc, p, dtype):
+    """One launch per step of the schedule: every rank ends with the root's
+    words (the oracle's broadcast), the same bytes as the one-pass broadcast,
+    and one launch per 64 non-empty messages of each step, plus the root's
+    own copy."""
+    import torch
+    n = 3 * 1024 + 7
+    x = rand_inputs(1, n, dtype, 40 + p)[0]
+    send = upload([x], dtype)[0]
+    for algo, k in STEPWISE_BCAST:
+        for root in sorted({0, p // 2, p - 1}):
+            want, led = rooted.broadcast(x, p, algo, root, k, dtype)
+            out = upload([np.zeros_like(x)] * p, dtype)
+            say(f"stepwise broadcast {algo} k={k} p={p} root={root} {dtype}")
+            _, launches = vc.vcoll_broadcast_stepwise(algo, send, out, root, k)
+            sync()
+            assert_bits_equal(download(out, dtype), np.stack([bits(w, dtype) for w in want]),
+                              f"stepwise {algo} k={k} p={p} root={root}")
+            one = torch.zeros_like(out)
+            vc.vcoll_broadcast(send, one, root)
+            sync()
+            assert torch.equal(one.view(torch.int16), out.view(torch.int16))
+            # the root's own copy, then per step one launch per 64 non-empty messages
+            per_step = {}
+            for m in led.msgs:
+                if m.count > 0:
+                    per_step[m.step] = per_step.get(m.step, 0) + 1
+            assert launches == 1 + sum(-(-c // 64) for c in per_step.values()), (algo, k, launches)
+
+
+def test_stepwise_broadcast_never_writes_send_and_keeps_the_root_buffer(vc):
+    """recv[root] may be the root's send buffer itself (nothing written there,
+    not even by the scatter + all-gather ring, which sends the root chunks it
+    holds) or a separate buffer (filled like every other rank's)."""
+    import torch
+    p, n = 8, 5000
+    x = rand_inputs(p, n, "f32", 77)
+    t = upload(x, "f32")
+    before = t.clone()
+    for algo, k in STEPWISE_BCAST:
+        out = upload([np.zeros(n, np.float32)] * p, "f32")
+        rows = [out[r] for r in range(p)]
+        rows[3] = t[3]                                     # root's own buffer is the send buffer
+        vc.vcoll_broadcast_stepwise(algo, t[3], rows, 3, k)
+        sync()
+        assert torch.equal(t, before)
+        for r in range(p):
+            assert torch.equal(rows[r], t[3]), (algo, r)
+
+
+def test_stepwise_broadcast_rejects_bad_calls(vc):
+    import torch
+    t = torch.zeros(4, 64, device="cuda")
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_broadcast_stepwise("chain", t[0].clone(), t, 0, 0)           # no blocks
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_broadcast_stepwise("ring", t[0].clone(), t, 0, 1)            # not a broadcast algorithm
+    with pytest.raises(vc.VcollError):
+        vc.vcoll_broadcast_stepwise("chain", t[0].clone(), t, 0, 65537)       # too many blocks

@@ -368,6 +368,26 @@ def test_static_stepwise_refuses_sizes_beyond_its_scratch_array():
     assert b"static scratch" in lib.vcoll_status_str(5)
 
 
+def test_stepwise_broadcast_validation():
+    """vcoll_broadcast_stepwise checks its schedule before any launch (no GPU
+    needed): the algorithm must be a broadcast one, the chain needs 1..65536
+    blocks, the root must be a rank; n = 0 is a no-op."""
+    lib = _lib()
+    P8 = _ptrs(8)
+    one = ctypes.c_void_p(0x1000)
+    launches = ctypes.c_int32(-1)
+    assert lib.vcoll_broadcast_stepwise(0, 8, 64, 0, 0, 1, one, P8, ctypes.byref(launches), None) == 2   # ring
+    assert launches.value == 0
+    assert lib.vcoll_broadcast_stepwise(6, 8, 64, 0, 0, 0, one, P8, None, None) == 1        # chain, 0 blocks
+    assert lib.vcoll_broadcast_stepwise(6, 8, 64, 0, 0, 65537, one, P8, None, None) == 1
+    assert lib.vcoll_broadcast_stepwise(3, 8, 64, 0, 8, 1, one, P8, None, None) == 1        # root out of range
+    assert lib.vcoll_broadcast_stepwise(3, 8, 64, 2, 0, 1, one, P8, None, None) == 1        # U8
+    assert lib.vcoll_broadcast_stepwise(3, 8, 0, 0, 0, 1, None, None, None, None) == 0      # n = 0
+    holes = _ptrs(8)
+    holes[5] = None
+    assert lib.vcoll_broadcast_stepwise(4, 8, 64, 0, 0, 1, one, holes, None, None) == 1
+
+
 def test_oversized_counts_and_buffers_are_refused():
     """Element counts above 2^48 and buffers above 2^56 bytes are refused
     before anything is enqueued, so no byte offset can overflow int64."""
