@@ -576,6 +576,7 @@ def extras(vc, torch, h, args):
         bucket_extras(vc, torch, h, ex, steps, warm)
     if "stepwise" in only:
         stepwise_extras(vc, torch, ex, steps, warm)
+        stepwise_broadcast_extras(vc, torch, ex, steps, warm)
     if "decode_prefill" in only:
         decode_prefill_extras(vc, torch, ex, steps, warm)
     if "graphs" in only:
@@ -662,6 +663,36 @@ def stepwise_extras(vc, torch, ex, steps, warm):
                 "us_per_launch": round(ms_step * 1e3 / launches, 2),
                 "fused_us": round(ms_fused * 1e3, 2), "slowdown_vs_fused": round(ms_step / ms_fused, 2)}
         del t, ts, os_
+    torch.cuda.empty_cache()
+
+
+def stepwise_broadcast_extras(vc, torch, ex, steps, warm):
+    """The broadcast family executed one launch per schedule step ([NCC] 5.5:
+    naive, binomial tree, pipelined chain; 4.2 scatter + all-gather), p = 8,
+    for the lecture's 8 MB example and a decode-sized 10 KiB message, beside
+    the one-pass broadcast and the lecture's own clock for the same
+    schedule (TPU ICI links: alpha = 1 us, 45 GB/s; ici_model_us)."""
+    p = 8
+    for label, nbytes in (("8MB", 8_000_000), ("10KiB", 10 * 1024)):
+        n = nbytes // 4
+        g = torch.Generator(device="cuda").manual_seed(11)
+        src = torch.randn(n, device="cuda", generator=g)
+        R2 = min(64, sets_for((p + 1) * nbytes))
+        outs = [torch.empty((p, n), device="cuda") for _ in range(R2)]
+        calls = [vc.prepare_broadcast(src, outs[i], 0) for i in range(R2)]
+        _, ms_one = time_launches(calls, steps, warm)
+        rec = {"one_pass_us": round(ms_one * 1e3, 2)}
+        for algo, k in (("naive", 1), ("tree", 1), ("scatter_allgather", 1), ("chain", 8), ("chain", 32)):
+            _, launches = vc.vcoll_broadcast_stepwise(algo, src, outs[0], 0, k)
+            calls = [vc.prepare_broadcast_stepwise(algo, src, outs[i], 0, k) for i in range(R2)]
+            _, ms = time_launches(calls, steps if nbytes < 2 ** 20 else 20, warm)
+            msgs, _, _, nsteps = vc.vcoll_ledger_rooted("broadcast", algo, p, n, "f32", 0, k)
+            rec[f"{algo}{k if algo == 'chain' else ''}"] = {
+                "us": round(ms * 1e3, 2), "steps": nsteps, "launches": launches,
+                "us_per_launch": round(ms * 1e3 / launches, 2),
+                "ici_model_us": round(vc.vcoll_model_clock(msgs, p, 1e-6, 45e9) * 1e6, 2)}
+        ex[f"stepwise_broadcast_p8_{label}"] = rec
+        del src, outs
     torch.cuda.empty_cache()
 
 

@@ -43,6 +43,9 @@ struct ReduceArgs {
   int32_t vec;                // every pointer 16-byte aligned: vector path allowed
   int32_t final_merges;       // order program (used when p is not compiled in)
   int32_t pace;               // space out the p-way store fan-out (large grids)
+  int32_t align;              // all-reduce tiles start on this byte boundary (256 when every buffer
+                              // has the same address mod 256, else 16)
+  int32_t phase;              // that common address mod `align` (0 for align 16)
   uint8_t rank[kMaxRanks];
   uint8_t merges[kMaxRanks];
 };

@@ -306,7 +306,14 @@ __global__ __launch_bounds__(BS) void reduce_kernel(const ReduceArgs a) {
   const bool vec = a.vec != 0 && (!RS || (off % VE) == 0);
 
   if (vec) {
-    const int64_t head = (VE - off % VE) % VE < cnt ? (VE - off % VE) % VE : cnt;
+    // the vector tiles of an all-reduce start on a 256-byte boundary of every
+    // buffer when the buffers allow it (whole cache lines per wave: chunk
+    // starts that are only 16-byte aligned cost p = 72 5 % extra HBM
+    // traffic); the elements before it and the ragged end take the element path
+    const int64_t align = RS ? 16 : a.align;
+    const int64_t mis = (a.phase + off * ES) % align;
+    const int64_t head_e = mis ? (align - mis) / ES : 0;
+    const int64_t head = head_e < cnt ? head_e : cnt;
     const int64_t nvec = (cnt - head) / VE;
     const int64_t e_base = off + head;
     const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * BS) + tid;
@@ -336,11 +343,8 @@ __global__ __launch_bounds__(BS) void reduce_kernel(const ReduceArgs a) {
     }
     if (blockIdx.x == 0) {
       const int64_t tail = cnt - head - nvec * VE;
-      if (tid < head) {
-        reduce_one<D, ALGO, P, RS>(a, c, p, rot, off + tid, off);
-      } else if (tid >= 16 && tid - 16 < tail) {
-        reduce_one<D, ALGO, P, RS>(a, c, p, rot, e_base + nvec * VE + (tid - 16), off);
-      }
+      for (int64_t i = tid; i < head + tail; i += BS)
+        reduce_one<D, ALGO, P, RS>(a, c, p, rot, i < head ? off + i : e_base + nvec * VE + (i - head), off);
     }
   } else {
     const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * BS * VE);

@@ -128,6 +128,13 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
   a.r = ch.r;
   a.p = p;
   a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv));
+  // a common address phase mod 256 lets the all-reduce tiles start on whole cache lines
+  const uintptr_t ph = reinterpret_cast<uintptr_t>(send[0]) & 255u;
+  bool same = true;
+  for (int r = 0; r < p && same; ++r)
+    same = (reinterpret_cast<uintptr_t>(send[r]) & 255u) == ph && (reinterpret_cast<uintptr_t>(recv[r]) & 255u) == ph;
+  a.align = same ? 256 : 16;
+  a.phase = same ? static_cast<int32_t>(ph) : 0;
   int64_t tv = 0;
   const int tiles = (!scatter && algo == VCOLL_RING && a.vec) ? burst_tiles(p, n, dtype, &tv) : 0;
   if (tiles > 0) {
