@@ -78,7 +78,7 @@ struct PushArgs {
   int32_t vec;                // rows and bases 16-byte aligned (copy path)
   int32_t tokens_per_tile;
   int32_t vec_out;            // FP8: receive rows 16-byte aligned (16-byte code stores)
-  int32_t pad;
+  int32_t segments;           // workgroups per tile, each one segment of every row (push_segments)
 };
 static_assert(sizeof(PushArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
@@ -94,6 +94,8 @@ struct CombineArgs {
   int32_t topk, p;
   int32_t vec;                       // rows and bases 16-byte aligned
   int32_t tokens_per_tile;
+  int32_t segments;                  // workgroups per tile, each one segment of every row (pull_segments)
+  int32_t pad;
 };
 static_assert(sizeof(CombineArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
@@ -101,6 +103,10 @@ hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t
 hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype dtype, hipStream_t stream);
 hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t stream);
 hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stream);
+// Workgroups that share one tile of token rows, each copying one segment of
+// every row (1 when rows are short, FP8 or not 16-byte aligned).
+int32_t push_segments(int64_t row_bytes, bool fp8, bool vec);
+int32_t pull_segments(int64_t row_bytes, bool vec);
 hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream);
 

@@ -310,11 +310,18 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
 constexpr int kPushUnroll = 4;     // 16-byte vectors in flight per thread (a 7168 bf16 row is 3.5)
 constexpr int kPushFp8Block = 512;  // threads per workgroup of the FP8 token-major dispatch
 
+// bf16 token rows longer than this many 16-byte vectors are cut into
+// segments of it, one per one-wave workgroup (the workgroups of one token
+// then write its copies in parallel): on the 7168-element MoE workload,
+// seven 2 KiB segments took the dispatch from 836 to 775 us on MI355X.
+constexpr int kPushSegVec = 128;
+
 template <bool FP8, int BS>
 __global__ __launch_bounds__(BS) void dispatch_push_kernel(const PushArgs a) {
   const int tid = threadIdx.x;
   const int i = blockIdx.y;                                    // sending rank
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * a.tokens_per_tile;
+  const int seg = static_cast<int>(blockIdx.x % a.segments);   // segment of every row of the tile
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x / a.segments) * a.tokens_per_tile;
   for (int64_t t = t0; t < t0 + a.tokens_per_tile && t < a.tokens; ++t) {
     const char* src = static_cast<const char*>(a.table[i]) + t * a.row_bytes;
     const int32_t* slot = a.slots[i] + 2 * t * a.topk;
@@ -349,8 +356,10 @@ __global__ __launch_bounds__(BS) void dispatch_push_kernel(const PushArgs a) {
         }
       }
     } else if (a.vec) {
-      const int64_t nvec = a.row_bytes / 16;
-      for (int64_t x0 = tid; x0 < nvec; x0 += kPushUnroll * BS) {
+      const int64_t nall = a.row_bytes / 16;
+      const int64_t per = (nall + a.segments - 1) / a.segments;
+      const int64_t nvec = (seg + 1) * per < nall ? (seg + 1) * per : nall;
+      for (int64_t x0 = seg * per + tid; x0 < nvec; x0 += kPushUnroll * BS) {
         u32x4 v[kPushUnroll];
 #pragma unroll
         for (int u = 0; u < kPushUnroll; ++u) {
@@ -386,13 +395,18 @@ __global__ __launch_bounds__(BS) void dispatch_push_kernel(const PushArgs a) {
 // scattering form of the same permutation writes rows in send order instead.
 
 constexpr int kCombineRows = 2;    // output rows whose loads are in flight together
+// Rows longer than this many 16-byte vectors are cut into segments of it,
+// one per one-wave workgroup: fourteen 1 KiB segments took the MoE
+// workload's combine from 1420 to 1337 us on MI355X.
+constexpr int kPullSegVec = 64;
 
 template <int BS>
 __global__ __launch_bounds__(BS) void combine_pull_kernel(const CombineArgs a) {
   const int tid = threadIdx.x;
   const int i = blockIdx.y;                                    // rank that owns the tokens
+  const int seg = static_cast<int>(blockIdx.x % a.segments);
   const int64_t total = a.tokens * a.topk;
-  const int64_t x_begin = static_cast<int64_t>(blockIdx.x) * a.tokens_per_tile * a.topk;
+  const int64_t x_begin = static_cast<int64_t>(blockIdx.x / a.segments) * a.tokens_per_tile * a.topk;
   const int64_t x_end = x_begin + static_cast<int64_t>(a.tokens_per_tile) * a.topk < total
                             ? x_begin + static_cast<int64_t>(a.tokens_per_tile) * a.topk
                             : total;
@@ -409,8 +423,10 @@ __global__ __launch_bounds__(BS) void combine_pull_kernel(const CombineArgs a) {
 #pragma unroll
     for (int q = 0; q < kCombineRows; ++q) src[q] = x + q < x_end ? source(x + q) : nullptr;
     if (a.vec) {
-      const int64_t nvec = a.row_bytes / 16;
-      for (int64_t v0 = tid; v0 < nvec; v0 += kPushUnroll * BS) {
+      const int64_t nall = a.row_bytes / 16;
+      const int64_t per = (nall + a.segments - 1) / a.segments;
+      const int64_t nvec = (seg + 1) * per < nall ? (seg + 1) * per : nall;
+      for (int64_t v0 = seg * per + tid; v0 < nvec; v0 += kPushUnroll * BS) {
         u32x4 w[kCombineRows][kPushUnroll];
 #pragma unroll
         for (int q = 0; q < kCombineRows; ++q)
@@ -488,6 +504,18 @@ hipError_t launch_dispatch_fp8(const Fp8Args& a, int32_t tiles, hipStream_t stre
   return launch(dispatch_fp8_kernel, dim3(static_cast<unsigned>(tiles)), a, stream);
 }
 
+int32_t push_segments(int64_t row_bytes, bool fp8, bool vec) {
+  if (fp8 || !vec) return 1;
+  const int64_t nvec = row_bytes / 16;
+  return static_cast<int32_t>(nvec > kPushSegVec ? (nvec + kPushSegVec - 1) / kPushSegVec : 1);
+}
+
+int32_t pull_segments(int64_t row_bytes, bool vec) {
+  if (!vec) return 1;
+  const int64_t nvec = row_bytes / 16;
+  return static_cast<int32_t>(nvec > kPullSegVec ? (nvec + kPullSegVec - 1) / kPullSegVec : 1);
+}
+
 hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream) {
   const int64_t tiles = (a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile;
   if (tiles == 0) return hipSuccess;
@@ -498,6 +526,10 @@ hipError_t launch_dispatch_push(const PushArgs& a, bool fp8, hipStream_t stream)
   // deduplicated plan's ~3; 1024 gained 6% and lost 20%. bf16 copies lost
   // 2.5% with 512 or 1024 and keep 256.
   if (fp8) return launch(dispatch_push_kernel<true, kPushFp8Block>, grid, kPushFp8Block, a, stream);
+  if (a.segments > 1) {
+    const dim3 seg_grid(static_cast<unsigned>(tiles * a.segments), a.p);
+    return launch(dispatch_push_kernel<false, 64>, seg_grid, 64, a, stream);
+  }
   return launch(dispatch_push_kernel<false, kBlock>, grid, kBlock, a, stream);
 }
 
@@ -507,6 +539,8 @@ hipError_t launch_combine_pull(const CombineArgs& a, hipStream_t stream) {
   // 512 threads per token's output rows: 2% faster than 256 on the MoE
   // workload (1024: 1% slower)
   constexpr int kPullBlock = 512;
+  if (a.segments > 1)
+    return launch(combine_pull_kernel<64>, dim3(static_cast<unsigned>(tiles * a.segments), a.p), 64, a, stream);
   return launch(combine_pull_kernel<kPullBlock>, dim3(static_cast<unsigned>(tiles), a.p), kPullBlock, a, stream);
 }
 

@@ -708,10 +708,14 @@ vcoll_status vcoll_moe_dispatch(int p, int64_t tokens, int topk, int64_t hidden,
     if (recv_rows[j] > 0) a.vec_out = a.vec_out && aligned16(recv[j]);
   // up to 16 KiB of token rows per workgroup (one 7168-element bf16 token)
   a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 16384 / rb)));
+  a.segments = push_segments(rb, fp8 != 0, vec);
   for (int i = 0; i < p; ++i) {
     a.table[i] = token_tables[i];
     a.slots[i] = slots[i];
   }
+  // the grid (tiles x segments workgroups of up to 512 threads) must stay within 2^32 threads
+  if ((a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile * a.segments > (int64_t(UINT32_MAX) >> 9))
+    return VCOLL_ERR_UNSUPPORTED;
   return from_hip(launch_dispatch_push(a, fp8 != 0, static_cast<hipStream_t>(stream)));
 }
 
@@ -751,6 +755,10 @@ vcoll_status vcoll_moe_combine(int p, int64_t tokens, int topk, int64_t hidden, 
   a.vec = vec;
   // up to 128 KiB of output rows per workgroup (one token's 8 rows of 7168 bf16)
   a.tokens_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 131072 / (topk * rb))));
+  a.segments = pull_segments(rb, vec);
+  // the grid (tiles x segments workgroups of up to 512 threads) must stay within 2^32 threads
+  if ((a.tokens + a.tokens_per_tile - 1) / a.tokens_per_tile * a.segments > (int64_t(UINT32_MAX) >> 9))
+    return VCOLL_ERR_UNSUPPORTED;
   return from_hip(launch_combine_pull(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -54,6 +54,8 @@ hipError_t launch_all_to_all(const A2AArgs& a, int32_t tiles, hipStream_t) {
 hipError_t launch_dispatch_fp8(const Fp8Args&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_dispatch_push(const PushArgs&, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_combine_pull(const CombineArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+int32_t push_segments(int64_t row_bytes, bool fp8, bool vec) { return fp8 || !vec ? 1 : int32_t((row_bytes / 16 + 127) / 128); }
+int32_t pull_segments(int64_t row_bytes, bool vec) { return vec ? int32_t((row_bytes / 16 + 63) / 64) : 1; }
 hipError_t launch_stream(vcoll_bench_kind, void*, const void*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_step(const StepArgs&, int32_t, hipStream_t) { ++g_launches; return hipSuccess; }
 int64_t burst_tile_max(vcoll_dtype dtype) { return dtype == VCOLL_F32 ? 25 * 256 : 16 * 256; }
