@@ -1227,16 +1227,18 @@ def sweep(vc, torch, out_path: str, max_bytes: int) -> int:
     return 1 if fails else 0
 
 
-def summarize_sweep(jsonl: str, command: str) -> int:
+def summarize_sweep(jsonl: str, command: str, parity_jsonl: str = "") -> int:
     """The sweep's JSON lines as a table in profiles/: microseconds where the
-    whole all-reduce moves less than 64 MiB (latency-bound), GB/s above."""
+    whole all-reduce moves less than 64 MiB (latency-bound), GB/s above;
+    with parity_jsonl (the VCOLL_PARITY_LOG of tests/test_gpu_sweep.py), the
+    fraction of every point's elements compared with the oracle."""
     recs = [json.loads(x) for x in open(jsonl)]
     sizes = sorted({r["bytes_per_rank"] for r in recs})
 
     def label(b):
         return f"{b >> 30} GiB" if b >= 2 ** 30 else (f"{b >> 20} MiB" if b >= 2 ** 20 else f"{b >> 10} KiB")
     bad = [r for r in recs if not (r["ranks_equal"] and r.get("stepwise_equal", True))]
-    lines = ["# Fused all-reduce message-size sweep (reduce_kernel, float32, one buffer set)", "",
+    lines = ["# Fused all-reduce message-size sweep (float32, one buffer set; the ring takes the two-phase burst_ring_kernel where the whole vector fits one generation of workgroups, reduce_kernel elsewhere)", "",
              f"Command: `{command}`", "",
              f"{len(recs)} points, {len(bad)} mismatches on the GPU-side checks: all ranks equal on every "
              f"point, and the stepwise execution equal on every element for "
@@ -1283,6 +1285,23 @@ def summarize_sweep(jsonl: str, command: str) -> int:
             lines.append(f"| {algo} | {p} | {alpha:.1f} | {beta / 1e12:.2f} | "
                          f"{alpha * 1e-6 * beta / 2 ** 20:.0f} |")
     lines.append("")
+    if parity_jsonl:
+        par = [json.loads(x) for x in open(parity_jsonl)]
+        frac = {}
+        for r in par:
+            frac.setdefault((r["p"], r["bytes_per_rank"]), []).append(r["verified"] / r["total"])
+        lines += ["## Elements compared with the oracle (tests/test_gpu_sweep.py, every algorithm)", "",
+                  f"{sum(1 for r in par if r['verified'] == r['total'])} of {len(par)} (p, size, algorithm) points "
+                  f"compared on every element; the others on every chunk boundary plus 16 random 1024-element "
+                  f"windows, the fraction below.", "",
+                  "| p | " + " | ".join(label(b) for b in sizes) + " |", "|---|" + "---|" * len(sizes)]
+        for p in sorted({r["p"] for r in recs}):
+            cells = []
+            for b in sizes:
+                f = frac.get((p, b))
+                cells.append("" if not f else ("100 %" if min(f) == 1 else f"{100 * min(f):.3g} %"))
+            lines.append(f"| {p} | " + " | ".join(cells) + " |")
+        lines.append("")
     with open(os.path.join(ROOT, "profiles", "reduce_kernel_sweep_p2-72_1KiB-1GiB.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -1316,6 +1335,8 @@ def main() -> int:
                     help="turn the counter runs of --traffic-set into a table in profiles/ and exit")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("TRACE_DIR", "NAME", "TITLE"),
                     help="turn a rocprofv3 --kernel-trace --stats directory into profiles/NAME.md and exit")
+    ap.add_argument("--parity-log", default="", help="with --summarize-sweep: the JSON lines tests/test_gpu_sweep.py "
+                    "writes to VCOLL_PARITY_LOG")
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", help="turn a sweep's JSON lines into a table in "
                     "profiles/ and exit")
     args = ap.parse_args()
@@ -1324,7 +1345,7 @@ def main() -> int:
     if args.summarize_stats:
         return summarize_stats(*args.summarize_stats, args.profile_command)
     if args.summarize_sweep:
-        return summarize_sweep(args.summarize_sweep, args.profile_command)
+        return summarize_sweep(args.summarize_sweep, args.profile_command, args.parity_log)
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.profile_command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
