@@ -18,15 +18,9 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRawBufferFormat = 0x00020000;   // dword 3 of a raw (untyped) buffer resource
-constexpr int kLoadNT = 2;                     // cache policy: non-temporal
-constexpr int kStoreThrough = 1 | 2 | 16;      // cache policy: sc0 | nt | sc1
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void* base, int64_t byte_off, int64_t total) {
   const int64_t left = total - byte_off;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + byte_off, 0,
-                                           static_cast<int>(left < (int64_t(1) << 30) ? left : (int64_t(1) << 30)),
-                                           kRawBufferFormat);
+  return raw_rsrc(base, byte_off, static_cast<int>(left < (int64_t(1) << 30) ? left : (int64_t(1) << 30)));
 }
 
 template <int V, int BS, int SPOL>
@@ -37,7 +31,7 @@ __global__ __launch_bounds__(BS) void copy_kernel(const void* src, void* dst, in
   u32x4 x[V];
 #pragma unroll
   for (int j = 0; j < V; ++j)
-    x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s, threadIdx.x * 16, j * BS * 16, kLoadNT));
+    x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s, threadIdx.x * 16, j * BS * 16, kPolicyNT));
 #pragma unroll
   for (int j = 0; j < V; ++j)
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[j]), d, threadIdx.x * 16, j * BS * 16, SPOL);
@@ -53,7 +47,7 @@ __global__ __launch_bounds__(BS) void read_kernel(const void* src, void* sink, i
   u32x4 acc = {0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < V; ++j)
-    acc ^= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s, threadIdx.x * 16, j * BS * 16, kLoadNT));
+    acc ^= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s, threadIdx.x * 16, j * BS * 16, kPolicyNT));
   const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (x == never) static_cast<uint32_t*>(sink)[0] = x;
 }
@@ -65,7 +59,7 @@ __global__ __launch_bounds__(BS) void write_kernel(void* dst, int64_t bytes) {
   const u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < V; ++j)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), d, threadIdx.x * 16, j * BS * 16, kStoreThrough);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), d, threadIdx.x * 16, j * BS * 16, kPolicyThrough);
 }
 
 template <int V, int BS>
@@ -81,12 +75,12 @@ hipError_t launch_stream(vcoll_bench_kind kind, void* dst, const void* src, int6
   switch (kind) {
     case VCOLL_BENCH_COPY: {
       void* args[] = {&src, &dst, &bytes};
-      return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel<2, 64, kStoreThrough>),
+      return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel<2, 64, kPolicyThrough>),
                              dim3(tiles_of<2, 64>(bytes)), dim3(64), args, 0, stream);
     }
     case VCOLL_BENCH_COPY_PLAIN: {
       void* args[] = {&src, &dst, &bytes};
-      return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel<4, 256, kLoadNT>),
+      return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel<4, 256, kPolicyNT>),
                              dim3(tiles_of<4, 256>(bytes)), dim3(256), args, 0, stream);
     }
     case VCOLL_BENCH_READ: {

@@ -89,6 +89,21 @@ __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off));
 }
 
+// Buffer-instruction access: a resource whose base is the same for the whole
+// wave (a tile start in one buffer) and whose size clips the accesses (loads
+// past it return 0, stores past it are dropped); each lane adds a 32-bit
+// offset. A per-lane base would make the compiler loop over the distinct
+// bases, so callers keep the base uniform. Cache-policy bits of gfx950
+// buffer instructions: sc0 = 1, nt = 2, sc1 = 16.
+constexpr int kRawBufferFormat = 0x00020000;    // dword 3 of a raw (untyped) buffer resource
+constexpr int kPolicyNT = 2;                    // non-temporal
+constexpr int kPolicyThrough = 1 | 2 | 16;      // sc0 | nt | sc1: streamed past every cache level
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int64_t byte_off, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + byte_off, 0, bytes,
+                                           kRawBufferFormat);
+}
+
 template <int K, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (K < N) {

@@ -11,19 +11,25 @@ namespace {
 using namespace dev;
 
 // ----------------------------------------------------------------------------
-// store of a fan-out (one load, several copies stored): streaming
-// (non-temporal) or cached. Measured on MI355X, the large fan-outs write
-// faster through L2 with cached stores: the all-gather and broadcast beyond
-// 1 GiB written (4-6%) and the bf16 token-major MoE dispatch, 8 copies of
-// each token row (3%). One-to-one movers (all-to-all, combine, FP8 codes)
-// lost 1-8% with cached stores and keep streaming ones.
+// store of a fan-out (one load, several copies stored): streamed past every
+// cache level, or cached. The streamed form is a buffer store whose resource
+// base is the workgroup's tile in the destination (uniform), the lane's
+// place in it a 32-bit offset. Measured on MI355X (launches that write up to
+// 1 GiB): sc0|nt|sc1 stores ran 7-19% faster than nt-only global stores (an
+// all-gather of 3.125 MiB f32 blocks at p = 8 and a 25 MiB broadcast to 8
+// buffers +19%, 1 MiB blocks at p = 8 +7%, 64 KiB bf16 blocks at p = 72 +3%).
+// The large fan-outs write faster through L2 with cached stores: the
+// all-gather and broadcast beyond 1 GiB written (4-6%) and the bf16
+// token-major MoE dispatch, 8 copies of each token row (3%). One-to-one
+// movers (all-to-all, combine, FP8 codes) lost 1-8% with cached stores and
+// keep streaming ones.
 
 template <bool NT>
-__device__ __forceinline__ void fan_st16(void* base, int64_t byte_off, u32x4 v) {
+__device__ __forceinline__ void fan_st16(void* base, int64_t tile_off, int lane_off, u32x4 v) {
   if constexpr (NT) {
-    st16(base, byte_off, v);
+    __builtin_amdgcn_raw_buffer_store_b128(v, raw_rsrc(base, tile_off, 0x7fffffff), lane_off, 0, kPolicyThrough);
   } else {
-    *reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off) = v;
+    *reinterpret_cast<u32x4*>(static_cast<char*>(base) + tile_off + lane_off) = v;
   }
 }
 
@@ -40,6 +46,7 @@ __global__ __launch_bounds__(BS) void all_gather_kernel(const GatherArgs a) {
   if (a.vec) {
     const int64_t nvec = bytes / 16;
     const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * BS) + tid;
+    const int64_t tile_off = dst_off + static_cast<int64_t>(blockIdx.x) * (V * BS) * 16;
     u32x4 x[V];
     bool valid[V];
 #pragma unroll
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(BS) void all_gather_kernel(const GatherArgs a) {
     for (int r = 0; r < a.p; ++r) {
 #pragma unroll
       for (int j = 0; j < V; ++j)
-        if (valid[j]) fan_st16<NT>(a.ptr.dst[r], dst_off + (v0 + j * BS) * 16, x[j]);
+        if (valid[j]) fan_st16<NT>(a.ptr.dst[r], tile_off, (tid + j * BS) * 16, x[j]);
     }
   } else {
     using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
@@ -82,6 +89,7 @@ __global__ __launch_bounds__(BS) void broadcast_kernel(const BcastArgs a) {
   if (a.vec) {
     const int64_t nvec = a.n / VE;
     const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (V * BS) + tid;
+    const int64_t tile_off = static_cast<int64_t>(blockIdx.x) * (V * BS) * 16;
     u32x4 x[V];
     bool valid[V];
 #pragma unroll
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(BS) void broadcast_kernel(const BcastArgs a) {
     for (int r = 0; r < a.q; ++r) {
 #pragma unroll
       for (int j = 0; j < V; ++j)
-        if (valid[j]) fan_st16<NT>(a.dst[r], (v0 + j * BS) * 16, x[j]);
+        if (valid[j]) fan_st16<NT>(a.dst[r], tile_off, (tid + j * BS) * 16, x[j]);
     }
     // the last n mod VE elements
     if (blockIdx.x == 0 && tid < a.n - nvec * VE) {
@@ -282,7 +290,6 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
   const A2ABlock& B = a.b[lo];
   const int r0 = (t - B.tile_start) * a.rows_per_tile;
   const int tid = threadIdx.x;
-  const int64_t nvec = a.hidden / 8;                   // 16-byte vectors; 16 of them per group
   for (int rr = 0; rr < a.rows_per_tile; ++rr) {
     const int k = r0 + rr;
     if (k >= B.rows) break;
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(BS) void dispatch_push_kernel(const PushArgs a) {
 #pragma unroll
           for (int u = 0; u < kPushUnroll; ++u) {
             const int64_t x = x0 + u * BS;
-            if (x < nvec) fan_st16<false>(d, x * 16, v[u]);
+            if (x < nvec) fan_st16<false>(d, x * 16, 0, v[u]);
           }
         }
       }

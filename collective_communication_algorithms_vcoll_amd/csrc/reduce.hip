@@ -620,13 +620,6 @@ hipError_t launch_reduce_dtype(const ReduceArgs& a, vcoll_algo algo, bool scatte
 constexpr int kBurstBlock = 256;                 // one wave per SIMD
 constexpr int kBurstVecF32 = 25;                 // float32: 100 sums + 25 vectors in flight per thread
 constexpr int kBurstVecBf16 = 16;                // bf16: 128 sums + 16 vectors in flight
-constexpr int kBufferFormat = 0x00020000;        // dword 3 of a raw (untyped) buffer resource
-constexpr int kPolicyNT = 2;                     // non-temporal (streamed) loads and stores
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t byte_off, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + byte_off, 0, bytes,
-                                           kBufferFormat);
-}
 
 template <int D, int K>
 __global__ __launch_bounds__(kBurstBlock) void burst_ring_kernel(const BurstArgs a) {
@@ -647,7 +640,7 @@ __global__ __launch_bounds__(kBurstBlock) void burst_ring_kernel(const BurstArgs
   // chunk c's chain starts at rank c + 1 and ends with rank c
   int rank = c + 1 == p ? 0 : c + 1;
   {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(a.src[rank], off, bytes);
+    const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.src[rank], off, bytes);
 #pragma unroll
     for (int j = 0; j < K; ++j)
       buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, j * kBurstBlock * 16, kPolicyNT));
@@ -672,20 +665,20 @@ __global__ __launch_bounds__(kBurstBlock) void burst_ring_kernel(const BurstArgs
   using F_ = std::false_type;
   auto next_rsrc = [&]() {
     rank = rank + 1 == p ? 0 : rank + 1;
-    return tile_rsrc(a.src[rank], off, bytes);
+    return raw_rsrc(a.src[rank], off, bytes);
   };
   if (p == 1) {
-    leaf(T_{}, F_{}, tile_rsrc(a.src[rank], off, bytes));
+    leaf(T_{}, F_{}, raw_rsrc(a.src[rank], off, bytes));
   } else {
     leaf(T_{}, T_{}, next_rsrc());
     for (int k = 1; k < p - 1; ++k) leaf(F_{}, T_{}, next_rsrc());
-    leaf(F_{}, F_{}, tile_rsrc(a.src[rank], off, bytes));
+    leaf(F_{}, F_{}, raw_rsrc(a.src[rank], off, bytes));
   }
   u32x4 out[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) out[j] = S::narrow(acc[j]);
   for (int d = 0; d < p; ++d) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(a.dst[d], off, bytes);
+    const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.dst[d], off, bytes);
 #pragma unroll
     for (int j = 0; j < K; ++j)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out[j]), r, vo, j * kBurstBlock * 16, kPolicyNT);
