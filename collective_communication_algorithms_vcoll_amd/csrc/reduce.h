@@ -65,10 +65,23 @@ hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo
 struct BurstArgs {
   const void* src[kMaxRanks];
   void* dst[kMaxRanks];
-  int64_t q;                  // chunk length in elements
+  int64_t q;                  // chunk length in elements: chunk c holds q + (c < r) of them
+  int32_t r;
   int32_t p;
-  int32_t tv;                 // 16-byte vectors per tile (at most burst_tile_max)
+  int32_t tv;                 // 16-byte vectors per tile (a multiple of 8, at most burst_tile_max)
+  int32_t align;              // 128: every buffer has address phase `phase` mod 128, tiles start on
+  int32_t phase;              // 128-byte cache lines; 16: tiles start on any 16-byte boundary
+  int32_t pad;
 };
+
+// First 16-byte vector of a burst tile in a chunk whose elements start at e0
+// (VE elements per vector): the first whole vector, moved up to an `align`
+// boundary of every buffer (which all have address phase `phase` mod align).
+__host__ __device__ inline int64_t burst_first_vector(int64_t e0, int ve, int32_t align, int32_t phase) {
+  const int64_t v = (e0 + ve - 1) / ve;
+  const int64_t mis = (phase + v * 16) % align;
+  return mis ? v + (align - mis) / 16 : v;
+}
 static_assert(sizeof(BurstArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Largest tile (16-byte vectors) one workgroup of the burst kernel holds.

@@ -75,6 +75,16 @@ bool all_aligned(int p, const void* const* ptrs) {
   return true;
 }
 
+// The address of every send and receive buffer mod `m` (a power of two), or
+// -1 when they differ.
+int32_t common_phase(int p, const void* const* send, void* const* recv, uintptr_t m) {
+  const uintptr_t ph = reinterpret_cast<uintptr_t>(send[0]) & (m - 1);
+  for (int r = 0; r < p; ++r)
+    if ((reinterpret_cast<uintptr_t>(send[r]) & (m - 1)) != ph || (reinterpret_cast<uintptr_t>(recv[r]) & (m - 1)) != ph)
+      return -1;
+  return static_cast<int32_t>(ph);
+}
+
 // Compute units of the current device, read once per device (0 when no
 // device can be queried, which turns the burst kernel off).
 int device_cus() {
@@ -98,14 +108,20 @@ constexpr int64_t kBurstMinTile = 3072;
 // Tiles per chunk for the two-phase ring all-reduce, or 0 when the one-pass
 // kernel is the better choice: the whole vector must fit in one generation
 // of workgroups (one per compute unit) at between kBurstMinTile and
-// burst_tile_max vectors each, with chunks of whole 16-byte vectors.
-int burst_tiles(int p, int64_t n, vcoll_dtype dtype, int64_t* tv) {
-  const int64_t ve = 16 / elem_bytes(dtype);
-  if (n % (static_cast<int64_t>(p) * ve) != 0) return 0;
+// burst_tile_max vectors each. A chunk's tiles cover the 16-byte vectors
+// wholly inside it (the kernel sums the few elements around its ends one by
+// one), so the largest such count over the chunks sets the tile.
+int burst_tiles(int p, const Chunks& ch, vcoll_dtype dtype, int32_t align, int32_t phase, int64_t* tv) {
+  const int ve = 16 / static_cast<int>(elem_bytes(dtype));
   const int per_chunk = device_cus() / p;
   if (per_chunk < 1) return 0;
-  const int64_t cv = n / p / ve;
-  const int64_t t = (cv + per_chunk - 1) / per_chunk;
+  int64_t cv = 0;
+  for (int c = 0; c < p; ++c) {
+    const int64_t e0 = ch.off(c), e1 = e0 + ch.count(c);
+    const int64_t whole = e1 / ve - burst_first_vector(e0, ve, align, phase);
+    if (whole > cv) cv = whole;
+  }
+  const int64_t t = ((cv + per_chunk - 1) / per_chunk + 7) / 8 * 8;   // whole 128-byte cache lines
   if (t < kBurstMinTile || t > burst_tile_max(dtype)) return 0;
   *tv = t;
   return static_cast<int>((cv + t - 1) / t);
@@ -128,15 +144,15 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
   a.r = ch.r;
   a.p = p;
   a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv));
-  // a common address phase mod 256 lets the all-reduce tiles start on whole cache lines
-  const uintptr_t ph = reinterpret_cast<uintptr_t>(send[0]) & 255u;
-  bool same = true;
-  for (int r = 0; r < p && same; ++r)
-    same = (reinterpret_cast<uintptr_t>(send[r]) & 255u) == ph && (reinterpret_cast<uintptr_t>(recv[r]) & 255u) == ph;
-  a.align = same ? 256 : 16;
-  a.phase = same ? static_cast<int32_t>(ph) : 0;
+  // a common address phase mod 256 (mod 128) lets the tiles start on whole
+  // cache lines of every buffer
+  const int32_t ph256 = common_phase(p, send, recv, 256), ph128 = common_phase(p, send, recv, 128);
+  a.align = ph256 >= 0 ? 256 : 16;
+  a.phase = ph256 >= 0 ? ph256 : 0;
+  const int32_t burst_align = ph128 >= 0 ? 128 : 16, burst_phase = ph128 >= 0 ? ph128 : 0;
   int64_t tv = 0;
-  const int tiles = (!scatter && algo == VCOLL_RING && a.vec) ? burst_tiles(p, n, dtype, &tv) : 0;
+  const int tiles = (!scatter && algo == VCOLL_RING && a.vec)
+                        ? burst_tiles(p, ch, dtype, burst_align, burst_phase, &tv) : 0;
   if (tiles > 0) {
     BurstArgs b;
     std::memset(&b, 0, sizeof(b));
@@ -145,8 +161,11 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
       b.dst[r] = recv[r];
     }
     b.q = ch.q;
+    b.r = static_cast<int32_t>(ch.r);
     b.p = p;
     b.tv = static_cast<int32_t>(tv);
+    b.align = burst_align;
+    b.phase = burst_phase;
     return from_hip(launch_burst_ring(b, dtype, tiles, static_cast<hipStream_t>(stream)));
   }
   const OrderProgram prog = order_program(algo, p);

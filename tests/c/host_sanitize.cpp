@@ -63,9 +63,18 @@ int64_t burst_tile_max(vcoll_dtype dtype) { return dtype == VCOLL_F32 ? 25 * 256
 static long g_burst = 0;
 namespace vcoll {
 hipError_t launch_burst_ring(const BurstArgs& a, vcoll_dtype dtype, int tiles, hipStream_t) {
-  // every tile starts inside its chunk, and the tiles cover the chunk
-  const int64_t cv = a.q / (dtype == VCOLL_F32 ? 4 : 8);
-  if (!(a.tv >= 1 && a.tv <= burst_tile_max(dtype) && int64_t(tiles - 1) * a.tv < cv && int64_t(tiles) * a.tv >= cv)) {
+  // the tiles cover the whole vectors of the largest chunk, and every tile
+  // starts inside it
+  const int64_t ve = dtype == VCOLL_F32 ? 4 : 8;
+  int64_t cv = 0;
+  for (int c = 0; c < a.p; ++c) {
+    const int64_t e0 = c * a.q + (c < a.r ? c : a.r), e1 = e0 + a.q + (c < a.r ? 1 : 0);
+    const int64_t whole = e1 / ve - burst_first_vector(e0, static_cast<int>(ve), a.align, a.phase);
+    cv = whole > cv ? whole : cv;
+  }
+  if (!(a.tv >= 1 && a.tv <= burst_tile_max(dtype) && a.tv % 8 == 0 && int64_t(tiles - 1) * a.tv < cv &&
+        int64_t(tiles) * a.tv >= cv && a.r >= 0 && a.r < a.p && (a.align == 16 || a.align == 128) &&
+        a.phase >= 0 && a.phase < a.align && a.phase % 16 == 0)) {
     std::fprintf(stderr, "burst tiling does not cover the chunk\n");
     std::abort();
   }
@@ -334,8 +343,25 @@ int main() {
     CHECK(vcoll_allreduce(VCOLL_RING, 8, 6553600, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
     CHECK(g_burst == before + 1);
     CHECK(vcoll_allreduce(VCOLL_RABENSEIFNER, 8, 6553600, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
-    CHECK(vcoll_allreduce(VCOLL_RING, 8, 6553600 + 8, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
     CHECK(vcoll_allreduce(VCOLL_RING, 8, 1 << 20, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(vcoll_allreduce(VCOLL_RING, 8, 2 * 6553600, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(g_burst == before + 1);
+    // chunks that are not whole vectors (n mod p*VE != 0) take it too
+    CHECK(vcoll_allreduce(VCOLL_RING, 8, 6553600 + 5, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
+    CHECK(g_burst == before + 2);
+    CHECK(vcoll_allreduce(VCOLL_RING, 8, 6553600 - 3, VCOLL_BF16, send, recv, nullptr) == VCOLL_OK);
+    CHECK(g_burst == before + 3);
+  }
+  {
+    // p = 72 x 16 MiB float32: 58,254 or 58,255 elements per chunk
+    void* send[72];
+    void* recv[72];
+    for (int r = 0; r < 72; ++r) {
+      send[r] = reinterpret_cast<void*>(uintptr_t(0x100000) * (r + 1));
+      recv[r] = reinterpret_cast<void*>(uintptr_t(0x100000) * (r + 73));
+    }
+    const long before = g_burst;
+    CHECK(vcoll_allreduce(VCOLL_RING, 72, 1 << 22, VCOLL_F32, send, recv, nullptr) == VCOLL_OK);
     CHECK(g_burst == before + 1);
   }
   std::printf("OK %ld launches recorded\n", g_launches);

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import assert_bits_equal, bits, download, say, upload
+from tests.gpu_util import assert_bits_equal, bits, download, say, upload, upload_list
 
 pytestmark = pytest.mark.gpu
 
@@ -25,13 +25,21 @@ def vc():
 
 def burst_tile(p, n, dtype, cus=256):
     """Vectors per tile the library picks, or 0 if it takes the one-pass kernel
-    (the same rule as the host library, restated for the test's shapes)."""
+    (the same rule as the host library, restated for the test's shapes): the
+    largest count of 16-byte vectors lying wholly inside one chunk, spread
+    over the compute units a chunk gets, in whole 128-byte lines. (The
+    library also moves each chunk's first tile up to a 128-byte boundary,
+    which can shorten a chunk by up to 7 vectors; the shapes below are far
+    from the thresholds.)"""
     ve = 4 if dtype == "f32" else 8
-    if n % (p * ve):
-        return 0
     per_chunk = cus // p
-    cv = n // p // ve
-    t = -(-cv // per_chunk)
+    q, r = divmod(n, p)
+    cv = 0
+    for c in range(p):
+        e0 = c * q + min(c, r)
+        e1 = e0 + q + (c < r)
+        cv = max(cv, e1 // ve - -(-e0 // ve))
+    t = (-(-cv // per_chunk) + 7) // 8 * 8
     tmax = (25 if dtype == "f32" else 16) * 256
     return t if 3072 <= t <= tmax else 0
 
@@ -46,6 +54,12 @@ CASES = [
     (72, 4_320_000, "f32"),             # 3 tiles per chunk, run-time rank count
     (8, 7_168_000, "bf16"),             # bfloat16: 16 vectors (128 elements) per thread
     (16, 6_825_984, "bf16"),
+    # chunks that are not whole vectors: each chunk's end elements go one by one
+    (72, 4_194_304, "f32"),             # 16 MiB per rank: 58,254 or 58,255 elements per chunk
+    (8, 6_553_604, "f32"),              # 4 chunks one element longer
+    (3, 4_800_004, "f32"),
+    (16, 6_826_008, "bf16"),
+    (5, 7_000_008, "bf16"),
 ]
 
 
@@ -66,6 +80,28 @@ def test_two_phase_ring_matches_oracle(vc, p, n, dtype):
     vc.vcoll_allreduce("ring", t, t)
     torch.cuda.synchronize()
     assert_bits_equal(download(t, dtype), want, f"in-place ring p={p} n={n} {dtype}")
+
+
+# separately allocated rank buffers whose length is not a whole number of
+# 16-byte vectors: the last chunk's final elements share no vector with a
+# neighbour and still go one by one
+LIST_CASES = [(8, 6_553_601, "f32"), (8, 6_553_603, "f32"), (16, 6_825_989, "bf16"), (72, 4_194_307, "f32")]
+
+
+@pytest.mark.parametrize("p,n,dtype", LIST_CASES, ids=[f"p{p}-n{n}-{d}" for p, n, d in LIST_CASES])
+def test_two_phase_ring_ragged_buffer_lengths(vc, p, n, dtype):
+    import torch
+    assert burst_tile(p, n, dtype) > 0
+    x = [workloads.rank_window(workloads.TAG_TEST * 1000 + 760 + p, r, 0, n, ("normal", 0.0, 1.0), dtype)
+         for r in range(p)]
+    want, _ = oracle.allreduce(x, "ring", dtype)
+    send = upload_list(x, dtype)
+    recv = [torch.empty_like(t) for t in send]
+    say(f"two-phase ring, separate buffers, p={p} n={n} {dtype}")
+    vc.vcoll_allreduce("ring", send, recv)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert_bits_equal(download(recv[r], dtype), bits(want[r], dtype), f"rank {r}")
 
 
 def test_two_phase_ring_special_values(vc):
