@@ -451,12 +451,12 @@ def cfg4(vc, torch, cpu_leg: bool) -> dict:
     recv = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K)
     push = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, recv=recv)          # noqa: E731
     _, ms = time_launches([push], 10, 2)
-    res["dispatch"] = roof("dispatch_push_kernel<bf16, 256>", p8 * T * rb + rows * rb, ms)
+    res["dispatch"] = roof("dispatch_push_kernel<false, 64> (bf16, 2 KiB row segments)", p8 * T * rb + rows * rb, ms)
     # combine: token-major (each (token, slot) row pulled from its expert output)
     back = vc.vcoll_moe_combine(recv, slots_g, T, K)
     pull = lambda: vc.vcoll_moe_combine(recv, slots_g, T, K, out=back)                    # noqa: E731
     _, ms = time_launches([pull], 10, 2)
-    res["combine"] = roof("combine_pull_kernel<512>", 2 * rows * rb, ms)
+    res["combine"] = roof("combine_pull_kernel<64> (1 KiB row segments)", 2 * rows * rb, ms)
     torch.cuda.synchronize()
     res["combine_of_dispatch_is_identity"] = all(
         torch.equal(back[i].view(T, K, H).view(torch.int16), toks[i].view(torch.int16).unsqueeze(1).expand(T, K, H))
@@ -465,7 +465,7 @@ def cfg4(vc, torch, cpu_leg: bool) -> dict:
     f8 = vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True)
     push8 = lambda: vc.vcoll_moe_dispatch(toks, slots_g, recv_rows, K, fp8=True, recv=f8)  # noqa: E731
     _, ms = time_launches([push8], 10, 2)
-    res["dispatch_fp8"] = roof("dispatch_push_kernel<fp8, 512>", p8 * T * rb + rows * orb, ms)
+    res["dispatch_fp8"] = roof("dispatch_push_kernel<true, 512> (FP8)", p8 * T * rb + rows * orb, ms)
     del f8
     # the plain block transpose on the same splits (send buffers already in
     # destination-block order)
@@ -827,9 +827,9 @@ def moe_variants(vc, torch) -> dict:
     _, ms_dt = time_launches([d4], 10, 2)
     _, ms_d8t = time_launches([d5], 10, 2)
     offrank = lambda sp: int(sp.sum() - np.trace(sp))                              # noqa: E731
-    res["dispatch_dedup_token_major"] = roof("dispatch_push_kernel<bf16, 256>, deduplicated plan",
+    res["dispatch_dedup_token_major"] = roof("dispatch_push_kernel<false, 64>, deduplicated plan",
                                              uniq + rows_u * rb, ms_dt)
-    res["dispatch_dedup_token_major_fp8"] = roof("dispatch_push_kernel<fp8, 512>, deduplicated plan",
+    res["dispatch_dedup_token_major_fp8"] = roof("dispatch_push_kernel<true, 512> (FP8), deduplicated plan",
                                                  uniq + rows_u * orb, ms_d8t)
     res["dedup"] = {
         "rows": rows_u, "rows_plain": rows, "offrank_rows": offrank(su), "offrank_rows_plain": offrank(splits),
@@ -990,15 +990,15 @@ TRAFFIC_GROUPS = {
         ("ring reduce-scatter, p=16 x 192 MiB bf16", "reduce_kernel<1, 0, 16, 1, true, false, 64>", 3_422_552_064),
         ("all-gather of 12 MiB bf16 blocks, p=16", "all_gather_kernel<2, 1, 64, false>", 3_422_552_064),
         ("variable-split all-to-all of the MoE splits (plain)", "all_to_all_kernel<1024>", None),
-        ("token-major MoE dispatch, bf16", "dispatch_push_kernel<false, 256>", None),
+        ("token-major MoE dispatch, bf16", "dispatch_push_kernel<false, 64>", None),
         ("token-major MoE dispatch, FP8", "dispatch_push_kernel<true, 512>", None),
-        ("token-major MoE combine", "combine_pull_kernel<512>", None),
+        ("token-major MoE combine", "combine_pull_kernel<64>", None),
         ("row-major MoE dispatch, gather map (all-to-all)", "all_to_all_kernel<256>", None),
         ("row-major FP8 dispatch (gather + quantise)", "dispatch_fp8_kernel", None),
     ],
     "sweep": [
         ("copy, 200 MiB read + 200 MiB written (counter scale)", "copy_kernel<2, 64", 419_430_400),
-        ("ring all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 0, 0, 1, false, false, 256>",
+        ("ring all-reduce, p=72 x 16 MiB f32 (two-phase, ragged chunks)", "burst_ring_kernel<0, 25>",
          2 * 72 * 16 * 2 ** 20),
         ("tree all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
          2 * 72 * 16 * 2 ** 20),
@@ -1007,7 +1007,7 @@ TRAFFIC_GROUPS = {
         ("tree all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
          2 * 72 * 256 * 2 ** 20),
         ("ring reduce-scatter, p=72 x 64 MiB f32 (unaligned chunk starts)",
-         "reduce_kernel<0, 0, 0, 1, true, false, 256>", 73 * 64 * 2 ** 20),
+         "reduce_scatter_shifted_kernel<0>", 73 * 64 * 2 ** 20),
         ("ring all-reduce, p=16 x 16 MiB f32", "burst_ring_kernel<0, 25>", 2 * 16 * 16 * 2 ** 20),
         ("ring all-reduce, p=16 x 64 MiB f32", "reduce_kernel<0, 0, 16, 1, false, true, 64>", 2 * 16 * 64 * 2 ** 20),
         ("ring all-reduce, p=8 x 1 GiB f32", "reduce_kernel<0, 0, 8, 2, false, true, 256>", 2 * 8 * 2 ** 30),
@@ -1086,8 +1086,8 @@ def traffic_set(vc, torch, launches: int, group: str) -> int:
         src_g = [torch.from_numpy(src_rows[i][:int(splits[i].sum())].copy()).cuda() for i in range(p8)]
         run(lambda: vc.vcoll_moe_dispatch_fp8(toks, splits, src_g, tm8))
         uniq = p8 * T * rb                          # every token row once
-        filled = {"all_to_all_kernel<1024>": 2 * rows * rb, "dispatch_push_kernel<false, 256>": uniq + rows * rb,
-                  "dispatch_push_kernel<true, 512>": uniq + rows * orb, "combine_pull_kernel<512>": 2 * rows * rb,
+        filled = {"all_to_all_kernel<1024>": 2 * rows * rb, "dispatch_push_kernel<false, 64>": uniq + rows * rb,
+                  "dispatch_push_kernel<true, 512>": uniq + rows * orb, "combine_pull_kernel<64>": 2 * rows * rb,
                   "all_to_all_kernel<256>": uniq + rows * rb, "dispatch_fp8_kernel": uniq + rows * orb}
     else:
         copy_ref()
