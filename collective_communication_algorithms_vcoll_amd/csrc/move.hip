@@ -15,9 +15,13 @@ using namespace dev;
 // cache level, or cached. The streamed form is a buffer store whose resource
 // base is the workgroup's tile in the destination (uniform), the lane's
 // place in it a 32-bit offset. Measured on MI355X (launches that write up to
-// 1 GiB): sc0|nt|sc1 stores ran 7-19% faster than nt-only global stores (an
-// all-gather of 3.125 MiB f32 blocks at p = 8 and a 25 MiB broadcast to 8
-// buffers +19%, 1 MiB blocks at p = 8 +7%, 64 KiB bf16 blocks at p = 72 +3%).
+// 1 GiB): with the source still in the Infinity Cache, sc0|nt|sc1 stores ran
+// 7-19% faster than nt-only global stores (an all-gather of 3.125 MiB f32
+// blocks at p = 8 and a 25 MiB broadcast to 8 buffers +19%, 1 MiB blocks at
+// p = 8 +7%); with the source read from HBM the two are within 2% (64 KiB
+// bf16 blocks at p = 72 +2%), and every fan-out shape tried -- one load then
+// all stores per tile, or a whole chip-wide read phase before the writes --
+// runs at 5.4-5.5 TB/s.
 // The large fan-outs write faster through L2 with cached stores: the
 // all-gather and broadcast beyond 1 GiB written (4-6%) and the bf16
 // token-major MoE dispatch, 8 copies of each token row (3%). One-to-one

@@ -28,14 +28,20 @@
  *     with VCOLL_ERR_INVALID_ARG, so every byte offset fits in int64.
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
  *     stream) and the call returns before it completes. The library never
- *     synchronizes, never allocates device memory, and keeps no state
- *     between calls. A failed launch returns VCOLL_ERR_HIP; faults of
- *     running kernels surface at the caller's next synchronization.
+ *     synchronizes and never allocates device memory at run time. Its only
+ *     state is two per-device caches filled on first use and kept until the
+ *     process ends (the device's compute-unit count, which sizes the
+ *     two-phase all-reduce, and the address of the static scratch array of
+ *     vcoll_allreduce_stepwise_static), plus that array itself. A failed
+ *     launch returns VCOLL_ERR_HIP; faults of running kernels surface at
+ *     the caller's next synchronization.
  *   - `send` / `recv` are host arrays of p device pointers, read only during
  *     the call. The caller owns every device buffer.
  *   - Rank buffers are contiguous arrays of the storage type. When every
  *     pointer of a call is 16-byte aligned the kernels move 16-byte vectors;
  *     otherwise they fall back to element-wise access (slower, same result).
+ *     Buffers that also share their address mod 128 (or 256) get tiles on
+ *     whole cache lines, which the all-reduces need for full speed.
  *   - Arithmetic: float32 adds, round to nearest even, no fused
  *     multiply-add, denormals kept. bfloat16 inputs widen exactly to
  *     float32, all p-1 adds of an element happen in float32, and the result
