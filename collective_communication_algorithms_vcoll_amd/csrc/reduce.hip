@@ -169,6 +169,91 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
   }
 }
 
+// kElemBatch elements e0 + u*stride at once (those below `limit`): the loads
+// of all of them go out together, so a thread waits on memory once per batch
+// of ranks rather than once per element (the path of buffers that are not
+// 16-byte aligned, where every element is reduced this way).
+constexpr int kElemBatch = 4;
+
+template <int D, int ALGO, int P, bool RS>
+__device__ __forceinline__ void reduce_elems(const ReduceArgs& a, int c, int p, int rot, int64_t e0,
+                                             int64_t stride, int64_t limit, int64_t off) {
+  using S = Storage<D>;
+  using E = typename S::elem;
+  constexpr int U = kElemBatch;
+  int64_t e[U];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    e[u] = e0 + u * stride;
+    ok[u] = e[u] < limit;
+  }
+  float res[U];
+  if constexpr (P > 0) {
+    const void* const* L = leaf_row<ALGO>(a, c);
+    E raw[P][U];
+    static_for<0, P>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw[k][u] = ok[u] ? static_cast<const E*>(L[k])[e[u]] : E(0);
+    });
+    float st[Prog<ALGO, P>::depth][U];
+    run_program<ALGO, P, 0, 0>(st, [&](auto kc, float(&d)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) d[u] = S::widen1(raw[decltype(kc)::value][u]);
+    });
+#pragma unroll
+    for (int u = 0; u < U; ++u) res[u] = st[0][u];
+  } else {
+    constexpr int B = 16;                        // ranks whose loads are in flight together
+    float st[kRuntimeDepth][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) res[u] = 0.0f;
+    for (int k0 = 0; k0 < p; k0 += B) {
+      E raw[B][U];
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (k0 + b < p) {
+          const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : k0 + b;
+#pragma unroll
+          for (int u = 0; u < U; ++u) raw[b][u] = ok[u] ? static_cast<const E*>(a.leaf[rank])[e[u]] : E(0);
+        }
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (k0 + b < p) {
+          float v[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) v[u] = S::widen1(raw[b][u]);
+          if constexpr (ALGO == VCOLL_RING) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) res[u] = k0 + b == 0 ? v[u] : res[u] + v[u];
+          } else {
+            rt_push<U>(st, v);
+            for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<U>(st);
+          }
+        }
+    }
+    if constexpr (ALGO != VCOLL_RING) {
+      for (int m = 0; m < a.final_merges; ++m) rt_merge<U>(st);
+#pragma unroll
+      for (int u = 0; u < U; ++u) res[u] = st[0][u];
+    }
+  }
+  E out[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) out[u] = S::narrow1(res[u]);
+  if constexpr (RS) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) static_cast<E*>(a.dst[c])[e[u] - off] = out[u];
+  } else {
+    for (int r = 0; r < p; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ok[u]) static_cast<E*>(a.dst[r])[e[u]] = out[u];
+  }
+}
+
 // ----------------------------------------------------------------------------
 // V 16-byte vectors per thread, fixed p: all p*V loads are issued before the
 // first add, the order program runs in registers, then p*V (or V) stores.
@@ -347,12 +432,11 @@ __global__ __launch_bounds__(BS) void reduce_kernel(const ReduceArgs a) {
         reduce_one<D, ALGO, P, RS>(a, c, p, rot, i < head ? off + i : e_base + nvec * VE + (i - head), off);
     }
   } else {
+    static_assert((V * VE) % kElemBatch == 0, "whole element batches per thread");
     const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (V * BS * VE);
 #pragma unroll 1
-    for (int j = 0; j < V * VE; ++j) {
-      const int64_t i = e0 + j * BS + tid;
-      if (i < cnt) reduce_one<D, ALGO, P, RS>(a, c, p, rot, off + i, off);
-    }
+    for (int j = 0; j < V * VE; j += kElemBatch)
+      reduce_elems<D, ALGO, P, RS>(a, c, p, rot, off + e0 + j * BS + tid, BS, off + cnt, off);
   }
 }
 

@@ -130,22 +130,52 @@ def test_allreduce_tiny_and_max_p(vc, p, n):
             assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"{algo} p={p} n={n}")
 
 
+# element path: compiled p, run-time p (batches of 16 ranks), several tiles
+# per chunk with a ragged end
+UNALIGNED_SHAPES = [(8, 5000), (5, 70001), (16, 100003), (72, 30011)]
+
+
 @pytest.mark.parametrize("algo", ALGOS)
-def test_allreduce_unaligned_buffers_use_element_path(vc, algo):
+@pytest.mark.parametrize("p,n", UNALIGNED_SHAPES, ids=[f"p{p}-n{n}" for p, n in UNALIGNED_SHAPES])
+def test_allreduce_unaligned_buffers_use_element_path(vc, algo, p, n):
     import torch
-    p, n = 8, 5000
+    if algo == "rabenseifner" and p & (p - 1):
+        pytest.skip("halving and doubling need a power-of-two p")
     for dtype in ("f32", "bf16"):
-        x = rand_inputs(p, n, dtype, seed=11)
+        x = rand_inputs(p, n, dtype, seed=11 + p)
         want, _ = oracle.allreduce(x, algo, dtype)
         big = upload([np.concatenate([v[:1], v]) for v in x], dtype)
         send = [big[r, 1:] for r in range(p)]                 # 1 element off 16-byte alignment
         out_big = torch.zeros_like(big)
         recv = [out_big[r, 1:] for r in range(p)]
-        say(f"unaligned vcoll_allreduce algo={algo} dtype={dtype}")
+        say(f"unaligned vcoll_allreduce algo={algo} p={p} n={n} dtype={dtype}")
         vc.vcoll_allreduce(algo, send, recv)
         sync()
-        got = download(out_big, dtype)[:, 1:]
-        assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"unaligned {algo} {dtype}")
+        got = download(out_big, dtype)
+        assert_bits_equal(got[:, 1:], np.stack([bits(w, dtype) for w in want]), f"unaligned {algo} {dtype}")
+        assert not got[:, 0].any(), "element before the buffers written"
+
+
+@pytest.mark.parametrize("algo", ["ring", "rabenseifner"])
+@pytest.mark.parametrize("p,n", UNALIGNED_SHAPES, ids=[f"p{p}-n{n}" for p, n in UNALIGNED_SHAPES])
+def test_reduce_scatter_unaligned_buffers_use_element_path(vc, algo, p, n):
+    import torch
+    if algo == "rabenseifner" and p & (p - 1):
+        pytest.skip("halving and doubling need a power-of-two p")
+    for dtype in ("f32", "bf16"):
+        x = rand_inputs(p, n, dtype, seed=23 + p)
+        want, _ = oracle.reduce_scatter(x, algo, dtype)
+        big = upload([np.concatenate([v[:1], v]) for v in x], dtype)
+        send = [big[r, 1:] for r in range(p)]
+        outs = [torch.zeros(len(w) + 1, dtype=big.dtype, device=big.device) for w in want]
+        recv = [o[1:] for o in outs]
+        say(f"unaligned vcoll_reduce_scatter algo={algo} p={p} n={n} dtype={dtype}")
+        vc.vcoll_reduce_scatter(algo, send, recv)
+        sync()
+        for r in range(p):
+            got = download(outs[r], dtype)
+            assert_bits_equal(got[1:], bits(want[r], dtype), f"unaligned RS {algo} rank {r} {dtype}")
+            assert got[0] == 0, "element before the output written"
 
 
 @pytest.mark.parametrize("algo", ALGOS)
