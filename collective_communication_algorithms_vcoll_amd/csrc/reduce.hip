@@ -205,7 +205,11 @@ __device__ __forceinline__ void reduce_elems(const ReduceArgs& a, int c, int p, 
 #pragma unroll
     for (int u = 0; u < U; ++u) res[u] = st[0][u];
   } else {
-    constexpr int B = 16;                        // ranks whose loads are in flight together
+    // ranks whose loads are in flight together: 8 keeps the kernel's register
+    // count (set by its vector path) where it was; 16 took the run-time
+    // trees from 5 to 4 waves per SIMD and p = 72 tree all-reduces of 4 and
+    // 16 MiB per rank 2-9 % slower, for 6 % on unaligned buffers
+    constexpr int B = 8;
     float st[kRuntimeDepth][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) res[u] = 0.0f;
