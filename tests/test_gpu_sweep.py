@@ -1,14 +1,14 @@
 """Every point of the message-size sweep (p in {2, 4, 8, 16, 72}, 1 KiB to
 1 GiB per rank, four algorithms) against the oracle.
 
-Every element is compared wherever a point's p*n is at most 2^30 elements
-(4 GiB of inputs): the seeded inputs and the oracle's outputs are produced
+Every element is compared wherever a point's p*n is at most 1.6e9 elements
+(6.4 GB of inputs): the seeded inputs and the oracle's outputs are produced
 window by window by a pool of CPU workers. Beyond that (p = 8 and 16 at
-1 GiB per rank, p = 72 from 64 MiB) the inputs come from torch's device
-generator and every chunk boundary plus 16 random windows of 1024 elements
-are copied back and compared; each test states the fraction of elements it
-verified, and with VCOLL_PARITY_LOG set appends one JSON line per point to
-that file."""
+1 GiB per rank, p = 72 at 256 MiB and 1 GiB) the inputs come from torch's
+device generator and every chunk boundary plus 16 random windows of 1024
+elements are copied back and compared; each test states the fraction of
+elements it verified, and with VCOLL_PARITY_LOG set appends one JSON line
+per point to that file."""
 import json
 import os
 
@@ -22,7 +22,7 @@ from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
 
-FULL_LIMIT = 2 ** 30           # p*n elements verified in full up to here
+FULL_LIMIT = 1_600_000_000     # p*n elements verified in full up to here (p = 72 x 80 MiB: 1.5e9)
 IN_PROCESS = 2 ** 22           # below this the oracle runs in the test process
 
 
