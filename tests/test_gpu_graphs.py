@@ -25,11 +25,16 @@ def test_captured_allreduces_replay_exactly(vc):
     g = torch.Generator(device="cuda").manual_seed(21)
     x = torch.randn((p, n), device="cuda", generator=g)
     y = torch.randn((16, 1 << 16), device="cuda", generator=g).to(torch.bfloat16)
+    # the two-phase ring kernel (chunks one element apart) and a broadcast fan-out
+    z = torch.randn((8, 3_276_804), device="cuda", generator=g)
+    bsrc = torch.randn(1 << 20, device="cuda", generator=g)
     outs = {a: torch.empty_like(x) for a in ("ring", "rd", "rabenseifner", "tree")}
-    oy = torch.empty_like(y)
+    oy, oz = torch.empty_like(y), torch.empty_like(z)
+    ob = torch.empty((8, 1 << 20), device="cuda")
     # eager results
     want = {a: vc.vcoll_allreduce(a, x).clone() for a in outs}
     want_y = vc.vcoll_allreduce("rabenseifner", y).clone()
+    want_z = vc.vcoll_allreduce("ring", z).clone()
     stepwise_want, _ = vc.vcoll_allreduce_stepwise("ring", x)
     stepwise_want = stepwise_want.clone()
     so = torch.empty_like(x)
@@ -46,8 +51,10 @@ def test_captured_allreduces_replay_exactly(vc):
             vc.vcoll_allreduce(a, x, o)
         vc.vcoll_allreduce("rabenseifner", y, oy)
         vc.vcoll_allreduce_stepwise("ring", x, so)
+        vc.vcoll_allreduce("ring", z, oz)
+        vc.vcoll_broadcast(bsrc, ob, 0)
     for rep in range(4):
-        for o in list(outs.values()) + [oy, so]:
+        for o in list(outs.values()) + [oy, so, oz, ob]:
             o.fill_(float("nan"))                        # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
@@ -56,6 +63,8 @@ def test_captured_allreduces_replay_exactly(vc):
             assert torch.equal(o.view(torch.int32), want[a].view(torch.int32)), (rep, a)
         assert torch.equal(oy.view(torch.int16), want_y.view(torch.int16)), rep
         assert torch.equal(so.view(torch.int32), stepwise_want.view(torch.int32)), rep
+        assert torch.equal(oz.view(torch.int32), want_z.view(torch.int32)), rep
+        assert all(torch.equal(ob[r].view(torch.int32), bsrc.view(torch.int32)) for r in range(8)), rep
 
 
 def test_captured_all_to_all_and_moe_dispatch_replay(vc):
