@@ -46,6 +46,8 @@ struct ReduceArgs {
   int32_t align;              // all-reduce tiles start on this byte boundary (256 when every buffer
                               // has the same address mod 256, else 16)
   int32_t phase;              // that common address mod `align` (0 for align 16)
+  int32_t src_align;          // 128 when every input buffer has address phase `src_phase` mod 128
+  int32_t src_phase;          // (the unaligned reduce-scatter then loads whole lines), else 16 and 0
   uint8_t rank[kMaxRanks];
   uint8_t merges[kMaxRanks];
 };

@@ -447,63 +447,95 @@ __global__ __launch_bounds__(BS) void reduce_kernel(const ReduceArgs a) {
 // ----------------------------------------------------------------------------
 // ring reduce-scatter with a run-time p and chunk starts that are not 16-byte
 // aligned. The output recv[c] is aligned, the inputs are not: element j of
-// chunk c is input element off + j. Each lane sums the ring chain over the
-// ALIGNED input vector u (elements a0 + u*VE .. +VE, a0 = off - shift), which
-// is the sum at those input positions; output vector u then takes the last
-// VE - shift sums of vector u and the first `shift` sums of vector u + 1,
-// which the next lane holds (one wave shuffle per output vector, not per
-// rank). A wave covers 64 aligned vectors and stores 63 output vectors, so
-// the vector its last lane needs is always inside the wave (waves overlap by
-// one vector: 1/64 of the loads twice). The positions before the chunk start
-// are summed in chunk c's order but never stored. The last output vectors,
-// whose neighbour would reach past the chunk, and the ragged end take the
-// element path. Measured on MI355X, p = 72 x 64 MiB per rank: the element
-// path for every element of such chunks ran at 5.5 TB/s.
+// chunk c is input element off + j. Each lane sums the ring chain over one
+// ALIGNED input vector; output vector j then takes the last VE - shift sums
+// of input vector j and the first `shift` sums of input vector j + 1, which
+// the next lane holds (one wave shuffle per output vector, not per rank).
+// Two wave shapes:
+//  * LINES = false: a wave loads 64 consecutive input vectors and stores the
+//    63 outputs whose both vectors it holds (waves overlap by one vector);
+//  * LINES = true: a wave's 64 input vectors start on a 128-byte line of
+//    every input (when the inputs share an address phase mod 128), so its
+//    loads are whole lines, and it stores all 64 outputs that start in
+//    them; the vector after the wave, which the last output needs, is
+//    summed by the wave's last lane as well (one extra 16-byte load per
+//    rank, from a line the next wave loads).
+// The chunk's last output vectors, whose neighbour would reach past the
+// chunk, and its ragged end take the element path. Measured on MI355X with
+// f32: p = 72 x 64 MiB per rank ran 855 us with 63-output waves (whose loads
+// straddle lines: 1.09x the algorithmic bytes read) and 795 us with
+// line-aligned ones (6.17 TB/s, the aligned p = 64 case's rate), p = 24 x
+// 64 MiB 294 -> 275 us; but the extra registers of the line-aligned shape
+// (84 instead of 44, 5 waves per SIMD instead of 8) cost 2-4 % on grids of
+// one or two workgroup generations (p = 72 at 4 and 16 MiB) and 5 % for
+// bf16, so the host takes it for f32 grids of many generations only.
+// The element path for every element of such chunks ran at 5.5 TB/s.
 
-constexpr int kShiftWaveOut = 63;                                // output vectors per wave
-
-template <int D>
+template <int D, bool LINES>
 __global__ __launch_bounds__(kBlock) void reduce_scatter_shifted_kernel(const ReduceArgs a) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
-  constexpr int ES = 16 / VE;
   constexpr int B = 8;                                           // ranks whose loads are in flight together
+  constexpr int kWaveOut = LINES ? 64 : 63;                      // output vectors per wave
   const int c = blockIdx.y;
   const int p = a.p;
   const int64_t off = c * a.q + (c < a.r ? c : a.r);
   const int64_t cnt = a.q + (c < a.r ? 1 : 0);
   const int rot = (c + 1) % p;
   const int shift = static_cast<int>(off % VE);
-  const int64_t nvec = (cnt + shift) / VE >= 1 ? (cnt + shift) / VE - 1 : 0;
+  const int64_t nvec = (cnt + shift) / VE >= 1 ? (cnt + shift) / VE - 1 : 0;   // output vectors
+  // input vector v0 holds element off; the waves start at `base`, d vectors
+  // before it (the line start at or before it, or v0 itself)
+  const int64_t v0 = off / VE;
+  int64_t base = v0;
+  if (LINES && a.src_align > 16) {
+    base -= ((a.src_phase + v0 * 16) % a.src_align) / 16;
+    if (base < 0) base = 0;
+  }
+  const int64_t d = v0 - base;
   const int lane = threadIdx.x & 63;
-  const int64_t u = (static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6)) * kShiftWaveOut + lane;
-  const bool load = u <= nvec;                                   // vector nvec is only a neighbour
-  const int64_t boff = (off - shift + u * VE) * ES;
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6)) * kWaveOut + lane;
+  const int64_t last = d + nvec;                                 // input vector last is only a neighbour
+  const bool own = t >= d && t <= last;
+  const int64_t boff = (base + t) * 16;
   float acc[VE];
+  [[maybe_unused]] float acc2[VE];
+  [[maybe_unused]] const bool extra = LINES && lane == 63 && t + 1 >= d && t + 1 <= last;
   for (int k0 = 0; k0 < p; k0 += B) {
     u32x4 raw[B];
+    [[maybe_unused]] u32x4 raw2[B];
 #pragma unroll
     for (int b = 0; b < B; ++b)
-      if (k0 + b < p) raw[b] = load ? ld16(a.leaf[(rot + k0 + b) % p], boff) : u32x4{0, 0, 0, 0};
+      if (k0 + b < p) {
+        const void* src = a.leaf[(rot + k0 + b) % p];
+        raw[b] = own ? ld16(src, boff) : u32x4{0, 0, 0, 0};
+        if constexpr (LINES) raw2[b] = extra ? ld16(src, boff + 16) : u32x4{0, 0, 0, 0};
+      }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       if (k0 + b < p) {
         float v[VE];
         S::widen(raw[b], v);
-        if (k0 + b == 0) {
 #pragma unroll
-          for (int i = 0; i < VE; ++i) acc[i] = v[i];
-        } else {
+        for (int i = 0; i < VE; ++i) acc[i] = k0 + b == 0 ? v[i] : acc[i] + v[i];
+        if constexpr (LINES) {
+          S::widen(raw2[b], v);
 #pragma unroll
-          for (int i = 0; i < VE; ++i) acc[i] = acc[i] + v[i];
+          for (int i = 0; i < VE; ++i) acc2[i] = k0 + b == 0 ? v[i] : acc2[i] + v[i];
         }
       }
     }
   }
   float nb[VE];
 #pragma unroll
-  for (int i = 0; i < VE; ++i) nb[i] = __shfl_down(acc[i], 1);
-  if (lane < kShiftWaveOut && u < nvec) {
+  for (int i = 0; i < VE; ++i) {
+    nb[i] = __shfl_down(acc[i], 1);
+    if constexpr (LINES) {
+      if (lane == 63) nb[i] = acc2[i];
+    }
+  }
+  const int64_t j = t - d;                                       // output vector of this lane
+  if (lane < kWaveOut && j >= 0 && j < nvec) {
     float o[VE];
 #pragma unroll
     for (int i = 0; i < VE; ++i) {
@@ -513,13 +545,17 @@ __global__ __launch_bounds__(kBlock) void reduce_scatter_shifted_kernel(const Re
         if (shift == k) x = i + k < VE ? acc[i + k] : nb[i + k - VE];
       o[i] = x;
     }
-    st16(a.dst[c], u * 16, S::narrow(o));
+    st16(a.dst[c], j * 16, S::narrow(o));
   }
   if (blockIdx.x == 0) {
     const int64_t tail = cnt - nvec * VE;                        // < 2 * VE
     if (threadIdx.x < tail) reduce_one<D, VCOLL_RING, 0, true>(a, c, p, rot, off + nvec * VE + threadIdx.x, off);
   }
 }
+
+// Waves (of the line-aligned shape) from which the unaligned reduce-scatter
+// takes it: about four generations of 8 waves per SIMD on 256 compute units.
+constexpr int64_t kShiftLinesMinWaves = 32768;
 
 // ----------------------------------------------------------------------------
 // small chunks with the run-time order program (p not compiled in): a
@@ -645,10 +681,20 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
       bool aligned = true;
       for (int c = 0; c < chunks && aligned; ++c) aligned = (c * a.q + (c < a.r ? c : a.r)) % VE == 0;
       if (a.vec && !aligned) {
-        const int64_t per_group = static_cast<int64_t>(kBlock / 64) * kShiftWaveOut;
-        const int64_t out_vecs = (max_chunk + VE - 1) / VE;
-        const dim3 sg(static_cast<unsigned>((out_vecs + per_group - 1) / per_group), chunks);
-        return launch(reduce_scatter_shifted_kernel<D>, sg, args, stream);
+        // waves cover d + nvec input vectors per chunk: d < 8 (the line start
+        // before the chunk, line-aligned shape only), nvec < the chunk's vectors
+        const int64_t in_vecs = (max_chunk + VE - 1) / VE + 8;
+        const int64_t waves = (in_vecs + 63) / 64 * chunks;
+        if constexpr (D == VCOLL_F32) {
+          if (waves >= kShiftLinesMinWaves) {
+            const int64_t per_group = static_cast<int64_t>(kBlock / 64) * 64;
+            const dim3 sg(static_cast<unsigned>((in_vecs + per_group - 1) / per_group), chunks);
+            return launch(reduce_scatter_shifted_kernel<D, true>, sg, args, stream);
+          }
+        }
+        const int64_t per_group = static_cast<int64_t>(kBlock / 64) * 63;
+        const dim3 sg(static_cast<unsigned>((in_vecs + per_group - 1) / per_group), chunks);
+        return launch(reduce_scatter_shifted_kernel<D, false>, sg, args, stream);
       }
     }
     return launch(reduce_kernel<D, ALGO, P, V, RS, false, BS>, grid, BS, args, stream);

@@ -75,12 +75,13 @@ bool all_aligned(int p, const void* const* ptrs) {
   return true;
 }
 
-// The address of every send and receive buffer mod `m` (a power of two), or
-// -1 when they differ.
+// The address of every send (and, when given, receive) buffer mod `m` (a
+// power of two), or -1 when they differ.
 int32_t common_phase(int p, const void* const* send, void* const* recv, uintptr_t m) {
   const uintptr_t ph = reinterpret_cast<uintptr_t>(send[0]) & (m - 1);
   for (int r = 0; r < p; ++r)
-    if ((reinterpret_cast<uintptr_t>(send[r]) & (m - 1)) != ph || (reinterpret_cast<uintptr_t>(recv[r]) & (m - 1)) != ph)
+    if ((reinterpret_cast<uintptr_t>(send[r]) & (m - 1)) != ph ||
+        (recv && (reinterpret_cast<uintptr_t>(recv[r]) & (m - 1)) != ph))
       return -1;
   return static_cast<int32_t>(ph);
 }
@@ -149,6 +150,9 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
   const int32_t ph256 = common_phase(p, send, recv, 256), ph128 = common_phase(p, send, recv, 128);
   a.align = ph256 >= 0 ? 256 : 16;
   a.phase = ph256 >= 0 ? ph256 : 0;
+  const int32_t src128 = common_phase(p, send, nullptr, 128);
+  a.src_align = src128 >= 0 ? 128 : 16;
+  a.src_phase = src128 >= 0 ? src128 : 0;
   const int32_t burst_align = ph128 >= 0 ? 128 : 16, burst_phase = ph128 >= 0 ? ph128 : 0;
   int64_t tv = 0;
   const int tiles = (!scatter && algo == VCOLL_RING && a.vec)

@@ -306,6 +306,29 @@ def test_reduce_scatter_with_unaligned_chunk_starts(vc, p, dtype):
             assert_bits_equal(download(got[c], dtype), bits(want[c], dtype), f"RS ring p={p} n={n} chunk {c}")
 
 
+@pytest.mark.parametrize("pad", [20, 4], ids=["common-line-phase", "phases-differ"])
+def test_reduce_scatter_unaligned_chunk_starts_line_aligned_waves(vc, pad):
+    """The same at a size whose grid spans many workgroup generations, where
+    f32 takes the wave shape that starts every wave on a 128-byte line of the
+    inputs (pad 20: rows a whole number of lines apart, so every row has the
+    same address mod 128) or, when the rows' phases differ (pad 4: rows 64
+    bytes apart mod 128), on 16-byte bounds."""
+    import torch
+    p, n = 24, 16_777_216 + 12                       # 64 MiB per rank, chunks of 699,051 or 699,050
+    x = rand_inputs(p, n, "f32", seed=611 + pad)
+    want, _ = oracle.reduce_scatter(x, "ring", "f32")
+    offs = oracle.chunk_bounds(n, p)
+    assert {o % 4 for o in offs[:-1]} - {0}, "no unaligned chunk start"
+    big = torch.zeros((p, n + pad), dtype=torch.float32, device="cuda")
+    big[:, :n].copy_(torch.from_numpy(np.stack(x)))
+    send = [big[r, :n] for r in range(p)]
+    say(f"vcoll_reduce_scatter ring p={p} n={n} row pad {pad} (line-aligned waves)")
+    got = vc.vcoll_reduce_scatter("ring", send)
+    sync()
+    for c in range(p):
+        assert_bits_equal(download(got[c], "f32"), bits(want[c], "f32"), f"RS ring p={p} pad {pad} chunk {c}")
+
+
 def test_non_power_of_two_halving_and_doubling_are_refused(vc):
     import torch
     t = torch.zeros(3, 96, device="cuda")
