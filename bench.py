@@ -1007,7 +1007,7 @@ TRAFFIC_GROUPS = {
         ("tree all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
          2 * 72 * 256 * 2 ** 20),
         ("ring reduce-scatter, p=72 x 64 MiB f32 (unaligned chunk starts)",
-         "reduce_scatter_shifted_kernel<0>", 73 * 64 * 2 ** 20),
+         "reduce_scatter_shifted_kernel<0, true>", 73 * 64 * 2 ** 20),
         ("ring all-reduce, p=16 x 16 MiB f32", "burst_ring_kernel<0, 25>", 2 * 16 * 16 * 2 ** 20),
         ("ring all-reduce, p=16 x 64 MiB f32", "reduce_kernel<0, 0, 16, 1, false, true, 64>", 2 * 16 * 64 * 2 ** 20),
         ("ring all-reduce, p=8 x 1 GiB f32", "reduce_kernel<0, 0, 8, 2, false, true, 256>", 2 * 8 * 2 ** 30),

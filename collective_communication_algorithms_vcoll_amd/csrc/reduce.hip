@@ -463,9 +463,9 @@ __global__ __launch_bounds__(BS) void reduce_kernel(const ReduceArgs a) {
 // The chunk's last output vectors, whose neighbour would reach past the
 // chunk, and its ragged end take the element path. Measured on MI355X with
 // f32: p = 72 x 64 MiB per rank ran 855 us with 63-output waves (whose loads
-// straddle lines: 1.09x the algorithmic bytes read) and 795 us with
-// line-aligned ones (6.17 TB/s, the aligned p = 64 case's rate), p = 24 x
-// 64 MiB 294 -> 275 us; but the extra registers of the line-aligned shape
+// straddle lines: 1.09x the algorithmic bytes read) and 783 us with
+// line-aligned ones (6.25 TB/s, above the aligned p = 64 case's 6.17), p =
+// 24 x 64 MiB 294 -> 269 us; but the extra registers of the line-aligned shape
 // (84 instead of 44, 5 waves per SIMD instead of 8) cost 2-4 % on grids of
 // one or two workgroup generations (p = 72 at 4 and 16 MiB) and 5 % for
 // bf16, so the host takes it for f32 grids of many generations only.
@@ -509,7 +509,9 @@ __global__ __launch_bounds__(kBlock) void reduce_scatter_shifted_kernel(const Re
       if (k0 + b < p) {
         const void* src = a.leaf[(rot + k0 + b) % p];
         raw[b] = own ? ld16(src, boff) : u32x4{0, 0, 0, 0};
-        if constexpr (LINES) raw2[b] = extra ? ld16(src, boff + 16) : u32x4{0, 0, 0, 0};
+        // a cached load: its line is the next wave's first (1.3 % faster than streamed)
+        if constexpr (LINES)
+          raw2[b] = extra ? *reinterpret_cast<const u32x4*>(static_cast<const char*>(src) + boff + 16) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
