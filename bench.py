@@ -553,7 +553,7 @@ def cfg5(vc, torch, cpu_leg: bool) -> dict:
     return res
 
 
-EXTRA_SECTIONS = ("ceilings", "cfg1", "bucket", "stepwise", "decode_prefill", "graphs", "cfg3", "cfg4",
+EXTRA_SECTIONS = ("ceilings", "cfg1", "bucket", "stepwise", "decode_prefill", "graphs", "layouts", "cfg3", "cfg4",
                   "moe_variants", "cfg5", "host")
 
 
@@ -581,6 +581,8 @@ def extras(vc, torch, h, args):
         decode_prefill_extras(vc, torch, ex, steps, warm)
     if "graphs" in only:
         graph_extras(vc, torch, ex)
+    if "layouts" in only:
+        ex["layouts"] = layout_extras(vc, torch, steps, warm)
     if "cfg3" in only:
         ex["cfg3"] = cfg3(vc, torch, scrub, cpu_leg)
     if "cfg4" in only:
@@ -711,6 +713,37 @@ def decode_prefill_extras(vc, torch, ex, steps, warm):
             ex[f"p8_{label}_{algo}"] = roof(f"reduce_kernel<f32, {algo}, p=8>", 2 * 8 * nbytes, mean_ms)
         del t, ts, os_
     torch.cuda.empty_cache()
+
+
+def layout_extras(vc, torch, steps, warm) -> dict:
+    """The ring all-reduce at p = 8 and p = 72, 16 MiB per rank, in four rank
+    buffer layouts: rows of one [p, n] tensor a whole number of cache lines
+    apart; separately allocated rows whose length is not a multiple of
+    p * 4 elements (ragged chunks, common address phase); rows of one
+    [p, n] tensor 16 bytes off a line apart (address phases differ mod 128);
+    and rows of odd length (not 16-byte aligned: the element path)."""
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(9)
+    for p in (8, 72):
+        n0 = 16 * 2 ** 20 // 4
+        for label, n, separate in (("lines_apart", n0, False), ("ragged_chunks", n0 + 4, True),
+                                   ("phases_differ", n0 + 4, False), ("unaligned_rows", n0 + 1, False)):
+            sets = []
+            for _ in range(2):
+                if separate:
+                    x = [torch.randn(n, device="cuda", generator=g) for _ in range(p)]
+                    y = [torch.empty(n, device="cuda") for _ in range(p)]
+                else:
+                    x = torch.randn((p, n), device="cuda", generator=g)
+                    y = torch.empty_like(x)
+                sets.append((x, y))
+            calls = [vc.prepare_allreduce("ring", x, y) for x, y in sets]
+            _, ms = time_launches(calls, max(10, steps // 2), warm)
+            kernel = "burst_ring_kernel" if label in ("lines_apart", "ragged_chunks", "phases_differ") else "reduce_kernel"
+            out[f"p{p}_{label}"] = roof(f"{kernel} (ring, n = {n:,})", 2 * p * n * 4, ms)
+            del sets, calls
+            torch.cuda.empty_cache()
+    return out
 
 
 def graph_extras(vc, torch, ex):

@@ -96,6 +96,7 @@ __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
 // bases, so callers keep the base uniform. Cache-policy bits of gfx950
 // buffer instructions: sc0 = 1, nt = 2, sc1 = 16.
 constexpr int kRawBufferFormat = 0x00020000;    // dword 3 of a raw (untyped) buffer resource
+constexpr int kPolicyCached = 0;                // default: through L2, which merges partial lines
 constexpr int kPolicyNT = 2;                    // non-temporal
 constexpr int kPolicyThrough = 1 | 2 | 16;      // sc0 | nt | sc1: streamed past every cache level
 

@@ -763,9 +763,12 @@ hipError_t launch_reduce_dtype(const ReduceArgs& a, vcoll_algo algo, bool scatte
 // p = 72 x 16 MiB float32, whose chunk starts are only 16-byte aligned:
 // tiles on 16-byte boundaries ran at 4.4 TB/s, on cache lines with the end
 // elements first at 5.7 TB/s, and last at 5.9 TB/s. Buffers whose addresses
-// differ mod 128 cannot all have their tiles on whole lines; there the
-// kernel runs at about 4.8 TB/s (p = 8 x 6,553,604 float32 in one [p, n]
-// tensor).
+// differ mod 128 cannot all have their tiles on whole lines; there two
+// waves write parts of one line, and the stores go through L2 (default
+// policy), which merges those parts: against streaming stores, p = 8 x 16
+// MiB with rows 16 bytes off a line apart went from 54.3 to 47.2 us and
+// p = 72 from 524 to 474 us, while aligned layouts and the DDP bucket
+// stayed within 1 %. (Cached loads lost 5 %.)
 
 constexpr int kBurstBlock = 256;                 // one wave per SIMD
 constexpr int kBurstVecF32 = 25;                 // float32: 100 sums + 25 vectors in flight per thread
@@ -876,7 +879,8 @@ __global__ __launch_bounds__(kBurstBlock) void burst_ring_kernel(const BurstArgs
     const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.dst[d], off, bytes);
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out[j]), r, vo, j * kBurstBlock * 16, kPolicyNT);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out[j]), r, vo, j * kBurstBlock * 16,
+                                             kPolicyCached);
   }
   if (blockIdx.x == 0) edges();
 }
