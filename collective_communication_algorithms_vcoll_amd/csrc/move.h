@@ -18,6 +18,8 @@ struct GatherArgs {
   int64_t m;                  // elements per rank
   int32_t p;
   int32_t vec;                // pointers aligned and m * esize a multiple of 16
+  int32_t lines;              // every output on a 128-byte line and m * esize a multiple of 128
+  int32_t pad;
 };
 
 // Broadcast: the root's n elements copied to q receive buffers. Grid: x = tiles.
@@ -27,6 +29,8 @@ struct BcastArgs {
   int64_t n;
   int32_t q;
   int32_t vec;                // every pointer 16-byte aligned
+  int32_t lines;              // every receive buffer on a 128-byte line
+  int32_t pad;
 };
 
 // One (i -> j) block of an all-to-all.

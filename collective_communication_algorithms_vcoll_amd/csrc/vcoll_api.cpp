@@ -277,6 +277,8 @@ vcoll_status vcoll_all_gather(vcoll_algo algo, int p, int64_t m, vcoll_dtype dty
   a.p = p;
   a.vec = all_aligned(p, send) && all_aligned(p, const_cast<const void* const*>(recv)) &&
           (m * elem_bytes(dtype)) % 16 == 0;
+  a.lines = common_phase(p, const_cast<const void* const*>(recv), nullptr, 128) == 0 &&
+            (m * elem_bytes(dtype)) % 128 == 0;
   return from_hip(launch_all_gather(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -401,11 +403,13 @@ vcoll_status vcoll_broadcast(int p, int64_t n, vcoll_dtype dtype, int root, cons
   a.src = send;
   a.n = n;
   a.vec = aligned16(send);
+  a.lines = 1;
   for (int r = 0; r < p; ++r) {
     if (r == root && (recv[r] == nullptr || recv[r] == send)) continue;
     if (!recv[r]) return VCOLL_ERR_INVALID_ARG;
     a.dst[a.q++] = recv[r];
     a.vec = a.vec && aligned16(recv[r]);
+    a.lines = a.lines && (reinterpret_cast<uintptr_t>(recv[r]) & 127u) == 0;
   }
   return from_hip(launch_broadcast(a, dtype, static_cast<hipStream_t>(stream)));
 }
