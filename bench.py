@@ -54,7 +54,7 @@ METRIC = "all-reduce effective HBM GB/s (p=8, 25 MB/rank fp32) + % of HBM roofli
 PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
 # the headline kernel in libvcoll.so: the two-phase ring all-reduce, float32, 25 vectors per thread
-HEADLINE_SYMBOL = "burst_ring_kernelILi0ELi25EE"
+HEADLINE_SYMBOL = "burst_ring_kernelILi0ELi25ELi0EE"
 
 
 def _elf_sections(data: bytes) -> list:
@@ -889,7 +889,7 @@ def _csv_rows(root: str, suffix: str):
     return rows
 
 
-HEADLINE_KERNEL = "burst_ring_kernel<0, 25>"
+HEADLINE_KERNEL = "burst_ring_kernel<0, 25, 0>"
 COPY_KERNEL = "copy_kernel<2, 64"
 
 
@@ -987,7 +987,8 @@ def summarize_stats(trace_dir: str, name: str, title: str, command: str) -> int:
     lines = [f"# rocprofv3 kernel statistics: {title}", "", f"Command: `{command}`", "",
              "Template arguments of reduce_kernel: dtype (0 f32, 1 bf16), algorithm (0 ring, 1 recursive doubling, "
              "2 Rabenseifner, 3 tree), p (0: read at run time), vectors per thread, reduce-scatter, large-grid "
-             "variant, workgroup size; of burst_ring_kernel: dtype, vectors per thread.", "",
+             "variant, workgroup size; of burst_ring_kernel: dtype, vectors per thread, store cache policy "
+             "(0 through L2, 2 streamed).", "",
              "| kernel | calls | average us | min us | max us | p10 us | median us | p90 us |",
              "|---|---|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
@@ -1014,7 +1015,7 @@ def summarize_stats(trace_dir: str, name: str, title: str, command: str) -> int:
 # marker launch separates consecutive workloads in the counter records.
 TRAFFIC_GROUPS = {
     "hot": [
-        ("two-phase ring all-reduce, p=8 x 25 MiB f32 (headline)", "burst_ring_kernel<0, 25>", 419_430_400),
+        ("two-phase ring all-reduce, p=8 x 25 MiB f32 (headline)", "burst_ring_kernel<0, 25, 0>", 419_430_400),
         ("hierarchical 2x4 all-reduce, p=8 x 25 MiB f32", "hier_kernel<0, 2, 4, true>", 419_430_400),
         ("tree reduce to one root, p=8 x 25 MiB f32", "reduce_kernel<0, 3, 8, 2, true, false, 256>", 235_929_600),
         ("broadcast of 25 MiB f32 to 8 buffers", "broadcast_kernel<4, 4, 64, true>", 235_929_600),
@@ -1031,7 +1032,7 @@ TRAFFIC_GROUPS = {
     ],
     "sweep": [
         ("copy, 200 MiB read + 200 MiB written (counter scale)", "copy_kernel<2, 64", 419_430_400),
-        ("ring all-reduce, p=72 x 16 MiB f32 (two-phase, ragged chunks)", "burst_ring_kernel<0, 25>",
+        ("ring all-reduce, p=72 x 16 MiB f32 (two-phase, ragged chunks)", "burst_ring_kernel<0, 25, 0>",
          2 * 72 * 16 * 2 ** 20),
         ("tree all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
          2 * 72 * 16 * 2 ** 20),
@@ -1041,7 +1042,7 @@ TRAFFIC_GROUPS = {
          2 * 72 * 256 * 2 ** 20),
         ("ring reduce-scatter, p=72 x 64 MiB f32 (unaligned chunk starts)",
          "reduce_scatter_shifted_kernel<0, true>", 73 * 64 * 2 ** 20),
-        ("ring all-reduce, p=16 x 16 MiB f32", "burst_ring_kernel<0, 25>", 2 * 16 * 16 * 2 ** 20),
+        ("ring all-reduce, p=16 x 16 MiB f32", "burst_ring_kernel<0, 25, 0>", 2 * 16 * 16 * 2 ** 20),
         ("ring all-reduce, p=16 x 64 MiB f32", "reduce_kernel<0, 0, 16, 1, false, true, 64>", 2 * 16 * 64 * 2 ** 20),
         ("ring all-reduce, p=8 x 1 GiB f32", "reduce_kernel<0, 0, 8, 2, false, true, 256>", 2 * 8 * 2 ** 30),
     ],

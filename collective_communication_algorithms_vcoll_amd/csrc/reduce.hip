@@ -767,8 +767,9 @@ hipError_t launch_reduce_dtype(const ReduceArgs& a, vcoll_algo algo, bool scatte
 // waves write parts of one line, and the stores go through L2 (default
 // policy), which merges those parts: against streaming stores, p = 8 x 16
 // MiB with rows 16 bytes off a line apart went from 54.3 to 47.2 us and
-// p = 72 from 524 to 474 us, while aligned layouts and the DDP bucket
-// stayed within 1 %. (Cached loads lost 5 %.)
+// p = 72 from 524 to 474 us; aligned layouts gained 1-4 % with the buffers
+// cycled out of the Infinity Cache (p = 4 to 16 at 16 MiB, the DDP bucket),
+// except p = 2 (below). (Cached loads lost 5 %.)
 
 constexpr int kBurstBlock = 256;                 // one wave per SIMD
 constexpr int kBurstVecF32 = 25;                 // float32: 100 sums + 25 vectors in flight per thread
@@ -802,7 +803,7 @@ __device__ __forceinline__ void burst_one(const BurstArgs& a, int first_rank, in
   for (int r = 0; r < p; ++r) static_cast<E*>(a.dst[r])[e] = out;
 }
 
-template <int D, int K>
+template <int D, int K, int SPOL>
 __global__ __launch_bounds__(kBurstBlock) void burst_ring_kernel(const BurstArgs a) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
@@ -879,8 +880,7 @@ __global__ __launch_bounds__(kBurstBlock) void burst_ring_kernel(const BurstArgs
     const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.dst[d], off, bytes);
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out[j]), r, vo, j * kBurstBlock * 16,
-                                             kPolicyCached);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out[j]), r, vo, j * kBurstBlock * 16, SPOL);
   }
   if (blockIdx.x == 0) edges();
 }
@@ -893,8 +893,16 @@ int64_t burst_tile_max(vcoll_dtype dtype) {
 
 hipError_t launch_burst_ring(const BurstArgs& a, vcoll_dtype dtype, int tiles, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.p));
-  if (dtype == VCOLL_F32) return launch(burst_ring_kernel<VCOLL_F32, kBurstVecF32>, grid, kBurstBlock, a, stream);
-  return launch(burst_ring_kernel<VCOLL_BF16, kBurstVecBf16>, grid, kBurstBlock, a, stream);
+  // the write phase stores through L2 (see above), except for p <= 2, where
+  // streaming stores measured 3.5 % faster (p = 2 x 16 MiB, buffers cycled
+  // out of the Infinity Cache; p = 4 to 16 and the DDP bucket gained 1-4 %
+  // from cached stores)
+  const bool cached = a.p > 2;
+  if (dtype == VCOLL_F32)
+    return cached ? launch(burst_ring_kernel<VCOLL_F32, kBurstVecF32, kPolicyCached>, grid, kBurstBlock, a, stream)
+                  : launch(burst_ring_kernel<VCOLL_F32, kBurstVecF32, kPolicyNT>, grid, kBurstBlock, a, stream);
+  return cached ? launch(burst_ring_kernel<VCOLL_BF16, kBurstVecBf16, kPolicyCached>, grid, kBurstBlock, a, stream)
+                : launch(burst_ring_kernel<VCOLL_BF16, kBurstVecBf16, kPolicyNT>, grid, kBurstBlock, a, stream);
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype dtype, vcoll_algo algo, bool scatter,
