@@ -428,6 +428,8 @@ vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, 
   a.r = 0;
   a.p = p;
   a.vec = all_aligned(p, send) && aligned16(recv);
+  a.align = 16;                     // one chunk starting at element 0: no tile realignment
+  a.src_align = 16;
   // the tree runs on ranks relative to the root: leaf v is rank (v + root) mod p
   const OrderProgram prog = order_program(VCOLL_BINARY_TREE, p);
   for (int k = 0; k < p; ++k) a.leaf[k] = send[(prog.rank[k] + root) % p];   // leaves in program order

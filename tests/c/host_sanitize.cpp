@@ -32,17 +32,29 @@ namespace vcoll {
 hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype, vcoll_algo, bool, int64_t max_chunk, int chunks,
                          hipStream_t) {
   if (a.p < 1 || a.p > kMaxRanks || chunks < 1 || max_chunk < 0) std::abort();
+  // the input phase the unaligned reduce-scatter aligns its waves to: 128
+  // only when every input shares it
+  if (!(a.src_align == 16 || a.src_align == 128) || a.src_phase < 0 || a.src_phase >= a.src_align ||
+      a.src_phase % 16 != 0)
+    std::abort();
   ++g_launches;
   return hipSuccess;
 }
 hipError_t launch_hierarchical(const HierArgs&, vcoll_dtype, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype, hipStream_t) {
+hipError_t launch_all_gather(const GatherArgs& a, vcoll_dtype dtype, hipStream_t) {
   if (a.p < 1 || a.m < 0) std::abort();
+  // whole-line tiles: every output on a 128-byte line and blocks a whole number of lines
+  bool lines = a.m * (dtype == VCOLL_F32 ? 4 : 2) % 128 == 0;
+  for (int r = 0; r < a.p; ++r) lines = lines && reinterpret_cast<uintptr_t>(a.ptr.dst[r]) % 128 == 0;
+  if ((a.lines != 0) != lines) std::abort();
   ++g_launches;
   return hipSuccess;
 }
 hipError_t launch_broadcast(const BcastArgs& a, vcoll_dtype, hipStream_t) {
   if (a.q < 0 || a.q > kMaxRanks) std::abort();
+  bool lines = true;
+  for (int r = 0; r < a.q; ++r) lines = lines && reinterpret_cast<uintptr_t>(a.dst[r]) % 128 == 0;
+  if ((a.lines != 0) != lines) std::abort();
   ++g_launches;
   return hipSuccess;
 }
