@@ -553,8 +553,8 @@ def cfg5(vc, torch, cpu_leg: bool) -> dict:
     return res
 
 
-EXTRA_SECTIONS = ("ceilings", "cfg1", "bucket", "stepwise", "decode_prefill", "graphs", "layouts", "cfg3", "cfg4",
-                  "moe_variants", "cfg5", "host")
+EXTRA_SECTIONS = ("ceilings", "cfg1", "bucket", "stepwise", "decode_prefill", "graphs", "cfg3", "cfg4",
+                  "moe_variants", "cfg5", "layouts", "host")
 
 
 def extras(vc, torch, h, args):
@@ -581,8 +581,6 @@ def extras(vc, torch, h, args):
         decode_prefill_extras(vc, torch, ex, steps, warm)
     if "graphs" in only:
         graph_extras(vc, torch, ex)
-    if "layouts" in only:
-        ex["layouts"] = layout_extras(vc, torch, steps, warm)
     if "cfg3" in only:
         ex["cfg3"] = cfg3(vc, torch, scrub, cpu_leg)
     if "cfg4" in only:
@@ -591,6 +589,8 @@ def extras(vc, torch, h, args):
         ex["moe_variants"] = moe_variants(vc, torch)
     if "cfg5" in only:
         ex["cfg5"] = cfg5(vc, torch, cpu_leg)
+    if "layouts" in only:                 # last: its many allocations must not shift the configurations' buffers
+        ex["layouts"] = layout_extras(vc, torch, steps, warm)
     if "host" in only:
         ex["host_schedule_and_ledger"] = host_rows(vc)
     return ex
