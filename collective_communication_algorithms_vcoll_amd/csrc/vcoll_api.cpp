@@ -62,6 +62,26 @@ bool fits(int64_t rows, int64_t row_bytes) {
   return row_bytes <= 0 || rows <= (int64_t(1) << 56) / row_bytes;
 }
 
+// Row counts of an all-to-all: every entry >= 0 and each rank's sent and
+// received totals within INT32_MAX rows (row indices are int32) and within
+// the byte bound of fits(); the per-rank totals go to `sent` and `got`.
+bool valid_splits(int p, const int64_t* splits, int64_t row_bytes, std::vector<int64_t>& sent,
+                  std::vector<int64_t>& got) {
+  sent.assign(p, 0);
+  got.assign(p, 0);
+  for (int i = 0; i < p; ++i)
+    for (int j = 0; j < p; ++j) {
+      const int64_t s = splits[i * p + j];
+      if (s < 0 || s > INT32_MAX) return false;
+      sent[i] += s;
+      got[j] += s;
+      if (sent[i] > INT32_MAX || got[j] > INT32_MAX) return false;
+    }
+  for (int i = 0; i < p; ++i)
+    if (!fits(sent[i], row_bytes) || !fits(got[i], row_bytes)) return false;
+  return true;
+}
+
 bool all_set(int p, const void* const* ptrs) {
   if (!ptrs) return false;
   for (int r = 0; r < p; ++r)
@@ -289,19 +309,11 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
                               void* stream) {
   if (!valid_p(p) || !valid_count(row_elems) || !valid_a2a_dtype(dtype) || !splits) return VCOLL_ERR_INVALID_ARG;
   const int64_t rb = row_elems * elem_bytes(dtype);
-  std::vector<int64_t> sent(p, 0), got(p, 0);
-  for (int i = 0; i < p; ++i)
-    for (int j = 0; j < p; ++j) {
-      const int64_t s = splits[i * p + j];
-      if (s < 0 || s > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
-      sent[i] += s;
-      got[j] += s;
-      if (sent[i] > INT32_MAX || got[j] > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
-    }
+  std::vector<int64_t> sent, got;
+  if (!valid_splits(p, splits, rb, sent, got)) return VCOLL_ERR_INVALID_ARG;
   auto gathers = [&](int i) { return src_rows && src_rows[i]; };
   auto scatters = [&](int j) { return dst_rows && dst_rows[j]; };
   for (int i = 0; i < p; ++i) {
-    if (!fits(sent[i], rb) || !fits(got[i], rb)) return VCOLL_ERR_INVALID_ARG;
     if (sent[i] > 0 && rb > 0 && (!send || !send[i])) return VCOLL_ERR_INVALID_ARG;
     if (got[i] > 0 && rb > 0 && (!recv || !recv[i])) return VCOLL_ERR_INVALID_ARG;
     if (gathers(i) && (!src_table_rows || src_table_rows[i] < 0 || src_table_rows[i] > INT32_MAX ||
@@ -366,9 +378,10 @@ vcoll_status vcoll_ledger(vcoll_op op, vcoll_algo algo, int p, int64_t n, vcoll_
   if (op < VCOLL_OP_ALLREDUCE || op > VCOLL_OP_ALL_TO_ALL) return VCOLL_ERR_INVALID_ARG;
   if (!(op == VCOLL_OP_ALL_TO_ALL ? valid_a2a_dtype(dtype) : valid_dtype(dtype))) return VCOLL_ERR_INVALID_ARG;
   if (op == VCOLL_OP_ALL_TO_ALL) {
-    if (!splits || !valid_count(row_elems)) return VCOLL_ERR_INVALID_ARG;
-    for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
-      if (splits[k] < 0) return VCOLL_ERR_INVALID_ARG;
+    std::vector<int64_t> sent, got;
+    if (!splits || !valid_count(row_elems) ||
+        !valid_splits(p, splits, row_elems * elem_bytes(dtype), sent, got))
+      return VCOLL_ERR_INVALID_ARG;
   } else {
     if (!valid_count(n) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
     const vcoll_status combo = check_combination(op, algo, p);
@@ -660,8 +673,8 @@ vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* spl
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !splits || (tokens > 0 && (!dst_rows || !slots)))
     return VCOLL_ERR_INVALID_ARG;
   if (!pairs_fit(tokens, topk)) return VCOLL_ERR_INVALID_ARG;
-  for (int64_t k = 0; k < static_cast<int64_t>(p) * p; ++k)
-    if (splits[k] < 0) return VCOLL_ERR_INVALID_ARG;
+  std::vector<int64_t> sent, got;                                // receive rows are int32 in the slots
+  if (!valid_splits(p, splits, 0, sent, got)) return VCOLL_ERR_INVALID_ARG;
   return moe_slots(p, tokens, topk, splits, dst_rows, slots);
 }
 
@@ -670,20 +683,10 @@ vcoll_status vcoll_moe_dedup_slots(int p, int64_t tokens, int topk, const int64_
   if (!valid_p(p) || !valid_count(tokens) || topk < 1 || !splits_unique) return VCOLL_ERR_INVALID_ARG;
   if (!pairs_fit(tokens, topk)) return VCOLL_ERR_INVALID_ARG;
   if (tokens > 0 && (!src_unique || !slots)) return VCOLL_ERR_INVALID_ARG;
-  for (int i = 0; i < p; ++i) {
-    int64_t sent = 0;
-    for (int j = 0; j < p; ++j) {
-      const int64_t v = splits_unique[static_cast<size_t>(i) * p + j];
-      if (v < 0) return VCOLL_ERR_INVALID_ARG;
-      sent += v;
-    }
-    if (sent > tokens * topk) return VCOLL_ERR_INVALID_ARG;      // src_unique holds tokens*topk entries per rank
-  }
-  for (int j = 0; j < p; ++j) {                                  // receive rows are int32 in the slots
-    int64_t got = 0;
-    for (int i = 0; i < p; ++i) got += splits_unique[static_cast<size_t>(i) * p + j];
-    if (got > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
-  }
+  std::vector<int64_t> sent, got;                                // receive rows are int32 in the slots
+  if (!valid_splits(p, splits_unique, 0, sent, got)) return VCOLL_ERR_INVALID_ARG;
+  for (int i = 0; i < p; ++i)
+    if (sent[i] > tokens * topk) return VCOLL_ERR_INVALID_ARG;  // src_unique holds tokens*topk entries per rank
   return moe_dedup_slots(p, tokens, topk, splits_unique, src_unique, slots);
 }
 

@@ -247,7 +247,10 @@ vcoll_status vcoll_ledger_rooted(vcoll_op op, vcoll_algo algo, int p, int64_t n,
  * Host only. From splits [p*p] and dst_rows [p][tokens*topk] of
  * vcoll_moe_plan it fills slots [p][tokens*topk][2] int32: for rank i's
  * pair (t, k), the destination rank j and the row of recv[j] that the
- * plain dispatch (vcoll_all_to_all with src_rows) writes it to.
+ * plain dispatch (vcoll_all_to_all with src_rows) writes it to. splits
+ * within the limits of vcoll_all_to_all, at most tokens*topk rows sent per
+ * rank and every dst_rows entry in [0, tokens*topk), else
+ * VCOLL_ERR_INVALID_ARG (slots may then be partly written).
  */
 vcoll_status vcoll_moe_slots(int p, int64_t tokens, int topk, const int64_t* splits, const int32_t* dst_rows,
                              int32_t* slots);
@@ -412,9 +415,10 @@ vcoll_status vcoll_all_gather(vcoll_algo algo, int p, int64_t m, vcoll_dtype dty
  * Variable-split all-to-all ([NCC] 4.1: block j of device i goes to device j,
  * the transpose of the device-by-block matrix; 7.4: MoE dispatch/combine).
  * Rows have row_elems elements. `splits` is a host array [p*p]; splits[i*p+j]
- * >= 0 rows go from rank i to rank j. send[i] holds its blocks j = 0..p-1 in
- * order; recv[j] receives the blocks i = 0..p-1 in order. Rows are moved as
- * raw storage words.
+ * >= 0 rows go from rank i to rank j; the rows each rank sends, and those it
+ * receives, total at most INT32_MAX (else VCOLL_ERR_INVALID_ARG). send[i]
+ * holds its blocks j = 0..p-1 in order; recv[j] receives the blocks
+ * i = 0..p-1 in order. Rows are moved as raw storage words.
  *   src_rows (optional, host array of p device int32 pointers, entries may be
  *   NULL): when src_rows[i] is set, the k-th row rank i sends (block order)
  *   is row src_rows[i][k] of send[i], a table of src_table_rows[i] rows --
@@ -436,7 +440,8 @@ vcoll_status vcoll_all_to_all(int p, int64_t row_elems, vcoll_dtype dtype, const
  * Message ledger ([NCC] code note: a virtual cluster accounts every message;
  * 4.3 per-device bytes). Host only, no device work. Enumerates the messages
  * of `op` run with `algo` on p ranks of n elements (all-gather: m elements
- * per rank; all-to-all: `splits` and `row_elems`, algo ignored, direct
+ * per rank; all-to-all: `splits` and `row_elems` within the limits of
+ * vcoll_all_to_all, algo ignored, direct
  * schedule where step s-1 sends block i -> (i+s) mod p, s = 1..p-1, the
  * diagonal block being local). Each step is synchronous; recursive doubling
  * and Rabenseifner with p not a power of two add a pre-step (2j -> 2j+1) and

@@ -410,6 +410,13 @@ def test_oversized_counts_and_buffers_are_refused():
     P2 = _ptrs(2)
     assert lib.vcoll_all_to_all(2, 1 << 35, 1, sp, P2, P2, None, None, None, None, None) == 1
     assert lib.vcoll_all_to_all(2, big, 2, sp, P2, P2, None, None, None, None, None) == 1
+    # the all-to-all ledger takes the same split limits as the all-to-all:
+    # a block or a rank's total beyond INT32_MAX rows, or beyond 2^56 bytes
+    for bad in ((1 << 62, 0, 0, 1), (2 ** 31 - 1, 1, 0, 1), (1 << 21, 0, 0, 1)):
+        spb = (ctypes.c_int64 * 4)(*bad)
+        assert lib.vcoll_ledger(3, 0, 2, 0, 1, spb, 1 << 35, None, 0, ctypes.byref(n), None, None, None) == 1
+        assert lib.vcoll_all_to_all(2, 1 << 35, 1, spb, P2, P2, None, None, None, None, None) == 1
+    assert lib.vcoll_ledger(3, 0, 2, 0, 1, sp, 1, None, 0, ctypes.byref(n), None, None, None) == 0
     # token-major dispatch: tokens x row bytes above 2^56
     idx = (ctypes.c_void_p * 2)(0x3000, 0x3000)
     rr = (ctypes.c_int64 * 2)(1, 1)
