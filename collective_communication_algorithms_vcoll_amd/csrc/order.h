@@ -123,4 +123,29 @@ constexpr OrderProgram order_program(int algo, int p) {
   return g;
 }
 
+// The tree programs above are binary counters over groups: a group is one
+// leaf, or a folded pair of leaves added to each other first; after group q
+// the counter closes ctz(q + 1) complete subtrees (older partial + newer),
+// and at the end the subtrees still open, one per set bit of the group
+// count, are added from the smallest up. Fills first[q] = the program leaf
+// that starts group q (first[groups] = p) and returns the group count; the
+// ring, a chain, has no groups (returns 0).
+constexpr int order_groups(int algo, int p, int* first) {
+  if (algo == VCOLL_RING) return 0;
+  if (algo == VCOLL_BINARY_TREE) {
+    for (int q = 0; q <= p; ++q) first[q] = q;
+    return p;
+  }
+  const Fold f(p);
+  const int bits = floor_log2(f.p2);
+  int k = 0;
+  for (int q = 0; q < f.p2; ++q) {
+    const int nr = (algo == VCOLL_RABENSEIFNER) ? bitrev_int(q, bits) : q;
+    first[q] = k;
+    k += nr < f.r ? 2 : 1;
+  }
+  first[f.p2] = k;
+  return f.p2;
+}
+
 }  // namespace vcoll

@@ -32,26 +32,27 @@ constexpr bool has_fixed_kernel(int p) { return p == 2 || p == 4 || p == 8 || p 
 // in chunk c's summation order (the host resolves the ring's per-chunk
 // rotation and the trees' leaf order), so a workgroup fetches its p source
 // pointers with one wide scalar load. For any other p, the ring has
-// leaf[r] = send[r] and the kernel rotates it per chunk; the trees have
-// leaf[k] = the k-th leaf of the program (send[rank[k]]), so no leaf costs
-// a lookup of rank[] on the device.
+// leaf[r] = send[r] and the kernel rotates it per chunk; the trees are given
+// by the groups of their program (order_groups): leaf[q] is the buffer of
+// group q's first leaf and leaf[kMaxRanks + q] that of its second (a folded
+// pair) or null, for q < groups, so a kernel finds every buffer by the group
+// index alone.
 struct ReduceArgs {
   const void* leaf[kFixedMax * kFixedMax];
   void* dst[kMaxRanks];
   int64_t q, r;               // chunk c: off = c*q + min(c, r), count = q + (c < r)
   int32_t p;
   int32_t vec;                // every pointer 16-byte aligned: vector path allowed
-  int32_t final_merges;       // order program (used when p is not compiled in)
+  int32_t groups;             // tree programs with p not compiled in: the group count
   int32_t pace;               // space out the p-way store fan-out (large grids)
   int32_t align;              // all-reduce tiles start on this byte boundary (256 when every buffer
                               // has the same address mod 256, else 16)
   int32_t phase;              // that common address mod `align` (0 for align 16)
   int32_t src_align;          // 128 when every input buffer has address phase `src_phase` mod 128
   int32_t src_phase;          // (the unaligned reduce-scatter then loads whole lines), else 16 and 0
-  uint8_t rank[kMaxRanks];
-  uint8_t merges[kMaxRanks];
 };
 static_assert(sizeof(ReduceArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+static_assert(kFixedMax * kFixedMax >= 2 * kMaxRanks, "room for the groups' two leaves");
 
 // grid y = chunks: p for all-reduce and reduce-scatter, 1 for a reduce to
 // one root (q = n, r = 0, dst[0] = the root's buffer, scatter = true).

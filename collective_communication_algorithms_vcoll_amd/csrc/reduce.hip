@@ -84,29 +84,127 @@ __device__ __forceinline__ const void* const* leaf_row(const ReduceArgs& a, int 
 }
 
 // ----------------------------------------------------------------------------
-// order programs read at run time (any p): a shift-register stack keeps every
-// index a compile-time constant, so the stack lives in registers
+// tree orders with p known only at run time: the binary counter of
+// order_groups. Group q closes ctz(q + 1) subtrees, so with q the index of a
+// fully unrolled loop every close adds fixed registers (no stack to shift,
+// no per-leaf merge count to read); the host lays out each group's leaf
+// buffers. Against a shift-register stack driven by the program's merge
+// counts, on MI355X: p = 72 tree all-reduces of 1 MiB per rank 58 -> 41-49
+// us, 4 MiB 130 -> 119-123 us, 64 MiB within 1 %.
 
-constexpr int kRuntimeDepth = 9;   // deepest stack of any program with p <= 128
+constexpr int kLevels = 8;         // open subtrees of a counter over up to 128 groups
 
-template <int N>
-__device__ __forceinline__ void rt_push(float (&st)[kRuntimeDepth][N], const float* v) {
+// Add group Q's value v (destroyed) to the counter.
+template <int Q, int N>
+__device__ __forceinline__ void counter_add(float (&lvl)[kLevels][N], float (&v)[N]) {
+  constexpr int closes = ctz_int(Q + 1);
+  static_assert(closes < kLevels, "at most 128 groups");
 #pragma unroll
-  for (int s = kRuntimeDepth - 1; s > 0; --s)
+  for (int l = 0; l < closes; ++l)
 #pragma unroll
-    for (int i = 0; i < N; ++i) st[s][i] = st[s - 1][i];
+    for (int i = 0; i < N; ++i) v[i] = lvl[l][i] + v[i];
 #pragma unroll
-  for (int i = 0; i < N; ++i) st[0][i] = v[i];
+  for (int i = 0; i < N; ++i) lvl[closes][i] = v[i];
 }
 
+// The sum over all `groups` groups: the open subtrees (one per set bit of
+// the count) from the smallest up, each older one added to the running sum.
 template <int N>
-__device__ __forceinline__ void rt_merge(float (&st)[kRuntimeDepth][N]) {
+__device__ __forceinline__ void counter_total(const float (&lvl)[kLevels][N], int groups, float (&out)[N]) {
+  bool first = true;
 #pragma unroll
-  for (int i = 0; i < N; ++i) st[0][i] = st[1][i] + st[0][i];
+  for (int l = 0; l < kLevels; ++l) {
+    if ((groups >> l) & 1) {
 #pragma unroll
-  for (int s = 1; s < kRuntimeDepth - 1; ++s)
+      for (int i = 0; i < N; ++i) out[i] = first ? lvl[l][i] : lvl[l][i] + out[i];
+      first = false;
+    }
+  }
+}
+
+// Groups of a run-time tree program whose loads a thread keeps in flight
+// together (a folded pair loads two leaves) on the per-thread paths. 8
+// against 4 on MI355X: p = 24 x 256 KiB per rank 9.9 against 11.0 us, p = 72
+// x 1 MiB 41 against 45 us (the latency-bound sizes, where fewer batches
+// mean fewer waits); 4 was 3 % faster for the binomial tree at p = 24 x 16
+// MiB. Build-time override: -DVCOLL_TREE_BATCH=<power of two>.
+#ifndef VCOLL_TREE_BATCH
+#define VCOLL_TREE_BATCH 8
+#endif
+constexpr int kTreeBatch = VCOLL_TREE_BATCH;
+
+// Add group q0 + b of a batch of B groups (B a power of two, q0 a multiple
+// of B) to the counter. Group q0 + b closes ctz(b + 1) subtrees for b < B -
+// 1, a compile-time count, and the batch's last group log2(B) + ctz(q0 / B +
+// 1): its levels past log2(B) are predicated on that count, so every
+// register index stays fixed while the batches run in a loop. (Unrolling
+// all 128 groups instead gives the argument block so many uses that the
+// compiler copies it to scratch memory.)
+template <int B, int b, int N>
+__device__ __forceinline__ void counter_push(float (&lvl)[kLevels][N], float (&v)[N], int q0) {
+  static_assert(B >= 2 && (B & (B - 1)) == 0 && kMaxRanks % B == 0 && b < B, "batches of a power of two");
+  if constexpr (b < B - 1) {
+    counter_add<b>(lvl, v);
+  } else {
+    constexpr int LB = ctz_int(B);
+    // selects, not branches: a conditional store per level is merged by the
+    // compiler into one store through a chosen pointer, which moves the
+    // counter to scratch memory
+    const int extra = __builtin_ctz(static_cast<unsigned>(q0 / B + 1));
 #pragma unroll
-    for (int i = 0; i < N; ++i) st[s][i] = st[s + 1][i];
+    for (int l = 0; l < LB; ++l)
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = lvl[l][i] + v[i];
+#pragma unroll
+    for (int l = LB; l < kLevels - 1; ++l) {
+      const bool close = l - LB < extra;
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = close ? lvl[l][i] + v[i] : v[i];
+    }
+#pragma unroll
+    for (int l = LB; l < kLevels; ++l) {
+      const bool keep = l - LB == extra;
+#pragma unroll
+      for (int i = 0; i < N; ++i) lvl[l][i] = keep ? v[i] : lvl[l][i];
+    }
+  }
+}
+
+// Run a tree program (groups in a.leaf, see ReduceArgs) B groups at a time:
+// issue(s0, s1, pair, b) starts the loads of group q0 + b's first leaf
+// (buffer s0) and, for a folded pair, its second (s1) into slot b of the
+// caller's registers, every load of a batch before the first value is
+// taken; take(b, pair, v) widens slot b into v, the pair's two leaves added.
+// Every buffer is found by the group index alone, so the loads of a batch
+// wait on nothing.
+template <int ALGO, int B, int N, class Issue, class Take>
+__device__ __forceinline__ void run_groups(const ReduceArgs& a, float (&out)[N], const Issue& issue,
+                                           const Take& take) {
+  constexpr bool kPairs = ALGO != VCOLL_BINARY_TREE;             // the binomial tree folds nothing
+  const int groups = a.groups;
+  float lvl[kLevels][N];
+#pragma unroll 1
+  for (int q0 = 0; q0 < groups; q0 += B) {
+    bool pair[B];
+    static_for<0, B>([&](auto bb) {
+      constexpr int b = decltype(bb)::value;
+      const int q = q0 + b;
+      if (q < groups) {
+        const void* s1 = kPairs ? a.leaf[kMaxRanks + q] : nullptr;
+        pair[b] = s1 != nullptr;
+        issue(a.leaf[q], s1, pair[b], bb);
+      }
+    });
+    static_for<0, B>([&](auto bb) {
+      constexpr int b = decltype(bb)::value;
+      if (q0 + b < groups) {
+        float v[N];
+        take(bb, pair[b], v);
+        counter_push<B, b>(lvl, v, q0);
+      }
+    });
+  }
+  counter_total(lvl, groups, out);
 }
 
 // ----------------------------------------------------------------------------
@@ -131,34 +229,36 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int c, int p, in
     });
     result = st[0][0];
   } else {
-    // loads go out kOneBatch ranks at a time, so a long program (p up to
-    // 128) waits for memory p / kOneBatch times rather than p times
+    // loads go out kOneBatch ranks (groups) at a time, so a long program (p
+    // up to 128) waits for memory p / kOneBatch times rather than p times
     constexpr int kOneBatch = 16;
-    float st[kRuntimeDepth][1];
-    result = 0.0f;
-    for (int k0 = 0; k0 < p; k0 += kOneBatch) {
-      E raw[kOneBatch];
+    if constexpr (ALGO == VCOLL_RING) {
+      result = 0.0f;
+      for (int k0 = 0; k0 < p; k0 += kOneBatch) {
+        E raw[kOneBatch];
 #pragma unroll
-      for (int b = 0; b < kOneBatch; ++b)
-        if (k0 + b < p) {
-          const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : k0 + b;
-          raw[b] = static_cast<const E*>(a.leaf[rank])[e];
-        }
+        for (int b = 0; b < kOneBatch; ++b)
+          if (k0 + b < p) raw[b] = static_cast<const E*>(a.leaf[(rot + k0 + b) % p])[e];
 #pragma unroll
-      for (int b = 0; b < kOneBatch; ++b)
-        if (k0 + b < p) {
-          const float v = S::widen1(raw[b]);
-          if constexpr (ALGO == VCOLL_RING) {
-            result = k0 + b == 0 ? v : result + v;
-          } else {
-            rt_push<1>(st, &v);
-            for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<1>(st);
-          }
-        }
-    }
-    if constexpr (ALGO != VCOLL_RING) {
-      for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
-      result = st[0][0];
+        for (int b = 0; b < kOneBatch; ++b)
+          if (k0 + b < p) result = k0 + b == 0 ? S::widen1(raw[b]) : result + S::widen1(raw[b]);
+      }
+    } else {
+      E raw[kOneBatch], raw2[kOneBatch];
+      float res[1];
+      run_groups<ALGO, kOneBatch, 1>(
+          a, res,
+          [&](const void* s0, const void* s1, bool pair, auto bc) {
+            constexpr int b = decltype(bc)::value;
+            raw[b] = static_cast<const E*>(s0)[e];
+            if (pair) raw2[b] = static_cast<const E*>(s1)[e];
+          },
+          [&](auto bc, bool pair, float(&v)[1]) {
+            constexpr int b = decltype(bc)::value;
+            v[0] = S::widen1(raw[b]);
+            if (pair) v[0] = v[0] + S::widen1(raw2[b]);
+          });
+      result = res[0];
     }
   }
   const E out = S::narrow1(result);
@@ -210,37 +310,47 @@ __device__ __forceinline__ void reduce_elems(const ReduceArgs& a, int c, int p, 
     // trees from 5 to 4 waves per SIMD and p = 72 tree all-reduces of 4 and
     // 16 MiB per rank 2-9 % slower, for 6 % on unaligned buffers
     constexpr int B = 8;
-    float st[kRuntimeDepth][U];
+    if constexpr (ALGO == VCOLL_RING) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) res[u] = 0.0f;
-    for (int k0 = 0; k0 < p; k0 += B) {
-      E raw[B][U];
+      for (int u = 0; u < U; ++u) res[u] = 0.0f;
+      for (int k0 = 0; k0 < p; k0 += B) {
+        E raw[B][U];
 #pragma unroll
-      for (int b = 0; b < B; ++b)
-        if (k0 + b < p) {
-          const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : k0 + b;
+        for (int b = 0; b < B; ++b)
+          if (k0 + b < p) {
+            const void* src = a.leaf[(rot + k0 + b) % p];
 #pragma unroll
-          for (int u = 0; u < U; ++u) raw[b][u] = ok[u] ? static_cast<const E*>(a.leaf[rank])[e[u]] : E(0);
-        }
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-        if (k0 + b < p) {
-          float v[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) v[u] = S::widen1(raw[b][u]);
-          if constexpr (ALGO == VCOLL_RING) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) res[u] = k0 + b == 0 ? v[u] : res[u] + v[u];
-          } else {
-            rt_push<U>(st, v);
-            for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<U>(st);
+            for (int u = 0; u < U; ++u) raw[b][u] = ok[u] ? static_cast<const E*>(src)[e[u]] : E(0);
           }
-        }
-    }
-    if constexpr (ALGO != VCOLL_RING) {
-      for (int m = 0; m < a.final_merges; ++m) rt_merge<U>(st);
 #pragma unroll
-      for (int u = 0; u < U; ++u) res[u] = st[0][u];
+        for (int b = 0; b < B; ++b)
+          if (k0 + b < p) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) res[u] = k0 + b == 0 ? S::widen1(raw[b][u]) : res[u] + S::widen1(raw[b][u]);
+          }
+      }
+    } else {
+      E raw[kTreeBatch][U], raw2[kTreeBatch][U];
+      run_groups<ALGO, kTreeBatch, U>(
+          a, res,
+          [&](const void* s0, const void* s1, bool pair, auto bc) {
+            constexpr int b = decltype(bc)::value;
+#pragma unroll
+            for (int u = 0; u < U; ++u) raw[b][u] = ok[u] ? static_cast<const E*>(s0)[e[u]] : E(0);
+            if (pair) {
+#pragma unroll
+              for (int u = 0; u < U; ++u) raw2[b][u] = ok[u] ? static_cast<const E*>(s1)[e[u]] : E(0);
+            }
+          },
+          [&](auto bc, bool pair, float(&v)[U]) {
+            constexpr int b = decltype(bc)::value;
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = S::widen1(raw[b][u]);
+            if (pair) {
+#pragma unroll
+              for (int u = 0; u < U; ++u) v[u] = v[u] + S::widen1(raw2[b][u]);
+            }
+          });
     }
   }
   E out[U];
@@ -326,42 +436,43 @@ __device__ __forceinline__ void reduce_vector_runtime(const ReduceArgs& a, int c
                                                       int64_t boff, bool valid, int64_t out_shift) {
   using S = Storage<D>;
   constexpr int VE = S::kVE;
-  constexpr int B = 8;               // ranks whose loads are in flight together
+  constexpr int B = 8;               // ranks whose loads are in flight together (ring)
   float acc[VE];
-  float st[kRuntimeDepth][VE];
-  for (int k0 = 0; k0 < p; k0 += B) {
-    u32x4 raw[B];
+  if constexpr (ALGO == VCOLL_RING) {
+    for (int k0 = 0; k0 < p; k0 += B) {
+      u32x4 raw[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      if (k0 + b < p) {
-        const int rank = (ALGO == VCOLL_RING) ? (rot + k0 + b) % p : k0 + b;
-        raw[b] = valid ? ld16(a.leaf[rank], boff) : u32x4{0, 0, 0, 0};
-      }
-    }
+      for (int b = 0; b < B; ++b)
+        if (k0 + b < p) raw[b] = valid ? ld16(a.leaf[(rot + k0 + b) % p], boff) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      if (k0 + b < p) {
-        float v[VE];
-        S::widen(raw[b], v);
-        if constexpr (ALGO == VCOLL_RING) {
-          if (k0 + b == 0) {
+      for (int b = 0; b < B; ++b) {
+        if (k0 + b < p) {
+          float v[VE];
+          S::widen(raw[b], v);
 #pragma unroll
-            for (int i = 0; i < VE; ++i) acc[i] = v[i];
-          } else {
-#pragma unroll
-            for (int i = 0; i < VE; ++i) acc[i] = acc[i] + v[i];
-          }
-        } else {
-          rt_push<VE>(st, v);
-          for (int m = 0; m < a.merges[k0 + b]; ++m) rt_merge<VE>(st);
+          for (int i = 0; i < VE; ++i) acc[i] = k0 + b == 0 ? v[i] : acc[i] + v[i];
         }
       }
     }
-  }
-  if constexpr (ALGO != VCOLL_RING) {
-    for (int m = 0; m < a.final_merges; ++m) rt_merge<VE>(st);
+  } else {
+    u32x4 raw[kTreeBatch], raw2[kTreeBatch];
+    run_groups<ALGO, kTreeBatch, VE>(
+        a, acc,
+        [&](const void* s0, const void* s1, bool pair, auto bc) {
+          constexpr int b = decltype(bc)::value;
+          raw[b] = valid ? ld16(s0, boff) : u32x4{0, 0, 0, 0};
+          if (pair) raw2[b] = valid ? ld16(s1, boff) : u32x4{0, 0, 0, 0};
+        },
+        [&](auto bc, bool pair, float(&v)[VE]) {
+          constexpr int b = decltype(bc)::value;
+          S::widen(raw[b], v);
+          if (pair) {
+            float w[VE];
+            S::widen(raw2[b], w);
 #pragma unroll
-    for (int i = 0; i < VE; ++i) acc[i] = st[0][i];
+            for (int i = 0; i < VE; ++i) v[i] = v[i] + w[i];
+          }
+        });
   }
   if (!valid) return;
   const u32x4 out = S::narrow(acc);
@@ -560,78 +671,155 @@ __global__ __launch_bounds__(kBlock) void reduce_scatter_shifted_kernel(const Re
 constexpr int64_t kShiftLinesMinWaves = 32768;
 
 // ----------------------------------------------------------------------------
-// small chunks with the run-time order program (p not compiled in): a
-// workgroup stages a [p][kSmallTile] tile of its chunk in LDS with every load
-// of the tile in flight at once, runs the order program for each element out
-// of LDS, and fans the results out. Where the per-thread path would wait for
-// memory once per 8 or 16 ranks, this waits once.
+// small chunks with a run-time p: a workgroup stages a [slots][kSmallTile]
+// tile of its chunk in LDS with every load of the tile in flight at once,
+// sums each element out of LDS, and fans the results out. A slot is a rank
+// (ring) or a group of the tree program (a folded pair added on the way in).
+// Wave w moves slots w, w + 4, ...: each lane fetches two entries of every
+// pointer table with one vector load (one memory round trip for all of
+// them, where scalar loads of a workgroup alone on its compute unit miss the
+// scalar cache a few pointers at a time), and each slot's address is read
+// from the lane that holds it, uniform in the wave. The element accesses are
+// buffer instructions whose size (the tile's elements, or nothing for a
+// slot past the last) masks the rest, so no load or store waits on another
+// and no slot needs a branch. (Per-lane buffer lookups made every access of
+// a wave wait for the ones before it; a branch per slot cost p = 72 at 1 KiB
+// per rank 4 us, scalar pointer loads 4 us at p = 24.) Against per-lane
+// lookups and a shift-register stack for the trees, on MI355X: p = 24 at 1
+// KiB per rank ring 4.4 -> 3.7 us, trees 6.4 -> 3.9-4.0; p = 72 at 10 KiB
+// ring 8.8 -> 5.7, trees 14.3 -> 5.4-6.5, at 256 KiB ring 22.7 -> 14.5, trees
+// 31.9 -> 14.6-16.1 (p = 72 at 1 KiB: ring 5.4 -> 5.8, the cost of 32 slots
+// per wave).
 
 constexpr int kSmallTile = 64;                                   // elements of a chunk per workgroup
-constexpr int kSmallLoads = (kMaxRanks * kSmallTile + kBlock - 1) / kBlock;
 
-template <int D, int ALGO, bool RS>
+template <class E>
+__device__ __forceinline__ E buf_ld1(__amdgpu_buffer_rsrc_t r, int voff) {
+  if constexpr (sizeof(E) == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kPolicyCached);
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, kPolicyCached);
+}
+
+template <class E>
+__device__ __forceinline__ void buf_st1(E v, __amdgpu_buffer_rsrc_t r, int voff) {
+  if constexpr (sizeof(E) == 4) __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, kPolicyCached);
+  else __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, 0, kPolicyCached);
+}
+
+// Entry `i` (uniform, < 64) of a table whose entry l each lane l holds.
+__device__ __forceinline__ const void* lane_ptr(uint64_t held, int i) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(held), i);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(held >> 32), i);
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// NJ: slots per wave, 16 for p <= 64 (half the instructions) and 32 beyond.
+template <int D, int ALGO, bool RS, int NJ>
 __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a) {
   using S = Storage<D>;
   using E = typename S::elem;
-  __shared__ float val[kMaxRanks * kSmallTile];                  // [leaf r][element]
+  constexpr int ES = static_cast<int>(sizeof(E));
+  constexpr int kWaves = kBlock / 64;
+  constexpr int kPerWave = NJ;                                   // slots a wave moves, at most
+  static_assert((NJ == 16 || NJ == 32) && NJ * kWaves <= kMaxRanks, "16 or 32 slots per wave");
+  constexpr bool kPairs = ALGO != VCOLL_RING && ALGO != VCOLL_BINARY_TREE;
+  __shared__ float val[kMaxRanks * kSmallTile];                  // [slot][element]
   __shared__ float res[kSmallTile];
   const int c = blockIdx.y;
   const int p = a.p;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t off = c * a.q + (c < a.r ? c : a.r);
   const int64_t cnt = a.q + (c < a.r ? 1 : 0);
   const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kSmallTile;
   if (e0 >= cnt) return;                                         // the whole workgroup
   const int T = cnt - e0 < kSmallTile ? static_cast<int>(cnt - e0) : kSmallTile;
-  E raw[kSmallLoads];
+  const int64_t tile = (off + e0) * ES;                          // the tile's byte offset in every rank
+  const int slots = ALGO == VCOLL_RING ? p : a.groups;
+  static_assert(kMaxRanks == 128 && kWaves == 4, "two table entries per lane, slots below 64 for j < 16");
+  constexpr int kLow = 16;                                       // j < kLow: slot below 64
+  const uint64_t* const lt = reinterpret_cast<const uint64_t*>(a.leaf);
+  const uint64_t* const dt = reinterpret_cast<const uint64_t*>(a.dst);
+  constexpr bool kHigh = NJ > 16;                                // slots 64 and up
+  const uint64_t leaf_lo = lt[lane];                             // leaf[l], leaf[64 + l]
+  const uint64_t leaf_hi = kHigh ? lt[64 + lane] : 0;
+  [[maybe_unused]] uint64_t pair_lo = 0, pair_hi = 0;            // leaf[128 + l], leaf[192 + l]
+  if constexpr (kPairs) {
+    pair_lo = lt[kMaxRanks + lane];
+    pair_hi = kHigh ? lt[kMaxRanks + 64 + lane] : 0;
+  }
+  [[maybe_unused]] uint64_t dst_lo = 0, dst_hi = 0;              // dst[l], dst[64 + l]
+  if constexpr (!RS) {
+    dst_lo = dt[lane];
+    dst_hi = kHigh ? dt[64 + lane] : 0;
+  }
+  E x[kPerWave];
+  [[maybe_unused]] E y[kPerWave];
+  [[maybe_unused]] bool pair[kPerWave];
 #pragma unroll
-  for (int j = 0; j < kSmallLoads; ++j) {
-    const int idx = tid + j * kBlock;
-    if (idx < p * T) {
-      const int r = idx / T;
-      raw[j] = static_cast<const E*>(a.leaf[r])[off + e0 + (idx - r * T)];
+  for (int j = 0; j < kPerWave; ++j) {
+    const int s = wave + j * kWaves;                             // < kMaxRanks
+    const int bytes = s < slots ? T * ES : 0;
+    const int held = s - (j < kLow ? 0 : 64);
+    const void* first = lane_ptr(j < kLow ? leaf_lo : leaf_hi, held);
+    x[j] = buf_ld1<E>(raw_rsrc(first, tile, bytes), lane * ES);
+    if constexpr (kPairs) {
+      const void* second = lane_ptr(j < kLow ? pair_lo : pair_hi, held);
+      pair[j] = second != nullptr;
+      y[j] = buf_ld1<E>(raw_rsrc(pair[j] ? second : first, tile, pair[j] ? bytes : 0), lane * ES);
     }
   }
 #pragma unroll
-  for (int j = 0; j < kSmallLoads; ++j) {
-    const int idx = tid + j * kBlock;
-    if (idx < p * T) val[idx] = S::widen1(raw[j]);
+  for (int j = 0; j < kPerWave; ++j) {
+    float v = S::widen1(x[j]);
+    if constexpr (kPairs) v = pair[j] ? v + S::widen1(y[j]) : v;
+    val[(wave + j * kWaves) * kSmallTile + lane] = v;
   }
   __syncthreads();
-  if (tid < T) {
+  if (threadIdx.x < T) {
+    const int tid = threadIdx.x;
     float result;
     // the ring's chain is sequential in its adds, not in its LDS reads: the
     // reads of the next leaves go out ahead of the adds (p = 72 at 1 KiB per
     // rank 6.5 -> 5.1 us, at 256 KiB 25.8 -> 22.5 us)
     if constexpr (ALGO == VCOLL_RING) {
       int leaf = (c + 1) % p;                                    // chunk c's chain starts at rank c+1
-      result = val[leaf * T + tid];
+      result = val[leaf * kSmallTile + tid];
 #pragma unroll 8
       for (int k = 1; k < p; ++k) {
         leaf = leaf + 1 == p ? 0 : leaf + 1;
-        result = result + val[leaf * T + tid];
+        result = result + val[leaf * kSmallTile + tid];
       }
     } else {
-      float st[kRuntimeDepth][1];
-#pragma unroll 4
-      for (int k = 0; k < p; ++k) {
-        const float v = val[k * T + tid];
-        rt_push<1>(st, &v);
-        for (int m = 0; m < a.merges[k]; ++m) rt_merge<1>(st);
+      constexpr int B = 8;
+      float lvl[kLevels][1], out1[1];
+#pragma unroll 1
+      for (int q0 = 0; q0 < slots; q0 += B) {
+        float xs[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) xs[b] = val[(q0 + b) * kSmallTile + tid];   // q0 + b < kMaxRanks
+        static_for<0, B>([&](auto bb) {
+          constexpr int b = decltype(bb)::value;
+          if (q0 + b < slots) {
+            float v[1] = {xs[b]};
+            counter_push<B, b>(lvl, v, q0);
+          }
+        });
       }
-      for (int m = 0; m < a.final_merges; ++m) rt_merge<1>(st);
-      result = st[0][0];
+      counter_total(lvl, slots, out1);
+      result = out1[0];
     }
     res[tid] = result;
   }
   __syncthreads();
+  const E out = S::narrow1(res[lane]);                           // lanes past T store nothing
   if constexpr (RS) {
-    if (tid < T) static_cast<E*>(a.dst[c])[e0 + tid] = S::narrow1(res[tid]);
+    if (wave == 0) buf_st1<E>(out, raw_rsrc(a.dst[c], e0 * ES, T * ES), lane * ES);
   } else {
-    for (int idx = tid; idx < p * T; idx += kBlock) {
-      const int r = idx / T;
-      const int e = idx - r * T;
-      static_cast<E*>(a.dst[r])[off + e0 + e] = S::narrow1(res[e]);
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int r = wave + j * kWaves;
+      const void* dst = lane_ptr(j < kLow ? dst_lo : dst_hi, r - (j < kLow ? 0 : 64));
+      buf_st1<E>(out, raw_rsrc(dst, tile, r < p ? T * ES : 0), lane * ES);
     }
   }
 }
@@ -677,7 +865,8 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
   } else {
     if (max_chunk <= kSmallMax) {
       const dim3 small(static_cast<unsigned>((max_chunk + kSmallTile - 1) / kSmallTile), chunks);
-      return launch(reduce_small_kernel<D, ALGO, RS>, small, args, stream);
+      if (a.p <= 64) return launch(reduce_small_kernel<D, ALGO, RS, 16>, small, args, stream);
+      return launch(reduce_small_kernel<D, ALGO, RS, 32>, small, args, stream);
     }
     if constexpr (RS && ALGO == VCOLL_RING) {
       bool aligned = true;

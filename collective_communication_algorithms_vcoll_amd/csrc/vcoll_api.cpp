@@ -148,6 +148,20 @@ int burst_tiles(int p, const Chunks& ch, vcoll_dtype dtype, int32_t align, int32
   return static_cast<int>((cv + t - 1) / t);
 }
 
+// Leaf buffers of a tree program for the kernels with a run-time p: group q
+// of the program (order_groups) in leaf[q] and, for a folded pair, its
+// second leaf in leaf[kMaxRanks + q]; `input(k)` is the buffer of program
+// leaf k.
+template <class Input>
+void set_tree_groups(ReduceArgs& a, vcoll_algo algo, int p, const Input& input) {
+  int first[kMaxRanks + 1] = {};
+  a.groups = order_groups(algo, p, first);
+  for (int q = 0; q < a.groups; ++q) {
+    a.leaf[q] = input(first[q]);
+    a.leaf[kMaxRanks + q] = first[q + 1] - first[q] == 2 ? input(first[q] + 1) : nullptr;
+  }
+}
+
 vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
                            const void* const* send, void* const* recv, void* stream, bool scatter) {
   if (!valid_p(p) || !valid_count(n) || !valid_dtype(dtype) || !valid_algo(algo)) return VCOLL_ERR_INVALID_ARG;
@@ -200,14 +214,11 @@ vcoll_status reduce_common(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype,
     for (int c = 0; c < rows; ++c)
       for (int k = 0; k < p; ++k)
         a.leaf[c * kFixedMax + k] = send[algo == VCOLL_RING ? (c + 1 + k) % p : prog.rank[k]];
+  } else if (algo == VCOLL_RING) {
+    for (int k = 0; k < p; ++k) a.leaf[k] = send[k];
   } else {
-    for (int k = 0; k < p; ++k) a.leaf[k] = send[algo == VCOLL_RING ? k : prog.rank[k]];
+    set_tree_groups(a, algo, p, [&](int k) { return send[prog.rank[k]]; });
   }
-  for (int k = 0; k < p; ++k) {
-    a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
-    a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
-  }
-  a.final_merges = prog.final_merges;
   return from_hip(launch_reduce(a, dtype, algo, scatter, ch.count(0), p, static_cast<hipStream_t>(stream)));
 }
 
@@ -445,12 +456,12 @@ vcoll_status vcoll_reduce(vcoll_algo algo, int p, int64_t n, vcoll_dtype dtype, 
   a.src_align = 16;
   // the tree runs on ranks relative to the root: leaf v is rank (v + root) mod p
   const OrderProgram prog = order_program(VCOLL_BINARY_TREE, p);
-  for (int k = 0; k < p; ++k) a.leaf[k] = send[(prog.rank[k] + root) % p];   // leaves in program order
-  for (int k = 0; k < p; ++k) {
-    a.rank[k] = static_cast<uint8_t>(prog.rank[k]);
-    a.merges[k] = static_cast<uint8_t>(prog.merges[k]);
+  auto input = [&](int k) { return send[(prog.rank[k] + root) % p]; };
+  if (has_fixed_kernel(p)) {
+    for (int k = 0; k < p; ++k) a.leaf[k] = input(k);                         // leaves in program order
+  } else {
+    set_tree_groups(a, VCOLL_BINARY_TREE, p, input);
   }
-  a.final_merges = prog.final_merges;
   return from_hip(launch_reduce(a, dtype, VCOLL_BINARY_TREE, true, n, 1, static_cast<hipStream_t>(stream)));
 }
 
@@ -811,15 +822,9 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
   if (!valid_p(p) || hidden <= 0 || hidden % 128 != 0 || hidden > INT32_MAX / 2 || !splits || !token_rows ||
       !src_rows)
     return VCOLL_ERR_INVALID_ARG;
-  std::vector<int64_t> sent(p, 0), got(p, 0);
-  for (int i = 0; i < p; ++i)
-    for (int j = 0; j < p; ++j) {
-      const int64_t s = splits[i * p + j];
-      if (s < 0 || s > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
-      sent[i] += s;
-      got[j] += s;
-      if (sent[i] > INT32_MAX || got[j] > INT32_MAX) return VCOLL_ERR_INVALID_ARG;
-    }
+  const int64_t orb = hidden + hidden / 32;
+  std::vector<int64_t> sent, got;
+  if (!valid_splits(p, splits, orb, sent, got)) return VCOLL_ERR_INVALID_ARG;
   for (int i = 0; i < p; ++i) {
     if (sent[i] > 0 && (!tokens || !tokens[i] || !aligned16(tokens[i]) || !src_rows[i] ||
                         token_rows[i] < 0 || token_rows[i] > INT32_MAX))
@@ -827,7 +832,6 @@ vcoll_status vcoll_moe_dispatch_fp8(int p, int64_t hidden, const int64_t* splits
     if (got[i] > 0 && (!recv || !recv[i] || (reinterpret_cast<uintptr_t>(recv[i]) & 3u) != 0))
       return VCOLL_ERR_INVALID_ARG;
   }
-  const int64_t orb = hidden + hidden / 32;
   std::vector<int64_t> so, ro;
   block_offsets(p, splits, so, ro);
   const int32_t rows_per_tile = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, 32768 / (2 * hidden))));

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <random>
+#include <string>
 #include <vector>
 
 #include "bench.h"
@@ -29,7 +30,7 @@ extern "C" hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
 extern "C" hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }
 
 namespace vcoll {
-hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype, vcoll_algo, bool, int64_t max_chunk, int chunks,
+hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype, vcoll_algo algo, bool, int64_t max_chunk, int chunks,
                          hipStream_t) {
   if (a.p < 1 || a.p > kMaxRanks || chunks < 1 || max_chunk < 0) std::abort();
   // the input phase the unaligned reduce-scatter aligns its waves to: 128
@@ -37,6 +38,15 @@ hipError_t launch_reduce(const ReduceArgs& a, vcoll_dtype, vcoll_algo, bool, int
   if (!(a.src_align == 16 || a.src_align == 128) || a.src_phase < 0 || a.src_phase >= a.src_align ||
       a.src_phase % 16 != 0)
     std::abort();
+  // the tree programs' groups (the kernels with a run-time p read them): a
+  // first leaf for every group, a second one exactly for the folded pairs
+  if (algo != VCOLL_RING && !has_fixed_kernel(a.p)) {
+    int first[kMaxRanks + 1] = {};
+    const int g = order_groups(algo, a.p, first);
+    if (a.groups != g) std::abort();
+    for (int q = 0; q < g; ++q)
+      if (!a.leaf[q] || (a.leaf[kMaxRanks + q] != nullptr) != (first[q + 1] - first[q] == 2)) std::abort();
+  }
   ++g_launches;
   return hipSuccess;
 }
@@ -336,8 +346,51 @@ static void launches(std::mt19937_64& rng) {
   CHECK(g_launches == before);
 }
 
+// Every tree program (push / add stack machine of order_program) equals the
+// binary counter over its groups (order_groups), operand for operand: leaves
+// are written as their rank, a sum as (older+newer).
+static void group_programs() {
+  for (int algo : {VCOLL_RECURSIVE_DOUBLING, VCOLL_RABENSEIFNER, VCOLL_BINARY_TREE})
+    for (int p = 1; p <= kMaxRanks; ++p) {
+      const vcoll::OrderProgram prog = vcoll::order_program(algo, p);
+      std::vector<std::string> st;
+      auto merge = [&]() {
+        const std::string b = st.back();
+        st.pop_back();
+        st.back() = "(" + st.back() + "+" + b + ")";
+      };
+      for (int k = 0; k < p; ++k) {
+        st.push_back(std::to_string(prog.rank[k]));
+        for (int m = 0; m < prog.merges[k]; ++m) merge();
+      }
+      for (int m = 0; m < prog.final_merges; ++m) merge();
+      CHECK(st.size() == 1);
+      int first[kMaxRanks + 1] = {};
+      const int groups = vcoll::order_groups(algo, p, first);
+      CHECK(groups >= 1 && groups <= kMaxRanks && first[0] == 0 && first[groups] == p);
+      std::string lvl[8];
+      for (int q = 0; q < groups; ++q) {
+        const int k = first[q], n = first[q + 1] - k;
+        CHECK(n == 1 || n == 2);
+        std::string v = std::to_string(prog.rank[k]);
+        if (n == 2) v = "(" + v + "+" + std::to_string(prog.rank[k + 1]) + ")";
+        const int closes = vcoll::ctz_int(q + 1);
+        for (int l = 0; l < closes; ++l) v = "(" + lvl[l] + "+" + v + ")";
+        lvl[closes] = v;
+      }
+      std::string total;
+      for (int l = 0; l < 8; ++l)
+        if ((groups >> l) & 1) total = total.empty() ? lvl[l] : "(" + lvl[l] + "+" + total + ")";
+      if (total != st[0]) {
+        std::fprintf(stderr, "algo %d p %d: counter %s, program %s\n", algo, p, total.c_str(), st[0].c_str());
+        std::abort();
+      }
+    }
+}
+
 int main() {
   std::mt19937_64 rng(7);
+  group_programs();
   ledgers(rng);
   model();
   moe(rng);
