@@ -988,7 +988,8 @@ def summarize_stats(trace_dir: str, name: str, title: str, command: str) -> int:
              "Template arguments of reduce_kernel: dtype (0 f32, 1 bf16), algorithm (0 ring, 1 recursive doubling, "
              "2 Rabenseifner, 3 tree), p (0: read at run time), vectors per thread, reduce-scatter, large-grid "
              "variant, workgroup size; of burst_ring_kernel: dtype, vectors per thread, store cache policy "
-             "(0 through L2, 2 streamed).", "",
+             "(0 through L2, 2 streamed); of reduce_small_kernel: dtype, algorithm, reduce-scatter, slots per "
+             "wave.", "",
              "| kernel | calls | average us | min us | max us | p10 us | median us | p90 us |",
              "|---|---|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
