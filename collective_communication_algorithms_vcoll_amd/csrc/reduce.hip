@@ -824,10 +824,23 @@ __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a
   }
 }
 
-// Largest chunk (elements) that the run-time path stages through LDS: at
-// p = 72 this is 3x faster than the per-thread path up to 256 KiB per rank
-// and slower from 1 MiB, where the per-thread path's 16-byte accesses win.
-constexpr int64_t kSmallMax = 1024;
+// When the run-time path stages its chunks through LDS: always for chunks of
+// up to kSmallAlways elements, and up to kSmallMax while the grid has at
+// most kSmallMaxGroups workgroups. Its 4-byte accesses cost bandwidth that
+// the per-thread path's 16-byte ones save, so it wins while the call is
+// latency-bound. Measured on MI355X (float32, all four algorithms): chunks
+// of 1820-3972 elements on 1032-2100 workgroups (p = 24 x 256 KiB, p = 33 x
+// 512 KiB, p = 72 and p = 100 x 512 KiB per rank) 25-45 % faster than the
+// per-thread path; chunks of 2621-3641 elements on 4100 workgroups (p = 72
+// and p = 100 x 1 MiB) up to 35 % slower.
+constexpr int64_t kSmallAlways = 1024;
+constexpr int64_t kSmallMax = 4096;
+constexpr int64_t kSmallMaxGroups = 3072;
+
+inline bool use_small(int64_t max_chunk, int chunks) {
+  const int64_t groups = (max_chunk + kSmallTile - 1) / kSmallTile * chunks;
+  return max_chunk <= kSmallAlways || (max_chunk <= kSmallMax && groups <= kSmallMaxGroups);
+}
 
 // 16-byte vectors per thread of the reduce kernel (all are loaded before the
 // first add). Build-time override: -DVCOLL_V_P8=<n> for p = 8.
@@ -863,7 +876,7 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
     if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true, BS>, grid, BS, args, stream);
     return launch(reduce_kernel<D, ALGO, P, V, RS, false, BS>, grid, BS, args, stream);
   } else {
-    if (max_chunk <= kSmallMax) {
+    if (use_small(max_chunk, chunks)) {
       const dim3 small(static_cast<unsigned>((max_chunk + kSmallTile - 1) / kSmallTile), chunks);
       if (a.p <= 64) return launch(reduce_small_kernel<D, ALGO, RS, 16>, small, args, stream);
       return launch(reduce_small_kernel<D, ALGO, RS, 32>, small, args, stream);

@@ -574,6 +574,41 @@ def test_max_p_with_vector_chunks(vc, dtype):
     assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"AG p={p} m={m}")
 
 
+# chunks of 1025-4096 elements on at most 3072 workgroups also take the
+# LDS-staged path; (72, 72 * 3641) is past the workgroup bound (per-thread path)
+MID_SHAPES = [(24, 24 * 2731 + 5), (33, 33 * 3972 + 7), (72, 72 * 1820 + 11), (100, 100 * 1310 + 3),
+              (72, 72 * 3641)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p,n", MID_SHAPES, ids=[f"p{p}-n{n}" for p, n in MID_SHAPES])
+def test_mid_chunks_of_the_run_time_program(vc, p, n, dtype):
+    """The staged path's larger chunks (ragged, 29-63 tiles of 64 elements)
+    and the per-thread path just past its bound: all-reduce with every
+    algorithm, ring reduce-scatter, and a reduce to a root of a vector of at
+    most 4096 elements."""
+    from oracle import rooted
+    x = rand_inputs(p, n, dtype, 400 + p)
+    t = upload(x, dtype)
+    for algo in ALGOS:
+        say(f"mid-chunk all-reduce p={p} n={n} {algo} {dtype}")
+        want, _ = oracle.allreduce(x, algo, dtype)
+        got = download(vc.vcoll_allreduce(algo, t), dtype)
+        assert_bits_equal(got, np.stack([bits(w, dtype) for w in want]), f"{algo} p={p}")
+    say(f"mid-chunk reduce-scatter p={p} n={n} {dtype}")
+    rs = vc.vcoll_reduce_scatter("ring", t)
+    sync()
+    want, _ = oracle.reduce_scatter(x, "ring", dtype)
+    for c in range(p):
+        assert_bits_equal(download(rs[c], dtype), bits(want[c], dtype), f"rs chunk {c}")
+    xs = [r[:4000] for r in x]
+    say(f"reduce to a root p={p} n=4000 {dtype}")
+    red = vc.vcoll_reduce(upload(xs, dtype), root=p - 1)
+    sync()
+    want, _ = rooted.reduce(xs, p - 1, dtype)
+    assert_bits_equal(download(red, dtype), bits(want, dtype), "reduce")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("p", [3, 12, 72, 128])
 def test_small_chunks_of_the_run_time_program(vc, p, dtype):
