@@ -31,9 +31,9 @@ using namespace dev;
 // bf16 blocks of 32,776 elements 98.7 -> 81.9 us), within 1.5% on aligned
 // tiles. The large fan-outs write faster through L2 with cached stores
 // too: the all-gather and broadcast beyond 1 GiB written (4-6%) and the bf16
-// token-major MoE dispatch, 8 copies of each token row (3%). One-to-one
-// movers (all-to-all, combine, FP8 codes) lost 1-8% with cached stores and
-// keep streaming ones.
+// token-major MoE dispatch, 8 copies of each token row (3%; its FP8 codes
+// 2.2%). One-to-one movers (all-to-all, combine, the row-major FP8 codes)
+// lost 1-8% with cached stores and keep streaming ones.
 
 template <bool NT>
 __device__ __forceinline__ void fan_st16(void* base, int64_t tile_off, int lane_off, u32x4 v) {
@@ -275,11 +275,16 @@ __device__ __forceinline__ void quantise16(const u32x4 w0, const u32x4 w1, u32x4
 }
 
 // Store one lane's 16 codes (elements 16y .. 16y+15 of the row) and, from the
-// first lane of each group, the group's scale.
+// first lane of each group, the group's scale. CACHED: 16-byte code stores
+// through L2, which on MI355X made the token-major dispatch (8 copies of each
+// quantised row, rows of 7392 bytes that share cache lines) 2.2 % faster and
+// the row-major one (each row written once) 5 % slower than streaming ones.
+template <bool CACHED>
 __device__ __forceinline__ void store_codes(char* row, int64_t hidden, int64_t y, const u32x4 codes, float scale,
                                             bool vec) {
   if (vec) {
-    st16(row, y * 16, codes);
+    if constexpr (CACHED) *reinterpret_cast<u32x4*>(row + y * 16) = codes;
+    else st16(row, y * 16, codes);
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w) __builtin_nontemporal_store(codes[w], reinterpret_cast<uint32_t*>(row + y * 16) + w);
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(const Fp8Args a) {
       u32x4 codes;
       float scale;
       quantise16(ld16(src, y * 32), ld16(src, y * 32 + 16), codes, scale);
-      store_codes(dst, a.hidden, y, codes, scale, a.vec_out);
+      store_codes<false>(dst, a.hidden, y, codes, scale, a.vec_out);
     }
   }
 }
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(BS) void dispatch_push_kernel(const PushArgs a) {
           quantise16(w[2 * u], w[2 * u + 1], codes, scale);
           for (int k = 0; k < a.topk; ++k) {
             char* d = dest(k);
-            if (d) store_codes(d, a.hidden, y, codes, scale, a.vec_out);
+            if (d) store_codes<true>(d, a.hidden, y, codes, scale, a.vec_out);
           }
         }
       }
