@@ -107,8 +107,22 @@ __device__ __forceinline__ void hier_vector(const HierArgs& a, int l, int j, int
   }
 }
 
+// Threads per workgroup: two waves for the 16-rank shapes, four otherwise.
+// On MI355X, 128 against 256 threads took the 4 x 4 hierarchy of 16 x 192
+// MiB bf16 from 1206-1213 to 1163 us and of 16 x 16 MiB float32 from 126-127
+// to 121-122 us, and left 2 x 8 within 1 % (64 threads: 4 x 4 1161-1166 us,
+// 16 MiB 124 us). Build-time override: -DVCOLL_HIER_BS16=<threads>.
+#ifndef VCOLL_HIER_BS16
+#define VCOLL_HIER_BS16 128
+#endif
+template <int NN, int LL>
+constexpr int hier_block() {
+  return NN * LL == 16 ? VCOLL_HIER_BS16 : kBlock;
+}
+
 template <int D, int NN, int LL, bool LARGE>
-__global__ __launch_bounds__(kBlock) void hier_kernel(const HierArgs a) {
+__global__ __launch_bounds__((hier_block<NN, LL>())) void hier_kernel(const HierArgs a) {
+  constexpr int BS = hier_block<NN, LL>();
   using S = Storage<D>;
   constexpr int VE = S::kVE;
   constexpr int ES = 16 / VE;
@@ -121,10 +135,10 @@ __global__ __launch_bounds__(kBlock) void hier_kernel(const HierArgs a) {
     const int64_t head = (VE - off % VE) % VE < cnt ? (VE - off % VE) % VE : cnt;
     const int64_t nvec = (cnt - head) / VE;
     const int64_t e_base = off + head;
-    const int64_t v = static_cast<int64_t>(blockIdx.x) * kBlock + tid;
-    if (static_cast<int64_t>(blockIdx.x) * kBlock < nvec) {
+    const int64_t v = static_cast<int64_t>(blockIdx.x) * BS + tid;
+    if (static_cast<int64_t>(blockIdx.x) * BS < nvec) {
       const int64_t boff = (e_base + v * VE) * ES;
-      if ((static_cast<int64_t>(blockIdx.x) + 1) * kBlock <= nvec) {
+      if ((static_cast<int64_t>(blockIdx.x) + 1) * BS <= nvec) {
         hier_vector<D, NN, LL, LARGE, true>(a, l, j, boff, true);
       } else {
         hier_vector<D, NN, LL, LARGE, false>(a, l, j, boff, v < nvec);
@@ -136,10 +150,10 @@ __global__ __launch_bounds__(kBlock) void hier_kernel(const HierArgs a) {
       else if (tid >= 16 && tid - 16 < tail) hier_one<D>(a, N, Lc, l, j, e_base + nvec * VE + (tid - 16));
     }
   } else {
-    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (kBlock * VE);
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (BS * VE);
 #pragma unroll 1
     for (int k = 0; k < VE; ++k) {
-      const int64_t i = e0 + k * kBlock + tid;
+      const int64_t i = e0 + k * BS + tid;
       if (i < cnt) hier_one<D>(a, N, Lc, l, j, off + i);
     }
   }
@@ -148,35 +162,40 @@ __global__ __launch_bounds__(kBlock) void hier_kernel(const HierArgs a) {
 // ----------------------------------------------------------------------------
 // launchers
 
+// Grid (tiles of BS threads x VE elements, segment); large grids pace their
+// stores (VCOLL_PACE_MIN_GROUPS counted in four-wave workgroups).
 template <int D, int NN, int LL>
-hipError_t launch_hier_shape(const HierArgs& a, dim3 grid, bool large, hipStream_t stream) {
-  if (large) return launch(hier_kernel<D, NN, LL, true>, grid, a, stream);
-  return launch(hier_kernel<D, NN, LL, false>, grid, a, stream);
+hipError_t launch_hier_shape(const HierArgs& a, int64_t max_segment, hipStream_t stream) {
+  constexpr int BS = hier_block<NN, LL>();
+  constexpr int64_t per_tile = static_cast<int64_t>(BS) * Storage<D>::kVE;
+  const int64_t tiles = (max_segment + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  const int p = a.nodes * a.local;
+  const dim3 grid(static_cast<unsigned>(tiles), p);
+  const bool large = tiles * p * BS >= static_cast<int64_t>(VCOLL_PACE_MIN_GROUPS) * kBlock;
+  if constexpr (NN > 0) {
+    if (large) return launch(hier_kernel<D, NN, LL, true>, grid, BS, a, stream);
+  }
+  return launch(hier_kernel<D, NN, LL, false>, grid, BS, a, stream);
 }
 
 template <int D>
-hipError_t launch_hier_dtype(const HierArgs& a, dim3 grid, bool large, hipStream_t stream) {
+hipError_t launch_hier_dtype(const HierArgs& a, int64_t max_segment, hipStream_t stream) {
   const int N = a.nodes, L = a.local;
-  if (N == 2 && L == 8) return launch_hier_shape<D, 2, 8>(a, grid, large, stream);
-  if (N == 4 && L == 4) return launch_hier_shape<D, 4, 4>(a, grid, large, stream);
-  if (N == 4 && L == 8) return launch_hier_shape<D, 4, 8>(a, grid, large, stream);
-  if (N == 2 && L == 4) return launch_hier_shape<D, 2, 4>(a, grid, large, stream);
-  if (N == 8 && L == 8) return launch_hier_shape<D, 8, 8>(a, grid, large, stream);
-  if (N == 4 && L == 2) return launch_hier_shape<D, 4, 2>(a, grid, large, stream);
-  return launch(hier_kernel<D, 0, 0, false>, grid, a, stream);
+  if (N == 2 && L == 8) return launch_hier_shape<D, 2, 8>(a, max_segment, stream);
+  if (N == 4 && L == 4) return launch_hier_shape<D, 4, 4>(a, max_segment, stream);
+  if (N == 4 && L == 8) return launch_hier_shape<D, 4, 8>(a, max_segment, stream);
+  if (N == 2 && L == 4) return launch_hier_shape<D, 2, 4>(a, max_segment, stream);
+  if (N == 8 && L == 8) return launch_hier_shape<D, 8, 8>(a, max_segment, stream);
+  if (N == 4 && L == 2) return launch_hier_shape<D, 4, 2>(a, max_segment, stream);
+  return launch_hier_shape<D, 0, 0>(a, max_segment, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hierarchical(const HierArgs& a, vcoll_dtype dtype, int64_t max_segment, hipStream_t stream) {
-  const int64_t per_tile = static_cast<int64_t>(kBlock) * (dtype == VCOLL_F32 ? 4 : 8);
-  const int64_t tiles = (max_segment + per_tile - 1) / per_tile;
-  if (tiles == 0) return hipSuccess;
-  const int p = a.nodes * a.local;
-  const dim3 grid(static_cast<unsigned>(tiles), p);
-  const bool large = tiles * p >= VCOLL_PACE_MIN_GROUPS;
-  if (dtype == VCOLL_F32) return launch_hier_dtype<VCOLL_F32>(a, grid, large, stream);
-  return launch_hier_dtype<VCOLL_BF16>(a, grid, large, stream);
+  if (dtype == VCOLL_F32) return launch_hier_dtype<VCOLL_F32>(a, max_segment, stream);
+  return launch_hier_dtype<VCOLL_BF16>(a, max_segment, stream);
 }
 
 }  // namespace vcoll
