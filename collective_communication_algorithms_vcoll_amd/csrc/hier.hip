@@ -107,17 +107,17 @@ __device__ __forceinline__ void hier_vector(const HierArgs& a, int l, int j, int
   }
 }
 
-// Threads per workgroup: two waves for the 16-rank shapes, four otherwise.
-// On MI355X, 128 against 256 threads took the 4 x 4 hierarchy of 16 x 192
-// MiB bf16 from 1206-1213 to 1163 us and of 16 x 16 MiB float32 from 126-127
-// to 121-122 us, and left 2 x 8 within 1 % (64 threads: 4 x 4 1161-1166 us,
-// 16 MiB 124 us). Build-time override: -DVCOLL_HIER_BS16=<threads>.
-#ifndef VCOLL_HIER_BS16
-#define VCOLL_HIER_BS16 128
-#endif
+// Threads per workgroup by shape (p = NN x LL compiled in; a run-time shape
+// takes four waves). Measured on MI355X against four waves: p = 16, two
+// waves took the 4 x 4 hierarchy of 16 x 192 MiB bf16 from 1206-1213 to 1163
+// us and of 16 x 16 MiB float32 from 126-127 to 121-122 us (2 x 8 within 1
+// %); p = 32 (4 x 8 x 16 MiB float32) 234-236 -> 222 us with two waves; p =
+// 64 (8 x 8 x 8 MiB) 243-245 -> 220-221 us with one (two waves: 246); p = 8
+// keeps four, 0.5-1.5 % ahead on the 25 MiB bucket (two waves won 3.5 % at
+// 80 MiB).
 template <int NN, int LL>
 constexpr int hier_block() {
-  return NN * LL == 16 ? VCOLL_HIER_BS16 : kBlock;
+  return NN * LL == 16 || NN * LL == 32 ? 128 : (NN * LL == 64 ? 64 : kBlock);
 }
 
 template <int D, int NN, int LL, bool LARGE>
