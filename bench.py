@@ -1035,11 +1035,11 @@ TRAFFIC_GROUPS = {
         ("copy, 200 MiB read + 200 MiB written (counter scale)", "copy_kernel<2, 64", 419_430_400),
         ("ring all-reduce, p=72 x 16 MiB f32 (two-phase, ragged chunks)", "burst_ring_kernel<0, 25, 0>",
          2 * 72 * 16 * 2 ** 20),
-        ("tree all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
+        ("tree all-reduce, p=72 x 16 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 64>",
          2 * 72 * 16 * 2 ** 20),
-        ("ring all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 0, 0, 1, false, false, 256>",
+        ("ring all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 0, 0, 1, false, false, 64>",
          2 * 72 * 256 * 2 ** 20),
-        ("tree all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 256>",
+        ("tree all-reduce, p=72 x 256 MiB f32 (run-time order)", "reduce_kernel<0, 3, 0, 1, false, false, 64>",
          2 * 72 * 256 * 2 ** 20),
         ("ring reduce-scatter, p=72 x 64 MiB f32 (unaligned chunk starts)",
          "reduce_scatter_shifted_kernel<0, true>", 73 * 64 * 2 ** 20),

@@ -848,11 +848,17 @@ inline bool use_small(int64_t max_chunk, int chunks) {
 #define VCOLL_V_P8 2
 #endif
 // Threads per workgroup of the reduce kernel: one wave for p = 16 (measured
-// +1-3% on the 16 x 192 MiB bf16 all-reduce, +7% at 4 MiB per rank), four
-// waves otherwise.
+// +1-3% on the 16 x 192 MiB bf16 all-reduce, +7% at 4 MiB per rank) and for
+// a run-time p (p = 33, 72 and 100 at 1-64 MiB per rank, float32, every
+// algorithm: 3.5 % faster on geometric mean than four waves, 10 % at 2 MiB,
+// 3-4 % at 4 and 64 MiB, even at 1 MiB; two waves 2 %), four waves
+// otherwise. Build-time override for a run-time p: -DVCOLL_RT_BLOCK=<n>.
+#ifndef VCOLL_RT_BLOCK
+#define VCOLL_RT_BLOCK 64
+#endif
 template <int P>
 constexpr int block_size() {
-  return P == 16 ? 64 : kBlock;
+  return P == 16 ? 64 : (P == 0 ? VCOLL_RT_BLOCK : kBlock);
 }
 
 template <int P>
