@@ -890,11 +890,16 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
     if constexpr (RS && ALGO == VCOLL_RING) {
       bool aligned = true;
       for (int c = 0; c < chunks && aligned; ++c) aligned = (c * a.q + (c < a.r ? c : a.r)) % VE == 0;
-      if (a.vec && !aligned) {
+      if (a.vec) {
         // waves cover d + nvec input vectors per chunk: d < 8 (the line start
         // before the chunk, line-aligned shape only), nvec < the chunk's vectors
         const int64_t in_vecs = (max_chunk + VE - 1) / VE + 8;
         const int64_t waves = (in_vecs + 63) / 64 * chunks;
+        // the line-aligned shape also beats the reduce kernel on aligned
+        // chunks (float32 on MI355X: p = 33 x 64 MiB per rank 397 -> 370 us,
+        // p = 72 877 -> 812, p = 64 within 0.5 %); the 63-output shape does
+        // not (p = 64 x 16 MiB 180 -> 198 us), so aligned chunks take only
+        // the former
         if constexpr (D == VCOLL_F32) {
           if (waves >= kShiftLinesMinWaves) {
             const int64_t per_group = static_cast<int64_t>(kBlock / 64) * 64;
@@ -902,9 +907,11 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
             return launch(reduce_scatter_shifted_kernel<D, true>, sg, args, stream);
           }
         }
-        const int64_t per_group = static_cast<int64_t>(kBlock / 64) * 63;
-        const dim3 sg(static_cast<unsigned>((in_vecs + per_group - 1) / per_group), chunks);
-        return launch(reduce_scatter_shifted_kernel<D, false>, sg, args, stream);
+        if (!aligned) {
+          const int64_t per_group = static_cast<int64_t>(kBlock / 64) * 63;
+          const dim3 sg(static_cast<unsigned>((in_vecs + per_group - 1) / per_group), chunks);
+          return launch(reduce_scatter_shifted_kernel<D, false>, sg, args, stream);
+        }
       }
     }
     return launch(reduce_kernel<D, ALGO, P, V, RS, false, BS>, grid, BS, args, stream);

@@ -329,6 +329,28 @@ def test_reduce_scatter_unaligned_chunk_starts_line_aligned_waves(vc, pad):
         assert_bits_equal(download(got[c], "f32"), bits(want[c], "f32"), f"RS ring p={p} pad {pad} chunk {c}")
 
 
+@pytest.mark.parametrize("pad", [20, 4], ids=["common-line-phase", "phases-differ"])
+def test_reduce_scatter_aligned_chunk_starts_line_aligned_waves(vc, pad):
+    """Chunks that all start on 16-byte bounds, at a size with as many waves
+    (f32, run-time p): they take the same line-aligned wave shape with no
+    shift (every output vector is a lane's own sum), the chunk's last vector
+    and ragged end element by element."""
+    import torch
+    p, n = 24, 24 * 4 * 174_763                      # chunks of 699,052 elements, all 16-byte aligned
+    x = rand_inputs(p, n, "f32", seed=631 + pad)
+    want, _ = oracle.reduce_scatter(x, "ring", "f32")
+    offs = oracle.chunk_bounds(n, p)
+    assert all(o % 4 == 0 for o in offs), "an unaligned chunk start"
+    big = torch.zeros((p, n + pad), dtype=torch.float32, device="cuda")
+    big[:, :n].copy_(torch.from_numpy(np.stack(x)))
+    send = [big[r, :n] for r in range(p)]
+    say(f"vcoll_reduce_scatter ring p={p} n={n} row pad {pad} (aligned, line-aligned waves)")
+    got = vc.vcoll_reduce_scatter("ring", send)
+    sync()
+    for c in range(p):
+        assert_bits_equal(download(got[c], "f32"), bits(want[c], "f32"), f"RS ring p={p} pad {pad} chunk {c}")
+
+
 def test_non_power_of_two_halving_and_doubling_are_refused(vc):
     import torch
     t = torch.zeros(3, 96, device="cuda")
