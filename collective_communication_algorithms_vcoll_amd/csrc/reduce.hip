@@ -509,9 +509,12 @@ __global__ __launch_bounds__(BS) void reduce_kernel(const ReduceArgs a) {
     // the vector tiles of an all-reduce start on a 256-byte boundary of every
     // buffer when the buffers allow it (whole cache lines per wave: chunk
     // starts that are only 16-byte aligned cost p = 72 5 % extra HBM
-    // traffic); the elements before it and the ragged end take the element path
-    const int64_t align = RS ? 16 : a.align;
-    const int64_t mis = (a.phase + off * ES) % align;
+    // traffic), those of a reduce-scatter on a 128-byte line of every input
+    // (p = 72 x 16 MiB per rank, f32, 16-byte aligned chunks: 222.7 -> 200.4
+    // us on MI355X); the elements before it and the ragged end take the
+    // element path
+    const int64_t align = RS ? a.src_align : a.align;
+    const int64_t mis = ((RS ? a.src_phase : a.phase) + off * ES) % align;
     const int64_t head_e = mis ? (align - mis) / ES : 0;
     const int64_t head = head_e < cnt ? head_e : cnt;
     const int64_t nvec = (cnt - head) / VE;
