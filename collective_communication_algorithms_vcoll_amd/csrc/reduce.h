@@ -46,7 +46,7 @@ struct ReduceArgs {
   int32_t groups;             // tree programs with p not compiled in: the group count
   int32_t pace;               // space out the p-way store fan-out (large grids)
   int32_t align;              // all-reduce tiles start on this byte boundary (256 when every buffer
-                              // has the same address mod 256, else 16)
+                              // has the same address mod 256, else 128 when mod 128, else 16)
   int32_t phase;              // that common address mod `align` (0 for align 16)
   int32_t src_align;          // 128 when every input buffer has address phase `src_phase` mod 128
   int32_t src_phase;          // (the unaligned reduce-scatter then loads whole lines), else 16 and 0

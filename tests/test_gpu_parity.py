@@ -329,6 +329,21 @@ def test_reduce_scatter_unaligned_chunk_starts_line_aligned_waves(vc, pad):
         assert_bits_equal(download(got[c], "f32"), bits(want[c], "f32"), f"RS ring p={p} pad {pad} chunk {c}")
 
 
+def test_allreduce_rows_sharing_only_a_line_phase(vc):
+    """Rank rows 128 bytes apart mod 256 (a [8, n] tensor with n = 32 mod
+    64): the tiles start on a 128-byte line of every row instead; every
+    algorithm against the oracle."""
+    p, n = 8, 4_194_304 + 32
+    x = rand_inputs(p, n, "f32", 651)
+    t = upload(x, "f32")
+    assert t.stride(0) * 4 % 256 == 128
+    for algo in ALGOS:
+        say(f"all-reduce p={p} n={n} {algo}, rows sharing a line phase only")
+        want, _ = oracle.allreduce(x, algo, "f32")
+        got = download(vc.vcoll_allreduce(algo, t), "f32")
+        assert_bits_equal(got, np.stack([bits(w, "f32") for w in want]), f"{algo} p={p}")
+
+
 @pytest.mark.parametrize("pad", [20, 4], ids=["common-line-phase", "phases-differ"])
 def test_reduce_scatter_aligned_chunk_starts_line_aligned_waves(vc, pad):
     """Chunks that all start on 16-byte bounds, at a size with as many waves
