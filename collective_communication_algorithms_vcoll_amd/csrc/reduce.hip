@@ -691,8 +691,10 @@ constexpr int64_t kShiftLinesMinWaves = 32768;
 // lookups and a shift-register stack for the trees, on MI355X: p = 24 at 1
 // KiB per rank ring 4.4 -> 3.7 us, trees 6.4 -> 3.9-4.0; p = 72 at 10 KiB
 // ring 8.8 -> 5.7, trees 14.3 -> 5.4-6.5, at 256 KiB ring 22.7 -> 14.5, trees
-// 31.9 -> 14.6-16.1 (p = 72 at 1 KiB: ring 5.4 -> 5.8, the cost of 32 slots
-// per wave).
+// 31.9 -> 14.6-16.1. Then 24 slots per wave for p <= 96 and an LDS tile
+// sized to the slots moved: p = 72 at 1 KiB ring 5.8 -> 5.1 us, trees 5.4-6.6
+// -> 5.0-5.7, at 256 KiB ring 14.5 -> 11.5, trees 14.6-16.2 -> 11.9-13.2; p =
+// 96 12-23 % faster.
 
 constexpr int kSmallTile = 64;                                   // elements of a chunk per workgroup
 
@@ -715,7 +717,8 @@ __device__ __forceinline__ const void* lane_ptr(uint64_t held, int i) {
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// NJ: slots per wave, 16 for p <= 64 (half the instructions) and 32 beyond.
+// NJ: slots per wave, 16 for p <= 64 (half the instructions), 24 for p <= 96
+// and 32 beyond.
 template <int D, int ALGO, bool RS, int NJ>
 __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a) {
   using S = Storage<D>;
@@ -723,9 +726,9 @@ __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a
   constexpr int ES = static_cast<int>(sizeof(E));
   constexpr int kWaves = kBlock / 64;
   constexpr int kPerWave = NJ;                                   // slots a wave moves, at most
-  static_assert((NJ == 16 || NJ == 32) && NJ * kWaves <= kMaxRanks, "16 or 32 slots per wave");
+  static_assert((NJ == 16 || NJ == 24 || NJ == 32) && NJ * kWaves <= kMaxRanks, "16, 24 or 32 slots per wave");
   constexpr bool kPairs = ALGO != VCOLL_RING && ALGO != VCOLL_BINARY_TREE;
-  __shared__ float val[kMaxRanks * kSmallTile];                  // [slot][element]
+  __shared__ float val[NJ * kWaves * kSmallTile];                // [slot][element], every slot written
   __shared__ float res[kSmallTile];
   const int c = blockIdx.y;
   const int p = a.p;
@@ -799,7 +802,7 @@ __global__ __launch_bounds__(kBlock) void reduce_small_kernel(const ReduceArgs a
       for (int q0 = 0; q0 < slots; q0 += B) {
         float xs[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) xs[b] = val[(q0 + b) * kSmallTile + tid];   // q0 + b < kMaxRanks
+        for (int b = 0; b < B; ++b) xs[b] = val[(q0 + b) * kSmallTile + tid];   // q0 + b < NJ * kWaves
         static_for<0, B>([&](auto bb) {
           constexpr int b = decltype(bb)::value;
           if (q0 + b < slots) {
@@ -888,6 +891,7 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
     if (use_small(max_chunk, chunks)) {
       const dim3 small(static_cast<unsigned>((max_chunk + kSmallTile - 1) / kSmallTile), chunks);
       if (a.p <= 64) return launch(reduce_small_kernel<D, ALGO, RS, 16>, small, args, stream);
+      if (a.p <= 96) return launch(reduce_small_kernel<D, ALGO, RS, 24>, small, args, stream);
       return launch(reduce_small_kernel<D, ALGO, RS, 32>, small, args, stream);
     }
     if constexpr (RS && ALGO == VCOLL_RING) {
