@@ -65,6 +65,14 @@ __device__ __forceinline__ void push_leaf(float (&st)[SD][N], const float (&v)[N
   if constexpr (K == P - 1) merge_top<D + 1 - M, Prog<ALGO, P>::value.final_merges>(st);
 }
 
+// The program leaf that stands for rank r (p compiled in).
+template <int ALGO, int P>
+constexpr int leaf_of_rank(int r) {
+  for (int j = 0; j < P; ++j)
+    if (Prog<ALGO, P>::value.rank[j] == r) return j;
+  return r;
+}
+
 // Ranks whose loads a wave keeps in flight ahead of the one it is adding.
 // Large grids (which also pace their stores) issue all p ranks up front;
 // small, latency-bound grids run a pipeline of a few ranks, which measured
@@ -389,12 +397,18 @@ __device__ __forceinline__ void reduce_vectors_fixed(const ReduceArgs& a, int c,
   static_for<0, P + LAG>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     if constexpr (k < P) {
+      // the leaf whose loads go out at step k: the program's k-th, or, when
+      // every load goes out before the first add, the one of the k-th rank
+      // (Rabenseifner's program takes the ranks bit-reversed; issued in that
+      // order its p = 16 x 4 MiB all-reduce took 27-28 us against 23.5 for
+      // the other algorithms on MI355X, in rank order 23.6-24.0)
+      constexpr int kl = LAG == P ? leaf_of_rank<ALGO, P>(k) : k;
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         if constexpr (FULL) {
-          raw[k][j] = ld16(L[k], boff[j]);
+          raw[kl][j] = ld16(L[kl], boff[j]);
         } else {
-          raw[k][j] = valid[j] ? ld16(L[k], boff[j]) : u32x4{0, 0, 0, 0};
+          raw[kl][j] = valid[j] ? ld16(L[kl], boff[j]) : u32x4{0, 0, 0, 0};
         }
       }
     }
