@@ -887,6 +887,27 @@ constexpr int vectors_per_thread() {
   return P == 0 ? 1 : (P <= 4 ? 4 : (P <= 8 ? VCOLL_V_P8 : 1));
 }
 
+// p = 16 grids of at most this many one-vector workgroups take two vectors
+// per thread instead: on MI355X (float32, rank rows padded) p = 16 x 16 MiB
+// per rank 105 -> 90.7 us for the trees, 4-32 MiB 1-3 % faster, but 64 MiB
+// 4 % slower (349 -> 364 us).
+constexpr int64_t kP16TwoVectorMaxGroups = 32768;
+
+// The compiled-p kernel with V vectors per thread (the LARGE variant carries
+// the pacing and its load pipeline).
+template <int D, int ALGO, bool RS, int P, int V>
+hipError_t launch_fixed(const ReduceArgs& a, int64_t max_chunk, int chunks, hipStream_t stream) {
+  constexpr int BS = block_size<P>();
+  constexpr int64_t per_tile = static_cast<int64_t>(V) * BS * Storage<D>::kVE;
+  const int64_t tiles = (max_chunk + per_tile - 1) / per_tile;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles), chunks);
+  ReduceArgs args = a;
+  args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
+  if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true, BS>, grid, BS, args, stream);
+  return launch(reduce_kernel<D, ALGO, P, V, RS, false, BS>, grid, BS, args, stream);
+}
+
 template <int D, int ALGO, bool RS, int P>
 hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, hipStream_t stream) {
   constexpr int V = vectors_per_thread<P>();
@@ -899,9 +920,10 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
   ReduceArgs args = a;
   args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
   if constexpr (P > 0) {
-    // the compile-time variant carries the pacing (and its load pipeline)
-    if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true, BS>, grid, BS, args, stream);
-    return launch(reduce_kernel<D, ALGO, P, V, RS, false, BS>, grid, BS, args, stream);
+    if constexpr (P == 16) {
+      if (tiles * chunks <= kP16TwoVectorMaxGroups) return launch_fixed<D, ALGO, RS, P, 2>(a, max_chunk, chunks, stream);
+    }
+    return launch_fixed<D, ALGO, RS, P, V>(a, max_chunk, chunks, stream);
   } else {
     if (use_small(max_chunk, chunks)) {
       const dim3 small(static_cast<unsigned>((max_chunk + kSmallTile - 1) / kSmallTile), chunks);
