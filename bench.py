@@ -1018,7 +1018,7 @@ TRAFFIC_GROUPS = {
     "hot": [
         ("two-phase ring all-reduce, p=8 x 25 MiB f32 (headline)", "burst_ring_kernel<0, 25, 0>", 419_430_400),
         ("hierarchical 2x4 all-reduce, p=8 x 25 MiB f32", "hier_kernel<0, 2, 4, true>", 419_430_400),
-        ("tree reduce to one root, p=8 x 25 MiB f32", "reduce_kernel<0, 3, 8, 2, true, false, 256>", 235_929_600),
+        ("tree reduce to one root, p=8 x 25 MiB f32", "reduce_kernel<0, 3, 8, 4, true, false, 256>", 235_929_600),
         ("broadcast of 25 MiB f32 to 8 buffers", "broadcast_kernel<4, 4, 64, true>", 235_929_600),
         ("copy, 200 MiB read + 200 MiB written (counter scale)", "copy_kernel<2, 64", 419_430_400),
         ("fused ring all-reduce, p=16 x 192 MiB bf16", "reduce_kernel<1, 0, 16, 1, false, true, 64>", 6_442_450_944),
@@ -1045,7 +1045,7 @@ TRAFFIC_GROUPS = {
          "reduce_scatter_shifted_kernel<0, true>", 73 * 64 * 2 ** 20),
         ("ring all-reduce, p=16 x 16 MiB f32", "burst_ring_kernel<0, 25, 0>", 2 * 16 * 16 * 2 ** 20),
         ("ring all-reduce, p=16 x 64 MiB f32", "reduce_kernel<0, 0, 16, 1, false, true, 64>", 2 * 16 * 64 * 2 ** 20),
-        ("ring all-reduce, p=8 x 1 GiB f32", "reduce_kernel<0, 0, 8, 2, false, true, 256>", 2 * 8 * 2 ** 30),
+        ("ring all-reduce, p=8 x 1 GiB f32", "reduce_kernel<0, 0, 8, 4, false, true, 256>", 2 * 8 * 2 ** 30),
     ],
 }
 

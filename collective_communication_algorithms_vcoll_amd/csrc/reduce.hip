@@ -864,9 +864,13 @@ inline bool use_small(int64_t max_chunk, int chunks) {
 }
 
 // 16-byte vectors per thread of the reduce kernel (all are loaded before the
-// first add). Build-time override: -DVCOLL_V_P8=<n> for p = 8.
+// first add). p = 8: four against two on MI355X (float32, rank rows padded,
+// ring and recursive doubling, with the pacing bound below counted in
+// two-vector workgroups) 10 % faster at 4 MiB per rank, 4-6 % at 16-128 MiB,
+// 1 % at 256 MiB, and 1 % slower for the trees on the 25 MiB bucket.
+// Build-time override: -DVCOLL_V_P8=<n> for p = 8.
 #ifndef VCOLL_V_P8
-#define VCOLL_V_P8 2
+#define VCOLL_V_P8 4
 #endif
 // Threads per workgroup of the reduce kernel: one wave for p = 16 (measured
 // +1-3% on the 16 x 192 MiB bf16 all-reduce, +7% at 4 MiB per rank) and for
@@ -903,7 +907,10 @@ hipError_t launch_fixed(const ReduceArgs& a, int64_t max_chunk, int chunks, hipS
   if (tiles == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(tiles), chunks);
   ReduceArgs args = a;
-  args.pace = !RS && tiles * a.p >= VCOLL_PACE_MIN_GROUPS;
+  // the pacing bound was measured in workgroups of the p = 8 kernel's
+  // two-vector shape; its four-vector workgroups count twice (counted once,
+  // 16-28 MiB per rank fell back to the unpaced variant and lost 2-8 %)
+  args.pace = !RS && tiles * a.p * (P == 8 ? (V + 1) / 2 : 1) >= VCOLL_PACE_MIN_GROUPS;
   if (args.pace) return launch(reduce_kernel<D, ALGO, P, V, RS, true, BS>, grid, BS, args, stream);
   return launch(reduce_kernel<D, ALGO, P, V, RS, false, BS>, grid, BS, args, stream);
 }
