@@ -891,6 +891,13 @@ constexpr int vectors_per_thread() {
   return P == 0 ? 1 : (P <= 4 ? 4 : (P <= 8 ? VCOLL_V_P8 : 1));
 }
 
+// p = 8 grids of fewer than this many four-vector workgroups take two
+// vectors per thread: latency-bound, they need the workgroups. On MI355X
+// (float32) two vectors ran 0.5-2 MiB per rank (up to 128 four-vector
+// workgroups) in 3.8-5.6 us against 4.6-6.7 with four, but 3 MiB (192) in
+// 10.8 us against 8.2.
+constexpr int64_t kP8FourVectorMinGroups = 192;
+
 // p = 16 grids of at most this many one-vector workgroups take two vectors
 // per thread instead: on MI355X (float32, rank rows padded) p = 16 x 16 MiB
 // per rank 105 -> 90.7 us for the trees, 4-32 MiB 1-3 % faster, but 64 MiB
@@ -929,6 +936,9 @@ hipError_t launch_reduce_p(const ReduceArgs& a, int64_t max_chunk, int chunks, h
   if constexpr (P > 0) {
     if constexpr (P == 16) {
       if (tiles * chunks <= kP16TwoVectorMaxGroups) return launch_fixed<D, ALGO, RS, P, 2>(a, max_chunk, chunks, stream);
+    }
+    if constexpr (P == 8 && V == 4) {
+      if (tiles * chunks < kP8FourVectorMinGroups) return launch_fixed<D, ALGO, RS, P, 2>(a, max_chunk, chunks, stream);
     }
     return launch_fixed<D, ALGO, RS, P, V>(a, max_chunk, chunks, stream);
   } else {
